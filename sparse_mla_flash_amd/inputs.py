@@ -1,0 +1,310 @@
+"""Seeded synthetic inputs for SparseFlashAttentionGrad workloads.
+
+This module only draws random numbers and lays them out; it holds none of the
+operator's arithmetic (no logits, softmax or gradients).  Both the test suite
+(for the CPU oracle and the HIP library) and the benchmark take their inputs
+from here, so the two sides always see bit-identical tensors.
+
+Tensor layouts follow the operator's parameter list (SparseFlashAttentionGrad
+README, "parameters" section): BSND query-side tensors are [B, S1, N1, D], key
+side [B, S2, 1, D]; TND packs tokens as [T, N, D].  Floating-point tensors are
+returned as bfloat16 bit patterns (uint16) drawn as fp32 N(0, 1) and rounded to
+nearest-even; sparseIndices are int32 with -1 marking skipped slots.
+
+Random streams: numpy ``SeedSequence(seed).spawn(6)`` in the fixed order
+query, key, queryRope, keyRope, dOut, indices.  ``value`` is a separate copy of
+``key`` (the operator requires value == key but the library must not assume the
+two buffers alias).
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import List, Optional
+
+import numpy as np
+
+D_NOPE = 512
+D_ROPE = 64
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (nearest, ties to even); returns uint16 bits."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    bias = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def bf16_bits_to_f64(b: np.ndarray) -> np.ndarray:
+    return bf16_bits_to_f32(b).astype(np.float64)
+
+
+@dataclasses.dataclass
+class Problem:
+    """One synthetic SparseFlashAttentionGrad workload (shapes + seeded tensors)."""
+
+    layout: str                      # "BSND" or "TND"
+    B: int                           # batches (BSND) or sequences (TND)
+    S1: int                          # BSND: padded query length; TND: total query tokens
+    S2: int                          # BSND: padded key length; TND: total key tokens
+    N1: int
+    topk: int
+    sparse_mode: int                 # 0 or 3
+    seq_q: Optional[List[int]]       # per-batch valid query lengths (required for TND)
+    seq_kv: Optional[List[int]]
+    scale: float                     # fp32 scaleValue
+    D: int = D_NOPE
+    Dr: int = D_ROPE
+    deterministic: bool = False
+    name: str = ""
+    # tensors (filled by generate())
+    q: Optional[np.ndarray] = None       # uint16 bf16 bits
+    k: Optional[np.ndarray] = None
+    v: Optional[np.ndarray] = None
+    qr: Optional[np.ndarray] = None
+    kr: Optional[np.ndarray] = None
+    dout: Optional[np.ndarray] = None
+    idx: Optional[np.ndarray] = None     # int32
+
+    # ---- geometry ---------------------------------------------------------
+    @property
+    def rows(self) -> int:
+        """Total query rows (padded rows included for BSND)."""
+        return self.B * self.S1 if self.layout == "BSND" else self.S1
+
+    @property
+    def keys(self) -> int:
+        return self.B * self.S2 if self.layout == "BSND" else self.S2
+
+    def lq(self, b: int) -> int:
+        if self.seq_q is None:
+            return self.S1
+        return int(self.seq_q[b])
+
+    def lkv(self, b: int) -> int:
+        if self.seq_kv is None:
+            return self.S2
+        return int(self.seq_kv[b])
+
+    def q_offset(self, b: int) -> int:
+        """First global query row of batch b."""
+        if self.layout == "BSND":
+            return b * self.S1
+        return int(sum(self.seq_q[:b]))
+
+    def k_offset(self, b: int) -> int:
+        if self.layout == "BSND":
+            return b * self.S2
+        return int(sum(self.seq_kv[:b]))
+
+    def q_shape(self, width: int):
+        if self.layout == "BSND":
+            return (self.B, self.S1, self.N1, width)
+        return (self.S1, self.N1, width)
+
+    def k_shape(self, width: int):
+        if self.layout == "BSND":
+            return (self.B, self.S2, 1, width)
+        return (self.S2, 1, width)
+
+    def idx_shape(self):
+        if self.layout == "BSND":
+            return (self.B, self.S1, 1, self.topk)
+        return (self.S1, 1, self.topk)
+
+    def stat_shape(self):
+        if self.layout == "BSND":
+            return (self.B, self.N1, self.S1)
+        return (self.N1, self.S1)
+
+
+# ---------------------------------------------------------------------------
+# index patterns
+# ---------------------------------------------------------------------------
+
+def _distinct(rng: np.random.Generator, lo: int, hi: int, k: int) -> np.ndarray:
+    """k distinct integers drawn uniformly from [lo, hi], in random order."""
+    n = hi - lo + 1
+    return (rng.choice(n, size=k, replace=False) + lo).astype(np.int64)
+
+
+def _causal_hi(p: Problem, b: int, i: int) -> int:
+    """Largest key position a query at row i of batch b may select (-1: none)."""
+    lkv = p.lkv(b)
+    if p.sparse_mode == 3:
+        return min(i + lkv - p.lq(b), lkv - 1)
+    return lkv - 1
+
+
+def _row_uniform(p: Problem, rng, b: int, i: int) -> np.ndarray:
+    """Distinct uniform over the valid range; short ranges take all keys, -1 padded."""
+    out = np.full(p.topk, -1, dtype=np.int64)
+    hi = _causal_hi(p, b, i)
+    if hi < 0:
+        return out
+    n = hi + 1
+    if n <= p.topk:
+        out[:n] = rng.permutation(n)
+    else:
+        out[:] = _distinct(rng, 0, hi, p.topk)
+    return out
+
+
+def _row_window(p: Problem, rng, b: int, i: int, window: int) -> np.ndarray:
+    """Half from the local window [pos-window+1, pos], half uniform over the rest."""
+    out = np.full(p.topk, -1, dtype=np.int64)
+    hi = _causal_hi(p, b, i)
+    if hi < 0:
+        return out
+    n = hi + 1
+    if n <= p.topk:
+        out[:n] = rng.permutation(n)
+        return out
+    half = p.topk // 2
+    wlo = max(0, hi - window + 1)
+    wn = hi - wlo + 1
+    loc = _distinct(rng, wlo, hi, min(half, wn))
+    need = p.topk - len(loc)
+    chosen = set(loc.tolist())
+    far: list = []
+    # rejection sampling over [0, hi] minus what the window already holds
+    while len(far) < need:
+        cand = rng.integers(0, n, size=2 * (need - len(far)) + 16)
+        for c in cand.tolist():
+            if c not in chosen:
+                chosen.add(c)
+                far.append(c)
+                if len(far) == need:
+                    break
+    sel = np.concatenate([loc, np.asarray(far, dtype=np.int64)])
+    out[:] = sel[rng.permutation(len(sel))]
+    return out
+
+
+def _rows_hot_cold(p: Problem, rng, b: int) -> np.ndarray:
+    """Mode-0 rows where every query selects all hot keys plus distinct cold keys.
+
+    Hot keys are 10% of the key range; with topk above that count each query
+    takes all of them (the most the skew allows) and fills the rest uniformly
+    from the cold keys.  Slot order is shuffled.
+    """
+    lkv = p.lkv(b)
+    nhot = max(1, int(round(0.1 * lkv)))
+    perm = rng.permutation(lkv)
+    hot, cold = perm[:nhot], perm[nhot:]
+    lq = p.lq(b)
+    rows = np.full((p.S1 if p.layout == "BSND" else lq, p.topk), -1, dtype=np.int64)
+    take_hot = min(nhot, p.topk)
+    for i in range(lq):
+        h = hot if take_hot == nhot else hot[rng.choice(nhot, take_hot, replace=False)]
+        ncold = min(p.topk - take_hot, len(cold))
+        c = cold[rng.choice(len(cold), ncold, replace=False)] if ncold > 0 else np.empty(0, np.int64)
+        sel = np.concatenate([h, c])
+        rows[i, : len(sel)] = sel[rng.permutation(len(sel))]
+    return rows
+
+
+def _indices(p: Problem, rng: np.random.Generator, kind: str, window: int) -> np.ndarray:
+    idx = np.full((p.rows, p.topk), -1, dtype=np.int64)
+    for b in range(p.B):
+        base = p.q_offset(b)
+        if kind == "hot_cold":
+            r = _rows_hot_cold(p, rng, b)
+            idx[base: base + r.shape[0]] = r
+            continue
+        for i in range(p.lq(b)):
+            if kind == "uniform":
+                idx[base + i] = _row_uniform(p, rng, b, i)
+            elif kind == "window":
+                idx[base + i] = _row_window(p, rng, b, i, window)
+            else:
+                raise ValueError(f"unknown index kind {kind!r}")
+    return idx.astype(np.int32)
+
+
+# ---------------------------------------------------------------------------
+# generation
+# ---------------------------------------------------------------------------
+
+def _normal_bf16(rng: np.random.Generator, shape, chunk: int = 1 << 24) -> np.ndarray:
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.uint16)
+    for s in range(0, n, chunk):
+        e = min(n, s + chunk)
+        out[s:e] = f32_to_bf16_bits(rng.standard_normal(e - s, dtype=np.float32))
+    return out.reshape(shape)
+
+
+def generate(p: Problem, seed: int, index_kind: str = "uniform", window: int = 4096,
+             fill: str = "normal") -> Problem:
+    """Fill p's tensors from ``seed``.
+
+    fill="normal": N(0,1) bf16 values (the benchmark workloads).
+    fill="ones": every float tensor is 1.0 (the all-ones sample input of the
+    dense FlashAttention-grad page), indices still random.
+    """
+    ss = np.random.SeedSequence(seed).spawn(6)
+    rq, rk, rqr, rkr, rdo, ridx = (np.random.default_rng(s) for s in ss)
+    if fill == "normal":
+        p.q = _normal_bf16(rq, p.q_shape(p.D))
+        p.k = _normal_bf16(rk, p.k_shape(p.D))
+        p.qr = _normal_bf16(rqr, p.q_shape(p.Dr))
+        p.kr = _normal_bf16(rkr, p.k_shape(p.Dr))
+        p.dout = _normal_bf16(rdo, p.q_shape(p.D))
+    elif fill == "ones":
+        one = np.uint16(0x3F80)
+        p.q = np.full(p.q_shape(p.D), one, np.uint16)
+        p.k = np.full(p.k_shape(p.D), one, np.uint16)
+        p.qr = np.full(p.q_shape(p.Dr), one, np.uint16)
+        p.kr = np.full(p.k_shape(p.Dr), one, np.uint16)
+        p.dout = np.full(p.q_shape(p.D), one, np.uint16)
+    else:
+        raise ValueError(fill)
+    p.v = p.k.copy()
+    p.idx = _indices(p, ridx, index_kind, window).reshape(p.idx_shape())
+    return p
+
+
+def fp32(x: float) -> float:
+    return float(np.float32(x))
+
+
+def problem(layout="BSND", B=1, S1=128, S2=128, N1=8, topk=64, sparse_mode=3, seq_q=None,
+            seq_kv=None, scale=None, D=D_NOPE, Dr=D_ROPE, deterministic=False, name="") -> Problem:
+    if scale is None:
+        scale = 1.0 / math.sqrt(D + Dr)
+    if layout == "TND":
+        assert seq_q is not None and seq_kv is not None
+        S1, S2 = int(sum(seq_q)), int(sum(seq_kv))
+    return Problem(layout=layout, B=B, S1=S1, S2=S2, N1=N1, topk=topk, sparse_mode=sparse_mode,
+                   seq_q=None if seq_q is None else [int(x) for x in seq_q],
+                   seq_kv=None if seq_kv is None else [int(x) for x in seq_kv],
+                   scale=fp32(scale), D=D, Dr=Dr, deterministic=deterministic, name=name)
+
+
+# The five benchmark workloads (shapes and index structure).  Seed = workload number.
+WORKLOADS = {
+    1: dict(spec=dict(layout="BSND", B=1, S1=128, S2=4096, N1=8, topk=1024, sparse_mode=3,
+                      name="bsnd_s128q_4096k_n8_topk1024_causal"), kind="uniform"),
+    2: dict(spec=dict(layout="BSND", B=1, S1=8192, S2=8192, N1=64, topk=2048, sparse_mode=3,
+                      name="bsnd_s8192_n64_topk2048_causal"), kind="uniform"),
+    3: dict(spec=dict(layout="TND", B=4, seq_q=[2048, 4096, 8192, 16384],
+                      seq_kv=[2048, 4096, 8192, 16384], N1=128, topk=2048, sparse_mode=3,
+                      name="tnd_varlen_2k-16k_n128_topk2048_causal"), kind="uniform"),
+    4: dict(spec=dict(layout="BSND", B=1, S1=16384, S2=131072, N1=128, topk=2048, sparse_mode=3,
+                      name="bsnd_s16384q_131072k_n128_topk2048_window_causal"), kind="window"),
+    5: dict(spec=dict(layout="BSND", B=2, S1=4096, S2=32768, N1=48, topk=8192, sparse_mode=0,
+                      deterministic=True, name="bsnd_b2_s4096q_32768k_n48_topk8192_hotcold_det"),
+            kind="hot_cold"),
+}
+
+
+def workload(n: int, seed: Optional[int] = None) -> Problem:
+    w = WORKLOADS[n]
+    p = problem(**w["spec"])
+    return generate(p, n if seed is None else seed, index_kind=w["kind"])

@@ -1,0 +1,77 @@
+"""Host-side checks of the seeded input generators (no GPU, no oracle)."""
+
+import numpy as np
+import pytest
+
+from sparse_mla_flash_amd import inputs
+
+
+def _rows(p):
+    """(global row, batch, position) for every active query row."""
+    for b in range(p.B):
+        for i in range(p.lq(b)):
+            yield p.q_offset(b) + i, b, i
+
+
+def test_bf16_rounding_is_nearest_even():
+    x = np.array([1.0, 1.00390625, 1.01171875, -2.5, 3.0e-5, 1.0 + 2 ** -8], np.float32)
+    bits = inputs.f32_to_bf16_bits(x)
+    back = inputs.bf16_bits_to_f32(bits)
+    # 1 + 2^-8 is a tie between 1 and 1 + 2^-7: ties go to the even mantissa (1.0)
+    assert back[5] == 1.0
+    assert back[0] == 1.0 and back[3] == -2.5
+    assert np.all(np.abs(back - x) <= np.abs(x) * 2 ** -8)
+
+
+@pytest.mark.parametrize("mode", [0, 3])
+def test_uniform_indices_are_distinct_valid_and_padded(mode):
+    p = inputs.problem("BSND", B=2, S1=40, S2=50, N1=2, topk=16, sparse_mode=mode, seq_q=[40, 33],
+                       seq_kv=[50, 20])
+    inputs.generate(p, 3)
+    idx = p.idx.reshape(p.rows, p.topk)
+    for g, b, i in _rows(p):
+        hi = min(i + p.lkv(b) - p.lq(b), p.lkv(b) - 1) if mode == 3 else p.lkv(b) - 1
+        row = idx[g]
+        valid = row[row >= 0]
+        assert len(set(valid.tolist())) == len(valid)
+        assert valid.min(initial=0) >= 0 and valid.max(initial=0) <= max(hi, 0)
+        assert len(valid) == min(p.topk, max(hi + 1, 0))
+        # padding sits at the tail
+        assert (row[len(valid):] == -1).all()
+    # padded query rows of batch 1 hold no selections
+    assert (idx[p.q_offset(1) + 33:] == -1).all()
+
+
+def test_window_indices_half_local():
+    p = inputs.problem("BSND", B=1, S1=64, S2=4096, N1=1, topk=64, sparse_mode=3)
+    inputs.generate(p, 4, index_kind="window", window=256)
+    idx = p.idx.reshape(p.rows, p.topk)
+    for g, b, i in _rows(p):
+        pos = i + 4096 - 64
+        row = idx[g]
+        assert len(set(row.tolist())) == 64 and row.min() >= 0 and row.max() <= pos
+        assert (row >= pos - 255).sum() >= 32
+
+
+def test_hot_cold_indices():
+    p = inputs.problem("BSND", B=2, S1=8, S2=200, N1=1, topk=60, sparse_mode=0)
+    inputs.generate(p, 5, index_kind="hot_cold")
+    idx = p.idx.reshape(p.rows, p.topk)
+    for b in range(2):
+        rows = idx[b * 8:(b + 1) * 8]
+        counts = np.bincount(rows.reshape(-1), minlength=200)
+        hot = np.nonzero(counts == 8)[0]
+        assert len(hot) >= 20                     # the 20 hot keys are in every row
+        for r in rows:
+            assert len(set(r.tolist())) == 60 and r.min() >= 0
+
+
+def test_generation_is_seeded():
+    a = inputs.generate(inputs.problem("TND", B=2, seq_q=[5, 7], seq_kv=[9, 7], N1=2, topk=8), 11)
+    b = inputs.generate(inputs.problem("TND", B=2, seq_q=[5, 7], seq_kv=[9, 7], N1=2, topk=8), 11)
+    c = inputs.generate(inputs.problem("TND", B=2, seq_q=[5, 7], seq_kv=[9, 7], N1=2, topk=8), 12)
+    for name in ("q", "k", "qr", "kr", "dout", "idx"):
+        assert np.array_equal(getattr(a, name), getattr(b, name))
+    assert not np.array_equal(a.q, c.q)
+    assert np.array_equal(a.k, a.v) and a.k is not a.v
+    assert a.q.shape == (12, 2, 512) and a.k.shape == (16, 1, 512) and a.idx.shape == (12, 1, 8)
