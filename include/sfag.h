@@ -1,0 +1,144 @@
+/*
+ * sfag.h -- C ABI of the MI355X (gfx950) SparseFlashAttentionGrad library.
+ *
+ * The operation is the one defined on the SparseFlashAttentionGrad README
+ * (gitcode ops-transformer, attention/sparse_flash_attention_grad):
+ *   "function description": for every query token the key/value rows named by
+ *   sparseIndices are gathered, then
+ *     stage 1: dP = dO V^T,  dV[u] += P^T dO
+ *     stage 2: dS = P * (dP - FlashSoftmaxGrad(dO, out)),  FlashSoftmaxGrad = rowsum(dO * out)
+ *     stage 3: dQ = dS K[u] * scale,  dK[u] += dS^T Q * scale
+ *   with P rebuilt from the forward statistics softmaxMax / softmaxSum
+ *   ("parameters": both are intermediate outputs of the forward pass) and the
+ *   MLA split of every head into a 512-wide part and a 64-wide rope part
+ *   (queryRope / keyRope in, dQueryRope / dKeyRope out).
+ * The argument list mirrors the page's parameter table; the two-call pattern
+ * (size the workspace, then run on a stream) mirrors the workspace-query /
+ * execute pair of the CANN FlashAttention backward page ("function prototype").
+ *
+ * Conventions shared by every entry point
+ *   - All tensors are dense, row-major, contiguous.  Pointers named *_host are
+ *     host memory read during the call only; every other pointer is device
+ *     memory owned by the caller.  The library allocates no device memory and
+ *     keeps no pointer after a call returns.
+ *   - bf16 tensors are IEEE bfloat16 bit patterns (uint16).  Statistics are fp32.
+ *   - Layout "BSND": query-side [B, S1, N1, W], key-side [B, S2, 1, W],
+ *     sparseIndices [B, S1, 1, topk], statistics [B, N1, S1].
+ *     Layout "TND": query-side [T1, N1, W], key-side [T2, 1, W],
+ *     sparseIndices [T1, 1, topk], statistics [N1, T1]; sfag_dims.S1 = T1 and
+ *     .S2 = T2, and the per-sequence lengths are required.  (W = 512 or 64.)
+ *   - sparseIndices hold key positions relative to the start of the query's own
+ *     batch / sequence.  A slot is skipped (not an error) when its index is
+ *     negative, >= the sequence's key length, or, for sparseMode 3, greater than
+ *     i + Lkv - Lq for query position i (causal mask aligned at the bottom-right
+ *     vertex).  Query rows at or beyond the sequence's query length are padding.
+ *   - sparseMode 0 (no mask) and 3 (causal, bottom-right) are supported, as the
+ *     page's constraint section states; preTokens / nextTokens are accepted and
+ *     ignored in both modes.
+ *   - Outputs are overwritten completely: key rows selected by no query get
+ *     dK = dKRope = dV = 0, padded / empty query rows get dQ = dQRope = 0.
+ *   - Asynchrony: work is enqueued on `stream` (a hipStream_t, NULL = the
+ *     default stream) and the call returns; inputs must stay valid until the
+ *     stream reaches that point.
+ *   - Errors: every argument check runs before anything is enqueued; on a
+ *     non-OK status nothing was launched and outputs are untouched.  The text of
+ *     the last error of the calling thread is available from sfag_last_error().
+ *     Status codes 161001 / 161002 mirror the CANN null-pointer / invalid-
+ *     parameter codes (CANN FlashAttention backward page, "return codes").
+ *   - Determinism: with deterministic = 0 key gradients are summed with fp32
+ *     atomics (run-to-run bit differences are possible, as on the page, which
+ *     calls the operator non-deterministic by default, "constraints").  With
+ *     deterministic = 1 they are summed in a fixed order and results are
+ *     bit-identical across runs for the same inputs, shape and device.
+ */
+#ifndef SFAG_H
+#define SFAG_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SFAG_OK = 0,
+  SFAG_ERR_PARAM_NULLPTR = 161001, /* a required pointer is NULL */
+  SFAG_ERR_PARAM_INVALID = 161002, /* a shape, attribute or layout violates the constraints */
+  SFAG_ERR_UNSUPPORTED = 161901,   /* legal on the page but not built here (fp16, block size > 1, no rope) */
+  SFAG_ERR_WORKSPACE = 161902,     /* workspace NULL or smaller than sfag_get_workspace_size() */
+  SFAG_ERR_DEVICE = 161903         /* a HIP runtime / launch error */
+} sfag_status;
+
+typedef struct {
+  int64_t B;      /* batches (BSND) or sequences (TND), 1..256 */
+  int64_t S1;     /* BSND: padded query length; TND: total query tokens T1 (1..131072 per sequence) */
+  int64_t S2;     /* BSND: padded key length; TND: total key tokens T2 */
+  int64_t N1;     /* query heads: 1,2,3,4,6,8,12,16,24,32,48,64,128 */
+  int64_t N2;     /* key heads: must be 1 */
+  int64_t D;      /* head width: must be 512 */
+  int64_t Drope;  /* rope width: must be 64 */
+  int64_t topk;   /* selected keys per query token (>= 1; the page lists 1024..8192 step 1024) */
+} sfag_dims;
+
+/*
+ * Bytes of device workspace the backward call needs for these arguments.
+ * Validates every argument that does not need device pointers; returns the
+ * same status the backward call would return for them.
+ *   seq_len_q_host / seq_len_kv_host: B valid lengths (actualSeqLengthsQuery /
+ *     actualSeqLengthsKv); NULL means full S1 / S2 (BSND only).
+ *   sparse_block_size: must be 1 (sparseBlockSize; larger blocks -> UNSUPPORTED).
+ *   layout: "BSND" or "TND".
+ */
+sfag_status sfag_get_workspace_size(const sfag_dims* dims, const int32_t* seq_len_q_host,
+                                    const int32_t* seq_len_kv_host, float scale_value,
+                                    int64_t sparse_block_size, const char* layout,
+                                    int64_t sparse_mode, int64_t pre_tokens, int64_t next_tokens,
+                                    int32_t deterministic, uint64_t* workspace_size);
+
+/*
+ * SparseFlashAttentionGrad backward.
+ *   query [..,N1,512], key / value [..,1,512], query_rope [..,N1,64], key_rope [..,1,64],
+ *   d_out / out [..,N1,512]: bf16.  value must equal key (page constraint); it is
+ *   checked for NULL but never read, key supplies both roles.
+ *   sparse_indices: int32 [..,1,topk].
+ *   softmax_max / softmax_sum: fp32 statistics of the forward pass (layout above).
+ *   d_query, d_key, d_value, d_query_rope, d_key_rope: bf16 outputs shaped like
+ *   query, key, value, query_rope, key_rope.
+ *   workspace: device buffer of at least sfag_get_workspace_size() bytes, 256-byte
+ *   aligned; its contents on entry are ignored.
+ */
+sfag_status sfag_sparse_flash_attention_grad(
+    const void* query, const void* key, const void* value, const int32_t* sparse_indices,
+    const void* d_out, const void* out, const float* softmax_max, const float* softmax_sum,
+    const int32_t* seq_len_q_host, const int32_t* seq_len_kv_host, const void* query_rope,
+    const void* key_rope, const sfag_dims* dims, float scale_value, int64_t sparse_block_size,
+    const char* layout, int64_t sparse_mode, int64_t pre_tokens, int64_t next_tokens,
+    int32_t deterministic, void* d_query, void* d_key, void* d_value, void* d_query_rope,
+    void* d_key_rope, void* workspace, uint64_t workspace_size, void* stream);
+
+/*
+ * Sparse forward over the same selection (the step that produces the inputs
+ * `out`, softmaxMax and softmaxSum of the backward; SparseAttnSharedkv README,
+ * "function description": O = softmax(Q K~^T scale) V~ with K~ = V~, and the
+ * statistics described on the SparseFlashAttentionGrad page).  out [..,N1,512]
+ * bf16; softmax_max = maximum scaled logit over valid slots, softmax_sum =
+ * sum of exp(logit - max); rows without a valid slot get out = 0, max = sum = 0.
+ * Needs no workspace.  Same conventions and checks as the backward.
+ */
+sfag_status sfag_sparse_flash_attention_forward(
+    const void* query, const void* key, const void* value, const int32_t* sparse_indices,
+    const int32_t* seq_len_q_host, const int32_t* seq_len_kv_host, const void* query_rope,
+    const void* key_rope, const sfag_dims* dims, float scale_value, int64_t sparse_block_size,
+    const char* layout, int64_t sparse_mode, int64_t pre_tokens, int64_t next_tokens, void* out,
+    float* softmax_max, float* softmax_sum, void* stream);
+
+/* Text of the calling thread's last non-OK status ("" if none). */
+const char* sfag_last_error(void);
+
+/* Library version string. */
+const char* sfag_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SFAG_H */

@@ -1,0 +1,75 @@
+// sfag_launch.h -- kernel argument blocks and launchers shared by the host library and the
+// HIP kernels of the SparseFlashAttentionGrad library (internal; not part of the C ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sfag {
+
+// Per-batch valid query / key lengths, passed by value in the kernel arguments (B <= 256).
+struct Lens {
+  int32_t lq[256];
+  int32_t lkv[256];
+};
+
+struct BwdArgs {
+  const uint16_t* q;      // [rows, N1, 512] bf16
+  const uint16_t* qr;     // [rows, N1, 64]
+  const uint16_t* k;      // [keys, 512]  (also plays V)
+  const uint16_t* kr;     // [keys, 64]
+  const uint16_t* dout;   // [rows, N1, 512]
+  const uint16_t* out;    // [rows, N1, 512]
+  const int32_t* idx;     // [rows, topk]
+  const float* smax;      // statistics (BSND [B, N1, S1], TND [N1, T1])
+  const float* ssum;
+  uint16_t* dq;           // [rows, N1, 512]
+  uint16_t* dqr;          // [rows, N1, 64]
+  float* acc;             // [keys, 1088] fp32 accumulator (atomic mode)
+  float* partial;         // [head groups, pairs_per_launch, 1088] (deterministic mode)
+  Lens lens;
+  int64_t S1;             // BSND S1 / TND T1 (statistics head stride)
+  int64_t S2;             // BSND S2 / TND T2
+  int64_t row_begin;      // first query row of this launch
+  int64_t pairs_per_launch;
+  int B, N1, topk, mode3, layout_tnd;
+  float scale;
+};
+
+struct FwdArgs {
+  const uint16_t* q;
+  const uint16_t* qr;
+  const uint16_t* k;
+  const uint16_t* kr;
+  const int32_t* idx;
+  uint16_t* out;
+  float* smax;
+  float* ssum;
+  Lens lens;
+  int64_t S1;
+  int64_t S2;
+  int B, N1, topk, mode3, layout_tnd;
+  float scale;
+};
+
+// statistics element of head h of a query row (BSND [B, N1, S1], TND [N1, T1])
+template <typename Geo>
+__host__ __device__ inline int64_t stat_index(int tnd, const Geo& g, int64_t row, int N1, int64_t S1, int h) {
+  return tnd ? (int64_t)h * S1 + row : ((int64_t)g.b * N1 + h) * S1 + g.i;
+}
+
+hipError_t launch_bwd_main(const BwdArgs& a, int64_t nrows, int hg_count, bool partial, hipStream_t st);
+hipError_t launch_fwd(const FwdArgs& a, int64_t nrows, int hg_count, hipStream_t st);
+hipError_t launch_fill_zero(float* p, int64_t nfloats, hipStream_t st);
+hipError_t launch_cast(const float* acc, uint16_t* dk, uint16_t* dkr, uint16_t* dv, int64_t keys,
+                       hipStream_t st);
+hipError_t launch_pair_keys(const BwdArgs& a, uint64_t* keys, int64_t nrows, hipStream_t st);
+hipError_t launch_det_reduce(const uint64_t* sorted, int64_t n, const float* partial,
+                             int64_t pairs_per_launch, int hg_count, float* acc, int64_t keys,
+                             hipStream_t st);
+hipError_t sort_pair_keys(void* temp, size_t temp_bytes, const uint64_t* in, uint64_t* out, int64_t n,
+                          int end_bit, hipStream_t st);
+size_t sort_temp_bytes(int64_t n, int end_bit);
+hipError_t set_bwd_attributes();
+hipError_t set_fwd_attributes();
+
+}  // namespace sfag

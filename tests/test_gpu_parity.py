@@ -1,0 +1,117 @@
+"""GPU backward / forward vs the fp64 oracle on the same seeded inputs.
+
+Every output tensor must satisfy max abs error <= 2e-2 and relative L2 error
+<= 5e-3 against the oracle evaluated on the operator's own inputs (bf16 out,
+fp32 statistics).  Sizes are small enough for the oracle to finish in seconds
+while spanning several 32-key chunks, several 16-head tiles and a ragged tail;
+edge cases cover padding, empty rows, invalid / duplicate indices, varlen TND
+with an empty sequence, S1 > S2 under the causal mode and every head-group
+shape the kernels special-case (N1 < 16, N1 not a multiple of 16, N1 = 128).
+"""
+
+import numpy as np
+import pytest
+
+from sparse_mla_flash_amd import inputs
+from tests.common import Case, compare, from_dev
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    # name: (problem kwargs, index kind, seed)
+    "bsnd_n8_causal_tail": (dict(layout="BSND", B=1, S1=40, S2=600, N1=8, topk=100, sparse_mode=3), "uniform", 1),
+    "bsnd_n64_short_prefix": (dict(layout="BSND", B=1, S1=150, S2=150, N1=64, topk=64, sparse_mode=3), "uniform", 2),
+    "bsnd_n128_nomask": (dict(layout="BSND", B=1, S1=24, S2=300, N1=128, topk=72, sparse_mode=0), "uniform", 3),
+    "bsnd_n48_padded_batches": (dict(layout="BSND", B=2, S1=40, S2=90, N1=48, topk=40, sparse_mode=3,
+                                     seq_q=[40, 17], seq_kv=[90, 31]), "uniform", 4),
+    "bsnd_n3": (dict(layout="BSND", B=1, S1=20, S2=100, N1=3, topk=33, sparse_mode=0), "uniform", 5),
+    "bsnd_n12_s1_gt_s2": (dict(layout="BSND", B=1, S1=70, S2=50, N1=12, topk=48, sparse_mode=3), "uniform", 6),
+    "tnd_n16_varlen_empty_seq": (dict(layout="TND", B=4, seq_q=[37, 0, 70, 5], seq_kv=[50, 3, 70, 9], N1=16,
+                                      topk=48, sparse_mode=3), "uniform", 7),
+    "tnd_n128_varlen": (dict(layout="TND", B=3, seq_q=[20, 33, 9], seq_kv=[64, 33, 40], N1=128, topk=40,
+                             sparse_mode=3), "uniform", 8),
+    "bsnd_n64_window": (dict(layout="BSND", B=1, S1=48, S2=2048, N1=64, topk=64, sparse_mode=3), "window", 9),
+    "bsnd_n48_hotcold_nomask": (dict(layout="BSND", B=2, S1=16, S2=400, N1=48, topk=96, sparse_mode=0),
+                                "hot_cold", 10),
+}
+
+
+def make(name):
+    kw, kind, seed = CASES[name]
+    p = inputs.problem(**kw, name=name)
+    inputs.generate(p, seed, index_kind=kind, window=256)
+    return p
+
+
+def check_all(case: Case, outs, label=""):
+    dq, dk, dv, dqr, dkr = (from_dev(t) for t in outs)
+    rdq, rdqr = case.ref_dq()
+    rdk, rdkr, rdv = case.ref_dkv()
+    res = {}
+    res["dq"] = compare(label + "dq", dq, rdq)
+    res["dq_rope"] = compare(label + "dq_rope", dqr, rdqr)
+    res["dk"] = compare(label + "dk", dk, rdk)
+    res["dk_rope"] = compare(label + "dk_rope", dkr, rdkr)
+    res["dv"] = compare(label + "dv", dv, rdv)
+    return res
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+@pytest.mark.parametrize("deterministic", [False, True])
+def test_backward_matches_oracle(name, deterministic):
+    case = Case(make(name))
+    outs = case.run_gpu(deterministic=deterministic)
+    res = check_all(case, outs, f"{name}/det={int(deterministic)}/")
+    print(name, deterministic, {k: f"{v[0]:.2e}/{v[1]:.2e}" for k, v in res.items()})
+
+
+def test_invalid_and_duplicate_indices():
+    """Negative, out-of-range and causally masked indices are skipped; duplicates add."""
+    p = inputs.problem("BSND", B=1, S1=33, S2=80, N1=16, topk=50, sparse_mode=3)
+    inputs.generate(p, 21)
+    r = np.random.default_rng(5)
+    idx = r.integers(-3, 90, size=(33, 50)).astype(np.int32)
+    idx[:, 1] = idx[:, 0]                              # duplicated slot in every row
+    p.idx = idx.reshape(p.idx_shape())
+    case = Case(p)
+    check_all(case, case.run_gpu(), "messy/")
+    check_all(case, case.run_gpu(deterministic=True), "messy-det/")
+
+
+def test_all_slots_invalid_gives_zeros():
+    p = inputs.problem("BSND", B=1, S1=8, S2=16, N1=8, topk=40, sparse_mode=3)
+    inputs.generate(p, 22)
+    p.idx = np.full(p.idx_shape(), -1, np.int32)
+    case = Case(p)
+    for det in (False, True):
+        for t in case.run_gpu(deterministic=det):
+            assert not from_dev(t).any()
+
+
+def test_slot_permutation_invariance():
+    p = make("bsnd_n64_short_prefix")
+    case = Case(p)
+    a = [from_dev(t) for t in case.run_gpu()]
+    perm = np.stack([np.random.default_rng(i).permutation(p.topk) for i in range(p.rows)])
+    p.idx = np.take_along_axis(p.idx.reshape(p.rows, p.topk), perm, axis=1).reshape(p.idx_shape())
+    case2 = Case(p)
+    b = [from_dev(t) for t in case2.run_gpu()]
+    for x, y in zip(a, b):
+        # only the order of fp32 accumulation changes
+        assert np.abs(x - y).max() <= 2e-2
+
+
+@pytest.mark.parametrize("name", ["bsnd_n64_short_prefix", "tnd_n16_varlen_empty_seq", "bsnd_n128_nomask",
+                                  "bsnd_n3"])
+def test_forward_matches_oracle(name):
+    import sparse_mla_flash_amd as sf
+    p = make(name)
+    case = Case(p)
+    d = case.device_inputs()
+    out, smax, ssum = sf.sparse_flash_attention_forward(
+        d["query"], d["key"], d["value"], d["sparse_indices"], p.seq_q, p.seq_kv, d["query_rope"],
+        d["key_rope"], scale_value=p.scale, layout=p.layout, sparse_mode=p.sparse_mode)
+    compare(name + "/out", from_dev(out), case.out64)
+    m, l = from_dev(smax), from_dev(ssum)
+    assert np.abs(m - case.m64).max() <= 1e-4 * max(1.0, np.abs(case.m64).max())
+    assert np.abs(l - case.l64).max() <= 1e-4 * max(1.0, np.abs(case.l64).max())
