@@ -132,6 +132,16 @@ sfag_status sfag_sparse_flash_attention_forward(
     const char* layout, int64_t sparse_mode, int64_t pre_tokens, int64_t next_tokens, void* out,
     float* softmax_max, float* softmax_sum, void* stream);
 
+/*
+ * Instrumentation: until called again, every backward call made by this thread records
+ * `before` (a hipEvent_t) on its stream right before the kernels that compute the key
+ * gradients and `after` right after them (default mode: the single main kernel;
+ * deterministic mode: the whole partial / sort / reduce sequence), so that a caller can
+ * time them with hipEventElapsedTime.  Both NULL (the default) disables recording.  The
+ * events stay owned by the caller.  Always returns SFAG_OK.
+ */
+sfag_status sfag_set_profile_events(void* before, void* after);
+
 /* Text of the calling thread's last non-OK status ("" if none). */
 const char* sfag_last_error(void);
 

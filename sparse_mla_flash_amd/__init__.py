@@ -31,7 +31,8 @@ SFAG_ERR_WORKSPACE = 161902
 SFAG_ERR_DEVICE = 161903
 
 EXPORTED = ("sfag_get_workspace_size", "sfag_sparse_flash_attention_grad",
-            "sfag_sparse_flash_attention_forward", "sfag_last_error", "sfag_version")
+            "sfag_sparse_flash_attention_forward", "sfag_set_profile_events", "sfag_last_error",
+            "sfag_version")
 
 
 class SfagError(RuntimeError):
@@ -72,6 +73,8 @@ def lib():
             vp, vp, vp, vp, i32p, i32p, vp, vp, ctypes.POINTER(Dims), ctypes.c_float,
             ctypes.c_int64, ctypes.c_char_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
             vp, vp, vp, vp]
+        L.sfag_set_profile_events.restype = ctypes.c_int
+        L.sfag_set_profile_events.argtypes = [vp, vp]
         L.sfag_last_error.restype = ctypes.c_char_p
         L.sfag_last_error.argtypes = []
         L.sfag_version.restype = ctypes.c_char_p
@@ -86,6 +89,11 @@ def sfag_last_error() -> str:
 
 def sfag_version() -> str:
     return lib().sfag_version().decode()
+
+
+def sfag_set_profile_events(before, after) -> int:
+    """Record caller-owned hipEvent_t handles around the key-gradient kernels of later calls."""
+    return lib().sfag_set_profile_events(before, after)
 
 
 def _check(status: int) -> None:

@@ -16,6 +16,8 @@
 namespace {
 
 thread_local std::string g_last_error;
+thread_local hipEvent_t g_ev_before = nullptr;
+thread_local hipEvent_t g_ev_after = nullptr;
 
 sfag_status fail(sfag_status st, const char* fmt, ...) {
   char buf[512];
@@ -198,6 +200,12 @@ const char* sfag_last_error(void) { return g_last_error.c_str(); }
 
 const char* sfag_version(void) { return "sfag-mi355x 0.1 (gfx950)"; }
 
+sfag_status sfag_set_profile_events(void* before, void* after) {
+  g_ev_before = reinterpret_cast<hipEvent_t>(before);
+  g_ev_after = reinterpret_cast<hipEvent_t>(after);
+  return ok();
+}
+
 sfag_status sfag_get_workspace_size(const sfag_dims* dims, const int32_t* seq_len_q_host,
                                     const int32_t* seq_len_kv_host, float scale_value,
                                     int64_t sparse_block_size, const char* layout, int64_t sparse_mode,
@@ -275,6 +283,7 @@ sfag_status sfag_sparse_flash_attention_grad(
   a.layout_tnd = p.tnd;
   a.scale = scale_value;
 
+  if (g_ev_before) SFAG_HIP(hipEventRecord(g_ev_before, s));
   if (!p.det) {
     a.row_begin = 0;
     a.pairs_per_launch = 0;
@@ -294,6 +303,7 @@ sfag_status sfag_sparse_flash_attention_grad(
       SFAG_HIP(sfag::launch_det_reduce(k1, nr * p.topk, a.partial, nr * p.topk, p.hg_count, acc, p.keys, s));
     }
   }
+  if (g_ev_after) SFAG_HIP(hipEventRecord(g_ev_after, s));
   SFAG_HIP(sfag::launch_cast(acc, static_cast<uint16_t*>(d_key), static_cast<uint16_t*>(d_key_rope),
                              static_cast<uint16_t*>(d_value), p.keys, s));
   return ok();
