@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -51,12 +52,51 @@ struct Plan {
   int mode3 = 0, det = 0, hg_count = 0;
   float scale = 0.f;
   sfag::Lens lens;                 // per-batch valid lengths
+  // path: key-major dense-masked dK / dV (dense = 1) or per-pair scatter (dense = 0)
+  int dense = 0;
+  double waste = 0.0;              // dense-masked (row, key) entries per valid pair (upper bound)
+  int64_t items = 0, maxblk = 0, np = 0;
   // workspace layout
   uint64_t off_acc = 0, off_partial = 0, off_keys0 = 0, off_keys1 = 0, off_sorttmp = 0;
+  uint64_t off_sorted = 0, off_count = 0, off_maxdup = 0, off_offs = 0, off_dsp = 0, off_part = 0, off_flag = 0;
   uint64_t sort_tmp_bytes = 0, bytes = 0;
   int64_t det_rows = 0;            // query rows per deterministic launch
   int end_bit = 64;
 };
+
+// Rows x candidate keys the key-major kernels visit vs. the most pairs the rows can hold:
+// per batch, query i may select keys 0..i + Lkv - Lq (sparseMode 3) or 0..Lkv-1 (mode 0).
+void path_stats(const Plan& p, double* range_sum, double* valid_max) {
+  double rs = 0, vm = 0;
+  for (int64_t b = 0; b < p.B; ++b) {
+    const double lq = p.lens.lq[b], lkv = p.lens.lkv[b], k = (double)p.topk;
+    if (lq <= 0 || lkv <= 0) continue;
+    if (!p.mode3) {
+      rs += lq * lkv;
+      vm += lq * std::min(k, lkv);
+      continue;
+    }
+    // range of row i is i + d for i >= i_lo, with d = Lkv - Lq + 1 (never above Lkv)
+    const double d = lkv - lq + 1;
+    const double ilo = std::max(0.0, 1.0 - d), ihi = lq - 1;
+    if (ihi < ilo) continue;
+    const auto series = [](double a, double z, double off) {  // sum_{i=a..z} (i + off)
+      return z < a ? 0.0 : (z - a + 1) * ((a + z) / 2.0 + off);
+    };
+    rs += series(ilo, ihi, d);
+    // rows whose range is at most topk contribute their range, the others topk
+    const double isplit = std::min(ihi, std::floor(k - d));  // last i with i + d <= topk
+    vm += series(ilo, isplit, d) + std::max(0.0, ihi - std::max(isplit, ilo - 1)) * k;
+  }
+  *range_sum = rs;
+  *valid_max = vm;
+}
+
+uint64_t next_pow2(uint64_t x) {
+  uint64_t v = 1;
+  while (v < x) v <<= 1;
+  return v;
+}
 
 bool n1_allowed(int64_t n) {
   static const int64_t ok_[] = {1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 48, 64, 128};
@@ -137,7 +177,46 @@ sfag_status make_plan(const sfag_dims* dims, const int32_t* sq, const int32_t* s
     return fail(SFAG_ERR_PARAM_INVALID, "problem too large");
 
   if (!need_ws) return SFAG_OK;
+
+  // choose the dK / dV path: the key-major kernels pay for every candidate key of a block a
+  // selecting row could have chosen; the scatter path pays 1088 fp32 adds per valid pair
+  double range_sum = 0, valid_max = 0;
+  path_stats(*p, &range_sum, &valid_max);
+  p->waste = valid_max > 0 ? range_sum / valid_max : 0.0;
+  p->dense = p->topk <= 16384 && p->waste <= 8.0;
+  if (const char* f = std::getenv("SFAG_FORCE_PATH")) {
+    if (std::strcmp(f, "dense") == 0 && p->topk <= 16384) p->dense = 1;
+    if (std::strcmp(f, "scatter") == 0) p->dense = 0;
+  }
   uint64_t off = 0;
+  if (p->dense) {
+    int64_t items = 0, maxblk = 0;
+    for (int64_t b = 0; b < p->B; ++b) {
+      const int64_t nblk = (p->lens.lkv[b] + sfag::kBk - 1) / sfag::kBk;
+      items += nblk * ((p->lens.lq[b] + sfag::kSegRows - 1) / sfag::kSegRows);
+      maxblk = std::max(maxblk, nblk);
+    }
+    p->items = items;
+    p->maxblk = maxblk;
+    p->np = (int64_t)next_pow2((uint64_t)p->topk);
+    const uint64_t pairs = (uint64_t)p->rows * p->topk;
+    p->off_sorted = off;
+    off = align_up(off + pairs * 4);
+    p->off_count = off;
+    off = align_up(off + (uint64_t)p->rows * 4);
+    p->off_maxdup = off;
+    off = align_up(off + (uint64_t)p->rows * 4);
+    p->off_offs = off;
+    off = align_up(off + (uint64_t)p->rows * (maxblk + 1) * 4);
+    p->off_dsp = off;
+    off = align_up(off + pairs * p->hg_count * 128 * 2);
+    p->off_part = off;
+    off = align_up(off + (uint64_t)p->hg_count * items * sfag::kBk * kDacc * 4);
+    p->off_flag = off;
+    off = align_up(off + (uint64_t)p->hg_count * std::max<int64_t>(items, 1) * 4);
+    p->bytes = off;
+    return SFAG_OK;
+  }
   p->off_acc = off;
   off = align_up(off + (uint64_t)p->keys * kDacc * sizeof(float));
   if (det) {
@@ -180,6 +259,7 @@ sfag_status init_device() {
   std::call_once(g_attr_once, [] {
     g_attr_err = sfag::set_bwd_attributes();
     if (g_attr_err == hipSuccess) g_attr_err = sfag::set_fwd_attributes();
+    if (g_attr_err == hipSuccess) g_attr_err = sfag::set_dense_attributes();
   });
   if (g_attr_err != hipSuccess)
     return fail(SFAG_ERR_DEVICE, "kernel attribute setup failed: %s", hipGetErrorString(g_attr_err));
@@ -258,7 +338,7 @@ sfag_status sfag_sparse_flash_attention_grad(
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   float* acc = reinterpret_cast<float*>(ws + p.off_acc);
-  SFAG_HIP(sfag::launch_fill_zero(acc, p.keys * kDacc, s));
+  if (!p.dense) SFAG_HIP(sfag::launch_fill_zero(acc, p.keys * kDacc, s));
 
   sfag::BwdArgs a{};
   a.q = static_cast<const uint16_t*>(query);
@@ -281,13 +361,56 @@ sfag_status sfag_sparse_flash_attention_grad(
   a.topk = (int)p.topk;
   a.mode3 = p.mode3;
   a.layout_tnd = p.tnd;
+  a.hgc = p.hg_count;
   a.scale = scale_value;
+
+  if (p.dense) {
+    sfag::DenseArgs da{};
+    da.q = a.q;
+    da.qr = a.qr;
+    da.dout = a.dout;
+    da.idx = sparse_indices;
+    da.sorted = reinterpret_cast<int32_t*>(ws + p.off_sorted);
+    da.count = reinterpret_cast<int32_t*>(ws + p.off_count);
+    da.maxdup = reinterpret_cast<int32_t*>(ws + p.off_maxdup);
+    da.offs = reinterpret_cast<int32_t*>(ws + p.off_offs);
+    da.dsp = reinterpret_cast<uint16_t*>(ws + p.off_dsp);
+    da.part = reinterpret_cast<float*>(ws + p.off_part);
+    da.flag = reinterpret_cast<int32_t*>(ws + p.off_flag);
+    da.dk = static_cast<uint16_t*>(d_key);
+    da.dkr = static_cast<uint16_t*>(d_key_rope);
+    da.dv = static_cast<uint16_t*>(d_value);
+    da.lens = p.lens;
+    da.S1 = p.S1;
+    da.S2 = p.S2;
+    da.B = (int)p.B;
+    da.N1 = (int)p.N1;
+    da.topk = (int)p.topk;
+    da.mode3 = p.mode3;
+    da.layout_tnd = p.tnd;
+    da.hgc = p.hg_count;
+    da.maxblk = (int)p.maxblk;
+    da.items = (int)p.items;
+    da.scale = scale_value;
+    a.sorted = da.sorted;
+    a.count = da.count;
+    a.dsp = reinterpret_cast<uint16_t*>(ws + p.off_dsp);
+    a.row_begin = 0;
+    a.pairs_per_launch = 0;
+    SFAG_HIP(sfag::launch_sort_rows(da, p.rows, (int)p.np, s));
+    SFAG_HIP(sfag::launch_bwd_main(a, p.rows, p.hg_count, 2, s));
+    if (g_ev_before) SFAG_HIP(hipEventRecord(g_ev_before, s));
+    SFAG_HIP(sfag::launch_kv_dense(da, s));
+    if (g_ev_after) SFAG_HIP(hipEventRecord(g_ev_after, s));
+    SFAG_HIP(sfag::launch_kv_reduce(da, p.keys, s));
+    return ok();
+  }
 
   if (g_ev_before) SFAG_HIP(hipEventRecord(g_ev_before, s));
   if (!p.det) {
     a.row_begin = 0;
     a.pairs_per_launch = 0;
-    SFAG_HIP(sfag::launch_bwd_main(a, p.rows, p.hg_count, false, s));
+    SFAG_HIP(sfag::launch_bwd_main(a, p.rows, p.hg_count, 0, s));
   } else {
     a.partial = reinterpret_cast<float*>(ws + p.off_partial);
     uint64_t* k0 = reinterpret_cast<uint64_t*>(ws + p.off_keys0);
@@ -297,7 +420,7 @@ sfag_status sfag_sparse_flash_attention_grad(
       const int64_t nr = std::min<int64_t>(p.det_rows, p.rows - r0);
       a.row_begin = r0;
       a.pairs_per_launch = nr * p.topk;
-      SFAG_HIP(sfag::launch_bwd_main(a, nr, p.hg_count, true, s));
+      SFAG_HIP(sfag::launch_bwd_main(a, nr, p.hg_count, 1, s));
       SFAG_HIP(sfag::launch_pair_keys(a, k0, nr, s));
       SFAG_HIP(sfag::sort_pair_keys(tmp, p.sort_tmp_bytes, k0, k1, nr * p.topk, p.end_bit, s));
       SFAG_HIP(sfag::launch_det_reduce(k1, nr * p.topk, a.partial, nr * p.topk, p.hg_count, acc, p.keys, s));

@@ -20,18 +20,31 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace sfag {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));   // 16-byte copies kept in VGPRs
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kDn = 512;          // nope width
 constexpr int kDr = 64;           // rope width
 constexpr int kDk = kDn + kDr;    // gathered key row width
 constexpr int kDacc = kDk + kDn;  // fp32 accumulator row: dK | dKRope | dV
+
+// Compile-time loop: calls f(std::integral_constant<int, I>) for I = B .. E-1, so register
+// arrays indexed inside the body see constant indices before scalar replacement runs.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
 
 __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);

@@ -12,6 +12,9 @@ struct Lens {
   int32_t lkv[256];
 };
 
+constexpr int kBk = 256;        // keys per block of the key-major dK / dV kernel
+constexpr int kSegRows = 512;   // query rows per segment of the key-major dK / dV kernel
+
 struct BwdArgs {
   const uint16_t* q;      // [rows, N1, 512] bf16
   const uint16_t* qr;     // [rows, N1, 64]
@@ -26,12 +29,36 @@ struct BwdArgs {
   uint16_t* dqr;          // [rows, N1, 64]
   float* acc;             // [keys, 1088] fp32 accumulator (atomic mode)
   float* partial;         // [head groups, pairs_per_launch, 1088] (deterministic mode)
+  const int32_t* sorted;  // [rows, topk] valid key positions, ascending (key-major mode)
+  const int32_t* count;   // [rows] number of valid positions (key-major mode)
+  uint16_t* dsp;          // [rows * topk, head groups, 128] bf16 dS | P per pair (key-major mode)
   Lens lens;
   int64_t S1;             // BSND S1 / TND T1 (statistics head stride)
   int64_t S2;             // BSND S2 / TND T2
   int64_t row_begin;      // first query row of this launch
   int64_t pairs_per_launch;
-  int B, N1, topk, mode3, layout_tnd;
+  int B, N1, topk, mode3, layout_tnd, hgc;
+  float scale;
+};
+
+struct DenseArgs {
+  const uint16_t* q;      // [rows, N1, 512]
+  const uint16_t* qr;     // [rows, N1, 64]
+  const uint16_t* dout;   // [rows, N1, 512]
+  const int32_t* idx;     // [rows, topk]
+  int32_t* sorted;        // [rows, topk]
+  int32_t* count;         // [rows]
+  int32_t* maxdup;        // [rows]
+  int32_t* offs;          // [rows, maxblk + 1]
+  const uint16_t* dsp;    // [rows * topk, hgc, 128]
+  float* part;            // [hgc, items, kBk, 1088]
+  int32_t* flag;          // [hgc, items]
+  uint16_t* dk;           // [keys, 512]
+  uint16_t* dkr;          // [keys, 64]
+  uint16_t* dv;           // [keys, 512]
+  Lens lens;
+  int64_t S1, S2;
+  int B, N1, topk, mode3, layout_tnd, hgc, maxblk, items;
   float scale;
 };
 
@@ -57,7 +84,8 @@ __host__ __device__ inline int64_t stat_index(int tnd, const Geo& g, int64_t row
   return tnd ? (int64_t)h * S1 + row : ((int64_t)g.b * N1 + h) * S1 + g.i;
 }
 
-hipError_t launch_bwd_main(const BwdArgs& a, int64_t nrows, int hg_count, bool partial, hipStream_t st);
+// mode 0: fp32 atomic dK/dV, 1: per-pair partials, 2: dS / P pair records for the key-major kernels
+hipError_t launch_bwd_main(const BwdArgs& a, int64_t nrows, int hg_count, int mode, hipStream_t st);
 hipError_t launch_fwd(const FwdArgs& a, int64_t nrows, int hg_count, hipStream_t st);
 hipError_t launch_fill_zero(float* p, int64_t nfloats, hipStream_t st);
 hipError_t launch_cast(const float* acc, uint16_t* dk, uint16_t* dkr, uint16_t* dv, int64_t keys,
@@ -69,6 +97,10 @@ hipError_t launch_det_reduce(const uint64_t* sorted, int64_t n, const float* par
 hipError_t sort_pair_keys(void* temp, size_t temp_bytes, const uint64_t* in, uint64_t* out, int64_t n,
                           int end_bit, hipStream_t st);
 size_t sort_temp_bytes(int64_t n, int end_bit);
+hipError_t launch_sort_rows(const DenseArgs& a, int64_t rows, int np, hipStream_t st);
+hipError_t launch_kv_dense(const DenseArgs& a, hipStream_t st);
+hipError_t launch_kv_reduce(const DenseArgs& a, int64_t keys, hipStream_t st);
+hipError_t set_dense_attributes();
 hipError_t set_bwd_attributes();
 hipError_t set_fwd_attributes();
 

@@ -19,7 +19,9 @@ def _bits(t):
     ("hot_cold", dict(layout="BSND", B=2, S1=64, S2=1000, N1=48, topk=256, sparse_mode=0)),
     ("uniform", dict(layout="TND", B=2, seq_q=[50, 70], seq_kv=[80, 70], N1=128, topk=64, sparse_mode=3)),
 ])
-def test_deterministic_runs_are_bit_identical(kind, kw):
+@pytest.mark.parametrize("path", ["dense", "scatter"])
+def test_deterministic_runs_are_bit_identical(kind, kw, path, monkeypatch):
+    monkeypatch.setenv("SFAG_FORCE_PATH", path)
     p = inputs.problem(**kw)
     inputs.generate(p, 31, index_kind=kind)
     case = Case(p)

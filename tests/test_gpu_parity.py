@@ -56,16 +56,23 @@ def check_all(case: Case, outs, label=""):
     return res
 
 
+@pytest.fixture(params=["dense", "scatter"])
+def path(request, monkeypatch):
+    """dK / dV path: key-major dense-masked kernels, or per-pair scatter (atomic / partials)."""
+    monkeypatch.setenv("SFAG_FORCE_PATH", request.param)
+    return request.param
+
+
 @pytest.mark.parametrize("name", sorted(CASES))
 @pytest.mark.parametrize("deterministic", [False, True])
-def test_backward_matches_oracle(name, deterministic):
+def test_backward_matches_oracle(name, deterministic, path):
     case = Case(make(name))
     outs = case.run_gpu(deterministic=deterministic)
-    res = check_all(case, outs, f"{name}/det={int(deterministic)}/")
-    print(name, deterministic, {k: f"{v[0]:.2e}/{v[1]:.2e}" for k, v in res.items()})
+    res = check_all(case, outs, f"{name}/{path}/det={int(deterministic)}/")
+    print(name, path, deterministic, {k: f"{v[0]:.2e}/{v[1]:.2e}" for k, v in res.items()})
 
 
-def test_invalid_and_duplicate_indices():
+def test_invalid_and_duplicate_indices(path):
     """Negative, out-of-range and causally masked indices are skipped; duplicates add."""
     p = inputs.problem("BSND", B=1, S1=33, S2=80, N1=16, topk=50, sparse_mode=3)
     inputs.generate(p, 21)
@@ -78,7 +85,7 @@ def test_invalid_and_duplicate_indices():
     check_all(case, case.run_gpu(deterministic=True), "messy-det/")
 
 
-def test_all_slots_invalid_gives_zeros():
+def test_all_slots_invalid_gives_zeros(path):
     p = inputs.problem("BSND", B=1, S1=8, S2=16, N1=8, topk=40, sparse_mode=3)
     inputs.generate(p, 22)
     p.idx = np.full(p.idx_shape(), -1, np.int32)
@@ -88,7 +95,7 @@ def test_all_slots_invalid_gives_zeros():
             assert not from_dev(t).any()
 
 
-def test_slot_permutation_invariance():
+def test_slot_permutation_invariance(path):
     p = make("bsnd_n64_short_prefix")
     case = Case(p)
     a = [from_dev(t) for t in case.run_gpu()]
@@ -115,3 +122,14 @@ def test_forward_matches_oracle(name):
     m, l = from_dev(smax), from_dev(ssum)
     assert np.abs(m - case.m64).max() <= 1e-4 * max(1.0, np.abs(case.m64).max())
     assert np.abs(l - case.l64).max() <= 1e-4 * max(1.0, np.abs(case.l64).max())
+
+
+def test_heavy_duplicates(path):
+    """Rows repeating a few keys many times: more than 256 positions fall in one 256-key block
+    and keys repeat dozens of times; every repeat contributes separately."""
+    p = inputs.problem("BSND", B=1, S1=24, S2=64, N1=16, topk=300, sparse_mode=0)
+    inputs.generate(p, 23)
+    r = np.random.default_rng(6)
+    p.idx = r.integers(0, 10, size=p.idx_shape()).astype(np.int32)
+    case = Case(p)
+    check_all(case, case.run_gpu(), "dups/")
