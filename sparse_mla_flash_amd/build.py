@@ -19,7 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsfag.so")
 
-SOURCES = ["sfag_bwd.hip", "sfag_dense.hip", "sfag_fwd.hip", "sfag_sort.hip", "sfag_api.cpp"]
+SOURCES = ["sfag_bwd.hip", "sfag_q.hip", "sfag_dense.hip", "sfag_fwd.hip", "sfag_sort.hip", "sfag_api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = [

@@ -59,6 +59,7 @@ struct Plan {
   // workspace layout
   uint64_t off_acc = 0, off_partial = 0, off_keys0 = 0, off_keys1 = 0, off_sorttmp = 0;
   uint64_t off_sorted = 0, off_count = 0, off_maxdup = 0, off_offs = 0, off_dsp = 0, off_part = 0, off_flag = 0;
+  uint64_t off_zero = 0;
   uint64_t sort_tmp_bytes = 0, bytes = 0;
   int64_t det_rows = 0;            // query rows per deterministic launch
   int end_bit = 64;
@@ -214,6 +215,8 @@ sfag_status make_plan(const sfag_dims* dims, const int32_t* sq, const int32_t* s
     off = align_up(off + (uint64_t)p->hg_count * items * sfag::kBk * kDacc * 4);
     p->off_flag = off;
     off = align_up(off + (uint64_t)p->hg_count * std::max<int64_t>(items, 1) * 4);
+    p->off_zero = off;
+    off = align_up(off + 576 * 2);
     p->bytes = off;
     return SFAG_OK;
   }
@@ -260,6 +263,7 @@ sfag_status init_device() {
     g_attr_err = sfag::set_bwd_attributes();
     if (g_attr_err == hipSuccess) g_attr_err = sfag::set_fwd_attributes();
     if (g_attr_err == hipSuccess) g_attr_err = sfag::set_dense_attributes();
+    if (g_attr_err == hipSuccess) g_attr_err = sfag::set_q_attributes();
   });
   if (g_attr_err != hipSuccess)
     return fail(SFAG_ERR_DEVICE, "kernel attribute setup failed: %s", hipGetErrorString(g_attr_err));
@@ -377,6 +381,7 @@ sfag_status sfag_sparse_flash_attention_grad(
     da.dsp = reinterpret_cast<uint16_t*>(ws + p.off_dsp);
     da.part = reinterpret_cast<float*>(ws + p.off_part);
     da.flag = reinterpret_cast<int32_t*>(ws + p.off_flag);
+    da.zero_row = reinterpret_cast<uint16_t*>(ws + p.off_zero);
     da.dk = static_cast<uint16_t*>(d_key);
     da.dkr = static_cast<uint16_t*>(d_key_rope);
     da.dv = static_cast<uint16_t*>(d_value);
@@ -395,10 +400,11 @@ sfag_status sfag_sparse_flash_attention_grad(
     a.sorted = da.sorted;
     a.count = da.count;
     a.dsp = reinterpret_cast<uint16_t*>(ws + p.off_dsp);
+    a.zero_row = da.zero_row;
     a.row_begin = 0;
     a.pairs_per_launch = 0;
     SFAG_HIP(sfag::launch_sort_rows(da, p.rows, (int)p.np, s));
-    SFAG_HIP(sfag::launch_bwd_main(a, p.rows, p.hg_count, 2, s));
+    SFAG_HIP(sfag::launch_bwd_q(a, p.rows, p.hg_count, s));
     if (g_ev_before) SFAG_HIP(hipEventRecord(g_ev_before, s));
     SFAG_HIP(sfag::launch_kv_dense(da, s));
     if (g_ev_after) SFAG_HIP(hipEventRecord(g_ev_after, s));

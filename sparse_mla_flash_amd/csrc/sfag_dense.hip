@@ -56,6 +56,8 @@ __global__ void __launch_bounds__(kThreads) sort_rows_kernel(DenseArgs a, int np
     __syncthreads();
   }
   const int64_t row = blockIdx.x;
+  if (row == 0)
+    for (int i = threadIdx.x; i < kDk; i += kThreads) a.zero_row[i] = 0;
   const RowGeo geo = row_geo(a.lens, cum, a.B, a.layout_tnd, a.S1, a.S2, row, a.mode3);
   for (int i = threadIdx.x; i < np; i += kThreads) {
     int32_t v = kNoKey;

@@ -77,6 +77,23 @@ __device__ __forceinline__ bf16x8 lds_frag_tr(const uint16_t* tile, int k0, int 
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// Padded (unswizzled) tiles: element (row, col) at row * pitch + col.  With a pitch of
+// 584 (576 + 8) or 72 (64 + 8) elements consecutive rows start 36 or 4 banks apart, so 16
+// lanes reading the same 16-byte column of 16 rows hit distinct banks, and every address is
+// a per-lane base plus a compile-time offset.
+__device__ __forceinline__ bf16x8 lds_read8p(const uint16_t* tile, int row, int col, int pitch) {
+  return *reinterpret_cast<const bf16x8*>(tile + row * pitch + col);
+}
+
+__device__ __forceinline__ bf16x8 lds_frag_trp(const uint16_t* tile, int k0, int n0, int pitch, int lane) {
+  const int g = lane >> 4, j = lane & 15;
+  const uint16_t* p = tile + (k0 + 8 * g + (j >> 2)) * pitch + n0 + 4 * (j & 3);
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * pitch));
+  const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
 __device__ __forceinline__ uint16_t f2bf(float f) {
   // round to nearest even; NaN stays NaN
   uint32_t u = __float_as_uint(f);

@@ -32,6 +32,7 @@ struct BwdArgs {
   const int32_t* sorted;  // [rows, topk] valid key positions, ascending (key-major mode)
   const int32_t* count;   // [rows] number of valid positions (key-major mode)
   uint16_t* dsp;          // [rows * topk, head groups, 128] bf16 dS | P per pair (key-major mode)
+  const uint16_t* zero_row;  // 576 zero bf16 (key-major mode: source of padding slots)
   Lens lens;
   int64_t S1;             // BSND S1 / TND T1 (statistics head stride)
   int64_t S2;             // BSND S2 / TND T2
@@ -53,6 +54,7 @@ struct DenseArgs {
   const uint16_t* dsp;    // [rows * topk, hgc, 128]
   float* part;            // [hgc, items, kBk, 1088]
   int32_t* flag;          // [hgc, items]
+  uint16_t* zero_row;     // 576 bf16, zeroed by the sort kernel
   uint16_t* dk;           // [keys, 512]
   uint16_t* dkr;          // [keys, 64]
   uint16_t* dv;           // [keys, 512]
@@ -97,6 +99,8 @@ hipError_t launch_det_reduce(const uint64_t* sorted, int64_t n, const float* par
 hipError_t sort_pair_keys(void* temp, size_t temp_bytes, const uint64_t* in, uint64_t* out, int64_t n,
                           int end_bit, hipStream_t st);
 size_t sort_temp_bytes(int64_t n, int end_bit);
+hipError_t launch_bwd_q(const BwdArgs& a, int64_t nrows, int hg_count, hipStream_t st);
+hipError_t set_q_attributes();
 hipError_t launch_sort_rows(const DenseArgs& a, int64_t rows, int np, hipStream_t st);
 hipError_t launch_kv_dense(const DenseArgs& a, hipStream_t st);
 hipError_t launch_kv_reduce(const DenseArgs& a, int64_t keys, hipStream_t st);

@@ -77,13 +77,17 @@ def test_tnd_lengths():
     assert status_of(ws, d, layout="TND", seq_len_q=[10, 21], seq_len_kv=[15, 25]) == sf.SFAG_ERR_PARAM_INVALID
 
 
-def test_accepted_envelope_and_workspace_sizes():
+def test_accepted_envelope_and_workspace_sizes(monkeypatch):
     for n1 in (1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 48, 64, 128):
         assert ws(dims(N1=n1)) > 0
     small = ws(dims(S2=1000))
     assert small >= 1000 * 1088 * 4
-    det = ws(dims(), deterministic=True)
-    assert det > ws(dims())
+    # the key-major path is deterministic by construction: same workspace in both modes
+    assert ws(dims(), deterministic=True) == ws(dims())
+    # the scatter path keeps per-pair partials and a sort buffer in deterministic mode
+    monkeypatch.setenv("SFAG_FORCE_PATH", "scatter")
+    assert ws(dims(), deterministic=True) > ws(dims())
+    monkeypatch.delenv("SFAG_FORCE_PATH")
     # pre/next tokens are accepted and ignored
     assert sf.sfag_get_workspace_size(dims(), None, None, 0.1, 1, "BSND", 0, -5, 7, False) == ws(dims(), sparse_mode=0)
 
