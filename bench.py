@@ -1,18 +1,21 @@
 #!/usr/bin/env python3
 """Benchmark of the SparseFlashAttentionGrad backward on one MI355X.
 
-One step = one full backward call (accumulator init, main kernel, cast) over the
-BSND workload S1 = S2 = 8192, N1 = 64, topk = 2048, causal (sparseMode 3), with
-every input already resident in HBM.  Prints one JSON line:
+One step = one full backward call (every launch of the library's backward: index sort,
+query-major kernel, key-major kernel, ordered reduce and cast) over the BSND workload
+S1 = S2 = 8192, N1 = 64, topk = 2048, causal (sparseMode 3), with every input already
+resident in HBM.  Prints one JSON line:
 
   value      effective TFLOP/s = valid (row, slot) pairs x N1 x 5504 flop / step time
              (5504 = the five topk-wide contractions: 2*576 score recompute,
              2*512 dP, 2*512 dV, 2*576 dQ, 2*576 dK)
-  roofline   the main kernel's algorithmic flops / its average duration, measured
-             with HIP events recorded on the library's stream around that kernel,
-             against the 2.5 PFLOP/s bf16 dense MFMA peak; `traffic` comes from the
-             committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary when it matches the
-             current kernel source, else null
+  roofline   the dominant kernel's algorithmic flops / its average duration, measured
+             with HIP events that the library records on its own stream around that
+             kernel, against the 2.5 PFLOP/s bf16 dense MFMA peak.  Key-major path: the
+             query-major kernel does 3328 flop per (pair, head) (scores, dP, dQ) and the
+             key-major kernel 2176 (dK, dV); scatter path: one kernel does all 5504.
+             `traffic` comes from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary
+             of that kernel when it matches the current kernel sources, else null
   cpu_baseline  the fp64 CPU oracle on a bounded sample of rows of the same workload
 
 Inputs are seeded synthetic tensors (sparse_mla_flash_amd.inputs); out / softmaxMax /
@@ -41,7 +44,11 @@ SCATTER_BYTES_PER_PAIR = 1088 * 4                                      # fp32 dK
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 HBM_PEAK_GBS = 8000.0
 METRIC = "effective TFLOP/s + ms/call, sparse attn bwd (S=8K, topk=2048, N1=64) on 1 MI355X"
-KERNEL_SOURCES = ["sparse_mla_flash_amd/csrc/sfag_bwd.hip", "sparse_mla_flash_amd/csrc/sfag_device.h"]
+FLOP_Q_KERNEL = 2 * 576 + 2 * 512 + 2 * 576                                  # 3328: S, dP, dQ
+FLOP_KV_KERNEL = 2 * 576 + 2 * 512                                           # 2176: dK, dV
+CSRC = os.path.join("sparse_mla_flash_amd", "csrc")
+KERNEL_SOURCES = sorted(os.path.join(CSRC, f) for f in os.listdir(os.path.join(ROOT, CSRC))
+                        if f.endswith((".hip", ".h", ".cpp")))
 
 
 def kernel_sha() -> str:
@@ -101,8 +108,8 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": n, "dispatches": 3}))
 
 
-def traffic_from_profile(workload_name: str):
-    path = os.path.join(ROOT, "profiles", f"bwd_main_{workload_name}_traffic.json")
+def traffic_from_profile(kernel: str, workload_name: str):
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload_name}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as fh:
@@ -198,30 +205,42 @@ def main():
     print("# warmup done", file=sys.stderr, flush=True)
 
     ev = HipEvents()
-    pairs_ev = [(ev.create(), ev.create()) for _ in range(args.steps)]
+    evs = [[ev.create() for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        sf.sfag_set_profile_events(*pairs_ev[i])
+        sf.sfag_set_profile_events(*evs[i])
         step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    sf.sfag_set_profile_events(None, None)
-    kern_ms = [ev.elapsed_ms(a, b) for a, b in pairs_ev]
-    for a, b in pairs_ev:
-        ev.destroy(a)
-        ev.destroy(b)
+    sf.sfag_set_profile_events()
+    path = "key-major" if sf.sfag_last_path() == 0 else "scatter"
+    s1 = sum(ev.elapsed_ms(e[0], e[1]) for e in evs) / args.steps
+    s2 = sum(ev.elapsed_ms(e[2], e[3]) for e in evs) / args.steps if path == "key-major" else 0.0
+    for e in evs:
+        for x in e:
+            ev.destroy(x)
 
     ms_per_step = (t1 - t0) / args.steps * 1e3
-    kern_avg = sum(kern_ms) / len(kern_ms)
     per_row = valid_per_row(p)
     npairs = int(per_row.sum())
     nominal = p.rows * p.topk
     flops = npairs * p.N1 * FLOP_PER_PAIR_HEAD
     value = flops / (ms_per_step * 1e-3) / 1e12
-    achieved = flops / (kern_avg * 1e-3) / 1e12
-    gather_gbs = npairs * GATHER_BYTES_PER_PAIR / (kern_avg * 1e-3) / 1e9
-    scatter_gbs = npairs * SCATTER_BYTES_PER_PAIR / (kern_avg * 1e-3) / 1e9
+    if path == "key-major":
+        stages = {"bwd_q_kernel": (s1, FLOP_Q_KERNEL), "kv_dense_kernel": (s2, FLOP_KV_KERNEL)}
+    else:
+        stages = {("bwd_main_kernel<partial> + sort + reduce" if det else "bwd_main_kernel<atomic>"):
+                  (s1, FLOP_PER_PAIR_HEAD)}
+    kernel = max(stages, key=lambda n: stages[n][0])
+    kern_avg, kflop = stages[kernel]
+    achieved = npairs * p.N1 * kflop / (kern_avg * 1e-3) / 1e12
+    # logical gather rate (one bf16 key row per valid pair, read by the kernel that forms the
+    # scores) and scatter rate (one fp32 dK | dKRope | dV row per valid pair)
+    gather_ms = s1
+    scatter_ms = s2 if path == "key-major" else s1
+    gather_gbs = npairs * GATHER_BYTES_PER_PAIR / (gather_ms * 1e-3) / 1e9
+    scatter_gbs = npairs * SCATTER_BYTES_PER_PAIR / (scatter_ms * 1e-3) / 1e9
     rec = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -244,9 +263,13 @@ def main():
         "roofline": {
             "bound": "mfma", "achieved": round(achieved, 3), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 5),
-            "traffic": traffic_from_profile(p.name),
-            "kernel": "bwd_main_kernel" + ("<partial> + sort + reduce" if det else "<atomic>"),
+            "traffic": traffic_from_profile(kernel.split("<")[0], p.name),
+            "kernel": kernel,
             "kernel_ms": round(kern_avg, 4),
+            "kernel_flop_per_pair_head": kflop,
+            "path": path,
+            "stages_ms": {n: round(v[0], 4) for n, v in stages.items()},
+            "stages_tflops": {n: round(npairs * p.N1 * v[1] / (v[0] * 1e-3) / 1e12, 2) for n, v in stages.items()},
             "gather_logical_gbs": round(gather_gbs, 1),
             "gather_hbm_frac": round(gather_gbs / HBM_PEAK_GBS, 4),
             "scatter_logical_gbs": round(scatter_gbs, 1),

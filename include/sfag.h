@@ -134,13 +134,23 @@ sfag_status sfag_sparse_flash_attention_forward(
 
 /*
  * Instrumentation: until called again, every backward call made by this thread records
- * `before` (a hipEvent_t) on its stream right before the kernels that compute the key
- * gradients and `after` right after them (default mode: the single main kernel;
- * deterministic mode: the whole partial / sort / reduce sequence), so that a caller can
- * time them with hipEventElapsedTime.  Both NULL (the default) disables recording.  The
- * events stay owned by the caller.  Always returns SFAG_OK.
+ * the given hipEvent_t handles on its stream around its two main stages, so that a caller
+ * can time them with hipEventElapsedTime:
+ *   stage 1 (`s1_begin`, `s1_end`): key-major path: the query-major kernel (scores, dS, P,
+ *     dQ); scatter path: the whole main sequence (main kernel, and in deterministic mode
+ *     the partial / sort / ordered-reduce launches);
+ *   stage 2 (`s2_begin`, `s2_end`): key-major path only: the key-major dK / dV kernel.
+ * A NULL handle is not recorded.  All NULL (the default) disables recording.  The events
+ * stay owned by the caller.  Always returns SFAG_OK.
  */
-sfag_status sfag_set_profile_events(void* before, void* after);
+sfag_status sfag_set_profile_events(void* s1_begin, void* s1_end, void* s2_begin, void* s2_end);
+
+/*
+ * dK / dV path taken by the calling thread's last successful backward call: 0 = key-major
+ * dense-masked kernels, 1 = per-pair scatter (atomic or partials), -1 = no call yet.  The
+ * path follows from the shapes alone (see sfag_sparse_flash_attention_grad).
+ */
+int32_t sfag_last_path(void);
 
 /* Text of the calling thread's last non-OK status ("" if none). */
 const char* sfag_last_error(void);

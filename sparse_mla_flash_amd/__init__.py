@@ -31,7 +31,7 @@ SFAG_ERR_WORKSPACE = 161902
 SFAG_ERR_DEVICE = 161903
 
 EXPORTED = ("sfag_get_workspace_size", "sfag_sparse_flash_attention_grad",
-            "sfag_sparse_flash_attention_forward", "sfag_set_profile_events", "sfag_last_error",
+            "sfag_sparse_flash_attention_forward", "sfag_set_profile_events", "sfag_last_path", "sfag_last_error",
             "sfag_version")
 
 
@@ -74,7 +74,9 @@ def lib():
             ctypes.c_int64, ctypes.c_char_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
             vp, vp, vp, vp]
         L.sfag_set_profile_events.restype = ctypes.c_int
-        L.sfag_set_profile_events.argtypes = [vp, vp]
+        L.sfag_set_profile_events.argtypes = [vp, vp, vp, vp]
+        L.sfag_last_path.restype = ctypes.c_int32
+        L.sfag_last_path.argtypes = []
         L.sfag_last_error.restype = ctypes.c_char_p
         L.sfag_last_error.argtypes = []
         L.sfag_version.restype = ctypes.c_char_p
@@ -91,9 +93,14 @@ def sfag_version() -> str:
     return lib().sfag_version().decode()
 
 
-def sfag_set_profile_events(before, after) -> int:
-    """Record caller-owned hipEvent_t handles around the key-gradient kernels of later calls."""
-    return lib().sfag_set_profile_events(before, after)
+def sfag_set_profile_events(s1_begin=None, s1_end=None, s2_begin=None, s2_end=None) -> int:
+    """Record caller-owned hipEvent_t handles around the two main stages of later calls."""
+    return lib().sfag_set_profile_events(s1_begin, s1_end, s2_begin, s2_end)
+
+
+def sfag_last_path() -> int:
+    """0: key-major dense path, 1: scatter path, -1: no backward call yet (this thread)."""
+    return lib().sfag_last_path()
 
 
 def _check(status: int) -> None:

@@ -17,8 +17,8 @@
 namespace {
 
 thread_local std::string g_last_error;
-thread_local hipEvent_t g_ev_before = nullptr;
-thread_local hipEvent_t g_ev_after = nullptr;
+thread_local hipEvent_t g_ev[4] = {nullptr, nullptr, nullptr, nullptr};
+thread_local int32_t g_last_path = -1;
 
 sfag_status fail(sfag_status st, const char* fmt, ...) {
   char buf[512];
@@ -55,11 +55,11 @@ struct Plan {
   // path: key-major dense-masked dK / dV (dense = 1) or per-pair scatter (dense = 0)
   int dense = 0;
   double waste = 0.0;              // dense-masked (row, key) entries per valid pair (upper bound)
-  int64_t items = 0, maxblk = 0, np = 0;
+  int64_t items = 0, citems = 0, maxblk = 0, np = 0;
   // workspace layout
   uint64_t off_acc = 0, off_partial = 0, off_keys0 = 0, off_keys1 = 0, off_sorttmp = 0;
   uint64_t off_sorted = 0, off_count = 0, off_maxdup = 0, off_offs = 0, off_dsp = 0, off_part = 0, off_flag = 0;
-  uint64_t off_zero = 0;
+  uint64_t off_zero = 0, off_ilist = 0, off_imap = 0;
   uint64_t sort_tmp_bytes = 0, bytes = 0;
   int64_t det_rows = 0;            // query rows per deterministic launch
   int end_bit = 64;
@@ -199,6 +199,23 @@ sfag_status make_plan(const sfag_dims* dims, const int32_t* sq, const int32_t* s
     }
     p->items = items;
     p->maxblk = maxblk;
+    // live items: the key blocks of a row segment that the causal mask leaves reachable form a
+    // prefix of the segment's blocks (same rule as the device-side list)
+    int64_t citems = 0;
+    for (int64_t b = 0; b < p->B; ++b) {
+      const int64_t lq = p->lens.lq[b], lkv = p->lens.lkv[b];
+      const int64_t nblk = (lkv + sfag::kBk - 1) / sfag::kBk, nseg = (lq + sfag::kSegRows - 1) / sfag::kSegRows;
+      for (int64_t seg = 0; seg < nseg; ++seg) {
+        if (!p->mode3) {
+          citems += nblk;
+          continue;
+        }
+        const int64_t i1 = std::min(lq, (seg + 1) * sfag::kSegRows);
+        const int64_t hi = i1 - 1 + lkv - lq;     // last key reachable from the segment
+        if (hi >= 0) citems += std::min(nblk, hi / sfag::kBk + 1);
+      }
+    }
+    p->citems = citems;
     p->np = (int64_t)next_pow2((uint64_t)p->topk);
     const uint64_t pairs = (uint64_t)p->rows * p->topk;
     p->off_sorted = off;
@@ -212,9 +229,13 @@ sfag_status make_plan(const sfag_dims* dims, const int32_t* sq, const int32_t* s
     p->off_dsp = off;
     off = align_up(off + pairs * p->hg_count * 128 * 2);
     p->off_part = off;
-    off = align_up(off + (uint64_t)p->hg_count * items * sfag::kBk * kDacc * 4);
+    off = align_up(off + (uint64_t)p->hg_count * citems * sfag::kBk * kDacc * 4);
     p->off_flag = off;
-    off = align_up(off + (uint64_t)p->hg_count * std::max<int64_t>(items, 1) * 4);
+    off = align_up(off + (uint64_t)p->hg_count * std::max<int64_t>(citems, 1) * 4);
+    p->off_ilist = off;
+    off = align_up(off + (uint64_t)std::max<int64_t>(citems, 1) * 4);
+    p->off_imap = off;
+    off = align_up(off + (uint64_t)std::max<int64_t>(items, 1) * 4);
     p->off_zero = off;
     off = align_up(off + 576 * 2);
     p->bytes = off;
@@ -284,11 +305,15 @@ const char* sfag_last_error(void) { return g_last_error.c_str(); }
 
 const char* sfag_version(void) { return "sfag-mi355x 0.1 (gfx950)"; }
 
-sfag_status sfag_set_profile_events(void* before, void* after) {
-  g_ev_before = reinterpret_cast<hipEvent_t>(before);
-  g_ev_after = reinterpret_cast<hipEvent_t>(after);
+sfag_status sfag_set_profile_events(void* s1_begin, void* s1_end, void* s2_begin, void* s2_end) {
+  g_ev[0] = reinterpret_cast<hipEvent_t>(s1_begin);
+  g_ev[1] = reinterpret_cast<hipEvent_t>(s1_end);
+  g_ev[2] = reinterpret_cast<hipEvent_t>(s2_begin);
+  g_ev[3] = reinterpret_cast<hipEvent_t>(s2_end);
   return ok();
 }
+
+int32_t sfag_last_path(void) { return g_last_path; }
 
 sfag_status sfag_get_workspace_size(const sfag_dims* dims, const int32_t* seq_len_q_host,
                                     const int32_t* seq_len_kv_host, float scale_value,
@@ -396,6 +421,9 @@ sfag_status sfag_sparse_flash_attention_grad(
     da.hgc = p.hg_count;
     da.maxblk = (int)p.maxblk;
     da.items = (int)p.items;
+    da.citems = (int)p.citems;
+    da.ilist = reinterpret_cast<int32_t*>(ws + p.off_ilist);
+    da.imap = reinterpret_cast<int32_t*>(ws + p.off_imap);
     da.scale = scale_value;
     a.sorted = da.sorted;
     a.count = da.count;
@@ -403,16 +431,20 @@ sfag_status sfag_sparse_flash_attention_grad(
     a.zero_row = da.zero_row;
     a.row_begin = 0;
     a.pairs_per_launch = 0;
+    SFAG_HIP(sfag::launch_item_list(da, s));
     SFAG_HIP(sfag::launch_sort_rows(da, p.rows, (int)p.np, s));
+    if (g_ev[0]) SFAG_HIP(hipEventRecord(g_ev[0], s));
     SFAG_HIP(sfag::launch_bwd_q(a, p.rows, p.hg_count, s));
-    if (g_ev_before) SFAG_HIP(hipEventRecord(g_ev_before, s));
+    if (g_ev[1]) SFAG_HIP(hipEventRecord(g_ev[1], s));
+    if (g_ev[2]) SFAG_HIP(hipEventRecord(g_ev[2], s));
     SFAG_HIP(sfag::launch_kv_dense(da, s));
-    if (g_ev_after) SFAG_HIP(hipEventRecord(g_ev_after, s));
+    if (g_ev[3]) SFAG_HIP(hipEventRecord(g_ev[3], s));
     SFAG_HIP(sfag::launch_kv_reduce(da, p.keys, s));
+    g_last_path = 0;
     return ok();
   }
 
-  if (g_ev_before) SFAG_HIP(hipEventRecord(g_ev_before, s));
+  if (g_ev[0]) SFAG_HIP(hipEventRecord(g_ev[0], s));
   if (!p.det) {
     a.row_begin = 0;
     a.pairs_per_launch = 0;
@@ -432,9 +464,10 @@ sfag_status sfag_sparse_flash_attention_grad(
       SFAG_HIP(sfag::launch_det_reduce(k1, nr * p.topk, a.partial, nr * p.topk, p.hg_count, acc, p.keys, s));
     }
   }
-  if (g_ev_after) SFAG_HIP(hipEventRecord(g_ev_after, s));
+  if (g_ev[1]) SFAG_HIP(hipEventRecord(g_ev[1], s));
   SFAG_HIP(sfag::launch_cast(acc, static_cast<uint16_t*>(d_key), static_cast<uint16_t*>(d_key_rope),
                              static_cast<uint16_t*>(d_value), p.keys, s));
+  g_last_path = 1;
   return ok();
 }
 

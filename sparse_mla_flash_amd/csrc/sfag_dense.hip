@@ -123,10 +123,62 @@ __global__ void __launch_bounds__(kThreads) sort_rows_kernel(DenseArgs a, int np
 }
 
 // ------------------------------------------------------------------------------------------
-// Workgroup = (item, column slice, head group).  Items are numbered per batch segment-major
-// (item = segment * blocks + block).  The linear workgroup id w is mapped so that the 8
-// column slices of one item run on the same XCD (w % 8) and consecutive items of one segment
-// share that XCD's L2 for the row data: x = w % 8, slice = (w / 8) % 8, item = 8 (w / 64) + x.
+// Live items: items (key block x row segment, numbered per batch segment-major: item =
+// segment * blocks + block) that the causal mask does not rule out, listed in item order.
+// imap[item] = position in the list or -1.  One workgroup; the host computes the same count.
+__global__ void __launch_bounds__(1024) item_list_kernel(DenseArgs a) {
+  __shared__ int32_t cum[2 * 257];
+  __shared__ int32_t ibase[257];
+  __shared__ int32_t wcount[16];
+  __shared__ int32_t s_base;
+  item_tables(a.lens, a.B, a.layout_tnd, a.S1, a.S2, cum, ibase);
+  if (threadIdx.x == 0) s_base = 0;
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int t0 = 0; t0 < a.items; t0 += 1024) {
+    const int t = t0 + threadIdx.x;
+    bool live = false;
+    if (t < a.items) {
+      int lo = 0, hi = a.B - 1;           // last batch whose first item is <= t
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (ibase[mid] <= t) lo = mid; else hi = mid - 1;
+      }
+      const int b = lo;
+      const int lq = a.lens.lq[b], lkv = a.lens.lkv[b];
+      const int nblk = (lkv + kBk - 1) / kBk;
+      const int local = t - ibase[b];
+      const int seg = local / nblk, lb = local % nblk;
+      const int i1 = min(lq, (seg + 1) * kSegRows);
+      live = !(a.mode3 && (i1 - 1) + lkv - lq < lb * kBk);
+    }
+    const uint64_t m = __ballot(live);
+    const int below = __popcll(m & ((1ull << lane) - 1ull));
+    if (lane == 0) wcount[wave] = __popcll(m);
+    __syncthreads();
+    int base = s_base;
+    for (int w = 0; w < wave; ++w) base += wcount[w];
+    if (t < a.items) {
+      const int k = live ? base + below : -1;
+      a.imap[t] = k < a.citems ? k : -1;
+      if (live && k < a.citems) a.ilist[k] = t;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int tot = 0;
+      for (int w = 0; w < 16; ++w) tot += wcount[w];
+      s_base += tot;
+    }
+    __syncthreads();
+  }
+}
+
+// Workgroup = (live item, column slice, head group).  Workgroups are dealt to the 8 XCDs
+// round-robin (x = w % 8), so XCD x is given the contiguous run of live items
+// [x n, x n + n) and walks it as  half (dK slices, then dV slices) > item > slice: the ~32
+// workgroups resident on one XCD are then 8 neighbouring key blocks of one row segment x the
+// 4 column slices of one half, which share the segment's Q / dO rows and dS / P records in
+// that XCD's L2.
 // Column slices 0..3: dK columns 144 s .. 144 s + 143 (the last one holds the rope columns);
 // 4..7: dV columns 128 (s - 4) .. + 127.  Wave w owns key tiles 4w .. 4w + 3 (64 keys).
 //
@@ -149,10 +201,15 @@ __global__ void __launch_bounds__(kThreads, 1) kv_dense_kernel(DenseArgs a) {
   __shared__ uint8_t s_dup[kSegCap];
 
   const int w = blockIdx.x;
-  const int item = 8 * (w >> 6) + (w & 7);
-  const int sl = (w >> 3) & 7;
+  const int xcd = w & 7, j = w >> 3;
+  const int per_xcd = (a.citems + 7) >> 3;
+  const int half = j / (4 * per_xcd), r = j - half * 4 * per_xcd;
+  const int citem = xcd * per_xcd + (r >> 2);
+  const int sl = 4 * half + (r & 3);
   const int hg = blockIdx.y;
-  if (item >= a.items) return;
+  if (half >= 2 || citem >= a.citems) return;
+  const int item = a.ilist[citem];
+  if (item < 0 || item >= a.items) return;     // host and device agree on the live count
   item_tables(a.lens, a.B, a.layout_tnd, a.S1, a.S2, cum, ibase);
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -169,7 +226,7 @@ __global__ void __launch_bounds__(kThreads, 1) kv_dense_kernel(DenseArgs a) {
   const int kb0 = lb * kBk;
   const int64_t qstart = cum[b];
   const int i0 = seg * kSegRows, i1 = min(lq, i0 + kSegRows);
-  int32_t* flag = a.flag + (int64_t)hg * a.items + item;
+  int32_t* flag = a.flag + (int64_t)hg * a.citems + citem;
   if (a.mode3 && (i1 - 1) + lkv - lq < kb0) {
     if (threadIdx.x == 0) *flag = 0;
     return;
@@ -406,7 +463,7 @@ __global__ void __launch_bounds__(kThreads, 1) kv_dense_kernel(DenseArgs a) {
     return;
   }
   const float mul = isdk ? a.scale : 1.f;
-  float* part = a.part + ((int64_t)hg * a.items + item) * (int64_t)kBk * kDacc;
+  float* part = a.part + ((int64_t)hg * a.citems + citem) * (int64_t)kBk * kDacc;
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
@@ -448,7 +505,8 @@ __global__ void __launch_bounds__(kThreads) kv_reduce_kernel(DenseArgs a) {
   if (live)
     for (int t = threadIdx.x; t < a.hgc * nseg; t += kThreads) {
       const int hg = t / nseg, seg = t % nseg;
-      fl[t] = a.flag[(int64_t)hg * a.items + ibase[b] + seg * nblk + lb];
+      const int ci = a.imap[ibase[b] + seg * nblk + lb];
+      fl[t] = (ci >= 0 && a.flag[(int64_t)hg * a.citems + ci]) ? ci : -1;
     }
   __syncthreads();
   for (int col = threadIdx.x; col < kDacc; col += kThreads) {
@@ -456,9 +514,9 @@ __global__ void __launch_bounds__(kThreads) kv_reduce_kernel(DenseArgs a) {
     if (live)
       for (int hg = 0; hg < a.hgc; ++hg)
         for (int seg = 0; seg < nseg; ++seg) {
-          if (!fl[hg * nseg + seg]) continue;
-          const int64_t it = ibase[b] + seg * nblk + lb;
-          s += a.part[(((int64_t)hg * a.items + it) * kBk + kr) * kDacc + col];
+          const int ci = fl[hg * nseg + seg];
+          if (ci < 0) continue;
+          s += a.part[(((int64_t)hg * a.citems + ci) * kBk + kr) * kDacc + col];
         }
     const uint16_t v = f2bf(s);
     if (col < kDn) a.dk[krow * kDn + col] = v;
@@ -473,10 +531,16 @@ hipError_t launch_sort_rows(const DenseArgs& a, int64_t rows, int np, hipStream_
   return hipGetLastError();
 }
 
-hipError_t launch_kv_dense(const DenseArgs& a, hipStream_t st) {
+hipError_t launch_item_list(const DenseArgs& a, hipStream_t st) {
   if (a.items == 0) return hipSuccess;
-  const unsigned groups = (unsigned)((a.items + 7) / 8);   // 8 items x 8 slices per group
-  hipLaunchKernelGGL(kv_dense_kernel, dim3(groups * 64, (unsigned)a.hgc), dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL(item_list_kernel, dim3(1), dim3(1024), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_dense(const DenseArgs& a, hipStream_t st) {
+  if (a.citems == 0) return hipSuccess;
+  const unsigned per_xcd = (unsigned)((a.citems + 7) / 8);   // 8 XCDs x per_xcd items x 8 slices
+  hipLaunchKernelGGL(kv_dense_kernel, dim3(per_xcd * 64, (unsigned)a.hgc), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 

@@ -52,15 +52,17 @@ struct DenseArgs {
   int32_t* maxdup;        // [rows]
   int32_t* offs;          // [rows, maxblk + 1]
   const uint16_t* dsp;    // [rows * topk, hgc, 128]
-  float* part;            // [hgc, items, kBk, 1088]
-  int32_t* flag;          // [hgc, items]
+  float* part;            // [hgc, citems, kBk, 1088]
+  int32_t* flag;          // [hgc, citems]
+  int32_t* ilist;         // [citems] live item -> item (key block x row segment)
+  int32_t* imap;          // [items]  item -> live item, -1 when the causal mask rules it out
   uint16_t* zero_row;     // 576 bf16, zeroed by the sort kernel
   uint16_t* dk;           // [keys, 512]
   uint16_t* dkr;          // [keys, 64]
   uint16_t* dv;           // [keys, 512]
   Lens lens;
   int64_t S1, S2;
-  int B, N1, topk, mode3, layout_tnd, hgc, maxblk, items;
+  int B, N1, topk, mode3, layout_tnd, hgc, maxblk, items, citems;
   float scale;
 };
 
@@ -102,6 +104,7 @@ size_t sort_temp_bytes(int64_t n, int end_bit);
 hipError_t launch_bwd_q(const BwdArgs& a, int64_t nrows, int hg_count, hipStream_t st);
 hipError_t set_q_attributes();
 hipError_t launch_sort_rows(const DenseArgs& a, int64_t rows, int np, hipStream_t st);
+hipError_t launch_item_list(const DenseArgs& a, hipStream_t st);
 hipError_t launch_kv_dense(const DenseArgs& a, hipStream_t st);
 hipError_t launch_kv_reduce(const DenseArgs& a, int64_t keys, hipStream_t st);
 hipError_t set_dense_attributes();

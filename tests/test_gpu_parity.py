@@ -104,8 +104,9 @@ def test_slot_permutation_invariance(path):
     case2 = Case(p)
     b = [from_dev(t) for t in case2.run_gpu()]
     for x, y in zip(a, b):
-        # only the order of fp32 accumulation changes
-        assert np.abs(x - y).max() <= 2e-2
+        # only the order of fp32 accumulation changes: a few bf16 rounding flips, each one
+        # ulp (2^-7 relative) of the output's magnitude
+        assert (np.abs(x - y) <= 2e-2 * np.maximum(1.0, np.abs(x))).all()
 
 
 @pytest.mark.parametrize("name", ["bsnd_n64_short_prefix", "tnd_n16_varlen_empty_seq", "bsnd_n128_nomask",
