@@ -127,12 +127,6 @@ class Problem:
 # index patterns
 # ---------------------------------------------------------------------------
 
-def _distinct(rng: np.random.Generator, lo: int, hi: int, k: int) -> np.ndarray:
-    """k distinct integers drawn uniformly from [lo, hi], in random order."""
-    n = hi - lo + 1
-    return (rng.choice(n, size=k, replace=False) + lo).astype(np.int64)
-
-
 def _causal_hi(p: Problem, b: int, i: int) -> int:
     """Largest key position a query at row i of batch b may select (-1: none)."""
     lkv = p.lkv(b)
@@ -141,48 +135,64 @@ def _causal_hi(p: Problem, b: int, i: int) -> int:
     return lkv - 1
 
 
-def _row_uniform(p: Problem, rng, b: int, i: int) -> np.ndarray:
-    """Distinct uniform over the valid range; short ranges take all keys, -1 padded."""
-    out = np.full(p.topk, -1, dtype=np.int64)
-    hi = _causal_hi(p, b, i)
-    if hi < 0:
-        return out
-    n = hi + 1
-    if n <= p.topk:
-        out[:n] = rng.permutation(n)
-    else:
-        out[:] = _distinct(rng, 0, hi, p.topk)
+def _distinct_rows(rng, n: np.ndarray, k: int, group: int = 32) -> np.ndarray:
+    """Row r: k distinct integers uniform over [0, n[r]) (n[r] >= k), in random order.
+
+    The k smallest of n[r] independent uniform sort keys sit at a uniformly random k-subset of
+    positions; a second set of keys shuffles them.  Rows are drawn in groups as one matrix."""
+    out = np.empty((len(n), k), dtype=np.int64)
+    for g0 in range(0, len(n), group):
+        ng = n[g0:g0 + group]
+        u = rng.random((len(ng), int(ng.max())))
+        u[np.arange(u.shape[1])[None, :] >= ng[:, None]] = 2.0      # outside the row's range
+        sel = np.argpartition(u, k - 1, axis=1)[:, :k]
+        order = np.argsort(rng.random((len(ng), k)), axis=1)
+        out[g0:g0 + group] = np.take_along_axis(sel, order, axis=1)
     return out
 
 
-def _row_window(p: Problem, rng, b: int, i: int, window: int) -> np.ndarray:
-    """Half from the local window [pos-window+1, pos], half uniform over the rest."""
-    out = np.full(p.topk, -1, dtype=np.int64)
-    hi = _causal_hi(p, b, i)
-    if hi < 0:
-        return out
+def _rows_uniform(p: Problem, rng, b: int) -> np.ndarray:
+    """Per query row: distinct uniform keys over the valid range; short ranges take all keys in
+    random order; -1 padded."""
+    lq = p.lq(b)
+    out = np.full((lq, p.topk), -1, dtype=np.int64)
+    n = np.array([_causal_hi(p, b, i) + 1 for i in range(lq)], dtype=np.int64)
+    for i in np.nonzero((n > 0) & (n <= p.topk))[0]:
+        out[i, :n[i]] = rng.permutation(int(n[i]))
+    long_rows = np.nonzero(n > p.topk)[0]
+    if len(long_rows):
+        out[long_rows] = _distinct_rows(rng, n[long_rows], p.topk)
+    return out
+
+
+def _rows_window(p: Problem, rng, b: int, window: int) -> np.ndarray:
+    """Per query row: half the slots distinct uniform from the local window [pos-window+1, pos],
+    the other half distinct uniform over the rest of [0, pos]; short ranges take all keys."""
+    lq = p.lq(b)
+    out = np.full((lq, p.topk), -1, dtype=np.int64)
+    hi = np.array([_causal_hi(p, b, i) for i in range(lq)], dtype=np.int64)
     n = hi + 1
-    if n <= p.topk:
-        out[:n] = rng.permutation(n)
+    for i in np.nonzero((n > 0) & (n <= p.topk))[0]:
+        out[i, :n[i]] = rng.permutation(int(n[i]))
+    rows = np.nonzero(n > p.topk)[0]
+    if not len(rows):
         return out
     half = p.topk // 2
-    wlo = max(0, hi - window + 1)
-    wn = hi - wlo + 1
-    loc = _distinct(rng, wlo, hi, min(half, wn))
-    need = p.topk - len(loc)
-    chosen = set(loc.tolist())
-    far: list = []
-    # rejection sampling over [0, hi] minus what the window already holds
-    while len(far) < need:
-        cand = rng.integers(0, n, size=2 * (need - len(far)) + 16)
-        for c in cand.tolist():
-            if c not in chosen:
-                chosen.add(c)
-                far.append(c)
-                if len(far) == need:
-                    break
-    sel = np.concatenate([loc, np.asarray(far, dtype=np.int64)])
-    out[:] = sel[rng.permutation(len(sel))]
+    wlo = np.maximum(0, hi[rows] - window + 1)
+    wn = hi[rows] - wlo + 1
+    loc_k = int(min(half, wn.min()))
+    loc = _distinct_rows(rng, wn, loc_k) + wlo[:, None]
+    for r, i in enumerate(rows):
+        need = p.topk - loc_k
+        picked = np.empty(0, dtype=np.int64)
+        while len(picked) < need:
+            cand = rng.integers(0, n[i], size=2 * (need - len(picked)) + 64)
+            _, first = np.unique(cand, return_index=True)
+            cand = cand[np.sort(first)]                                 # first draws, in draw order
+            cand = cand[~np.isin(cand, loc[r]) & ~np.isin(cand, picked)]
+            picked = np.concatenate([picked, cand[:need - len(picked)]])
+        sel = np.concatenate([loc[r], picked])
+        out[i] = sel[rng.permutation(len(sel))]
     return out
 
 
@@ -215,15 +225,13 @@ def _indices(p: Problem, rng: np.random.Generator, kind: str, window: int) -> np
         base = p.q_offset(b)
         if kind == "hot_cold":
             r = _rows_hot_cold(p, rng, b)
-            idx[base: base + r.shape[0]] = r
-            continue
-        for i in range(p.lq(b)):
-            if kind == "uniform":
-                idx[base + i] = _row_uniform(p, rng, b, i)
-            elif kind == "window":
-                idx[base + i] = _row_window(p, rng, b, i, window)
-            else:
-                raise ValueError(f"unknown index kind {kind!r}")
+        elif kind == "uniform":
+            r = _rows_uniform(p, rng, b)
+        elif kind == "window":
+            r = _rows_window(p, rng, b, window)
+        else:
+            raise ValueError(f"unknown index kind {kind!r}")
+        idx[base: base + r.shape[0]] = r
     return idx.astype(np.int32)
 
 
