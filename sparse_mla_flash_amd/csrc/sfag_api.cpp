@@ -59,7 +59,7 @@ struct Plan {
   // workspace layout
   uint64_t off_acc = 0, off_partial = 0, off_keys0 = 0, off_keys1 = 0, off_sorttmp = 0;
   uint64_t off_sorted = 0, off_count = 0, off_maxdup = 0, off_offs = 0, off_dsp = 0, off_part = 0, off_flag = 0;
-  uint64_t off_zero = 0, off_ilist = 0, off_imap = 0;
+  uint64_t off_zero = 0, off_ilist = 0, off_imap = 0, off_trash = 0;
   uint64_t sort_tmp_bytes = 0, bytes = 0;
   int64_t det_rows = 0;            // query rows per deterministic launch
   int end_bit = 64;
@@ -238,6 +238,8 @@ sfag_status make_plan(const sfag_dims* dims, const int32_t* sq, const int32_t* s
     off = align_up(off + (uint64_t)std::max<int64_t>(items, 1) * 4);
     p->off_zero = off;
     off = align_up(off + 576 * 2);
+    p->off_trash = off;                 // write-only sink for the records of invalid slots
+    off = align_up(off + 128 * 2);
     p->bytes = off;
     return SFAG_OK;
   }
@@ -429,6 +431,7 @@ sfag_status sfag_sparse_flash_attention_grad(
     a.count = da.count;
     a.dsp = reinterpret_cast<uint16_t*>(ws + p.off_dsp);
     a.zero_row = da.zero_row;
+    a.trash = reinterpret_cast<uint16_t*>(ws + p.off_trash);
     a.row_begin = 0;
     a.pairs_per_launch = 0;
     SFAG_HIP(sfag::launch_item_list(da, s));

@@ -94,6 +94,19 @@ __device__ __forceinline__ bf16x8 lds_frag_trp(const uint16_t* tile, int k0, int
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// Workgroup barrier for data exchanged through LDS by ds_write / ds_read only: waits for this
+// wave's LDS instructions (lgkmcnt(0); vmcnt and expcnt left at their maximum) but, unlike
+// __syncthreads(), not for global loads, stores or direct-to-LDS loads still in flight.  The
+// caller guarantees that no LDS location read after it is the target of a direct-to-LDS load
+// still in flight.  The empty asm statements keep the compiler from moving memory accesses
+// across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ uint16_t f2bf(float f) {
   // round to nearest even; NaN stays NaN
   uint32_t u = __float_as_uint(f);
@@ -103,6 +116,14 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
 }
 
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Two floats rounded to nearest even bf16 by the hardware conversion (v_cvt_pk_bf16_f32), lo in
+// bits 0..15.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
 
 // Geometry of one query row.  BSND: batch b = row / S1, keys of batch b start at b * S2.
 // TND: `cum` (LDS, filled by cum_lengths) holds the first query row of every sequence in

@@ -33,6 +33,7 @@ struct BwdArgs {
   const int32_t* count;   // [rows] number of valid positions (key-major mode)
   uint16_t* dsp;          // [rows * topk, head groups, 128] bf16 dS | P per pair (key-major mode)
   const uint16_t* zero_row;  // 576 zero bf16 (key-major mode: source of padding slots)
+  uint16_t* trash;        // 128 bf16 write-only sink (key-major mode: records of invalid slots)
   Lens lens;
   int64_t S1;             // BSND S1 / TND T1 (statistics head stride)
   int64_t S2;             // BSND S2 / TND T2

@@ -10,10 +10,18 @@
 // key-major kernel that forms dK = scale dS^T Q and dV = P^T dO (SparseFlashAttentionGrad
 // README, "function description", stages 1-3).
 //
-// Pipeline: the gathered key chunk is double-buffered in LDS.  While chunk c is multiplied,
-// the K rows of chunk c+1 stream from global memory directly into the other buffer
-// (global_load_lds; their key rows were staged in LDS one chunk earlier); two barriers per
-// chunk.
+// Work split of the 4 waves (an LDS read of up to 16 bytes per lane costs the same LDS time,
+// and a transposing read delivers only 8, so the split minimises LDS reads per MFMA):
+//   scores: wave (hh, dh) = (wave / 2, wave % 2) owns heads 32 hh .. 32 hh + 31 and half of
+//     the contraction: value dims 256 dh .. 256 dh + 255 and rope dims 32 dh .. 32 dh + 31.
+//     Its Q and dO fragments stay in registers for the whole row, so every 16-byte key
+//     fragment read from LDS feeds four MFMAs.  The two waves of a head half swap the
+//     partial sums of the key tile the other one finishes (16 keys) through LDS.
+//   dQ: wave w owns output dims 144 w .. 144 w + 143 for all 64 heads, so each gathered key
+//     element is read (transposed) once per workgroup.
+// Pipeline: key chunks are triple-buffered in LDS and gathered straight from global memory
+// one chunk ahead (global_load_lds).  The score MFMAs of chunk c and the dQ MFMAs of chunk
+// c - 1 sit in one block so that the scheduler can interleave them; two barriers per chunk.
 #include "sfag_device.h"
 #include "sfag_launch.h"
 
@@ -22,37 +30,42 @@ namespace sfag {
 namespace {
 constexpr int kKC = 32;
 constexpr int kThreads = 256;
-constexpr int kPitch = kDk + 8;                  // 584: padded row of Q / key tiles
+constexpr int kPitch = kDk + 8;                  // 584: padded key row (conflict-free 16-byte reads)
 constexpr int kRowChunks = kPitch / 8;           // 73 16-byte chunks per padded row
 constexpr int kHtPitch = 64 + 8;                 // DSt row pitch
-constexpr int kBlocks = (kKC * kRowChunks + 63) / 64;   // 37 blocks of 64 chunks per key tile
+constexpr int kBlocks = 40;                      // 64-chunk blocks per key tile: 37 hold data,
+                                                 // padded to 10 per wave (the rest load zeros)
+static_assert(kBlocks * 64 >= kKC * kRowChunks && kBlocks % 4 == 0, "gather blocks");
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kLdsQ = 64 * kPitch * 2;           // Qs [64 heads][584]
 constexpr int kLdsK = kBlocks * 64 * 16;         // one key chunk [32][584], rounded to whole blocks
-constexpr int kLdsHT = kKC * kHtPitch * 2;       // DSt [32 keys][72]
-constexpr int kLdsTotal = kLdsQ + 2 * kLdsK + kLdsHT + 3 * kKC * 8 + 3 * 64 * 4 + 2 * 257 * 4;
+constexpr int kLdsDS = kKC * kHtPitch * 2;       // DSt [32 keys][72]
+constexpr int kLdsX = 4 * 4 * 64 * 16;           // partial-sum exchange: [wave][4 tiles][64 lanes] f32x4
+constexpr int kLdsTotal = 3 * kLdsK + 3 * kLdsDS + kLdsX + 3 * kKC * 8 + 3 * 64 * 4 + 2 * 257 * 4;
 static_assert(kLdsTotal <= 160 * 1024, "LDS budget");
+// s_waitcnt operand: vmcnt(4), expcnt and lgkmcnt at their maximum.  Vector memory operations
+// complete in issue order, so this waits for all but the 4 most recent (the record stores).
+constexpr int kWaitAllButRecords = 0x0f74;
 }  // namespace
 
 __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  uint16_t* Qs = reinterpret_cast<uint16_t*>(smem);
-  uint16_t* Ks0 = reinterpret_cast<uint16_t*>(smem + kLdsQ);
-  uint16_t* Ks1 = reinterpret_cast<uint16_t*>(smem + kLdsQ + kLdsK);
-  uint16_t* DSt = reinterpret_cast<uint16_t*>(smem + kLdsQ + 2 * kLdsK);
-  int64_t* krow3 = reinterpret_cast<int64_t*>(smem + kLdsQ + 2 * kLdsK + kLdsHT);   // [3][32]
-  float* sD = reinterpret_cast<float*>(krow3 + 3 * kKC);
-  float* sM = sD + 64;
-  float* sIL = sM + 64;
-  int32_t* cum = reinterpret_cast<int32_t*>(sIL + 64);
+  // Separate LDS arrays (not one carved buffer): the compiler can then prove that the
+  // direct-to-LDS gather into one key buffer does not alias reads of the others, and does not
+  // wait for the gather before every LDS read.
+  __shared__ __attribute__((aligned(16))) uint16_t Kb0[kLdsK / 2], Kb1[kLdsK / 2], Kb2[kLdsK / 2];
+  __shared__ __attribute__((aligned(16))) uint16_t Db0[kKC * kHtPitch], Db1[kKC * kHtPitch], Db2[kKC * kHtPitch];
+  __shared__ __attribute__((aligned(16))) f32x4 X[4 * 4 * 64];        // partial-sum exchange [wave][4][64]
+  __shared__ int64_t krow3[3 * kKC];                                  // key rows of 3 chunks
+  __shared__ float sD[64], sM[64], sIL[64];
+  __shared__ int32_t cum[2 * 257];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, c = lane & 15;
-  const int64_t row = blockIdx.x;
+  const int hh = wave >> 1, dh = wave & 1;
+  // longest rows (highest positions under the causal mask) first
+  const int64_t row = (int64_t)gridDim.x - 1 - blockIdx.x;
   const int hg = blockIdx.y;
   const int h0 = hg * 64;
   const int nh = min(64, a.N1 - h0);
-  const int ntile = (nh + 15) >> 4;
   if (a.layout_tnd) {
     cum_lengths(a.lens, a.B, cum);
     __syncthreads();
@@ -67,17 +80,13 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
   const int32_t* srow = a.sorted + row * a.topk;
   const int nchunk = (count + kKC - 1) / kKC;
 
-  // ---- per-row setup: Q tile, statistics, D = rowsum(dO * out) ---------------------------
-  for (int cc = threadIdx.x; cc < 64 * (kDk / 8); cc += kThreads) {
-    const int h = cc / (kDk / 8), part = cc % (kDk / 8);
-    u32x4 v = u32x4{0u, 0u, 0u, 0u};
-    if (h < nh) {
-      const int64_t hh = row * a.N1 + h0 + h;
-      v = part < 64 ? *reinterpret_cast<const u32x4*>(a.q + hh * kDn + part * 8)
-                    : *reinterpret_cast<const u32x4*>(a.qr + hh * kDr + (part - 64) * 8);
-    }
-    *reinterpret_cast<u32x4*>(Qs + h * kPitch + part * 8) = v;
+  // ---- per-row setup --------------------------------------------------------------------------
+  // key rows of chunks 0 and 1
+  if (threadIdx.x < 2 * kKC) {
+    const int e = threadIdx.x;
+    krow3[e] = e < count ? geo.kstart + srow[e] : -1;
   }
+  // D = rowsum(dO * out) and the statistics of every head
   {
     const int h = threadIdx.x >> 2, part = threadIdx.x & 3;
     float d = 0.f;
@@ -109,38 +118,38 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
       sIL[h] = il;
     }
   }
-  // dO A fragments for this wave's head tile, staged through the key buffers
-  bf16x8 doA[16];
+  // Q and dO fragments of this wave, straight from global memory (A operands of S and dP:
+  // lane (g, c) holds head 16 ht + c, dims d0 + 8 g .. d0 + 8 g + 7); zero for padded heads
+  bf16x8 qA[2][9], doA[2][8];
 #pragma unroll
-  for (int ks = 0; ks < 16; ++ks) doA[ks] = bf16x8{};
-  {
-    uint16_t* stage = Ks0;   // 64 x 584 elements span both key buffers
-    for (int cc = threadIdx.x; cc < 64 * 64; cc += kThreads) {
-      const int h = cc >> 6, part = cc & 63;
-      u32x4 v = u32x4{0u, 0u, 0u, 0u};
-      if (h < nh) v = *reinterpret_cast<const u32x4*>(a.dout + (row * a.N1 + h0 + h) * kDn + part * 8);
-      *reinterpret_cast<u32x4*>(stage + h * kPitch + part * 8) = v;
-    }
-    __syncthreads();
-    if (wave < ntile) {
+  for (int ht = 0; ht < 2; ++ht) {
+    const int h = 32 * hh + 16 * ht + c;
+    const bool hv = h < nh;
+    const int64_t hrow = row * a.N1 + h0 + (hv ? h : 0);
+    const uint16_t* qrow = a.q + hrow * kDn + 256 * dh + 8 * g;
+    const uint16_t* drow = a.dout + hrow * kDn + 256 * dh + 8 * g;
 #pragma unroll
-      for (int ks = 0; ks < 16; ++ks) doA[ks] = lds_read8p(stage, 16 * wave + c, 32 * ks + 8 * g, kPitch);
+    for (int ks = 0; ks < 8; ++ks) {
+      const bf16x8 qv = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
+      const bf16x8 dv = *reinterpret_cast<const bf16x8*>(drow + 32 * ks);
+      qA[ht][ks] = hv ? qv : bf16x8{};
+      doA[ht][ks] = hv ? dv : bf16x8{};
     }
-  }
-  // key rows of chunks 0 and 1
-  if (threadIdx.x < 2 * kKC) {
-    const int e = threadIdx.x;
-    krow3[e] = e < count ? geo.kstart + srow[e] : -1;
+    const bf16x8 rv = *reinterpret_cast<const bf16x8*>(a.qr + hrow * kDr + 32 * dh + 8 * g);
+    qA[ht][8] = hv ? rv : bf16x8{};
   }
   __syncthreads();
-  float mrow[4], ilrow[4], drow[4];
+  // statistics of the 8 (head, key-tile) values this lane finishes: heads 32 hh + 16 ht + 4 g + v
+  float mrow[2][4], ilrow[2][4], drow_[2][4];
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int h = (16 * wave + 4 * g + v) & 63;
-    mrow[v] = sM[h];
-    ilrow[v] = sIL[h];
-    drow[v] = sD[h];
-  }
+  for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int h = 32 * hh + 16 * ht + 4 * g + v;
+      mrow[ht][v] = sM[h];
+      ilrow[ht][v] = sIL[h];
+      drow_[ht][v] = sD[h];
+    }
   const float zscale = a.scale * kLog2e;
 
   // Gather of one 32-key chunk straight from global memory into a key buffer: the buffer is
@@ -149,134 +158,193 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
   // Padding positions and slots past the row's valid count read the zero row.
 #define SFAG_GATHER_ASYNC(KS, KR)                                                              \
   {                                                                                            \
-    for (int blk = wave; blk < kBlocks; blk += 4) {                                            \
+    int64_t r_[kBlocks / 4];                                                                   \
+    _Pragma("unroll") for (int i = 0; i < kBlocks / 4; ++i) {                                  \
+      const int P = (wave + 4 * i) * 64 + lane;                                                \
+      const int rk = P / kRowChunks;                                                           \
+      r_[i] = rk < kKC ? (KR)[rk] : -1;                                                        \
+    }                                                                                          \
+    _Pragma("unroll") for (int i = 0; i < kBlocks / 4; ++i) {                                  \
+      const int blk = wave + 4 * i;                                                            \
       const int P = blk * 64 + lane;                                                           \
-      const int rk = P / kRowChunks, lc = P % kRowChunks;                                      \
-      const int64_t r = rk < kKC ? (KR)[rk] : -1;                                              \
+      const int lc = P % kRowChunks;                                                           \
+      const int64_t r = r_[i];                                                                 \
       const uint16_t* src = (r < 0 || lc >= kDk / 8) ? a.zero_row                              \
                           : (lc < 64 ? a.k + r * kDn + lc * 8 : a.kr + r * kDr + (lc - 64) * 8); \
       __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)((KS) + blk * 512), 16, 0, 0); \
     }                                                                                          \
   }
 
-  f32x4 dqacc[36];
-#pragma unroll
-  for (int ft = 0; ft < 36; ++ft) dqacc[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
+// Partial S and dP of chunk buffer KS over this wave's dims: 2 head tiles x 2 key tiles; key
+// tile slot 0 is the tile this wave finishes (keys 16 dh ..), slot 1 the one it hands over.
+#define SFAG_SCORES(KS)                                                                        \
+  {                                                                                            \
+    _Pragma("unroll") for (int ht = 0; ht < 2; ++ht)                                           \
+      _Pragma("unroll") for (int kt = 0; kt < 2; ++kt) {                                       \
+        sacc[ht][kt] = f32x4{0.f, 0.f, 0.f, 0.f};                                              \
+        pacc[ht][kt] = f32x4{0.f, 0.f, 0.f, 0.f};                                              \
+      }                                                                                        \
+    const uint16_t* kr0 = (KS) + (16 * dh + c) * kPitch + 8 * g;                               \
+    const uint16_t* kr1 = (KS) + (16 - 16 * dh + c) * kPitch + 8 * g;                          \
+    bf16x8 kb0 = *reinterpret_cast<const bf16x8*>(kr0 + 256 * dh);                             \
+    bf16x8 kb1 = *reinterpret_cast<const bf16x8*>(kr1 + 256 * dh);                             \
+    _Pragma("unroll") for (int ks = 0; ks < 9; ++ks) {                                         \
+      bf16x8 nb0 = kb0, nb1 = kb1;                                                             \
+      if (ks < 8) {                     /* fragments of the next step, read ahead */           \
+        const int col = ks < 7 ? 256 * dh + 32 * (ks + 1) : kDn + 32 * dh;                     \
+        nb0 = *reinterpret_cast<const bf16x8*>(kr0 + col);                                     \
+        nb1 = *reinterpret_cast<const bf16x8*>(kr1 + col);                                     \
+      }                                                                                        \
+      _Pragma("unroll") for (int ht = 0; ht < 2; ++ht) {                                       \
+        sacc[ht][0] = mfma(qA[ht][ks], kb0, sacc[ht][0]);                                      \
+        sacc[ht][1] = mfma(qA[ht][ks], kb1, sacc[ht][1]);                                      \
+        if (ks < 8) {                                                                          \
+          pacc[ht][0] = mfma(doA[ht][ks], kb0, pacc[ht][0]);                                   \
+          pacc[ht][1] = mfma(doA[ht][ks], kb1, pacc[ht][1]);                                   \
+        }                                                                                      \
+      }                                                                                        \
+      kb0 = nb0;                                                                               \
+      kb1 = nb1;                                                                               \
+    }                                                                                          \
+  }
 
-  SFAG_GATHER_ASYNC(Ks0, krow3)
+// dQ[64 heads][144 w .. 144 w + 143] += dS[64][32 keys] K[32 keys][dims] of the previous chunk
+#define SFAG_DQ(KS, DST)                                                                       \
+  {                                                                                            \
+    bf16x8 dsa[4];                                                                             \
+    _Pragma("unroll") for (int t = 0; t < 4; ++t) dsa[t] = lds_frag_trp((DST), 0, 16 * t, kHtPitch, lane); \
+    bf16x8 kb = lds_frag_trp((KS), 0, 144 * wave, kPitch, lane);                               \
+    _Pragma("unroll") for (int nt = 0; nt < 9; ++nt) {                                         \
+      bf16x8 nb = kb;                                                                          \
+      if (nt < 8) nb = lds_frag_trp((KS), 0, 144 * wave + 16 * (nt + 1), kPitch, lane);        \
+      _Pragma("unroll") for (int t = 0; t < 4; ++t) dqacc[t][nt] = mfma(dsa[t], kb, dqacc[t][nt]); \
+      kb = nb;                                                                                 \
+    }                                                                                          \
+  }
+
+// Hand the partial sums of key tile 1 - dh to the other wave of the head half.
+#define SFAG_XCHG()                                                                            \
+  {                                                                                            \
+    f32x4* xo = X + wave * 4 * 64;                                                             \
+    xo[0 * 64 + lane] = sacc[0][1];                                                            \
+    xo[1 * 64 + lane] = sacc[1][1];                                                            \
+    xo[2 * 64 + lane] = pacc[0][1];                                                            \
+    xo[3 * 64 + lane] = pacc[1][1];                                                            \
+    lds_barrier();                                                                             \
+  }
+
+// P and dS of key tile dh (own partials + the other wave's): records and the DSt tile of
+// this chunk.  Every lane issues exactly 4 record stores (invalid slots write to the sink),
+// so that the end-of-chunk wait can leave them in flight.
+#define SFAG_FINISH(CI, DST)                                                                   \
+  {                                                                                            \
+    const f32x4* xi = X + (wave ^ 1) * 4 * 64;                                                 \
+    const int c0 = (CI) * kKC;                                                                 \
+    const int key = 16 * dh + c;                                                               \
+    const int64_t* kr_cur = krow3 + ((CI) % 3) * kKC;                                          \
+    const bool valid = kr_cur[key] >= 0;                                                       \
+    uint16_t* rec = valid ? a.dsp + (((int64_t)row * a.topk + c0 + key) * a.hgc + hg) * 128 : a.trash; \
+    _Pragma("unroll") for (int ht = 0; ht < 2; ++ht) {                                         \
+      const f32x4 s = sacc[ht][0] + xi[ht * 64 + lane];                                        \
+      const f32x4 dp = pacc[ht][0] + xi[(2 + ht) * 64 + lane];                                 \
+      float p[4], ds[4];                                                                       \
+      _Pragma("unroll") for (int v = 0; v < 4; ++v) {                                          \
+        p[v] = valid ? exp2f(s[v] * zscale - mrow[ht][v]) * ilrow[ht][v] : 0.f;                \
+        ds[v] = p[v] * (dp[v] - drow_[ht][v]);                                                 \
+      }                                                                                        \
+      const uint32_t pw[2] = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};               \
+      const uint32_t dw[2] = {pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3])};           \
+      const int hcol = 32 * hh + 16 * ht + 4 * g;                                              \
+      *reinterpret_cast<uint2*>((DST) + key * kHtPitch + hcol) = make_uint2(dw[0], dw[1]);     \
+      *reinterpret_cast<uint2*>(rec + hcol) = make_uint2(dw[0], dw[1]);                        \
+      *reinterpret_cast<uint2*>(rec + 64 + hcol) = make_uint2(pw[0], pw[1]);                   \
+    }                                                                                          \
+  }
+
+  f32x4 sacc[2][2], pacc[2][2];
+  f32x4 dqacc[4][9];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int nt = 0; nt < 9; ++nt) dqacc[t][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  SFAG_GATHER_ASYNC(Kb0, krow3)
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  for (int ci = 0; ci < nchunk; ++ci) {
-    const int c0 = ci * kKC;
-    uint16_t* Ks = (ci & 1) ? Ks1 : Ks0;
-    uint16_t* Kn = (ci & 1) ? Ks0 : Ks1;
-    const int64_t* kr_cur = krow3 + (ci % 3) * kKC;
-    const int64_t* kr_nxt = krow3 + ((ci + 1) % 3) * kKC;
-    // loads of chunk ci+1 and the key rows of chunk ci+2 go out first
-    const bool more = ci + 1 < nchunk;
-    if (more) SFAG_GATHER_ASYNC(Kn, kr_nxt)
-    int64_t kr2 = -1;
-    if (threadIdx.x < kKC) {
-      const int e = c0 + 2 * kKC + threadIdx.x;
-      if (e < count) kr2 = geo.kstart + srow[e];
-    }
-
-    // ---- S, dP, P, dS for this wave's head tile --------------------------------------------
-    if (wave < ntile) {
-      f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-      f32x4 pacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-      for (int ks = 0; ks < kDk / 32; ++ks) {
-        const bf16x8 qa = lds_read8p(Qs, 16 * wave + c, 32 * ks + 8 * g, kPitch);
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-          const bf16x8 kb = lds_read8p(Ks, 16 * kt + c, 32 * ks + 8 * g, kPitch);
-          sacc[kt] = mfma(qa, kb, sacc[kt]);
-          if (ks < 16) pacc[kt] = mfma(doA[ks], kb, pacc[kt]);
-        }
-      }
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const int key = 16 * kt + c;
-        const bool valid = kr_cur[key] >= 0;
-        uint32_t pw[2], dw[2];
-#pragma unroll
-        for (int v2 = 0; v2 < 2; ++v2) {
-          uint32_t pbits = 0, dbits = 0;
-#pragma unroll
-          for (int h2 = 0; h2 < 2; ++h2) {
-            const int v = 2 * v2 + h2;
-            const float p = valid ? exp2f(sacc[kt][v] * zscale - mrow[v]) * ilrow[v] : 0.f;
-            const float ds = p * (pacc[kt][v] - drow[v]);
-            pbits |= (uint32_t)f2bf(p) << (16 * h2);
-            dbits |= (uint32_t)f2bf(ds) << (16 * h2);
-          }
-          pw[v2] = pbits;
-          dw[v2] = dbits;
-        }
-        const int hcol = 16 * wave + 4 * g;
-        *reinterpret_cast<uint2*>(DSt + key * kHtPitch + hcol) = make_uint2(dw[0], dw[1]);
-        if (valid) {
-          uint16_t* rec = a.dsp + (((int64_t)row * a.topk + c0 + key) * a.hgc + hg) * 128;
-          *reinterpret_cast<uint2*>(rec + hcol) = make_uint2(dw[0], dw[1]);
-          *reinterpret_cast<uint2*>(rec + 64 + hcol) = make_uint2(pw[0], pw[1]);
-        }
-      }
-    } else {
-      // head columns without real heads: zero records (the key-major kernel reads 64 heads)
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const int key = 16 * kt + c;
-        if (kr_cur[key] >= 0) {
-          const int hcol = 16 * wave + 4 * g;
-          uint16_t* rec = a.dsp + (((int64_t)row * a.topk + c0 + key) * a.hgc + hg) * 128;
-          *reinterpret_cast<uint2*>(rec + hcol) = make_uint2(0, 0);
-          *reinterpret_cast<uint2*>(rec + 64 + hcol) = make_uint2(0, 0);
-        }
-      }
-    }
-    __syncthreads();
-
-    // ---- dQ += dS K --------------------------------------------------------------------------
-    if (wave < ntile) {
-      const bf16x8 dsa = lds_frag_trp(DSt, 0, 16 * wave, kHtPitch, lane);
-#pragma unroll
-      for (int ft = 0; ft < 36; ++ft) dqacc[ft] = mfma(dsa, lds_frag_trp(Ks, 0, 16 * ft, kPitch, lane), dqacc[ft]);
-    }
-    if (threadIdx.x < kKC) krow3[((ci + 2) % 3) * kKC + threadIdx.x] = kr2;
-    __builtin_amdgcn_s_waitcnt(0);      // the next chunk's direct-to-LDS loads have landed
-    __syncthreads();
+// One chunk CI: gather of chunk CI + 1 into KN, scores of chunk CI (buffer KC), dQ of chunk
+// CI - 1 (buffers KP, DP; skipped for chunk 0), swap and finish into DC.  The key rows of
+// chunk CI + 2 are loaded branch-free and only used after the end-of-chunk wait.
+#define SFAG_CHUNK(CI, KC, KP, KN, DC, DP, WITH_DQ)                                            \
+  {                                                                                            \
+    const int ci_ = (CI);                                                                      \
+    if (ci_ + 1 < nchunk) SFAG_GATHER_ASYNC(KN, krow3 + ((ci_ + 1) % 3) * kKC)                 \
+    const int e2 = (ci_ + 2) * kKC + (int)threadIdx.x;                                         \
+    const int32_t sv = srow[min(e2, count - 1)];                                               \
+    SFAG_SCORES(KC)                                                                            \
+    SFAG_XCHG()                                                                                \
+    if (WITH_DQ) SFAG_DQ(KP, DP)                                                               \
+    SFAG_FINISH(ci_, DC)                                                                       \
+    /* everything but the 4 record stores just issued (chunk CI + 1 has landed) */            \
+    __builtin_amdgcn_s_waitcnt(kWaitAllButRecords);                                            \
+    if (threadIdx.x < kKC) krow3[((ci_ + 2) % 3) * kKC + threadIdx.x] = e2 < count ? geo.kstart + sv : -1; \
+    __syncthreads();                                                                           \
   }
 
-  // ---- dQ / dQRope out ------------------------------------------------------------------------
-  if (wave < ntile) {
+  SFAG_CHUNK(0, Kb0, Kb2, Kb1, Db0, Db2, false)
+  // chunk ci lives in key / dS buffers ci % 3; unrolled by 3 so every access names its buffer
+  int ci = 1;
+  for (; ci + 2 < nchunk; ci += 3) {
+    SFAG_CHUNK(ci, Kb1, Kb0, Kb2, Db1, Db0, true)
+    SFAG_CHUNK(ci + 1, Kb2, Kb1, Kb0, Db2, Db1, true)
+    SFAG_CHUNK(ci + 2, Kb0, Kb2, Kb1, Db0, Db2, true)
+  }
+  if (ci < nchunk) {
+    SFAG_CHUNK(ci, Kb1, Kb0, Kb2, Db1, Db0, true)
+    ++ci;
+  }
+  if (ci < nchunk) {
+    SFAG_CHUNK(ci, Kb2, Kb1, Kb0, Db2, Db1, true)
+    ++ci;
+  }
+  // dQ of the last chunk
+  switch ((nchunk - 1) % 3) {
+    case 0: SFAG_DQ(Kb0, Db0) break;
+    case 1: SFAG_DQ(Kb1, Db1) break;
+    default: SFAG_DQ(Kb2, Db2) break;
+  }
+
+#undef SFAG_GATHER_ASYNC
+#undef SFAG_SCORES
+#undef SFAG_DQ
+#undef SFAG_FINISH
+#undef SFAG_XCHG
+#undef SFAG_CHUNK
+
+  // ---- dQ / dQRope out: lane holds heads 16 t + 4 g + v, dims 144 w + 16 nt + c ------------------
 #pragma unroll
-    for (int ft = 0; ft < 36; ++ft) {
+  for (int t = 0; t < 4; ++t) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int h = 16 * wave + 4 * g + v;
-        if (h >= nh) continue;
-        const int col = 16 * ft + c;
-        const uint16_t bv = f2bf(dqacc[ft][v] * a.scale);
-        const int64_t hh = row * a.N1 + h0 + h;
-        if (col < kDn) a.dq[hh * kDn + col] = bv;
-        else a.dqr[hh * kDr + col - kDn] = bv;
+    for (int v = 0; v < 4; ++v) {
+      const int h = 16 * t + 4 * g + v;
+      if (h >= nh) continue;
+      const int64_t hh2 = row * a.N1 + h0 + h;
+#pragma unroll
+      for (int nt = 0; nt < 9; ++nt) {
+        const int col = 144 * wave + 16 * nt + c;
+        const uint16_t bv = f2bf(dqacc[t][nt][v] * a.scale);
+        if (col < kDn) a.dq[hh2 * kDn + col] = bv;
+        else a.dqr[hh2 * kDr + col - kDn] = bv;
       }
     }
   }
 }
 
-#undef SFAG_GATHER_ASYNC
-
 hipError_t launch_bwd_q(const BwdArgs& a, int64_t nrows, int hg_count, hipStream_t st) {
-  hipLaunchKernelGGL(bwd_q_kernel, dim3((unsigned)nrows, (unsigned)hg_count), dim3(kThreads), kLdsTotal, st, a);
+  hipLaunchKernelGGL(bwd_q_kernel, dim3((unsigned)nrows, (unsigned)hg_count), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
-hipError_t set_q_attributes() {
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_q_kernel),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, kLdsTotal);
-}
+hipError_t set_q_attributes() { return hipSuccess; }
 
 }  // namespace sfag
