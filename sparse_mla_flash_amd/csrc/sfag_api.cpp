@@ -59,7 +59,7 @@ struct Plan {
   // workspace layout
   uint64_t off_acc = 0, off_partial = 0, off_keys0 = 0, off_keys1 = 0, off_sorttmp = 0;
   uint64_t off_sorted = 0, off_count = 0, off_maxdup = 0, off_offs = 0, off_dsp = 0, off_part = 0, off_flag = 0;
-  uint64_t off_zero = 0, off_ilist = 0, off_imap = 0, off_trash = 0;
+  uint64_t off_zero = 0, off_ilist = 0, off_imap = 0, off_trash = 0, off_kpos = 0;
   uint64_t sort_tmp_bytes = 0, bytes = 0;
   int64_t det_rows = 0;            // query rows per deterministic launch
   int end_bit = 64;
@@ -226,6 +226,8 @@ sfag_status make_plan(const sfag_dims* dims, const int32_t* sq, const int32_t* s
     off = align_up(off + (uint64_t)p->rows * 4);
     p->off_offs = off;
     off = align_up(off + (uint64_t)p->rows * (maxblk + 1) * 4);
+    p->off_kpos = off;
+    off = align_up(off + (uint64_t)p->rows * maxblk * sfag::kBk * 2);
     p->off_dsp = off;
     off = align_up(off + pairs * p->hg_count * 128 * 2);
     p->off_part = off;
@@ -405,6 +407,8 @@ sfag_status sfag_sparse_flash_attention_grad(
     da.count = reinterpret_cast<int32_t*>(ws + p.off_count);
     da.maxdup = reinterpret_cast<int32_t*>(ws + p.off_maxdup);
     da.offs = reinterpret_cast<int32_t*>(ws + p.off_offs);
+    da.kpos = reinterpret_cast<int16_t*>(ws + p.off_kpos);
+    da.kstride = (int)(p.maxblk * sfag::kBk);
     da.dsp = reinterpret_cast<uint16_t*>(ws + p.off_dsp);
     da.part = reinterpret_cast<float*>(ws + p.off_part);
     da.flag = reinterpret_cast<int32_t*>(ws + p.off_flag);

@@ -27,6 +27,7 @@ constexpr int kThreads = 256;
 constexpr int kHtChunks = 64 / 8;          // [key][64 heads] tile rows: 8 chunks
 constexpr int kBtChunks = 24;              // [64 heads][<=144 cols] tile rows padded to 192 cols
 constexpr int32_t kNoKey = 0x7fffffff;
+constexpr int kMapWin = 8192;              // keys per LDS window of the key -> position map
 
 // Per-batch tables in LDS: query / key row starts (cum, as in cum_lengths) and the first item
 // (key block x row segment) of every batch.
@@ -115,6 +116,23 @@ __global__ void __launch_bounds__(kThreads) sort_rows_kernel(DenseArgs a, int np
     }
     a.offs[row * (a.maxblk + 1) + lb] = lo;
   }
+  // key -> first sorted position map of this row (-1: not selected), built in LDS windows and
+  // written out whole, over every key block the row can reach
+  int16_t* win = reinterpret_cast<int16_t*>(keys + np);
+  const int map_end = (geo.active && geo.hi >= 0) ? min(a.kstride, ((geo.hi + kBk) / kBk) * kBk) : 0;
+  int16_t* kp = a.kpos + row * a.kstride;
+  for (int w0 = 0; w0 < map_end; w0 += kMapWin) {
+    const int w1 = min(map_end, w0 + kMapWin);
+    __syncthreads();
+    for (int k = threadIdx.x; k < w1 - w0; k += kThreads) win[k] = -1;
+    __syncthreads();
+    for (int i = threadIdx.x; i < cnt; i += kThreads) {
+      const int32_t key = keys[i];
+      if (key >= w0 && key < w1 && (i == 0 || keys[i - 1] != key)) win[key - w0] = (int16_t)i;
+    }
+    __syncthreads();
+    for (int k = threadIdx.x; k < w1 - w0; k += kThreads) kp[w0 + k] = win[k];
+  }
   __syncthreads();
   if (threadIdx.x == 0) {
     a.count[row] = cnt;
@@ -175,30 +193,216 @@ __global__ void __launch_bounds__(1024) item_list_kernel(DenseArgs a) {
 
 // Workgroup = (live item, column slice, head group).  Workgroups are dealt to the 8 XCDs
 // round-robin (x = w % 8), so XCD x is given the contiguous run of live items
-// [x n, x n + n) and walks it as  half (dK slices, then dV slices) > item > slice: the ~32
-// workgroups resident on one XCD are then 8 neighbouring key blocks of one row segment x the
-// 4 column slices of one half, which share the segment's Q / dO rows and dS / P records in
+// [x n, x n + n) and walks it as  half (dK slices, then dV slices) > item > slice: the
+// workgroups resident on one XCD are then neighbouring key blocks of one row segment x the 4
+// column slices of one half, which share the segment's Q / dO rows and dS / P records in
 // that XCD's L2.
 // Column slices 0..3: dK columns 144 s .. 144 s + 143 (the last one holds the rope columns);
 // 4..7: dV columns 128 (s - 4) .. + 127.  Wave w owns key tiles 4w .. 4w + 3 (64 keys).
 //
-// The A (dS or P) and B (Q or dO) tiles are double-buffered.  Per selecting row u (and per
-// repeat layer of a duplicated key) every thread
-//   issues the global loads of unit u+1 into registers, clears in the other buffer the tile
-//   rows it wrote for unit u-1, runs the MFMAs of unit u | barrier | stores unit u+1's
-//   records and B tile into the other buffer | barrier
-// so the loads of the next unit are in flight while the MFMAs of this one run, and a tile
-// row is never cleared and written in the same barrier interval.
-constexpr int kSegCap = kSegRows;   // rows of one segment staged in LDS
+// For every row u of the segment that selects keys of the block (a "unit"; a row that
+// repeats keys gives one unit per repeat layer L, the L-th occurrence of each key):
+//   A = [256 keys x 64 heads] of dS (dK slices) or P (dV slices), zero where the row did not
+//       select the key.  MFMA A fragments come straight from the pair records in global
+//       memory: lane (g, c) of key tile kt needs heads 8 g .. 8 g + 7 of key 16 kt + c, found
+//       through the row's key -> position map (unselected keys read the zero row).
+//   B = the row's [64 heads x cols] Q (or dO) slice, staged in LDS by direct-to-LDS loads
+//       and read with transposing reads.
+//   acc[keys][cols] += A B  on the 16x16x32 bf16 MFMA, fp32 in registers.
+// Pipeline per unit u: map entries of unit u + 2, record fragments of unit u + 1 and the B
+// tile of unit u + 1 are requested, then the MFMAs of unit u run; one barrier per unit.
+constexpr int kBtPitch = 152;                         // B tile row: up to 144 columns + 8
+constexpr int kBtRowChunks = kBtPitch / 8;            // 19 16-byte chunks per row
+constexpr int kBtBlocks = 20;                         // 64 rows x 19 chunks in 20 blocks of 64
+static_assert(kBtBlocks * 64 >= 64 * kBtRowChunks && kBtBlocks % 4 == 0, "B tile blocks");
+
+// Shared state of one key-major workgroup, set up by kv_dense_kernel.
+struct KvCtx {
+  const uint16_t* Bt0;
+  const uint16_t* Bt1;
+  const int16_t* s_row;
+  const uint16_t* s_lay;
+  int64_t qstart;
+  int i0, nrows, nunits, kb0, colbase, h0, nh, hg, which, citem;
+  bool isdk;
+};
+
+// Main loop of one workgroup with NFT column tiles (9: dK slice, 8: dV slice).  DUPS: some
+// row of the item repeats keys (units = (row, layer)); otherwise units are the rows.
+template <int NFT, bool DUPS>
+__device__ __forceinline__ void kv_dense_body(const DenseArgs& a, const KvCtx& x, uint16_t* Bt0, uint16_t* Bt1) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const uint16_t* zsrc = a.zero_row;
+  const int16_t* s_row = x.s_row;
+  const uint16_t* s_lay = x.s_lay;
+  const int nrows = x.nrows;
+  const int nunits = x.nunits;
+
+  // this lane's keys (one per key tile)
+  int kcol[4];
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) kcol[kt] = x.kb0 + 64 * wave + 16 * kt + c;
+  // B-tile chunks this lane loads: element offset in the row's Q / dO block; bit 30: rope
+  // block; bit 29: zero row (padding, padded heads, unused columns)
+  int boff[kBtBlocks / 4];
+#pragma unroll
+  for (int i = 0; i < kBtBlocks / 4; ++i) {
+    const int P = (int)threadIdx.x + kThreads * i;
+    const int h = P / kBtRowChunks, cc = P % kBtRowChunks;
+    const int col = x.colbase + 8 * cc;
+    if (h >= x.nh || cc >= 2 * NFT) boff[i] = 1 << 29;
+    else if (x.isdk && col >= kDn) boff[i] = (1 << 30) | ((x.h0 + h) * kDr + col - kDn);
+    else boff[i] = (x.h0 + h) * kDn + (x.isdk ? col : col - kDk);
+  }
+  const uint16_t* bmain = x.isdk ? a.q : a.dout;
+
+  auto next_unit = [&](int& ri, int& L) {
+    if (!DUPS) {
+      ri = (ri >= 0 && ri + 1 < nrows) ? ri + 1 : -1;
+      return;
+    }
+    if (ri < 0) return;
+    if (L + 1 < (int)s_lay[ri]) { ++L; return; }
+    L = 0;
+    ri = ri + 1 < nrows ? ri + 1 : -1;
+  };
+
+#define SFAG_MAP_LOAD(MP, RI)                                                                  \
+  {                                                                                            \
+    const int64_t row_ = x.qstart + x.i0 + s_row[max((RI), 0)];                                \
+    const int16_t* kp_ = a.kpos + row_ * a.kstride;                                            \
+    _Pragma("unroll") for (int kt = 0; kt < 4; ++kt) {                                         \
+      const int v_ = kp_[kcol[kt]];                                                            \
+      MP[kt] = (RI) < 0 ? -1 : v_;                                                             \
+    }                                                                                          \
+  }
+
+// Record fragments of unit (RI, L) from its map entries MP: lane (g, c) of key tile kt, head
+// step ks holds heads 32 ks + 8 g .. + 7 of key kcol[kt] (zeros when not selected).
+#define SFAG_A_LOAD(AF, MP, RI, L)                                                             \
+  {                                                                                            \
+    const int64_t row_ = x.qstart + x.i0 + s_row[max((RI), 0)];                                \
+    const uint16_t* rbase_ = a.dsp + (row_ * a.topk * a.hgc + x.hg) * 128 + x.which + 8 * g;   \
+    _Pragma("unroll") for (int kt = 0; kt < 4; ++kt) {                                         \
+      int e_ = MP[kt];                                                                         \
+      bool ok_ = e_ >= 0 && (RI) >= 0;                                                         \
+      if (DUPS && (L) > 0) {                                                                   \
+        e_ += (L);                                                                             \
+        ok_ = ok_ && e_ < a.topk && a.sorted[row_ * a.topk + min(e_, a.topk - 1)] == kcol[kt]; \
+      }                                                                                        \
+      const uint16_t* src_ = ok_ ? rbase_ + (int64_t)e_ * a.hgc * 128 : zsrc + 8 * g;          \
+      AF[kt][0] = *reinterpret_cast<const bf16x8*>(src_);                                      \
+      AF[kt][1] = *reinterpret_cast<const bf16x8*>(src_ + 32);                                 \
+    }                                                                                          \
+  }
+
+// B tile of unit RI into registers: thread t holds chunks t + 256 i of the padded
+// [64 heads][19 chunks] tile; SFAG_B_STORE writes them to LDS once the MFMAs reading the
+// other buffer have been issued.
+#define SFAG_B_LOAD(BS, RI)                                                                    \
+  {                                                                                            \
+    const int64_t row_ = x.qstart + x.i0 + s_row[max((RI), 0)];                                \
+    const uint16_t* mrow_ = bmain + row_ * a.N1 * kDn;                                         \
+    const uint16_t* rrow_ = a.qr + row_ * a.N1 * kDr;                                          \
+    _Pragma("unroll") for (int i = 0; i < kBtBlocks / 4; ++i) {                                \
+      const int o = boff[i];                                                                   \
+      const uint16_t* src = ((o & (1 << 29)) || (RI) < 0) ? zsrc : ((o & (1 << 30)) ? rrow_ : mrow_) + (o & ((1 << 29) - 1)); \
+      BS[i] = *reinterpret_cast<const u32x4*>(src);                                            \
+    }                                                                                          \
+  }
+#define SFAG_B_STORE(BT, BS)                                                                   \
+  {                                                                                            \
+    _Pragma("unroll") for (int i = 0; i < kBtBlocks / 4; ++i)                                  \
+      *reinterpret_cast<u32x4*>((BT) + (threadIdx.x + kThreads * i) * 8) = BS[i];              \
+  }
+
+// MFMAs of one unit: NFT column tiles x 2 head steps x 4 key tiles, B fragments by transposing
+// reads of the B tile, one (column tile, head step) ahead.
+#define SFAG_MMA(BT, AF)                                                                       \
+  {                                                                                            \
+    bf16x8 bf = lds_frag_trp((BT), 0, 0, kBtPitch, lane);                                      \
+    _Pragma("unroll") for (int q = 0; q < 2 * NFT; ++q) {                                      \
+      const int ft = q >> 1, ks = q & 1;                                                       \
+      bf16x8 nb = bf;                                                                          \
+      if (q + 1 < 2 * NFT) nb = lds_frag_trp((BT), 32 * ((q + 1) & 1), 16 * ((q + 1) >> 1), kBtPitch, lane); \
+      _Pragma("unroll") for (int kt = 0; kt < 4; ++kt) acc[kt][ft] = mfma(AF[kt][ks], bf, acc[kt][ft]); \
+      bf = nb;                                                                                 \
+    }                                                                                          \
+  }
+
+  f32x4 acc[4][NFT];
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+    for (int ft = 0; ft < NFT; ++ft) acc[kt][ft] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // prologue: map of units 0 and 1, B tile and record fragments of unit 0
+  int ri1 = 0, L1 = 0;                 // cursor of unit u + 1 (here: of unit 0)
+  int m0[4], m1[4];
+  bf16x8 f0[4][2], f1[4][2];
+  u32x4 bs[kBtBlocks / 4];
+  SFAG_MAP_LOAD(m0, ri1)
+  SFAG_B_LOAD(bs, ri1)
+  int ri2 = ri1, L2 = L1;
+  next_unit(ri2, L2);
+  SFAG_MAP_LOAD(m1, ri2)
+  SFAG_A_LOAD(f0, m0, ri1, L1)
+  SFAG_B_STORE(Bt0, bs)
+  ri1 = ri2;
+  L1 = L2;                             // cursor of unit 1
+  __syncthreads();
+
+  // unit u: loads of unit u + 1 (B tile, record fragments from map m1) and of the map of
+  // unit u + 2, MFMAs of unit u (buffer u & 1, fragments f0), then unit u + 1's B tile into
+  // the other buffer
+  for (int u = 0; u < nunits; ++u) {
+    uint16_t* BC = (u & 1) ? Bt1 : Bt0;
+    uint16_t* BN = (u & 1) ? Bt0 : Bt1;
+    int ri2_ = ri1, L2_ = L1;
+    next_unit(ri2_, L2_);
+    SFAG_B_LOAD(bs, ri1)
+    SFAG_MAP_LOAD(m0, ri2_)
+    SFAG_A_LOAD(f1, m1, ri1, L1)
+    SFAG_MMA(BC, f0)
+    SFAG_B_STORE(BN, bs)
+    __syncthreads();
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      f0[kt][0] = f1[kt][0];
+      f0[kt][1] = f1[kt][1];
+      m1[kt] = m0[kt];
+    }
+    ri1 = ri2_;
+    L1 = L2_;
+  }
+#undef SFAG_B_STORE
+#undef SFAG_MMA
+#undef SFAG_B_LOAD
+#undef SFAG_A_LOAD
+#undef SFAG_MAP_LOAD
+
+  const float mul = x.isdk ? a.scale : 1.f;
+  float* part = a.part + ((int64_t)x.hg * a.citems + x.citem) * (int64_t)kBk * kDacc;
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+    for (int ft = 0; ft < NFT; ++ft)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int kk = 16 * (4 * wave + kt) + 4 * g + v;
+        part[(int64_t)kk * kDacc + x.colbase + 16 * ft + c] = acc[kt][ft][v] * mul;
+      }
+}
 
 __global__ void __launch_bounds__(kThreads, 1) kv_dense_kernel(DenseArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t At2[2][kBk * 64];
-  __shared__ __attribute__((aligned(16))) uint16_t Bt2[2][64 * kBtChunks * 8];
+  __shared__ __attribute__((aligned(16))) uint16_t Bt0[kBtBlocks * 512], Bt1[kBtBlocks * 512];
   __shared__ int32_t cum[2 * 257];
   __shared__ int32_t ibase[257];
-  __shared__ int32_t s_b;
-  __shared__ int32_t s_lo[kSegCap], s_n[kSegCap];
-  __shared__ uint8_t s_dup[kSegCap];
+  __shared__ int32_t s_b, s_nrows;
+  __shared__ int16_t s_row[kSegRows];      // segment rows that select keys in the block, in order
+  __shared__ uint16_t s_lay[kSegRows];     // their repeat layers (1 without repeated keys)
+  __shared__ int32_t s_wcnt[4];
 
   const int w = blockIdx.x;
   const int xcd = w & 7, j = w >> 3;
@@ -227,254 +431,63 @@ __global__ void __launch_bounds__(kThreads, 1) kv_dense_kernel(DenseArgs a) {
   const int64_t qstart = cum[b];
   const int i0 = seg * kSegRows, i1 = min(lq, i0 + kSegRows);
   int32_t* flag = a.flag + (int64_t)hg * a.citems + citem;
-  if (a.mode3 && (i1 - 1) + lkv - lq < kb0) {
-    if (threadIdx.x == 0) *flag = 0;
-    return;
-  }
-  // per-row pair ranges of this block and repeat counts, staged once
-  for (int i = i0 + threadIdx.x; i < i1; i += kThreads) {
-    int lo = 0, n = 0, dup = 1;
-    if (!(a.mode3 && i + lkv - lq < kb0)) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+
+  // ordered list of the segment's rows with keys in the block
+  if (threadIdx.x == 0) s_nrows = 0;
+  for (int p0 = i0; p0 < i1; p0 += kThreads) {
+    const int i = p0 + threadIdx.x;
+    int n = 0, lay = 1;
+    if (i < i1 && !(a.mode3 && i + lkv - lq < kb0)) {
       const int64_t row = qstart + i;
       const int32_t* offr = a.offs + row * (a.maxblk + 1);
-      lo = offr[lb];
-      n = offr[lb + 1] - lo;
-      dup = n > 0 ? a.maxdup[row] : 1;
+      n = offr[lb + 1] - offr[lb];
+      if (n > 0) lay = a.maxdup[row];
     }
-    s_lo[i - i0] = lo;
-    s_n[i - i0] = n;
-    s_dup[i - i0] = (uint8_t)min(dup, 255);
-  }
-  for (int p = threadIdx.x; p < 2 * kBk * 8; p += kThreads)
-    *reinterpret_cast<uint4*>(&At2[0][0] + p * 8) = make_uint4(0, 0, 0, 0);
-  __syncthreads();
-
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int g = lane >> 4, c = lane & 15;
-  const bool isdk = sl < 4;
-  const int nft = isdk ? 9 : 8;
-  const int nbt = 64 * 2 * nft;                         // 16-byte pieces of the B tile
-  const int colbase = isdk ? 144 * sl : kDk + 128 * (sl - 4);
-  const int h0 = hg * 64;
-  const int nh = min(64, a.N1 - h0);
-  const int which = isdk ? 0 : 64;
-  const int piece = threadIdx.x & 7;
-
-  // ---- fast path: rows without repeated keys, one unit per (row, chunk of 256 positions) ----
-  int cur = -1, chunk = 0;
-  auto advance = [&](int& i, int& ch) {
-    if (i >= 0 && (ch + 1) * kBk < s_n[i - i0]) { ++ch; return; }
-    ch = 0;
-    for (i = (i < 0 ? i0 : i + 1); i < i1; ++i)
-      if (s_n[i - i0] > 0 && s_dup[i - i0] == 1) return;
-    i = -1;
-  };
-  u32x4 rec[8];
-  int key[8];                    // sorted key position of each prefetched record
-  u32x4 btp[5];
-  // B-tile pieces of this thread: element offset inside the row's Q / dO block (bit 31 set:
-  // inside the row's rope block); padded heads and pieces past the tile read a valid address
-  const uint16_t* bmain = (isdk ? a.q : a.dout) + (int64_t)h0 * kDn;
-  int boff[5];
-#pragma unroll
-  for (int k = 0; k < 5; ++k) {
-    const int p = min((int)threadIdx.x + kThreads * k, nbt - 1);
-    const int h = min(p / (2 * nft), nh - 1), ch8 = (p % (2 * nft)) * 8;
-    const int col = colbase + ch8;
-    if (isdk && col >= kDn) boff[k] = (int)(0x80000000u | (unsigned)(h * kDr + col - kDn));
-    else boff[k] = h * kDn + (isdk ? col : col - kDk);
-  }
-  int u_lo = 0, u_n = 0, u_ch = 0;
-
-#define SFAG_PF_REC(k)                                                                         \
-  {                                                                                            \
-    const int pr = (threadIdx.x >> 3) + 32 * (k) + kBk * u_ch;                                 \
-    const int e = u_lo + min(pr, u_n - 1);                                                     \
-    key[k] = srow_[e];                                                                         \
-    rec[k] = *reinterpret_cast<const u32x4*>(drow_ + (int64_t)e * a.hgc * 128);                \
-  }
-#define SFAG_PF_BT(k)                                                                          \
-  btp[k] = *reinterpret_cast<const u32x4*>((boff[k] < 0 ? rope_row : main_row) + (boff[k] & 0x7fffffff));
-#define SFAG_ST_REC(k)                                                                         \
-  {                                                                                            \
-    const int pr = (threadIdx.x >> 3) + 32 * (k) + kBk * u_ch;                                 \
-    key[k] = pr < u_n ? key[k] - kb0 : -1;                                                     \
-    if (key[k] >= 0) *reinterpret_cast<u32x4*>(At_ + swz(key[k], piece * 8, kHtChunks)) = rec[k]; \
-  }
-#define SFAG_ST_BT(k)                                                                          \
-  {                                                                                            \
-    const int p = threadIdx.x + kThreads * (k);                                                \
-    if (p < nbt) {                                                                             \
-      const int h = p / (2 * nft), ch8 = (p % (2 * nft)) * 8;                                  \
-      *reinterpret_cast<u32x4*>(Bt_ + swz(h, ch8, kBtChunks)) = h < nh ? btp[k] : u32x4{0u, 0u, 0u, 0u}; \
-    }                                                                                          \
-  }
-
-// Issue every global load of unit (I, CH) up front, with addresses clamped into range and no
-// branches; nothing consumes them before the MFMAs of the current unit.
-#define SFAG_PREFETCH(I, CH)                                                                   \
-  {                                                                                            \
-    const int64_t row_ = qstart + (I);                                                         \
-    u_lo = s_lo[(I) - i0];                                                                     \
-    u_n = s_n[(I) - i0];                                                                       \
-    u_ch = (CH);                                                                               \
-    const int32_t* srow_ = a.sorted + row_ * a.topk;                                           \
-    const uint16_t* drow_ = a.dsp + (row_ * a.topk * a.hgc + hg) * 128 + which + piece * 8;    \
-    SFAG_PF_REC(0) SFAG_PF_REC(1) SFAG_PF_REC(2) SFAG_PF_REC(3)                                \
-    SFAG_PF_REC(4) SFAG_PF_REC(5) SFAG_PF_REC(6) SFAG_PF_REC(7)                                \
-    if (u_ch == 0) {                                                                           \
-      const uint16_t* main_row = bmain + row_ * a.N1 * kDn;                                    \
-      const uint16_t* rope_row = a.qr + (row_ * a.N1 + h0) * kDr;                              \
-      SFAG_PF_BT(0) SFAG_PF_BT(1) SFAG_PF_BT(2) SFAG_PF_BT(3) SFAG_PF_BT(4)                    \
-    }                                                                                          \
-  }
-
-// Store the prefetched records into their key rows of buffer BUF and the B tile; key[k]
-// becomes the tile row written (-1: none) so that it can be cleared later.
-#define SFAG_STORE(BUF)                                                                        \
-  {                                                                                            \
-    uint16_t* At_ = At2[BUF];                                                                  \
-    uint16_t* Bt_ = Bt2[BUF];                                                                  \
-    SFAG_ST_REC(0) SFAG_ST_REC(1) SFAG_ST_REC(2) SFAG_ST_REC(3)                                \
-    SFAG_ST_REC(4) SFAG_ST_REC(5) SFAG_ST_REC(6) SFAG_ST_REC(7)                                \
-    if (u_ch == 0) {                                                                           \
-      SFAG_ST_BT(0) SFAG_ST_BT(1) SFAG_ST_BT(2) SFAG_ST_BT(3) SFAG_ST_BT(4)                    \
-    }                                                                                          \
-  }
-
-// MFMAs of one unit from buffer BUF: 4 key tiles x (8 or 9) column tiles x 2 head steps, the
-// B fragments read three column tiles at a time.
-#define SFAG_MMA(BUF)                                                                          \
-  {                                                                                            \
-    const uint16_t* At_ = At2[BUF];                                                            \
-    const uint16_t* Bt_ = Bt2[BUF];                                                            \
-    static_for<0, 2>([&](auto KS) {                                                            \
-      constexpr int ks = decltype(KS)::value;                                                  \
-      bf16x8 af[4];                                                                            \
-      static_for<0, 4>([&](auto KT) {                                                          \
-        constexpr int kt = decltype(KT)::value;                                                \
-        af[kt] = lds_read8(At_, 16 * (4 * wave + kt) + c, 32 * ks + 8 * g, kHtChunks);         \
-      });                                                                                      \
-      static_for<0, 3>([&](auto FG) {                                                          \
-        constexpr int fg = decltype(FG)::value;                                                \
-        bf16x8 bfr[3];                                                                         \
-        static_for<0, 3>([&](auto F) {                                                         \
-          constexpr int f = decltype(F)::value;                                                \
-          bfr[f] = lds_frag_tr(Bt_, 32 * ks, 16 * (3 * fg + f), kBtChunks, lane);              \
-        });                                                                                    \
-        static_for<0, 3>([&](auto F) {                                                         \
-          constexpr int ft = 3 * fg + decltype(F)::value;                                      \
-          if (ft < 8 || isdk)                                                                  \
-            static_for<0, 4>([&](auto KT) {                                                    \
-              constexpr int kt = decltype(KT)::value;                                          \
-              acc[kt][ft] = mfma(af[kt], bfr[decltype(F)::value], acc[kt][ft]);                \
-            });                                                                                \
-        });                                                                                    \
-      });                                                                                      \
-    });                                                                                        \
-  }
-
-  f32x4 acc[4][9];
-#pragma unroll
-  for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-    for (int ft = 0; ft < 9; ++ft) acc[kt][ft] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  advance(cur, chunk);
-  bool any = cur >= 0;
-  if (any) {
-    SFAG_PREFETCH(cur, chunk);
-    SFAG_STORE(0);
-  }
-  __syncthreads();
-  int buf = 0;
-  while (cur >= 0) {
-    int nxt = cur, nchunk = chunk;
-    advance(nxt, nchunk);
-    if (nxt >= 0) SFAG_PREFETCH(nxt, nchunk);   // later chunks of a row keep btp from its first load
-    // clear the other buffer's A tile (its last unit's MFMAs finished before the last barrier)
-    {
-      u32x4* Ac = reinterpret_cast<u32x4*>(At2[buf ^ 1]);
-#pragma unroll
-      for (int k = 0; k < kBk * 8 / kThreads; ++k) Ac[threadIdx.x + kThreads * k] = u32x4{0u, 0u, 0u, 0u};
-    }
-    if (buf == 0) SFAG_MMA(0) else SFAG_MMA(1)
+    const uint64_t m = __ballot(n > 0);
+    if (lane == 0) s_wcnt[wave] = __popcll(m);
     __syncthreads();
-    if (nxt >= 0) {
-      if (buf == 0) SFAG_STORE(1) else SFAG_STORE(0)
+    int base = s_nrows;
+    for (int v = 0; v < wave; ++v) base += s_wcnt[v];
+    if (n > 0) {
+      const int at = base + __popcll(m & ((1ull << lane) - 1ull));
+      s_row[at] = (int16_t)(i - i0);
+      s_lay[at] = (uint16_t)min(lay, 65535);
     }
     __syncthreads();
-    buf ^= 1;
-    cur = nxt;
-    chunk = nchunk;
+    if (threadIdx.x == 0) s_nrows += s_wcnt[0] + s_wcnt[1] + s_wcnt[2] + s_wcnt[3];
+    __syncthreads();
   }
-
-  // ---- slow path: rows that repeat a key.  Every repeat contributes separately, so such a
-  // row is applied in layers (the L-th occurrence of each key) and 256-position chunks, with
-  // the whole tile cleared each time.  Never taken when indices are distinct.
-  for (int i = i0; i < i1; ++i) {
-    if (s_n[i - i0] == 0 || s_dup[i - i0] == 1) continue;
-    any = true;
-    const int64_t row = qstart + i;
-    const int lo = s_lo[i - i0], n = s_n[i - i0];
-    const int32_t* srow = a.sorted + row * a.topk;
-    for (int L = 0; L < (int)s_dup[i - i0]; ++L) {
-      for (int ch = 0; ch * kBk < n; ++ch) {
-        __syncthreads();
-        for (int p = threadIdx.x; p < kBk * 8; p += kThreads)
-          *reinterpret_cast<uint4*>(&At2[0][0] + p * 8) = make_uint4(0, 0, 0, 0);
-        for (int p = threadIdx.x; p < nbt; p += kThreads) {
-          const int h = p / (2 * nft), ch8 = (p % (2 * nft)) * 8;
-          const int col = colbase + ch8;
-          uint4 v = make_uint4(0, 0, 0, 0);
-          if (h < nh) {
-            const int64_t hh = row * a.N1 + h0 + h;
-            v = isdk ? *reinterpret_cast<const uint4*>(col < kDn ? a.q + hh * kDn + col : a.qr + hh * kDr + (col - kDn))
-                     : *reinterpret_cast<const uint4*>(a.dout + hh * kDn + (col - kDk));
-          }
-          *reinterpret_cast<uint4*>(Bt2[0] + swz(h, ch8, kBtChunks)) = v;
-        }
-        __syncthreads();
-        for (int p = threadIdx.x; p < kBk * 8; p += kThreads) {
-          const int pr = ch * kBk + (p >> 3);
-          if (pr >= n) continue;
-          const int e = lo + pr;
-          const int32_t kk = srow[e];
-          const bool occ = e - L >= lo && srow[e - L] == kk && (e - L == lo || srow[e - L - 1] != kk);
-          if (!occ) continue;
-          const uint4 v = *reinterpret_cast<const uint4*>(
-              a.dsp + ((row * a.topk + e) * a.hgc + hg) * 128 + which + (p & 7) * 8);
-          *reinterpret_cast<uint4*>(At2[0] + swz(kk - kb0, (p & 7) * 8, kHtChunks)) = v;
-        }
-        __syncthreads();
-        SFAG_MMA(0)
-      }
-    }
-  }
-#undef SFAG_PREFETCH
-#undef SFAG_STORE
-#undef SFAG_MMA
-#undef SFAG_PF_REC
-#undef SFAG_PF_BT
-#undef SFAG_ST_REC
-#undef SFAG_ST_BT
-  if (!any) {
+  const int nrows = s_nrows;
+  int nunits = 0;                       // units: one per (row, repeat layer)
+  for (int t = 0; t < nrows; ++t) nunits += s_lay[t];
+  if (nrows == 0) {
     if (threadIdx.x == 0) *flag = 0;
     return;
   }
-  const float mul = isdk ? a.scale : 1.f;
-  float* part = a.part + ((int64_t)hg * a.citems + citem) * (int64_t)kBk * kDacc;
-#pragma unroll
-  for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-    for (int ft = 0; ft < 9; ++ft) {
-      if (ft >= nft) continue;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int kk = 16 * (4 * wave + kt) + 4 * g + v;
-        part[(int64_t)kk * kDacc + colbase + 16 * ft + c] = acc[kt][ft][v] * mul;
-      }
-    }
+  KvCtx x;
+  x.s_row = s_row;
+  x.s_lay = s_lay;
+  x.qstart = qstart;
+  x.i0 = i0;
+  x.nrows = nrows;
+  x.nunits = nunits;
+  x.kb0 = kb0;
+  x.isdk = sl < 4;
+  x.colbase = x.isdk ? 144 * sl : kDk + 128 * (sl - 4);
+  x.h0 = hg * 64;
+  x.nh = min(64, a.N1 - x.h0);
+  x.hg = hg;
+  x.which = x.isdk ? 0 : 64;
+  x.citem = citem;
+  const bool dups = nunits > nrows;          // some row repeats keys
+  if (x.isdk) {
+    if (dups) kv_dense_body<9, true>(a, x, Bt0, Bt1);
+    else kv_dense_body<9, false>(a, x, Bt0, Bt1);
+  } else {
+    if (dups) kv_dense_body<8, true>(a, x, Bt0, Bt1);
+    else kv_dense_body<8, false>(a, x, Bt0, Bt1);
+  }
   if (threadIdx.x == 0) *flag = 1;
 }
 
@@ -527,7 +540,7 @@ __global__ void __launch_bounds__(kThreads) kv_reduce_kernel(DenseArgs a) {
 
 // ------------------------------------------------------------------------------------------
 hipError_t launch_sort_rows(const DenseArgs& a, int64_t rows, int np, hipStream_t st) {
-  hipLaunchKernelGGL(sort_rows_kernel, dim3((unsigned)rows), dim3(kThreads), (size_t)np * 4, st, a, np);
+  hipLaunchKernelGGL(sort_rows_kernel, dim3((unsigned)rows), dim3(kThreads), (size_t)np * 4 + kMapWin * 2, st, a, np);
   return hipGetLastError();
 }
 
@@ -551,7 +564,7 @@ hipError_t launch_kv_reduce(const DenseArgs& a, int64_t keys, hipStream_t st) {
 
 hipError_t set_dense_attributes() {
   return hipFuncSetAttribute(reinterpret_cast<const void*>(&sort_rows_kernel),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, 65536);
+                             hipFuncAttributeMaxDynamicSharedMemorySize, 65536 + kMapWin * 2);
 }
 
 }  // namespace sfag

@@ -52,6 +52,7 @@ struct DenseArgs {
   int32_t* count;         // [rows]
   int32_t* maxdup;        // [rows]
   int32_t* offs;          // [rows, maxblk + 1]
+  int16_t* kpos;          // [rows, kstride] first sorted position of each key, -1: not selected
   const uint16_t* dsp;    // [rows * topk, hgc, 128]
   float* part;            // [hgc, citems, kBk, 1088]
   int32_t* flag;          // [hgc, citems]
@@ -63,7 +64,7 @@ struct DenseArgs {
   uint16_t* dv;           // [keys, 512]
   Lens lens;
   int64_t S1, S2;
-  int B, N1, topk, mode3, layout_tnd, hgc, maxblk, items, citems;
+  int B, N1, topk, mode3, layout_tnd, hgc, maxblk, items, citems, kstride;
   float scale;
 };
 
