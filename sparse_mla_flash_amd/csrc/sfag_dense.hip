@@ -215,6 +215,7 @@ constexpr int kBtPitch = 152;                         // B tile row: up to 144 c
 constexpr int kBtRowChunks = kBtPitch / 8;            // 19 16-byte chunks per row
 constexpr int kBtBlocks = 20;                         // 64 rows x 19 chunks in 20 blocks of 64
 static_assert(kBtBlocks * 64 >= 64 * kBtRowChunks && kBtBlocks % 4 == 0, "B tile blocks");
+constexpr int kUnitLoads = kBtBlocks / 4 + 4 + 8;    // global loads issued per unit: B, map, records
 
 // Shared state of one key-major workgroup, set up by kv_dense_kernel.
 struct KvCtx {
@@ -256,6 +257,7 @@ __device__ __forceinline__ void kv_dense_body(const DenseArgs& a, const KvCtx& x
     else boff[i] = (x.h0 + h) * kDn + (x.isdk ? col : col - kDk);
   }
   const uint16_t* bmain = x.isdk ? a.q : a.dout;
+  const int rstride = a.hgc * 128;     // elements between the records of consecutive slots
 
   auto next_unit = [&](int& ri, int& L) {
     if (!DUPS) {
@@ -272,10 +274,8 @@ __device__ __forceinline__ void kv_dense_body(const DenseArgs& a, const KvCtx& x
   {                                                                                            \
     const int64_t row_ = x.qstart + x.i0 + s_row[max((RI), 0)];                                \
     const int16_t* kp_ = a.kpos + row_ * a.kstride;                                            \
-    _Pragma("unroll") for (int kt = 0; kt < 4; ++kt) {                                         \
-      const int v_ = kp_[kcol[kt]];                                                            \
-      MP[kt] = (RI) < 0 ? -1 : v_;                                                             \
-    }                                                                                          \
+    /* used only by the next unit's record loads, which also check RI */                      \
+    _Pragma("unroll") for (int kt = 0; kt < 4; ++kt) MP[kt] = kp_[kcol[kt]];                   \
   }
 
 // Record fragments of unit (RI, L) from its map entries MP: lane (g, c) of key tile kt, head
@@ -291,9 +291,14 @@ __device__ __forceinline__ void kv_dense_body(const DenseArgs& a, const KvCtx& x
         e_ += (L);                                                                             \
         ok_ = ok_ && e_ < a.topk && a.sorted[row_ * a.topk + min(e_, a.topk - 1)] == kcol[kt]; \
       }                                                                                        \
-      const uint16_t* src_ = ok_ ? rbase_ + (int64_t)e_ * a.hgc * 128 : zsrc + 8 * g;          \
-      AF[kt][0] = *reinterpret_cast<const bf16x8*>(src_);                                      \
-      AF[kt][1] = *reinterpret_cast<const bf16x8*>(src_ + 32);                                 \
+      /* lanes of unselected keys load nothing (their fragment is zero) */                  \
+      const uint16_t* src_ = rbase_ + (uint32_t)(max(e_, 0) * rstride);                        \
+      AF[kt][0] = bf16x8{};                                                                    \
+      AF[kt][1] = bf16x8{};                                                                    \
+      if (ok_) {                                                                               \
+        AF[kt][0] = *reinterpret_cast<const bf16x8*>(src_);                                    \
+        AF[kt][1] = *reinterpret_cast<const bf16x8*>(src_ + 32);                               \
+      }                                                                                        \
     }                                                                                          \
   }
 
@@ -318,16 +323,26 @@ __device__ __forceinline__ void kv_dense_body(const DenseArgs& a, const KvCtx& x
   }
 
 // MFMAs of one unit: NFT column tiles x 2 head steps x 4 key tiles, B fragments by transposing
-// reads of the B tile, one (column tile, head step) ahead.
+// reads of the B tile, three (column tile, head step) steps ahead.
+#define SFAG_BFRAG(BT, Q) lds_frag_trp((BT), 32 * ((Q) & 1), 16 * ((Q) >> 1), kBtPitch, lane)
 #define SFAG_MMA(BT, AF)                                                                       \
   {                                                                                            \
-    bf16x8 bf = lds_frag_trp((BT), 0, 0, kBtPitch, lane);                                      \
+    bf16x8 bq[2 * NFT];                                                                        \
+    bq[0] = SFAG_BFRAG(BT, 0);                                                                 \
+    bq[1] = SFAG_BFRAG(BT, 1);                                                                 \
+    bq[2] = SFAG_BFRAG(BT, 2);                                                                 \
     _Pragma("unroll") for (int q = 0; q < 2 * NFT; ++q) {                                      \
+      if (q + 3 < 2 * NFT) bq[q + 3] = SFAG_BFRAG(BT, q + 3);                                  \
       const int ft = q >> 1, ks = q & 1;                                                       \
-      bf16x8 nb = bf;                                                                          \
-      if (q + 1 < 2 * NFT) nb = lds_frag_trp((BT), 32 * ((q + 1) & 1), 16 * ((q + 1) >> 1), kBtPitch, lane); \
-      _Pragma("unroll") for (int kt = 0; kt < 4; ++kt) acc[kt][ft] = mfma(AF[kt][ks], bf, acc[kt][ft]); \
-      bf = nb;                                                                                 \
+      _Pragma("unroll") for (int kt = 0; kt < 4; ++kt) acc[kt][ft] = mfma(AF[kt][ks], bq[q], acc[kt][ft]); \
+    }                                                                                          \
+    /* issue order: the next unit's global loads (B tile, map, records), the first three     \
+       fragments, then (fragment three steps ahead, 4 MFMAs) pairs */                         \
+    __builtin_amdgcn_sched_group_barrier(0x020, kUnitLoads, 0);                                \
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);                                         \
+    _Pragma("unroll") for (int q = 0; q < 2 * NFT; ++q) {                                      \
+      if (q + 3 < 2 * NFT) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                  \
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);                                       \
     }                                                                                          \
   }
 
@@ -337,47 +352,54 @@ __device__ __forceinline__ void kv_dense_body(const DenseArgs& a, const KvCtx& x
 #pragma unroll
     for (int ft = 0; ft < NFT; ++ft) acc[kt][ft] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // prologue: map of units 0 and 1, B tile and record fragments of unit 0
+  // Rotating registers (loaded one unit before they are used): f1 = record fragments, m0 =
+  // map, bs2 = B tile.  Each unit first moves them into f0 / m1 / bs (their loads were issued
+  // a whole unit earlier), then issues the next loads into the freed registers.
+  // prologue: B tile of unit 0 stored; f1 = fragments of unit 0, m0 = map of unit 1,
+  // bs2 = B tile of unit 1
   int ri1 = 0, L1 = 0;                 // cursor of unit u + 1 (here: of unit 0)
   int m0[4], m1[4];
   bf16x8 f0[4][2], f1[4][2];
-  u32x4 bs[kBtBlocks / 4];
-  SFAG_MAP_LOAD(m0, ri1)
+  u32x4 bs[kBtBlocks / 4], bs2[kBtBlocks / 4];
+  SFAG_MAP_LOAD(m1, ri1)
   SFAG_B_LOAD(bs, ri1)
   int ri2 = ri1, L2 = L1;
   next_unit(ri2, L2);
-  SFAG_MAP_LOAD(m1, ri2)
-  SFAG_A_LOAD(f0, m0, ri1, L1)
+  SFAG_A_LOAD(f1, m1, ri1, L1)
+  SFAG_MAP_LOAD(m0, ri2)
   SFAG_B_STORE(Bt0, bs)
+  SFAG_B_LOAD(bs2, ri2)
   ri1 = ri2;
   L1 = L2;                             // cursor of unit 1
   __syncthreads();
 
-  // unit u: loads of unit u + 1 (B tile, record fragments from map m1) and of the map of
-  // unit u + 2, MFMAs of unit u (buffer u & 1, fragments f0), then unit u + 1's B tile into
-  // the other buffer
+  // unit u: rotate, then loads of the B tile and map of unit u + 2 and of the record fragments
+  // of unit u + 1, MFMAs of unit u (buffer u & 1), unit u + 1's B tile into the other buffer
   for (int u = 0; u < nunits; ++u) {
     uint16_t* BC = (u & 1) ? Bt1 : Bt0;
     uint16_t* BN = (u & 1) ? Bt0 : Bt1;
-    int ri2_ = ri1, L2_ = L1;
-    next_unit(ri2_, L2_);
-    SFAG_B_LOAD(bs, ri1)
-    SFAG_MAP_LOAD(m0, ri2_)
-    SFAG_A_LOAD(f1, m1, ri1, L1)
-    SFAG_MMA(BC, f0)
-    SFAG_B_STORE(BN, bs)
-    __syncthreads();
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
       f0[kt][0] = f1[kt][0];
       f0[kt][1] = f1[kt][1];
       m1[kt] = m0[kt];
     }
+#pragma unroll
+    for (int i = 0; i < kBtBlocks / 4; ++i) bs[i] = bs2[i];
+    int ri2_ = ri1, L2_ = L1;
+    next_unit(ri2_, L2_);
+    SFAG_B_LOAD(bs2, ri2_)
+    SFAG_MAP_LOAD(m0, ri2_)
+    SFAG_A_LOAD(f1, m1, ri1, L1)
+    SFAG_MMA(BC, f0)
+    SFAG_B_STORE(BN, bs)
+    __syncthreads();
     ri1 = ri2_;
     L1 = L2_;
   }
 #undef SFAG_B_STORE
 #undef SFAG_MMA
+#undef SFAG_BFRAG
 #undef SFAG_B_LOAD
 #undef SFAG_A_LOAD
 #undef SFAG_MAP_LOAD
@@ -461,6 +483,7 @@ __global__ void __launch_bounds__(kThreads, 1) kv_dense_kernel(DenseArgs a) {
   const int nrows = s_nrows;
   int nunits = 0;                       // units: one per (row, repeat layer)
   for (int t = 0; t < nrows; ++t) nunits += s_lay[t];
+  const bool dups = nunits > nrows;     // some row repeats keys
   if (nrows == 0) {
     if (threadIdx.x == 0) *flag = 0;
     return;
@@ -480,7 +503,6 @@ __global__ void __launch_bounds__(kThreads, 1) kv_dense_kernel(DenseArgs a) {
   x.hg = hg;
   x.which = x.isdk ? 0 : 64;
   x.citem = citem;
-  const bool dups = nunits > nrows;          // some row repeats keys
   if (x.isdk) {
     if (dups) kv_dense_body<9, true>(a, x, Bt0, Bt1);
     else kv_dense_body<9, false>(a, x, Bt0, Bt1);
