@@ -107,6 +107,19 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// B fragment of a 16x16x32 MFMA (lane (g, c): rows 8 g .. 8 g + 7 of column n0 + c) from a
+// chunk-major tile: element (row k, column n) at ((n / 8) * 32 + k) * 8 + n % 8, i.e. 16-byte
+// chunks of 8 columns stored [column chunk][32 rows]; two transposing reads.
+__device__ __forceinline__ bf16x8 lds_frag_tr_cm(const uint16_t* tile, int n0, int lane) {
+  const int g = lane >> 4, j = lane & 15;
+  const int k = 8 * g + (j >> 2), n = n0 + 4 * (j & 3);
+  const uint16_t* p = tile + ((n >> 3) * 32 + k) * 8 + (n & 7);
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * 8));
+  const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
 __device__ __forceinline__ uint16_t f2bf(float f) {
   // round to nearest even; NaN stays NaN
   uint32_t u = __float_as_uint(f);

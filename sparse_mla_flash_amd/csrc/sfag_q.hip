@@ -19,7 +19,10 @@
 //     partial sums of the key tile the other one finishes (16 keys) through LDS.
 //   dQ: wave w owns output dims 144 w .. 144 w + 143 for all 64 heads, so each gathered key
 //     element is read (transposed) once per workgroup.
-// Pipeline: key chunks are triple-buffered in LDS and gathered straight from global memory
+// Key tiles are stored chunk-major in LDS ([72 chunks of 16 B][32 keys]): one direct-to-LDS
+// block (64 lanes x 16 B) is then two chunk columns of all 32 keys, so a gathering lane always
+// handles the same key (lane % 32) and each of its loads is one add to that key's row address.
+// Pipeline: key tiles are triple-buffered in LDS and gathered straight from global memory
 // one chunk ahead (global_load_lds).  The score MFMAs of chunk c and the dQ MFMAs of chunk
 // c - 1 sit in one block so that the scheduler can interleave them; two barriers per chunk.
 #include "sfag_device.h"
@@ -30,17 +33,15 @@ namespace sfag {
 namespace {
 constexpr int kKC = 32;
 constexpr int kThreads = 256;
-constexpr int kPitch = kDk + 8;                  // 584: padded key row (conflict-free 16-byte reads)
-constexpr int kRowChunks = kPitch / 8;           // 73 16-byte chunks per padded row
+constexpr int kChunks = kDk / 8;                 // 72 16-byte chunks per key row (64 value + 8 rope)
 constexpr int kHtPitch = 64 + 8;                 // DSt row pitch
-constexpr int kBlocks = 40;                      // 64-chunk blocks per key tile: 37 hold data,
-                                                 // padded to 10 per wave (the rest load zeros)
-static_assert(kBlocks * 64 >= kKC * kRowChunks && kBlocks % 4 == 0, "gather blocks");
+constexpr int kBlocks = kChunks / 2;             // 36 direct-to-LDS blocks (2 chunk columns) per tile
+static_assert(kBlocks % 4 == 0, "gather blocks per wave");
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kLdsK = kBlocks * 64 * 16;         // one key chunk [32][584], rounded to whole blocks
+constexpr int kLdsK = kBlocks * 64 * 16;         // one key tile, chunk-major: [72 chunks][32 keys][16 B]
 constexpr int kLdsDS = kKC * kHtPitch * 2;       // DSt [32 keys][72]
 constexpr int kLdsX = 4 * 4 * 64 * 16;           // partial-sum exchange: [wave][4 tiles][64 lanes] f32x4
-constexpr int kLdsTotal = 3 * kLdsK + 3 * kLdsDS + kLdsX + 3 * kKC * 8 + 3 * 64 * 4 + 2 * 257 * 4;
+constexpr int kLdsTotal = 3 * kLdsK + 3 * kLdsDS + kLdsX + 3 * 64 * 4 + 2 * 257 * 4;
 static_assert(kLdsTotal <= 160 * 1024, "LDS budget");
 // s_waitcnt operand: vmcnt(4), expcnt and lgkmcnt at their maximum.  Vector memory operations
 // complete in issue order, so this waits for all but the 4 most recent (the record stores).
@@ -54,11 +55,11 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t Kb0[kLdsK / 2], Kb1[kLdsK / 2], Kb2[kLdsK / 2];
   __shared__ __attribute__((aligned(16))) uint16_t Db0[kKC * kHtPitch], Db1[kKC * kHtPitch], Db2[kKC * kHtPitch];
   __shared__ __attribute__((aligned(16))) f32x4 X[4 * 4 * 64];        // partial-sum exchange [wave][4][64]
-  __shared__ int64_t krow3[3 * kKC];                                  // key rows of 3 chunks
   __shared__ float sD[64], sM[64], sIL[64];
   __shared__ int32_t cum[2 * 257];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar
   const int g = lane >> 4, c = lane & 15;
   const int hh = wave >> 1, dh = wave & 1;
   // longest rows (highest positions under the causal mask) first
@@ -81,11 +82,9 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
   const int nchunk = (count + kKC - 1) / kKC;
 
   // ---- per-row setup --------------------------------------------------------------------------
-  // key rows of chunks 0 and 1
-  if (threadIdx.x < 2 * kKC) {
-    const int e = threadIdx.x;
-    krow3[e] = e < count ? geo.kstart + srow[e] : -1;
-  }
+  // gathering lanes: key slot gkey of every chunk, chunk column gcol of every block
+  const int gkey = lane & 31, gcol = lane >> 5;
+  int32_t gsv = srow[min(gkey, count - 1)];               // sorted position of chunk 0's key
   // D = rowsum(dO * out) and the statistics of every head
   {
     const int h = threadIdx.x >> 2, part = threadIdx.x & 3;
@@ -152,25 +151,19 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
     }
   const float zscale = a.scale * kLog2e;
 
-  // Gather of one 32-key chunk straight from global memory into a key buffer: the buffer is
-  // 37 blocks of 64 consecutive 16-byte chunks, and lane i of a block lands at chunk
-  // block * 64 + i (global_load_lds), so each lane loads the source chunk of that position.
-  // Padding positions and slots past the row's valid count read the zero row.
-#define SFAG_GATHER_ASYNC(KS, KR)                                                              \
+  // Gather of chunk CH (this lane's key: sorted position SV) into key buffer KS: block b of the
+  // tile holds chunk columns 2 b and 2 b + 1; wave w loads blocks w, w + 4, ..., w + 32 (the
+  // last one: rope chunks).  Slots past the row's valid count read the zero row.
+#define SFAG_GATHER_ASYNC(KS, CH, SV)                                                          \
   {                                                                                            \
-    int64_t r_[kBlocks / 4];                                                                   \
-    _Pragma("unroll") for (int i = 0; i < kBlocks / 4; ++i) {                                  \
-      const int P = (wave + 4 * i) * 64 + lane;                                                \
-      const int rk = P / kRowChunks;                                                           \
-      r_[i] = rk < kKC ? (KR)[rk] : -1;                                                        \
-    }                                                                                          \
-    _Pragma("unroll") for (int i = 0; i < kBlocks / 4; ++i) {                                  \
-      const int blk = wave + 4 * i;                                                            \
-      const int P = blk * 64 + lane;                                                           \
-      const int lc = P % kRowChunks;                                                           \
-      const int64_t r = r_[i];                                                                 \
-      const uint16_t* src = (r < 0 || lc >= kDk / 8) ? a.zero_row                              \
-                          : (lc < 64 ? a.k + r * kDn + lc * 8 : a.kr + r * kDr + (lc - 64) * 8); \
+    const bool ok_ = (CH) * kKC + gkey < count;                                                \
+    const int64_t r_ = geo.kstart + (SV);                                                      \
+    const uint16_t* pk_ = ok_ ? a.k + r_ * kDn : a.zero_row;                                   \
+    const uint16_t* pr_ = ok_ ? a.kr + r_ * kDr : a.zero_row;                                  \
+    _Pragma("unroll") for (int j = 0; j < kBlocks / 4; ++j) {                                  \
+      const int blk = wave + 4 * j;                                                            \
+      const uint16_t* src = j < kBlocks / 4 - 1 ? pk_ + (2 * blk + gcol) * 8                   \
+                                                : pr_ + (2 * blk + gcol - 64) * 8;             \
       __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)((KS) + blk * 512), 16, 0, 0); \
     }                                                                                          \
   }
@@ -184,16 +177,18 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
         sacc[ht][kt] = f32x4{0.f, 0.f, 0.f, 0.f};                                              \
         pacc[ht][kt] = f32x4{0.f, 0.f, 0.f, 0.f};                                              \
       }                                                                                        \
-    const uint16_t* kr0 = (KS) + (16 * dh + c) * kPitch + 8 * g;                               \
-    const uint16_t* kr1 = (KS) + (16 - 16 * dh + c) * kPitch + 8 * g;                          \
-    bf16x8 kb0 = *reinterpret_cast<const bf16x8*>(kr0 + 256 * dh);                             \
-    bf16x8 kb1 = *reinterpret_cast<const bf16x8*>(kr1 + 256 * dh);                             \
+    /* chunk-major tile: element (chunk, key) at (chunk * 32 + key) * 8; lane (g, c) of step  \
+       ks reads chunk 32 dh + 4 ks + g (value dims) or 64 + 4 dh + g (rope) */                 \
+    const uint16_t* kr0 = (KS) + (g * kKC + 16 * dh + c) * 8;                                  \
+    const uint16_t* kr1 = (KS) + (g * kKC + 16 - 16 * dh + c) * 8;                             \
+    bf16x8 kb0 = *reinterpret_cast<const bf16x8*>(kr0 + 32 * dh * kKC * 8);                    \
+    bf16x8 kb1 = *reinterpret_cast<const bf16x8*>(kr1 + 32 * dh * kKC * 8);                    \
     _Pragma("unroll") for (int ks = 0; ks < 9; ++ks) {                                         \
       bf16x8 nb0 = kb0, nb1 = kb1;                                                             \
       if (ks < 8) {                     /* fragments of the next step, read ahead */           \
-        const int col = ks < 7 ? 256 * dh + 32 * (ks + 1) : kDn + 32 * dh;                     \
-        nb0 = *reinterpret_cast<const bf16x8*>(kr0 + col);                                     \
-        nb1 = *reinterpret_cast<const bf16x8*>(kr1 + col);                                     \
+        const int ch = ks < 7 ? 32 * dh + 4 * (ks + 1) : 64 + 4 * dh;                          \
+        nb0 = *reinterpret_cast<const bf16x8*>(kr0 + ch * kKC * 8);                            \
+        nb1 = *reinterpret_cast<const bf16x8*>(kr1 + ch * kKC * 8);                            \
       }                                                                                        \
       _Pragma("unroll") for (int ht = 0; ht < 2; ++ht) {                                       \
         sacc[ht][0] = mfma(qA[ht][ks], kb0, sacc[ht][0]);                                      \
@@ -206,6 +201,17 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
       kb0 = nb0;                                                                               \
       kb1 = nb1;                                                                               \
     }                                                                                          \
+    /* issue order: per step one of the next chunk's gather loads (issued just before this   \
+       block; they drain through the load path while the MFMAs run), the next step's key     \
+       fragments, the step's MFMAs */                                                         \
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                                         \
+    _Pragma("unroll") for (int ks = 0; ks < 8; ++ks) {                                         \
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                                       \
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                                       \
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);                                       \
+    }                                                                                          \
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                                         \
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);                                         \
   }
 
 // dQ[64 heads][144 w .. 144 w + 143] += dS[64][32 keys] K[32 keys][dims] of the previous chunk
@@ -213,10 +219,10 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
   {                                                                                            \
     bf16x8 dsa[4];                                                                             \
     _Pragma("unroll") for (int t = 0; t < 4; ++t) dsa[t] = lds_frag_trp((DST), 0, 16 * t, kHtPitch, lane); \
-    bf16x8 kb = lds_frag_trp((KS), 0, 144 * wave, kPitch, lane);                               \
+    bf16x8 kb = lds_frag_tr_cm((KS), 144 * wave, lane);                                        \
     _Pragma("unroll") for (int nt = 0; nt < 9; ++nt) {                                         \
       bf16x8 nb = kb;                                                                          \
-      if (nt < 8) nb = lds_frag_trp((KS), 0, 144 * wave + 16 * (nt + 1), kPitch, lane);        \
+      if (nt < 8) nb = lds_frag_tr_cm((KS), 144 * wave + 16 * (nt + 1), lane);                 \
       _Pragma("unroll") for (int t = 0; t < 4; ++t) dqacc[t][nt] = mfma(dsa[t], kb, dqacc[t][nt]); \
       kb = nb;                                                                                 \
     }                                                                                          \
@@ -241,8 +247,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
     const f32x4* xi = X + (wave ^ 1) * 4 * 64;                                                 \
     const int c0 = (CI) * kKC;                                                                 \
     const int key = 16 * dh + c;                                                               \
-    const int64_t* kr_cur = krow3 + ((CI) % 3) * kKC;                                          \
-    const bool valid = kr_cur[key] >= 0;                                                       \
+    const bool valid = c0 + key < count;                                                       \
     uint16_t* rec = valid ? a.dsp + (((int64_t)row * a.topk + c0 + key) * a.hgc + hg) * 128 : a.trash; \
     _Pragma("unroll") for (int ht = 0; ht < 2; ++ht) {                                         \
       const f32x4 s = sacc[ht][0] + xi[ht * 64 + lane];                                        \
@@ -268,26 +273,27 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
 #pragma unroll
     for (int nt = 0; nt < 9; ++nt) dqacc[t][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  SFAG_GATHER_ASYNC(Kb0, krow3)
+  SFAG_GATHER_ASYNC(Kb0, 0, gsv)
+  gsv = srow[min(kKC + gkey, count - 1)];                 // chunk 1
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
 // One chunk CI: gather of chunk CI + 1 into KN, scores of chunk CI (buffer KC), dQ of chunk
-// CI - 1 (buffers KP, DP; skipped for chunk 0), swap and finish into DC.  The key rows of
-// chunk CI + 2 are loaded branch-free and only used after the end-of-chunk wait.
+// CI - 1 (buffers KP, DP; skipped for chunk 0), swap and finish into DC.  The sorted position
+// of this lane's key of chunk CI + 2 is loaded branch-free and only used after the
+// end-of-chunk wait.
 #define SFAG_CHUNK(CI, KC, KP, KN, DC, DP, WITH_DQ)                                            \
   {                                                                                            \
     const int ci_ = (CI);                                                                      \
-    if (ci_ + 1 < nchunk) SFAG_GATHER_ASYNC(KN, krow3 + ((ci_ + 1) % 3) * kKC)                 \
-    const int e2 = (ci_ + 2) * kKC + (int)threadIdx.x;                                         \
-    const int32_t sv = srow[min(e2, count - 1)];                                               \
+    if (ci_ + 1 < nchunk) SFAG_GATHER_ASYNC(KN, ci_ + 1, gsv)                                  \
+    const int32_t sv = srow[min((ci_ + 2) * kKC + gkey, count - 1)];                           \
     SFAG_SCORES(KC)                                                                            \
     SFAG_XCHG()                                                                                \
     if (WITH_DQ) SFAG_DQ(KP, DP)                                                               \
     SFAG_FINISH(ci_, DC)                                                                       \
     /* everything but the 4 record stores just issued (chunk CI + 1 has landed) */            \
     __builtin_amdgcn_s_waitcnt(kWaitAllButRecords);                                            \
-    if (threadIdx.x < kKC) krow3[((ci_ + 2) % 3) * kKC + threadIdx.x] = e2 < count ? geo.kstart + sv : -1; \
+    gsv = sv;                                                                                  \
     __syncthreads();                                                                           \
   }
 
