@@ -59,7 +59,7 @@ struct Plan {
   // workspace layout
   uint64_t off_acc = 0, off_partial = 0, off_keys0 = 0, off_keys1 = 0, off_sorttmp = 0;
   uint64_t off_sorted = 0, off_count = 0, off_maxdup = 0, off_offs = 0, off_dsp = 0, off_part = 0, off_flag = 0;
-  uint64_t off_zero = 0, off_ilist = 0, off_imap = 0, off_trash = 0, off_kpos = 0;
+  uint64_t off_zero = 0, off_ilist = 0, off_imap = 0, off_trash = 0, off_kpos = 0, off_bt = 0;
   uint64_t sort_tmp_bytes = 0, bytes = 0;
   int64_t det_rows = 0;            // query rows per deterministic launch
   int end_bit = 64;
@@ -242,6 +242,8 @@ sfag_status make_plan(const sfag_dims* dims, const int32_t* sq, const int32_t* s
     off = align_up(off + 576 * 2);
     p->off_trash = off;                 // write-only sink for the records of invalid slots
     off = align_up(off + 128 * 2);
+    p->off_bt = off;                    // Q | QRope | dO, heads innermost (key-major B operand)
+    off = align_up(off + (uint64_t)p->rows * p->hg_count * kDacc * 64 * 2);
     p->bytes = off;
     return SFAG_OK;
   }
@@ -410,6 +412,7 @@ sfag_status sfag_sparse_flash_attention_grad(
     da.kpos = reinterpret_cast<int16_t*>(ws + p.off_kpos);
     da.kstride = (int)(p.maxblk * sfag::kBk);
     da.dsp = reinterpret_cast<uint16_t*>(ws + p.off_dsp);
+    da.bt = reinterpret_cast<uint16_t*>(ws + p.off_bt);
     da.part = reinterpret_cast<float*>(ws + p.off_part);
     da.flag = reinterpret_cast<int32_t*>(ws + p.off_flag);
     da.zero_row = reinterpret_cast<uint16_t*>(ws + p.off_zero);
@@ -443,6 +446,8 @@ sfag_status sfag_sparse_flash_attention_grad(
     if (g_ev[0]) SFAG_HIP(hipEventRecord(g_ev[0], s));
     SFAG_HIP(sfag::launch_bwd_q(a, p.rows, p.hg_count, s));
     if (g_ev[1]) SFAG_HIP(hipEventRecord(g_ev[1], s));
+    // after bwd_q, so that its 1.1 GB of writes do not flush what bwd_q finds in the caches
+    SFAG_HIP(sfag::launch_transpose_rows(da, p.rows, s));
     if (g_ev[2]) SFAG_HIP(hipEventRecord(g_ev[2], s));
     SFAG_HIP(sfag::launch_kv_dense(da, s));
     if (g_ev[3]) SFAG_HIP(hipEventRecord(g_ev[3], s));

@@ -15,6 +15,9 @@
 // Kernels:
 //   sort_rows_kernel   per row: valid key positions sorted ascending, their count, the largest
 //                      multiplicity of a repeated key, and the start of every 256-key block
+//   transpose_rows_kernel  per (row, head group): Q | QRope | dO as [1088 columns][64 heads],
+//                      the layout whose 16-byte pieces are MFMA B fragments of the contraction
+//                      over heads
 //   kv_dense_kernel    (item = key block x row segment, column slice, head group) partial sums
 //   kv_reduce_kernel   per key row: sum of the partials in (head group, segment) order -> bf16
 #include "sfag_device.h"
@@ -191,6 +194,63 @@ __global__ void __launch_bounds__(1024) item_list_kernel(DenseArgs a) {
   }
 }
 
+// ------------------------------------------------------------------------------------------
+// One workgroup per (row, head group): the row's 64 heads x 1088 columns (Q 512 | QRope 64 |
+// dO 512) rewritten column-major, bt[row][hg][col][h], heads past N1 zero.  Per 64-column
+// chunk the [64 heads][64 cols] tile goes through LDS (pitch 72) and comes back by
+// transposing reads: lane (g, c) of wave w gets heads 32 s + 8 g .. + 7 of column 16 w + c,
+// one 16-byte store.  The next chunk's loads are in flight during the current chunk's reads.
+constexpr int kTrPitch = 72;
+constexpr int kTrChunks = kDacc / 64;      // 17
+
+__global__ void __launch_bounds__(kThreads) transpose_rows_kernel(DenseArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[2][64 * kTrPitch];
+  const int64_t row = blockIdx.x;
+  const int hg = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const int h0 = hg * 64;
+  // this thread's two 16-byte pieces of a chunk: head hh[i], columns 8 cc[i] .. + 7
+  int hh[2], cc[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int P = (int)threadIdx.x + kThreads * i;
+    hh[i] = P >> 3;
+    cc[i] = P & 7;
+  }
+  auto load = [&](u32x4* r, int k) {
+    const int col0 = 64 * k;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int h = h0 + hh[i];
+      const uint16_t* src = a.zero_row;
+      if (h < a.N1) {
+        if (col0 < kDn) src = a.q + (row * a.N1 + h) * kDn + col0;
+        else if (col0 < kDk) src = a.qr + (row * a.N1 + h) * kDr + (col0 - kDn);
+        else src = a.dout + (row * a.N1 + h) * kDn + (col0 - kDk);
+        src += 8 * cc[i];
+      }
+      r[i] = *reinterpret_cast<const u32x4*>(src);
+    }
+  };
+  uint16_t* out = a.bt + (row * a.hgc + hg) * (int64_t)kDacc * 64;
+  u32x4 r[2];
+  load(r, 0);
+#pragma unroll 1
+  for (int k = 0; k < kTrChunks; ++k) {
+    uint16_t* t = tile[k & 1];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) *reinterpret_cast<u32x4*>(t + hh[i] * kTrPitch + 8 * cc[i]) = r[i];
+    if (k + 1 < kTrChunks) load(r, k + 1);
+    lds_barrier();
+#pragma unroll
+    for (int sh = 0; sh < 2; ++sh) {
+      const bf16x8 v = lds_frag_trp(t, 32 * sh, 16 * wave, kTrPitch, lane);
+      *reinterpret_cast<bf16x8*>(out + (64 * k + 16 * wave + c) * 64 + 32 * sh + 8 * g) = v;
+    }
+  }
+}
+
 // Workgroup = (live item, column slice, head group).  Workgroups are dealt to the 8 XCDs
 // round-robin (x = w % 8), so XCD x is given the contiguous run of live items
 // [x n, x n + n) and walks it as  half (dK slices, then dV slices) > item > slice: the
@@ -198,153 +258,66 @@ __global__ void __launch_bounds__(1024) item_list_kernel(DenseArgs a) {
 // column slices of one half, which share the segment's Q / dO rows and dS / P records in
 // that XCD's L2.
 // Column slices 0..3: dK columns 144 s .. 144 s + 143 (the last one holds the rope columns);
-// 4..7: dV columns 128 (s - 4) .. + 127.  Wave w owns key tiles 4w .. 4w + 3 (64 keys).
+// 4..7: dV columns 128 (s - 4) .. + 127.  Wave w owns keys kb0 + 64 w .. + 63.
 //
-// For every row u of the segment that selects keys of the block (a "unit"; a row that
-// repeats keys gives one unit per repeat layer L, the L-th occurrence of each key):
+// For every row of the segment that selects keys of the block (a "unit"; a row that repeats
+// keys gives one unit per repeat layer L, the L-th occurrence of each key):
 //   A = [256 keys x 64 heads] of dS (dK slices) or P (dV slices), zero where the row did not
 //       select the key.  MFMA A fragments come straight from the pair records in global
-//       memory: lane (g, c) of key tile kt needs heads 8 g .. 8 g + 7 of key 16 kt + c, found
-//       through the row's key -> position map (unselected keys read the zero row).
-//   B = the row's [64 heads x cols] Q (or dO) slice, staged in LDS by direct-to-LDS loads
-//       and read with transposing reads.
-//   acc[keys][cols] += A B  on the 16x16x32 bf16 MFMA, fp32 in registers.
-// Pipeline per unit u: map entries of unit u + 2, record fragments of unit u + 1 and the B
-// tile of unit u + 1 are requested, then the MFMAs of unit u run; one barrier per unit.
-constexpr int kBtPitch = 152;                         // B tile row: up to 144 columns + 8
-constexpr int kBtRowChunks = kBtPitch / 8;            // 19 16-byte chunks per row
-constexpr int kBtBlocks = 20;                         // 64 rows x 19 chunks in 20 blocks of 64
-static_assert(kBtBlocks * 64 >= 64 * kBtRowChunks && kBtBlocks % 4 == 0, "B tile blocks");
-constexpr int kUnitLoads = kBtBlocks / 4 + 4 + 8;    // global loads issued per unit: B, map, records
+//       memory: lane (g, c) handles keys kb0 + 64 w + 4 c + kt (kt = 0..3) as row c of key
+//       tile kt and needs heads 8 g .. 8 g + 7 (+ 32) of each, found through the row's
+//       key -> position map (one 8-byte load for the 4 keys); unselected keys load nothing.
+//   B = the row's [64 heads x cols] Q (or dO) slice, read from the column-major copy made by
+//       transpose_rows_kernel (one contiguous run of 2 KB per column tile), staged in LDS as
+//       [column][8 chunks of 8 heads + 1 pad chunk] and read as whole 16-byte fragments.
+//   acc[keys][cols] += A B  on the 16x16x32 bf16 MFMA, fp32 in registers; accumulator row
+//       4 g + v of key tile kt is key kb0 + 64 w + 4 (4 g + v) + kt.
+// Two workgroups share a CU (at most 256 registers per lane), so each unit is simple: its
+// records are requested and used at once, the map and the B tile of the next unit are
+// requested before its MFMAs, and the other workgroup runs while this one waits.
+constexpr int kBtColChunks = 9;                       // B tile column: 8 chunks of 8 heads + 1 pad
+constexpr int kBtElems = 144 * kBtColChunks * 8;      // up to 144 columns
 
 // Shared state of one key-major workgroup, set up by kv_dense_kernel.
 struct KvCtx {
-  const uint16_t* Bt0;
-  const uint16_t* Bt1;
   const int16_t* s_row;
   const uint16_t* s_lay;
   int64_t qstart;
-  int i0, nrows, nunits, kb0, colbase, h0, nh, hg, which, citem;
+  int i0, nrows, kb0, colbase, hg, which, citem;
   bool isdk;
 };
 
 // Main loop of one workgroup with NFT column tiles (9: dK slice, 8: dV slice).  DUPS: some
-// row of the item repeats keys (units = (row, layer)); otherwise units are the rows.
+// row of the item repeats keys, so units are (row, layer) pairs; otherwise units are rows.
 template <int NFT, bool DUPS>
-__device__ __forceinline__ void kv_dense_body(const DenseArgs& a, const KvCtx& x, uint16_t* Bt0, uint16_t* Bt1) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+__device__ __forceinline__ void kv_dense_units(const DenseArgs& a, const KvCtx& x, uint16_t* Bt0, uint16_t* Bt1) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int g = lane >> 4, c = lane & 15;
-  const uint16_t* zsrc = a.zero_row;
+  const int nrows = x.nrows;
   const int16_t* s_row = x.s_row;
   const uint16_t* s_lay = x.s_lay;
-  const int nrows = x.nrows;
-  const int nunits = x.nunits;
+  constexpr int kBLoads = (NFT * 128 + kThreads - 1) / kThreads;
+  constexpr int kQ = 2 * NFT;                        // (column tile, head step) steps
 
-  // this lane's keys (one per key tile)
-  int kcol[4];
+  // B tile: chunk P = t + 256 i of the row's contiguous run goes to LDS chunk 9 (P / 8) + P % 8;
+  // threads past the run copy chunk P - 128 into the pad chunk of column P - 1152
+  uint32_t bsrc[kBLoads];
+  int bdst[kBLoads];
 #pragma unroll
-  for (int kt = 0; kt < 4; ++kt) kcol[kt] = x.kb0 + 64 * wave + 16 * kt + c;
-  // B-tile chunks this lane loads: element offset in the row's Q / dO block; bit 30: rope
-  // block; bit 29: zero row (padding, padded heads, unused columns)
-  int boff[kBtBlocks / 4];
-#pragma unroll
-  for (int i = 0; i < kBtBlocks / 4; ++i) {
+  for (int i = 0; i < kBLoads; ++i) {
     const int P = (int)threadIdx.x + kThreads * i;
-    const int h = P / kBtRowChunks, cc = P % kBtRowChunks;
-    const int col = x.colbase + 8 * cc;
-    if (h >= x.nh || cc >= 2 * NFT) boff[i] = 1 << 29;
-    else if (x.isdk && col >= kDn) boff[i] = (1 << 30) | ((x.h0 + h) * kDr + col - kDn);
-    else boff[i] = (x.h0 + h) * kDn + (x.isdk ? col : col - kDk);
+    const bool pad = P >= NFT * 128;
+    bsrc[i] = (uint32_t)(pad ? P - 128 : P) * 16u;
+    bdst[i] = pad ? ((P - NFT * 128) * kBtColChunks + 8) * 8 : ((P >> 3) * kBtColChunks + (P & 7)) * 8;
   }
-  const uint16_t* bmain = x.isdk ? a.q : a.dout;
-  const int rstride = a.hgc * 128;     // elements between the records of consecutive slots
-
-  auto next_unit = [&](int& ri, int& L) {
-    if (!DUPS) {
-      ri = (ri >= 0 && ri + 1 < nrows) ? ri + 1 : -1;
-      return;
-    }
-    if (ri < 0) return;
-    if (L + 1 < (int)s_lay[ri]) { ++L; return; }
-    L = 0;
-    ri = ri + 1 < nrows ? ri + 1 : -1;
-  };
-
-#define SFAG_MAP_LOAD(MP, RI)                                                                  \
-  {                                                                                            \
-    const int64_t row_ = x.qstart + x.i0 + s_row[max((RI), 0)];                                \
-    const int16_t* kp_ = a.kpos + row_ * a.kstride;                                            \
-    /* used only by the next unit's record loads, which also check RI */                      \
-    _Pragma("unroll") for (int kt = 0; kt < 4; ++kt) MP[kt] = kp_[kcol[kt]];                   \
-  }
-
-// Record fragments of unit (RI, L) from its map entries MP: lane (g, c) of key tile kt, head
-// step ks holds heads 32 ks + 8 g .. + 7 of key kcol[kt] (zeros when not selected).
-#define SFAG_A_LOAD(AF, MP, RI, L)                                                             \
-  {                                                                                            \
-    const int64_t row_ = x.qstart + x.i0 + s_row[max((RI), 0)];                                \
-    const uint16_t* rbase_ = a.dsp + (row_ * a.topk * a.hgc + x.hg) * 128 + x.which + 8 * g;   \
-    _Pragma("unroll") for (int kt = 0; kt < 4; ++kt) {                                         \
-      int e_ = MP[kt];                                                                         \
-      bool ok_ = e_ >= 0 && (RI) >= 0;                                                         \
-      if (DUPS && (L) > 0) {                                                                   \
-        e_ += (L);                                                                             \
-        ok_ = ok_ && e_ < a.topk && a.sorted[row_ * a.topk + min(e_, a.topk - 1)] == kcol[kt]; \
-      }                                                                                        \
-      /* lanes of unselected keys load nothing (their fragment is zero) */                  \
-      const uint16_t* src_ = rbase_ + (uint32_t)(max(e_, 0) * rstride);                        \
-      AF[kt][0] = bf16x8{};                                                                    \
-      AF[kt][1] = bf16x8{};                                                                    \
-      if (ok_) {                                                                               \
-        AF[kt][0] = *reinterpret_cast<const bf16x8*>(src_);                                    \
-        AF[kt][1] = *reinterpret_cast<const bf16x8*>(src_ + 32);                               \
-      }                                                                                        \
-    }                                                                                          \
-  }
-
-// B tile of unit RI into registers: thread t holds chunks t + 256 i of the padded
-// [64 heads][19 chunks] tile; SFAG_B_STORE writes them to LDS once the MFMAs reading the
-// other buffer have been issued.
-#define SFAG_B_LOAD(BS, RI)                                                                    \
-  {                                                                                            \
-    const int64_t row_ = x.qstart + x.i0 + s_row[max((RI), 0)];                                \
-    const uint16_t* mrow_ = bmain + row_ * a.N1 * kDn;                                         \
-    const uint16_t* rrow_ = a.qr + row_ * a.N1 * kDr;                                          \
-    _Pragma("unroll") for (int i = 0; i < kBtBlocks / 4; ++i) {                                \
-      const int o = boff[i];                                                                   \
-      const uint16_t* src = ((o & (1 << 29)) || (RI) < 0) ? zsrc : ((o & (1 << 30)) ? rrow_ : mrow_) + (o & ((1 << 29) - 1)); \
-      BS[i] = *reinterpret_cast<const u32x4*>(src);                                            \
-    }                                                                                          \
-  }
-#define SFAG_B_STORE(BT, BS)                                                                   \
-  {                                                                                            \
-    _Pragma("unroll") for (int i = 0; i < kBtBlocks / 4; ++i)                                  \
-      *reinterpret_cast<u32x4*>((BT) + (threadIdx.x + kThreads * i) * 8) = BS[i];              \
-  }
-
-// MFMAs of one unit: NFT column tiles x 2 head steps x 4 key tiles, B fragments by transposing
-// reads of the B tile, three (column tile, head step) steps ahead.
-#define SFAG_BFRAG(BT, Q) lds_frag_trp((BT), 32 * ((Q) & 1), 16 * ((Q) >> 1), kBtPitch, lane)
-#define SFAG_MMA(BT, AF)                                                                       \
-  {                                                                                            \
-    bf16x8 bq[2 * NFT];                                                                        \
-    bq[0] = SFAG_BFRAG(BT, 0);                                                                 \
-    bq[1] = SFAG_BFRAG(BT, 1);                                                                 \
-    bq[2] = SFAG_BFRAG(BT, 2);                                                                 \
-    _Pragma("unroll") for (int q = 0; q < 2 * NFT; ++q) {                                      \
-      if (q + 3 < 2 * NFT) bq[q + 3] = SFAG_BFRAG(BT, q + 3);                                  \
-      const int ft = q >> 1, ks = q & 1;                                                       \
-      _Pragma("unroll") for (int kt = 0; kt < 4; ++kt) acc[kt][ft] = mfma(AF[kt][ks], bq[q], acc[kt][ft]); \
-    }                                                                                          \
-    /* issue order: the next unit's global loads (B tile, map, records), the first three     \
-       fragments, then (fragment three steps ahead, 4 MFMAs) pairs */                         \
-    __builtin_amdgcn_sched_group_barrier(0x020, kUnitLoads, 0);                                \
-    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);                                         \
-    _Pragma("unroll") for (int q = 0; q < 2 * NFT; ++q) {                                      \
-      if (q + 3 < 2 * NFT) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                  \
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);                                       \
-    }                                                                                          \
-  }
+  const int64_t bt_row = (int64_t)a.hgc * kDacc * 64;
+  const uint16_t* bt_base = a.bt + ((int64_t)x.hg * kDacc + x.colbase) * 64;
+  const uint32_t rstride = (uint32_t)a.hgc * 128u;
+  const int kmap = x.kb0 + 64 * wave + 4 * c;        // first of this lane's 4 keys
+  const int64_t row0 = x.qstart + x.i0;
+  const int64_t rec_row = (int64_t)a.topk * a.hgc * 128;
+  const uint16_t* rec_base = a.dsp + (int64_t)x.hg * 128 + x.which + 8 * g;
 
   f32x4 acc[4][NFT];
 #pragma unroll
@@ -352,57 +325,103 @@ __device__ __forceinline__ void kv_dense_body(const DenseArgs& a, const KvCtx& x
 #pragma unroll
     for (int ft = 0; ft < NFT; ++ft) acc[kt][ft] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Rotating registers (loaded one unit before they are used): f1 = record fragments, m0 =
-  // map, bs2 = B tile.  Each unit first moves them into f0 / m1 / bs (their loads were issued
-  // a whole unit earlier), then issues the next loads into the freed registers.
-  // prologue: B tile of unit 0 stored; f1 = fragments of unit 0, m0 = map of unit 1,
-  // bs2 = B tile of unit 1
-  int ri1 = 0, L1 = 0;                 // cursor of unit u + 1 (here: of unit 0)
-  int m0[4], m1[4];
-  bf16x8 f0[4][2], f1[4][2];
-  u32x4 bs[kBtBlocks / 4], bs2[kBtBlocks / 4];
-  SFAG_MAP_LOAD(m1, ri1)
-  SFAG_B_LOAD(bs, ri1)
-  int ri2 = ri1, L2 = L1;
-  next_unit(ri2, L2);
-  SFAG_A_LOAD(f1, m1, ri1, L1)
-  SFAG_MAP_LOAD(m0, ri2)
-  SFAG_B_STORE(Bt0, bs)
-  SFAG_B_LOAD(bs2, ri2)
-  ri1 = ri2;
-  L1 = L2;                             // cursor of unit 1
-  __syncthreads();
+#define KV_MAP_LOAD(MP, ROW)                                                                   \
+  MP = *reinterpret_cast<const i16x4*>(a.kpos + (row0 + (ROW)) * a.kstride + kmap);
+#define KV_B_LOAD(SP, ROW)                                                                     \
+  {                                                                                            \
+    const char* run_ = reinterpret_cast<const char*>(bt_base + (row0 + (ROW)) * bt_row);       \
+    _Pragma("unroll") for (int i = 0; i < kBLoads; ++i)                                        \
+      SP[i] = *reinterpret_cast<const u32x4*>(run_ + bsrc[i]);                                 \
+  }
+#define KV_B_STORE(BT, SP)                                                                     \
+  {                                                                                            \
+    _Pragma("unroll") for (int i = 0; i < kBLoads; ++i)                                        \
+      *reinterpret_cast<u32x4*>((BT) + bdst[i]) = SP[i];                                       \
+  }
+#define KV_BFRAG(BT, Q)                                                                        \
+  (*reinterpret_cast<const bf16x8*>((BT) + ((16 * ((Q) >> 1) + c) * kBtColChunks + 4 * ((Q) & 1) + g) * 8))
 
-  // unit u: rotate, then loads of the B tile and map of unit u + 2 and of the record fragments
-  // of unit u + 1, MFMAs of unit u (buffer u & 1), unit u + 1's B tile into the other buffer
-  for (int u = 0; u < nunits; ++u) {
+  // unit cursor: row index ri (into s_row) and repeat layer L; the next unit's row is rn
+  auto advance = [&](int& ri, int& L) {
+    if (DUPS && L + 1 < (int)s_lay[ri]) {
+      ++L;
+    } else {
+      L = 0;
+      ++ri;
+    }
+  };
+  int ri = 0, L = 0;
+  i16x4 mc;                                          // map of the current unit's row
+  u32x4 bs[kBLoads];
+  {
+    const int r0 = __builtin_amdgcn_readfirstlane((int)s_row[0]);
+    KV_MAP_LOAD(mc, r0)
+    KV_B_LOAD(bs, r0)
+    KV_B_STORE(Bt0, bs)
+  }
+  lds_barrier();
+
+  for (int u = 0; ri < nrows; ++u) {
     uint16_t* BC = (u & 1) ? Bt1 : Bt0;
     uint16_t* BN = (u & 1) ? Bt0 : Bt1;
+    const int r = __builtin_amdgcn_readfirstlane((int)s_row[ri]);
+    int ri2 = ri, L2 = L;
+    advance(ri2, L2);
+    const int rn = __builtin_amdgcn_readfirstlane((int)s_row[min(ri2, nrows - 1)]);
+    // records of this unit (layer L: the L-th occurrence of each key)
+    const uint16_t* rb = rec_base + (row0 + r) * rec_row;
+    bf16x8 f[4][2];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
-      f0[kt][0] = f1[kt][0];
-      f0[kt][1] = f1[kt][1];
-      m1[kt] = m0[kt];
+      int e = mc[kt];
+      bool ok = e >= 0;
+      if (DUPS && L > 0) {
+        e += L;
+        ok = ok && e < a.topk && a.sorted[(row0 + r) * a.topk + min(e, a.topk - 1)] == kmap + kt;
+      }
+      f[kt][0] = bf16x8{};
+      f[kt][1] = bf16x8{};
+      if (ok) {
+        const uint16_t* src = rb + (uint32_t)e * rstride;
+        f[kt][0] = *reinterpret_cast<const bf16x8*>(src);
+        f[kt][1] = *reinterpret_cast<const bf16x8*>(src + 32);
+      }
     }
+    i16x4 mn;
+    KV_MAP_LOAD(mn, rn)
+    KV_B_LOAD(bs, rn)
+    {
+      bf16x8 bq[kQ];
+      bq[0] = KV_BFRAG(BC, 0);
+      bq[1] = KV_BFRAG(BC, 1);
+      bq[2] = KV_BFRAG(BC, 2);
 #pragma unroll
-    for (int i = 0; i < kBtBlocks / 4; ++i) bs[i] = bs2[i];
-    int ri2_ = ri1, L2_ = L1;
-    next_unit(ri2_, L2_);
-    SFAG_B_LOAD(bs2, ri2_)
-    SFAG_MAP_LOAD(m0, ri2_)
-    SFAG_A_LOAD(f1, m1, ri1, L1)
-    SFAG_MMA(BC, f0)
-    SFAG_B_STORE(BN, bs)
-    __syncthreads();
-    ri1 = ri2_;
-    L1 = L2_;
+      for (int q = 0; q < kQ; ++q) {
+        if (q + 3 < kQ) bq[q + 3] = KV_BFRAG(BC, q + 3);
+        const int ft = q >> 1, ks = q & 1;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) acc[kt][ft] = mfma(f[kt][ks], bq[q], acc[kt][ft]);
+      }
+      // issue order: the next unit's map and B tile loads, three fragments, then (fragment
+      // three steps ahead, 4 MFMAs) pairs
+      __builtin_amdgcn_sched_group_barrier(0x020, kBLoads + 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+#pragma unroll
+      for (int q = 0; q < kQ; ++q) {
+        if (q + 3 < kQ) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      }
+    }
+    KV_B_STORE(BN, bs)
+    lds_barrier();
+    mc = mn;
+    ri = ri2;
+    L = L2;
   }
-#undef SFAG_B_STORE
-#undef SFAG_MMA
-#undef SFAG_BFRAG
-#undef SFAG_B_LOAD
-#undef SFAG_A_LOAD
-#undef SFAG_MAP_LOAD
+#undef KV_BFRAG
+#undef KV_B_STORE
+#undef KV_B_LOAD
+#undef KV_MAP_LOAD
 
   const float mul = x.isdk ? a.scale : 1.f;
   float* part = a.part + ((int64_t)x.hg * a.citems + x.citem) * (int64_t)kBk * kDacc;
@@ -412,13 +431,13 @@ __device__ __forceinline__ void kv_dense_body(const DenseArgs& a, const KvCtx& x
     for (int ft = 0; ft < NFT; ++ft)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int kk = 16 * (4 * wave + kt) + 4 * g + v;
+        const int kk = 64 * wave + 4 * (4 * g + v) + kt;
         part[(int64_t)kk * kDacc + x.colbase + 16 * ft + c] = acc[kt][ft][v] * mul;
       }
 }
 
-__global__ void __launch_bounds__(kThreads, 1) kv_dense_kernel(DenseArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t Bt0[kBtBlocks * 512], Bt1[kBtBlocks * 512];
+__global__ void __launch_bounds__(kThreads, 2) kv_dense_kernel(DenseArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t Bt0[kBtElems], Bt1[kBtElems];
   __shared__ int32_t cum[2 * 257];
   __shared__ int32_t ibase[257];
   __shared__ int32_t s_b, s_nrows;
@@ -494,21 +513,18 @@ __global__ void __launch_bounds__(kThreads, 1) kv_dense_kernel(DenseArgs a) {
   x.qstart = qstart;
   x.i0 = i0;
   x.nrows = nrows;
-  x.nunits = nunits;
   x.kb0 = kb0;
   x.isdk = sl < 4;
   x.colbase = x.isdk ? 144 * sl : kDk + 128 * (sl - 4);
-  x.h0 = hg * 64;
-  x.nh = min(64, a.N1 - x.h0);
   x.hg = hg;
   x.which = x.isdk ? 0 : 64;
   x.citem = citem;
   if (x.isdk) {
-    if (dups) kv_dense_body<9, true>(a, x, Bt0, Bt1);
-    else kv_dense_body<9, false>(a, x, Bt0, Bt1);
+    if (dups) kv_dense_units<9, true>(a, x, Bt0, Bt1);
+    else kv_dense_units<9, false>(a, x, Bt0, Bt1);
   } else {
-    if (dups) kv_dense_body<8, true>(a, x, Bt0, Bt1);
-    else kv_dense_body<8, false>(a, x, Bt0, Bt1);
+    if (dups) kv_dense_units<8, true>(a, x, Bt0, Bt1);
+    else kv_dense_units<8, false>(a, x, Bt0, Bt1);
   }
   if (threadIdx.x == 0) *flag = 1;
 }
@@ -569,6 +585,12 @@ hipError_t launch_sort_rows(const DenseArgs& a, int64_t rows, int np, hipStream_
 hipError_t launch_item_list(const DenseArgs& a, hipStream_t st) {
   if (a.items == 0) return hipSuccess;
   hipLaunchKernelGGL(item_list_kernel, dim3(1), dim3(1024), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_rows(const DenseArgs& a, int64_t rows, hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(transpose_rows_kernel, dim3((unsigned)rows, (unsigned)a.hgc), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
