@@ -30,7 +30,6 @@ constexpr int kThreads = 256;
 constexpr int kHtChunks = 64 / 8;          // [key][64 heads] tile rows: 8 chunks
 constexpr int kBtChunks = 24;              // [64 heads][<=144 cols] tile rows padded to 192 cols
 constexpr int32_t kNoKey = 0x7fffffff;
-constexpr int kMapWin = 8192;              // keys per LDS window of the key -> position map
 
 // Per-batch tables in LDS: query / key row starts (cum, as in cum_lengths) and the first item
 // (key block x row segment) of every batch.
@@ -51,93 +50,103 @@ __device__ __forceinline__ void item_tables(const Lens& L, int B, int tnd, int64
 }  // namespace
 
 // ------------------------------------------------------------------------------------------
+// Counting sort of one row's valid key positions.  The valid keys lie in [0, hi], which the
+// map covers in full blocks; the range is walked in windows of kSortWin keys.  Per window:
+// 16-bit occurrence counts in LDS (two per word, LDS atomics), then each thread takes 64
+// consecutive keys, and a block-wide exclusive scan of the threads' totals gives every key's
+// first sorted position.  From that one pass come the sorted list (each key written as often as
+// it occurs), the key -> first-position map (-1: not selected), the block starts (the position
+// of the first key >= 256 lb) and the largest multiplicity.  Slots past the count hold kNoKey.
+constexpr int kSortWin = 64 * kThreads;           // 16384 keys per window
+constexpr int kSortWords = kSortWin / 2;
+
 __global__ void __launch_bounds__(kThreads) sort_rows_kernel(DenseArgs a, int np) {
-  extern __shared__ __attribute__((aligned(16))) int32_t keys[];
+  (void)np;
+  __shared__ __attribute__((aligned(16))) uint32_t cw[kSortWords];   // 16-bit counts, 32 KB
   __shared__ int32_t cum[2 * 257];
-  __shared__ int32_t s_cnt, s_dup;
+  __shared__ int32_t s_wsum[kThreads / 64], s_base, s_dup;
   if (a.layout_tnd) {
     cum_lengths(a.lens, a.B, cum);
     __syncthreads();
   }
   const int64_t row = blockIdx.x;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   if (row == 0)
-    for (int i = threadIdx.x; i < kDk; i += kThreads) a.zero_row[i] = 0;
+    for (int i = t; i < kDk; i += kThreads) a.zero_row[i] = 0;
   const RowGeo geo = row_geo(a.lens, cum, a.B, a.layout_tnd, a.S1, a.S2, row, a.mode3);
-  for (int i = threadIdx.x; i < np; i += kThreads) {
-    int32_t v = kNoKey;
-    if (i < a.topk && geo.active) {
-      const int j = a.idx[row * a.topk + i];
-      if (j >= 0 && j <= geo.hi) v = j;
-    }
-    keys[i] = v;
-  }
-  if (threadIdx.x == 0) s_dup = 1;
-  __syncthreads();
-  // bitonic sort, ascending
-  for (int k = 2; k <= np; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = threadIdx.x; i < np; i += kThreads) {
-        const int ixj = i ^ j;
-        if (ixj > i) {
-          const int32_t x = keys[i], y = keys[ixj];
-          const bool up = (i & k) == 0;
-          if ((x > y) == up) {
-            keys[i] = y;
-            keys[ixj] = x;
-          }
-        }
-      }
-      __syncthreads();
-    }
-  }
-  if (threadIdx.x == 0) {
-    int lo = 0, hi = np;  // first kNoKey
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (keys[mid] < kNoKey) lo = mid + 1; else hi = mid;
-    }
-    s_cnt = lo;
-  }
-  __syncthreads();
-  const int cnt = s_cnt;
-  // longest run of one repeated key
-  for (int i = threadIdx.x; i < cnt; i += kThreads) {
-    if (i == 0 || keys[i - 1] != keys[i]) {
-      int e = i + 1;
-      while (e < cnt && keys[e] == keys[i]) ++e;
-      if (e - i > 1) atomicMax(&s_dup, e - i);
-    }
-  }
-  for (int i = threadIdx.x; i < a.topk; i += kThreads) a.sorted[row * a.topk + i] = keys[i];
-  const int nblk = (geo.lkv + kBk - 1) / kBk;
-  for (int lb = threadIdx.x; lb <= nblk; lb += kThreads) {
-    const int32_t start = lb * kBk;
-    int lo = 0, hi = cnt;
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (keys[mid] < start) lo = mid + 1; else hi = mid;
-    }
-    a.offs[row * (a.maxblk + 1) + lb] = lo;
-  }
-  // key -> first sorted position map of this row (-1: not selected), built in LDS windows and
-  // written out whole, over every key block the row can reach
-  int16_t* win = reinterpret_cast<int16_t*>(keys + np);
   const int map_end = (geo.active && geo.hi >= 0) ? min(a.kstride, ((geo.hi + kBk) / kBk) * kBk) : 0;
+  const int32_t* irow = a.idx + row * a.topk;
+  int32_t* srow = a.sorted + row * a.topk;
   int16_t* kp = a.kpos + row * a.kstride;
-  for (int w0 = 0; w0 < map_end; w0 += kMapWin) {
-    const int w1 = min(map_end, w0 + kMapWin);
+  int32_t* orow = a.offs + row * (a.maxblk + 1);
+  if (t == 0) {
+    s_base = 0;
+    s_dup = 1;
+  }
+  int dup = 1;
+  for (int w0 = 0; w0 < map_end; w0 += kSortWin) {
+    const int w1 = min(map_end, w0 + kSortWin);
+    for (int k = t; k < kSortWords; k += kThreads) cw[k] = 0u;
     __syncthreads();
-    for (int k = threadIdx.x; k < w1 - w0; k += kThreads) win[k] = -1;
-    __syncthreads();
-    for (int i = threadIdx.x; i < cnt; i += kThreads) {
-      const int32_t key = keys[i];
-      if (key >= w0 && key < w1 && (i == 0 || keys[i - 1] != key)) win[key - w0] = (int16_t)i;
+    for (int i = t; i < a.topk; i += kThreads) {
+      const int j = irow[i];
+      if (j >= 0 && j <= geo.hi && j >= w0 && j < w1) {
+        const int k = j - w0;
+        atomicAdd(&cw[k >> 1], 1u << (16 * (k & 1)));
+      }
     }
     __syncthreads();
-    for (int k = threadIdx.x; k < w1 - w0; k += kThreads) kp[w0 + k] = win[k];
+    // this thread's 64 keys: w0 + 64 t .. + 63 (32 count words)
+    const uint32_t* mine = &cw[32 * t];
+    int tsum = 0;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(mine + 4 * q);
+      tsum += (int)((v.x & 0xffffu) + (v.x >> 16) + (v.y & 0xffffu) + (v.y >> 16) + (v.z & 0xffffu) + (v.z >> 16) +
+                    (v.w & 0xffffu) + (v.w >> 16));
+    }
+    // block-wide exclusive scan of tsum
+    int incl = tsum;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(incl, d);
+      if (lane >= d) incl += y;
+    }
+    if (lane == 63) s_wsum[wave] = incl;
+    __syncthreads();
+    int pos = s_base + incl - tsum;
+    for (int v = 0; v < wave; ++v) pos += s_wsum[v];
+    const int k0 = w0 + 64 * t;
+    // w1 - w0 is a multiple of 256, so a thread's 64 keys are all inside or all outside
+    if (k0 < w1) {
+      if ((k0 & (kBk - 1)) == 0) orow[k0 / kBk] = pos;                   // block start
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {                                       // 8 keys per step
+        const u32x4 v = *reinterpret_cast<const u32x4*>(mine + 4 * q);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        i16x8 m;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int n = (int)((w[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+          m[e] = n > 0 ? (short)pos : (short)-1;
+          for (int r = 0; r < n; ++r) srow[pos + r] = k0 + 8 * q + e;
+          pos += n;
+          dup = max(dup, n);
+        }
+        *reinterpret_cast<i16x8*>(kp + k0 + 8 * q) = m;
+      }
+    }
+    __syncthreads();
+    if (t == kThreads - 1) s_base = pos;                                // total so far
+    __syncthreads();
   }
+  if (dup > 1) atomicMax(&s_dup, dup);
   __syncthreads();
-  if (threadIdx.x == 0) {
+  const int cnt = s_base;
+  for (int i = cnt + t; i < a.topk; i += kThreads) srow[i] = kNoKey;
+  const int nblk = (geo.lkv + kBk - 1) / kBk;
+  for (int lb = map_end / kBk + t; lb <= nblk; lb += kThreads) orow[lb] = cnt;
+  if (t == 0) {
     a.count[row] = cnt;
     a.maxdup[row] = s_dup;
   }
@@ -578,7 +587,7 @@ __global__ void __launch_bounds__(kThreads) kv_reduce_kernel(DenseArgs a) {
 
 // ------------------------------------------------------------------------------------------
 hipError_t launch_sort_rows(const DenseArgs& a, int64_t rows, int np, hipStream_t st) {
-  hipLaunchKernelGGL(sort_rows_kernel, dim3((unsigned)rows), dim3(kThreads), (size_t)np * 4 + kMapWin * 2, st, a, np);
+  hipLaunchKernelGGL(sort_rows_kernel, dim3((unsigned)rows), dim3(kThreads), 0, st, a, np);
   return hipGetLastError();
 }
 
@@ -606,9 +615,6 @@ hipError_t launch_kv_reduce(const DenseArgs& a, int64_t keys, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t set_dense_attributes() {
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(&sort_rows_kernel),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, 65536 + kMapWin * 2);
-}
+hipError_t set_dense_attributes() { return hipSuccess; }
 
 }  // namespace sfag
