@@ -55,7 +55,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t Kb0[kLdsK / 2], Kb1[kLdsK / 2], Kb2[kLdsK / 2];
   __shared__ __attribute__((aligned(16))) uint16_t Db0[kKC * kHtPitch], Db1[kKC * kHtPitch], Db2[kKC * kHtPitch];
   __shared__ __attribute__((aligned(16))) f32x4 X[4 * 4 * 64];        // partial-sum exchange [wave][4][64]
-  __shared__ float sD[64], sM[64], sIL[64];
+  __shared__ __attribute__((aligned(16))) float sD[64], sM[64], sIL[64];
   __shared__ int32_t cum[2 * 257];
 
   const int lane = threadIdx.x & 63;
@@ -138,17 +138,6 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
     qA[ht][8] = hv ? rv : bf16x8{};
   }
   __syncthreads();
-  // statistics of the 8 (head, key-tile) values this lane finishes: heads 32 hh + 16 ht + 4 g + v
-  float mrow[2][4], ilrow[2][4], drow_[2][4];
-#pragma unroll
-  for (int ht = 0; ht < 2; ++ht)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int h = 32 * hh + 16 * ht + 4 * g + v;
-      mrow[ht][v] = sM[h];
-      ilrow[ht][v] = sIL[h];
-      drow_[ht][v] = sD[h];
-    }
   const float zscale = a.scale * kLog2e;
 
   // Gather of chunk CH (this lane's key: sorted position SV) into key buffer KS: block b of the
@@ -181,35 +170,39 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
        ks reads chunk 32 dh + 4 ks + g (value dims) or 64 + 4 dh + g (rope) */                 \
     const uint16_t* kr0 = (KS) + (g * kKC + 16 * dh + c) * 8;                                  \
     const uint16_t* kr1 = (KS) + (g * kKC + 16 - 16 * dh + c) * 8;                             \
-    bf16x8 kb0 = *reinterpret_cast<const bf16x8*>(kr0 + 32 * dh * kKC * 8);                    \
-    bf16x8 kb1 = *reinterpret_cast<const bf16x8*>(kr1 + 32 * dh * kKC * 8);                    \
+    /* key fragments two steps ahead; step ks reads chunk 32 dh + 4 ks (ks < 8) or the rope  \
+       chunk 64 + 4 dh (ks = 8) */                                                            \
+    bf16x8 kf0[9], kf1[9];                                                                     \
+    _Pragma("unroll") for (int ks = 0; ks < 2; ++ks) {                                         \
+      kf0[ks] = *reinterpret_cast<const bf16x8*>(kr0 + (32 * dh + 4 * ks) * kKC * 8);          \
+      kf1[ks] = *reinterpret_cast<const bf16x8*>(kr1 + (32 * dh + 4 * ks) * kKC * 8);          \
+    }                                                                                          \
     _Pragma("unroll") for (int ks = 0; ks < 9; ++ks) {                                         \
-      bf16x8 nb0 = kb0, nb1 = kb1;                                                             \
-      if (ks < 8) {                     /* fragments of the next step, read ahead */           \
-        const int ch = ks < 7 ? 32 * dh + 4 * (ks + 1) : 64 + 4 * dh;                          \
-        nb0 = *reinterpret_cast<const bf16x8*>(kr0 + ch * kKC * 8);                            \
-        nb1 = *reinterpret_cast<const bf16x8*>(kr1 + ch * kKC * 8);                            \
+      if (ks + 2 < 9) {                                                                        \
+        const int ch = ks + 2 < 8 ? 32 * dh + 4 * (ks + 2) : 64 + 4 * dh;                      \
+        kf0[ks + 2] = *reinterpret_cast<const bf16x8*>(kr0 + ch * kKC * 8);                    \
+        kf1[ks + 2] = *reinterpret_cast<const bf16x8*>(kr1 + ch * kKC * 8);                    \
       }                                                                                        \
       _Pragma("unroll") for (int ht = 0; ht < 2; ++ht) {                                       \
-        sacc[ht][0] = mfma(qA[ht][ks], kb0, sacc[ht][0]);                                      \
-        sacc[ht][1] = mfma(qA[ht][ks], kb1, sacc[ht][1]);                                      \
+        sacc[ht][0] = mfma(qA[ht][ks], kf0[ks], sacc[ht][0]);                                  \
+        sacc[ht][1] = mfma(qA[ht][ks], kf1[ks], sacc[ht][1]);                                  \
         if (ks < 8) {                                                                          \
-          pacc[ht][0] = mfma(doA[ht][ks], kb0, pacc[ht][0]);                                   \
-          pacc[ht][1] = mfma(doA[ht][ks], kb1, pacc[ht][1]);                                   \
+          pacc[ht][0] = mfma(doA[ht][ks], kf0[ks], pacc[ht][0]);                               \
+          pacc[ht][1] = mfma(doA[ht][ks], kf1[ks], pacc[ht][1]);                               \
         }                                                                                      \
       }                                                                                        \
-      kb0 = nb0;                                                                               \
-      kb1 = nb1;                                                                               \
     }                                                                                          \
     /* issue order: per step one of the next chunk's gather loads (issued just before this   \
-       block; they drain through the load path while the MFMAs run), the next step's key     \
-       fragments, the step's MFMAs */                                                         \
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                                         \
-    _Pragma("unroll") for (int ks = 0; ks < 8; ++ks) {                                         \
+       block; they drain through the load path while the MFMAs run), the key fragments two   \
+       steps ahead, the step's MFMAs */                                                       \
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);                                         \
+    _Pragma("unroll") for (int ks = 0; ks < 7; ++ks) {                                         \
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                                       \
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                                       \
       __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);                                       \
     }                                                                                          \
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                                         \
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);                                         \
     __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                                         \
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);                                         \
   }
@@ -252,14 +245,17 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
     _Pragma("unroll") for (int ht = 0; ht < 2; ++ht) {                                         \
       const f32x4 s = sacc[ht][0] + xi[ht * 64 + lane];                                        \
       const f32x4 dp = pacc[ht][0] + xi[(2 + ht) * 64 + lane];                                 \
+      const int hcol = 32 * hh + 16 * ht + 4 * g;  /* heads hcol .. hcol + 3 */                 \
+      const f32x4 mv = *reinterpret_cast<const f32x4*>(sM + hcol);                             \
+      const f32x4 iv = *reinterpret_cast<const f32x4*>(sIL + hcol);                            \
+      const f32x4 dv = *reinterpret_cast<const f32x4*>(sD + hcol);                             \
       float p[4], ds[4];                                                                       \
       _Pragma("unroll") for (int v = 0; v < 4; ++v) {                                          \
-        p[v] = valid ? exp2f(s[v] * zscale - mrow[ht][v]) * ilrow[ht][v] : 0.f;                \
-        ds[v] = p[v] * (dp[v] - drow_[ht][v]);                                                 \
+        p[v] = valid ? exp2f(s[v] * zscale - mv[v]) * iv[v] : 0.f;                             \
+        ds[v] = p[v] * (dp[v] - dv[v]);                                                        \
       }                                                                                        \
       const uint32_t pw[2] = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};               \
       const uint32_t dw[2] = {pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3])};           \
-      const int hcol = 32 * hh + 16 * ht + 4 * g;                                              \
       *reinterpret_cast<uint2*>((DST) + key * kHtPitch + hcol) = make_uint2(dw[0], dw[1]);     \
       *reinterpret_cast<uint2*>(rec + hcol) = make_uint2(dw[0], dw[1]);                        \
       *reinterpret_cast<uint2*>(rec + 64 + hcol) = make_uint2(pw[0], pw[1]);                   \
