@@ -139,6 +139,22 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
   }
   __syncthreads();
   const float zscale = a.scale * kLog2e;
+  // Loop-invariant bases, held in SGPRs: the empty asm makes them opaque, so the compiler
+  // cannot re-load them from the kernel arguments inside the loop (a scalar load in flight
+  // forces LDS waits to drain completely).
+  auto uniform = [](const void* p) {               // a workgroup-uniform pointer, made scalar
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return reinterpret_cast<uint16_t*>(((uint64_t)hi << 32) | lo);
+  };
+  const uint16_t* kbase = uniform(a.k + geo.kstart * kDn);
+  const uint16_t* krbase = uniform(a.kr + geo.kstart * kDr);
+  const uint16_t* zrow = uniform(a.zero_row);
+  uint16_t* recrow = uniform(a.dsp + ((int64_t)row * a.topk * a.hgc + hg) * 128);   // slot 0 of this row
+  uint16_t* trash = uniform(a.trash);
+  const int recstride = a.hgc * 128;                                          // elements per slot
+  asm volatile("" : "+s"(kbase), "+s"(krbase), "+s"(zrow), "+s"(recrow), "+s"(trash));
 
   // Gather of chunk CH (this lane's key: sorted position SV) into key buffer KS: block b of the
   // tile holds chunk columns 2 b and 2 b + 1; wave w loads blocks w, w + 4, ..., w + 32 (the
@@ -146,9 +162,8 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
 #define SFAG_GATHER_ASYNC(KS, CH, SV)                                                          \
   {                                                                                            \
     const bool ok_ = (CH) * kKC + gkey < count;                                                \
-    const int64_t r_ = geo.kstart + (SV);                                                      \
-    const uint16_t* pk_ = ok_ ? a.k + r_ * kDn : a.zero_row;                                   \
-    const uint16_t* pr_ = ok_ ? a.kr + r_ * kDr : a.zero_row;                                  \
+    const uint16_t* pk_ = ok_ ? kbase + (int64_t)(SV) * kDn : zrow;                            \
+    const uint16_t* pr_ = ok_ ? krbase + (int64_t)(SV) * kDr : zrow;                           \
     _Pragma("unroll") for (int j = 0; j < kBlocks / 4; ++j) {                                  \
       const int blk = wave + 4 * j;                                                            \
       const uint16_t* src = j < kBlocks / 4 - 1 ? pk_ + (2 * blk + gcol) * 8                   \
@@ -241,7 +256,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
     const int c0 = (CI) * kKC;                                                                 \
     const int key = 16 * dh + c;                                                               \
     const bool valid = c0 + key < count;                                                       \
-    uint16_t* rec = valid ? a.dsp + (((int64_t)row * a.topk + c0 + key) * a.hgc + hg) * 128 : a.trash; \
+    uint16_t* rec = valid ? recrow + (int64_t)(c0 + key) * recstride : trash;                  \
     _Pragma("unroll") for (int ht = 0; ht < 2; ++ht) {                                         \
       const f32x4 s = sacc[ht][0] + xi[ht * 64 + lane];                                        \
       const f32x4 dp = pacc[ht][0] + xi[(2 + ht) * 64 + lane];                                 \
