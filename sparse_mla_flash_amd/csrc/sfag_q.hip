@@ -266,7 +266,9 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
       const f32x4 dv = *reinterpret_cast<const f32x4*>(sD + hcol);                             \
       float p[4], ds[4];                                                                       \
       _Pragma("unroll") for (int v = 0; v < 4; ++v) {                                          \
-        p[v] = valid ? exp2f(s[v] * zscale - mv[v]) * iv[v] : 0.f;                             \
+        /* v_exp_f32: results below 2^-126 flush to 0, far under bf16 resolution here */       \
+        const float e_ = __builtin_amdgcn_exp2f(s[v] * zscale - mv[v]) * iv[v];                \
+        p[v] = valid ? e_ : 0.f;                                                               \
         ds[v] = p[v] * (dp[v] - dv[v]);                                                        \
       }                                                                                        \
       const uint32_t pw[2] = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};               \
