@@ -449,7 +449,7 @@ __global__ void __launch_bounds__(kThreads, 2) kv_dense_kernel(DenseArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t Bt0[kBtElems], Bt1[kBtElems];
   __shared__ int32_t cum[2 * 257];
   __shared__ int32_t ibase[257];
-  __shared__ int32_t s_b, s_nrows;
+  __shared__ int32_t s_b, s_nrows, s_dups;
   __shared__ int16_t s_row[kSegRows];      // segment rows that select keys in the block, in order
   __shared__ uint16_t s_lay[kSegRows];     // their repeat layers (1 without repeated keys)
   __shared__ int32_t s_wcnt[4];
@@ -483,8 +483,12 @@ __global__ void __launch_bounds__(kThreads, 2) kv_dense_kernel(DenseArgs a) {
   int32_t* flag = a.flag + (int64_t)hg * a.citems + citem;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 
-  // ordered list of the segment's rows with keys in the block
-  if (threadIdx.x == 0) s_nrows = 0;
+  // ordered list of the segment's rows with keys in the block; s_dups: some listed row repeats
+  // keys (its units are (row, layer) pairs)
+  if (threadIdx.x == 0) {
+    s_nrows = 0;
+    s_dups = 0;
+  }
   for (int p0 = i0; p0 < i1; p0 += kThreads) {
     const int i = p0 + threadIdx.x;
     int n = 0, lay = 1;
@@ -503,15 +507,14 @@ __global__ void __launch_bounds__(kThreads, 2) kv_dense_kernel(DenseArgs a) {
       const int at = base + __popcll(m & ((1ull << lane) - 1ull));
       s_row[at] = (int16_t)(i - i0);
       s_lay[at] = (uint16_t)min(lay, 65535);
+      if (lay > 1) s_dups = 1;
     }
     __syncthreads();
     if (threadIdx.x == 0) s_nrows += s_wcnt[0] + s_wcnt[1] + s_wcnt[2] + s_wcnt[3];
     __syncthreads();
   }
   const int nrows = s_nrows;
-  int nunits = 0;                       // units: one per (row, repeat layer)
-  for (int t = 0; t < nrows; ++t) nunits += s_lay[t];
-  const bool dups = nunits > nrows;     // some row repeats keys
+  const bool dups = s_dups != 0;
   if (nrows == 0) {
     if (threadIdx.x == 0) *flag = 0;
     return;
