@@ -11,12 +11,11 @@
 // README, "function description", stages 1-3).
 //
 // Work split of the 4 waves (an LDS read of up to 16 bytes per lane costs the same LDS time,
-// and a transposing read delivers only 8, so the split minimises LDS reads per MFMA):
-//   scores: wave (hh, dh) = (wave / 2, wave % 2) owns heads 32 hh .. 32 hh + 31 and half of
-//     the contraction: value dims 256 dh .. 256 dh + 255 and rope dims 32 dh .. 32 dh + 31.
-//     Its Q and dO fragments stay in registers for the whole row, so every 16-byte key
-//     fragment read from LDS feeds four MFMAs.  The two waves of a head half swap the
-//     partial sums of the key tile the other one finishes (16 keys) through LDS.
+// and a transposing read delivers only 8):
+//   scores: wave w owns head tile w (heads 16 w .. 16 w + 15) over the whole contraction
+//     (512 value + 64 rope dims) for both 16-key tiles of the chunk.  Its Q and dO fragments
+//     stay in registers for the whole row; every 16-byte key fragment read from LDS feeds the
+//     S and dP MFMAs of its key tile, and no partial sums change hands.
 //   dQ: wave w owns output dims 144 w .. 144 w + 143 for all 64 heads, so each gathered key
 //     element is read (transposed) once per workgroup.
 // Key tiles are stored chunk-major in LDS ([72 chunks of 16 B][32 keys]): one direct-to-LDS
@@ -24,7 +23,7 @@
 // handles the same key (lane % 32) and each of its loads is one add to that key's row address.
 // Pipeline: key tiles are triple-buffered in LDS and gathered straight from global memory
 // one chunk ahead (global_load_lds).  The score MFMAs of chunk c and the dQ MFMAs of chunk
-// c - 1 sit in one block so that the scheduler can interleave them; two barriers per chunk.
+// c - 1 sit in one block so that the scheduler can interleave them; one barrier per chunk.
 #include "sfag_device.h"
 #include "sfag_launch.h"
 
@@ -40,8 +39,7 @@ static_assert(kBlocks % 4 == 0, "gather blocks per wave");
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kLdsK = kBlocks * 64 * 16;         // one key tile, chunk-major: [72 chunks][32 keys][16 B]
 constexpr int kLdsDS = kKC * kHtPitch * 2;       // DSt [32 keys][72]
-constexpr int kLdsX = 4 * 4 * 64 * 16;           // partial-sum exchange: [wave][4 tiles][64 lanes] f32x4
-constexpr int kLdsTotal = 3 * kLdsK + 3 * kLdsDS + kLdsX + 3 * 64 * 4 + 2 * 257 * 4;
+constexpr int kLdsTotal = 3 * kLdsK + 3 * kLdsDS + 3 * 64 * 4 + 2 * 257 * 4;
 static_assert(kLdsTotal <= 160 * 1024, "LDS budget");
 // s_waitcnt operand: vmcnt(4), expcnt and lgkmcnt at their maximum.  Vector memory operations
 // complete in issue order, so this waits for all but the 4 most recent (the record stores).
@@ -54,14 +52,12 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
   // wait for the gather before every LDS read.
   __shared__ __attribute__((aligned(16))) uint16_t Kb0[kLdsK / 2], Kb1[kLdsK / 2], Kb2[kLdsK / 2];
   __shared__ __attribute__((aligned(16))) uint16_t Db0[kKC * kHtPitch], Db1[kKC * kHtPitch], Db2[kKC * kHtPitch];
-  __shared__ __attribute__((aligned(16))) f32x4 X[4 * 4 * 64];        // partial-sum exchange [wave][4][64]
   __shared__ __attribute__((aligned(16))) float sD[64], sM[64], sIL[64];
   __shared__ int32_t cum[2 * 257];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar
   const int g = lane >> 4, c = lane & 15;
-  const int hh = wave >> 1, dh = wave & 1;
   // longest rows (highest positions under the causal mask) first
   const int64_t row = (int64_t)gridDim.x - 1 - blockIdx.x;
   const int hg = blockIdx.y;
@@ -118,24 +114,27 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
     }
   }
   // Q and dO fragments of this wave, straight from global memory (A operands of S and dP:
-  // lane (g, c) holds head 16 ht + c, dims d0 + 8 g .. d0 + 8 g + 7); zero for padded heads
-  bf16x8 qA[2][9], doA[2][8];
-#pragma unroll
-  for (int ht = 0; ht < 2; ++ht) {
-    const int h = 32 * hh + 16 * ht + c;
+  // lane (g, c) holds head 16 wave + c, dims 32 ks + 8 g .. + 7; steps 16 and 17 are the rope
+  // dims); zero for padded heads
+  bf16x8 qA[18], doA[16];
+  {
+    const int h = 16 * wave + c;
     const bool hv = h < nh;
     const int64_t hrow = row * a.N1 + h0 + (hv ? h : 0);
-    const uint16_t* qrow = a.q + hrow * kDn + 256 * dh + 8 * g;
-    const uint16_t* drow = a.dout + hrow * kDn + 256 * dh + 8 * g;
+    const uint16_t* qrow = a.q + hrow * kDn + 8 * g;
+    const uint16_t* drow = a.dout + hrow * kDn + 8 * g;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
+    for (int ks = 0; ks < 16; ++ks) {
       const bf16x8 qv = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
       const bf16x8 dv = *reinterpret_cast<const bf16x8*>(drow + 32 * ks);
-      qA[ht][ks] = hv ? qv : bf16x8{};
-      doA[ht][ks] = hv ? dv : bf16x8{};
+      qA[ks] = hv ? qv : bf16x8{};
+      doA[ks] = hv ? dv : bf16x8{};
     }
-    const bf16x8 rv = *reinterpret_cast<const bf16x8*>(a.qr + hrow * kDr + 32 * dh + 8 * g);
-    qA[ht][8] = hv ? rv : bf16x8{};
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8 rv = *reinterpret_cast<const bf16x8*>(a.qr + hrow * kDr + 32 * ks + 8 * g);
+      qA[16 + ks] = hv ? rv : bf16x8{};
+    }
   }
   __syncthreads();
   const float zscale = a.scale * kLog2e;
@@ -172,54 +171,44 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
     }                                                                                          \
   }
 
-// Partial S and dP of chunk buffer KS over this wave's dims: 2 head tiles x 2 key tiles; key
-// tile slot 0 is the tile this wave finishes (keys 16 dh ..), slot 1 the one it hands over.
+// S and dP of this wave's head tile for both key tiles of chunk buffer KS.
 #define SFAG_SCORES(KS)                                                                        \
   {                                                                                            \
-    _Pragma("unroll") for (int ht = 0; ht < 2; ++ht)                                           \
-      _Pragma("unroll") for (int kt = 0; kt < 2; ++kt) {                                       \
-        sacc[ht][kt] = f32x4{0.f, 0.f, 0.f, 0.f};                                              \
-        pacc[ht][kt] = f32x4{0.f, 0.f, 0.f, 0.f};                                              \
-      }                                                                                        \
+    _Pragma("unroll") for (int kt = 0; kt < 2; ++kt) {                                         \
+      sacc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};                                                    \
+      pacc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};                                                    \
+    }                                                                                          \
     /* chunk-major tile: element (chunk, key) at (chunk * 32 + key) * 8; lane (g, c) of step  \
-       ks reads chunk 32 dh + 4 ks + g (value dims) or 64 + 4 dh + g (rope) */                 \
-    const uint16_t* kr0 = (KS) + (g * kKC + 16 * dh + c) * 8;                                  \
-    const uint16_t* kr1 = (KS) + (g * kKC + 16 - 16 * dh + c) * 8;                             \
-    /* key fragments two steps ahead; step ks reads chunk 32 dh + 4 ks (ks < 8) or the rope  \
-       chunk 64 + 4 dh (ks = 8) */                                                            \
-    bf16x8 kf0[9], kf1[9];                                                                     \
+       ks reads chunk 4 ks + g of key 16 kt + c */                                             \
+    const uint16_t* kr0 = (KS) + (g * kKC + c) * 8;                                            \
+    const uint16_t* kr1 = (KS) + (g * kKC + 16 + c) * 8;                                       \
+    bf16x8 kf0[18], kf1[18];                /* key fragments, read two steps ahead */         \
     _Pragma("unroll") for (int ks = 0; ks < 2; ++ks) {                                         \
-      kf0[ks] = *reinterpret_cast<const bf16x8*>(kr0 + (32 * dh + 4 * ks) * kKC * 8);          \
-      kf1[ks] = *reinterpret_cast<const bf16x8*>(kr1 + (32 * dh + 4 * ks) * kKC * 8);          \
+      kf0[ks] = *reinterpret_cast<const bf16x8*>(kr0 + 4 * ks * kKC * 8);                      \
+      kf1[ks] = *reinterpret_cast<const bf16x8*>(kr1 + 4 * ks * kKC * 8);                      \
     }                                                                                          \
-    _Pragma("unroll") for (int ks = 0; ks < 9; ++ks) {                                         \
-      if (ks + 2 < 9) {                                                                        \
-        const int ch = ks + 2 < 8 ? 32 * dh + 4 * (ks + 2) : 64 + 4 * dh;                      \
-        kf0[ks + 2] = *reinterpret_cast<const bf16x8*>(kr0 + ch * kKC * 8);                    \
-        kf1[ks + 2] = *reinterpret_cast<const bf16x8*>(kr1 + ch * kKC * 8);                    \
+    _Pragma("unroll") for (int ks = 0; ks < 18; ++ks) {                                        \
+      if (ks + 2 < 18) {                                                                       \
+        kf0[ks + 2] = *reinterpret_cast<const bf16x8*>(kr0 + 4 * (ks + 2) * kKC * 8);          \
+        kf1[ks + 2] = *reinterpret_cast<const bf16x8*>(kr1 + 4 * (ks + 2) * kKC * 8);          \
       }                                                                                        \
-      _Pragma("unroll") for (int ht = 0; ht < 2; ++ht) {                                       \
-        sacc[ht][0] = mfma(qA[ht][ks], kf0[ks], sacc[ht][0]);                                  \
-        sacc[ht][1] = mfma(qA[ht][ks], kf1[ks], sacc[ht][1]);                                  \
-        if (ks < 8) {                                                                          \
-          pacc[ht][0] = mfma(doA[ht][ks], kf0[ks], pacc[ht][0]);                               \
-          pacc[ht][1] = mfma(doA[ht][ks], kf1[ks], pacc[ht][1]);                               \
-        }                                                                                      \
+      sacc[0] = mfma(qA[ks], kf0[ks], sacc[0]);                                                \
+      sacc[1] = mfma(qA[ks], kf1[ks], sacc[1]);                                                \
+      if (ks < 16) {                                                                           \
+        pacc[0] = mfma(doA[ks], kf0[ks], pacc[0]);                                             \
+        pacc[1] = mfma(doA[ks], kf1[ks], pacc[1]);                                             \
       }                                                                                        \
     }                                                                                          \
-    /* issue order: per step one of the next chunk's gather loads (issued just before this   \
-       block; they drain through the load path while the MFMAs run), the key fragments two   \
-       steps ahead, the step's MFMAs */                                                       \
+    /* issue order: the first four fragments, then per step one of the next chunk's gather   \
+       loads (steps 0-8), the fragments two steps ahead and the step's MFMAs */               \
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);                                         \
-    _Pragma("unroll") for (int ks = 0; ks < 7; ++ks) {                                         \
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                                       \
+    _Pragma("unroll") for (int ks = 0; ks < 16; ++ks) {                                        \
+      if (ks < 9) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                           \
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                                       \
-      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);                                       \
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);                                       \
     }                                                                                          \
-    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                                         \
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);                                         \
-    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                                         \
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);                                         \
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                         \
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                         \
   }
 
 // dQ[64 heads][144 w .. 144 w + 143] += dS[64][32 keys] K[32 keys][dims] of the previous chunk
@@ -236,40 +225,26 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
     }                                                                                          \
   }
 
-// Hand the partial sums of key tile 1 - dh to the other wave of the head half.
-#define SFAG_XCHG()                                                                            \
-  {                                                                                            \
-    f32x4* xo = X + wave * 4 * 64;                                                             \
-    xo[0 * 64 + lane] = sacc[0][1];                                                            \
-    xo[1 * 64 + lane] = sacc[1][1];                                                            \
-    xo[2 * 64 + lane] = pacc[0][1];                                                            \
-    xo[3 * 64 + lane] = pacc[1][1];                                                            \
-    lds_barrier();                                                                             \
-  }
-
-// P and dS of key tile dh (own partials + the other wave's): records and the DSt tile of
-// this chunk.  Every lane issues exactly 4 record stores (invalid slots write to the sink),
-// so that the end-of-chunk wait can leave them in flight.
+// P and dS of this wave's head tile for both key tiles: records and the DSt tile of this
+// chunk.  Every lane issues exactly 4 record stores (invalid slots write to the sink), so that
+// the end-of-chunk wait can leave them in flight.
 #define SFAG_FINISH(CI, DST)                                                                   \
   {                                                                                            \
-    const f32x4* xi = X + (wave ^ 1) * 4 * 64;                                                 \
     const int c0 = (CI) * kKC;                                                                 \
-    const int key = 16 * dh + c;                                                               \
-    const bool valid = c0 + key < count;                                                       \
-    uint16_t* rec = valid ? recrow + (int64_t)(c0 + key) * recstride : trash;                  \
-    _Pragma("unroll") for (int ht = 0; ht < 2; ++ht) {                                         \
-      const f32x4 s = sacc[ht][0] + xi[ht * 64 + lane];                                        \
-      const f32x4 dp = pacc[ht][0] + xi[(2 + ht) * 64 + lane];                                 \
-      const int hcol = 32 * hh + 16 * ht + 4 * g;  /* heads hcol .. hcol + 3 */                 \
-      const f32x4 mv = *reinterpret_cast<const f32x4*>(sM + hcol);                             \
-      const f32x4 iv = *reinterpret_cast<const f32x4*>(sIL + hcol);                            \
-      const f32x4 dv = *reinterpret_cast<const f32x4*>(sD + hcol);                             \
+    const int hcol = 16 * wave + 4 * g;          /* heads hcol .. hcol + 3 */                   \
+    const f32x4 mv = *reinterpret_cast<const f32x4*>(sM + hcol);                               \
+    const f32x4 iv = *reinterpret_cast<const f32x4*>(sIL + hcol);                              \
+    const f32x4 dv = *reinterpret_cast<const f32x4*>(sD + hcol);                               \
+    _Pragma("unroll") for (int kt = 0; kt < 2; ++kt) {                                         \
+      const int key = 16 * kt + c;                                                             \
+      const bool valid = c0 + key < count;                                                     \
+      uint16_t* rec = valid ? recrow + (int64_t)(c0 + key) * recstride : trash;                \
       float p[4], ds[4];                                                                       \
       _Pragma("unroll") for (int v = 0; v < 4; ++v) {                                          \
         /* v_exp_f32: results below 2^-126 flush to 0, far under bf16 resolution here */       \
-        const float e_ = __builtin_amdgcn_exp2f(s[v] * zscale - mv[v]) * iv[v];                \
+        const float e_ = __builtin_amdgcn_exp2f(sacc[kt][v] * zscale - mv[v]) * iv[v];         \
         p[v] = valid ? e_ : 0.f;                                                               \
-        ds[v] = p[v] * (dp[v] - dv[v]);                                                        \
+        ds[v] = p[v] * (pacc[kt][v] - dv[v]);                                                  \
       }                                                                                        \
       const uint32_t pw[2] = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};               \
       const uint32_t dw[2] = {pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3])};           \
@@ -279,7 +254,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
     }                                                                                          \
   }
 
-  f32x4 sacc[2][2], pacc[2][2];
+  f32x4 sacc[2], pacc[2];
   f32x4 dqacc[4][9];
 #pragma unroll
   for (int t = 0; t < 4; ++t)
@@ -292,7 +267,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
   __syncthreads();
 
 // One chunk CI: gather of chunk CI + 1 into KN, scores of chunk CI (buffer KC), dQ of chunk
-// CI - 1 (buffers KP, DP; skipped for chunk 0), swap and finish into DC.  The sorted position
+// CI - 1 (buffers KP, DP; skipped for chunk 0), finish into DC.  The sorted position
 // of this lane's key of chunk CI + 2 is loaded branch-free and only used after the
 // end-of-chunk wait.
 #define SFAG_CHUNK(CI, KC, KP, KN, DC, DP, WITH_DQ)                                            \
@@ -301,7 +276,6 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
     if (ci_ + 1 < nchunk) SFAG_GATHER_ASYNC(KN, ci_ + 1, gsv)                                  \
     const int32_t sv = srow[min((ci_ + 2) * kKC + gkey, count - 1)];                           \
     SFAG_SCORES(KC)                                                                            \
-    SFAG_XCHG()                                                                                \
     if (WITH_DQ) SFAG_DQ(KP, DP)                                                               \
     SFAG_FINISH(ci_, DC)                                                                       \
     /* everything but the 4 record stores just issued (chunk CI + 1 has landed) */            \
@@ -337,7 +311,6 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
 #undef SFAG_SCORES
 #undef SFAG_DQ
 #undef SFAG_FINISH
-#undef SFAG_XCHG
 #undef SFAG_CHUNK
 
   // ---- dQ / dQRope out: lane holds heads 16 t + 4 g + v, dims 144 w + 16 nt + c ------------------
