@@ -55,7 +55,7 @@ struct Plan {
   // path: key-major dense-masked dK / dV (dense = 1) or per-pair scatter (dense = 0)
   int dense = 0;
   double waste = 0.0;              // dense-masked (row, key) entries per valid pair (upper bound)
-  int64_t items = 0, citems = 0, maxblk = 0, np = 0;
+  int64_t items = 0, citems = 0, maxblk = 0;
   // workspace layout
   uint64_t off_acc = 0, off_partial = 0, off_keys0 = 0, off_keys1 = 0, off_sorttmp = 0;
   uint64_t off_sorted = 0, off_count = 0, off_maxdup = 0, off_offs = 0, off_dsp = 0, off_part = 0, off_flag = 0;
@@ -91,12 +91,6 @@ void path_stats(const Plan& p, double* range_sum, double* valid_max) {
   }
   *range_sum = rs;
   *valid_max = vm;
-}
-
-uint64_t next_pow2(uint64_t x) {
-  uint64_t v = 1;
-  while (v < x) v <<= 1;
-  return v;
 }
 
 bool n1_allowed(int64_t n) {
@@ -216,7 +210,6 @@ sfag_status make_plan(const sfag_dims* dims, const int32_t* sq, const int32_t* s
       }
     }
     p->citems = citems;
-    p->np = (int64_t)next_pow2((uint64_t)p->topk);
     const uint64_t pairs = (uint64_t)p->rows * p->topk;
     p->off_sorted = off;
     off = align_up(off + pairs * 4);
@@ -442,7 +435,7 @@ sfag_status sfag_sparse_flash_attention_grad(
     a.row_begin = 0;
     a.pairs_per_launch = 0;
     SFAG_HIP(sfag::launch_item_list(da, s));
-    SFAG_HIP(sfag::launch_sort_rows(da, p.rows, (int)p.np, s));
+    SFAG_HIP(sfag::launch_sort_rows(da, p.rows, s));
     if (g_ev[0]) SFAG_HIP(hipEventRecord(g_ev[0], s));
     SFAG_HIP(sfag::launch_bwd_q(a, p.rows, p.hg_count, s));
     if (g_ev[1]) SFAG_HIP(hipEventRecord(g_ev[1], s));

@@ -27,8 +27,6 @@ namespace sfag {
 
 namespace {
 constexpr int kThreads = 256;
-constexpr int kHtChunks = 64 / 8;          // [key][64 heads] tile rows: 8 chunks
-constexpr int kBtChunks = 24;              // [64 heads][<=144 cols] tile rows padded to 192 cols
 constexpr int32_t kNoKey = 0x7fffffff;
 
 // Per-batch tables in LDS: query / key row starts (cum, as in cum_lengths) and the first item
@@ -60,8 +58,7 @@ __device__ __forceinline__ void item_tables(const Lens& L, int B, int tnd, int64
 constexpr int kSortWin = 64 * kThreads;           // 16384 keys per window
 constexpr int kSortWords = kSortWin / 2;
 
-__global__ void __launch_bounds__(kThreads) sort_rows_kernel(DenseArgs a, int np) {
-  (void)np;
+__global__ void __launch_bounds__(kThreads) sort_rows_kernel(DenseArgs a) {
   __shared__ __attribute__((aligned(16))) uint32_t cw[kSortWords];   // 16-bit counts, 32 KB
   __shared__ int32_t cum[2 * 257];
   __shared__ int32_t s_wsum[kThreads / 64], s_base, s_dup;
@@ -589,8 +586,8 @@ __global__ void __launch_bounds__(kThreads) kv_reduce_kernel(DenseArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------
-hipError_t launch_sort_rows(const DenseArgs& a, int64_t rows, int np, hipStream_t st) {
-  hipLaunchKernelGGL(sort_rows_kernel, dim3((unsigned)rows), dim3(kThreads), 0, st, a, np);
+hipError_t launch_sort_rows(const DenseArgs& a, int64_t rows, hipStream_t st) {
+  hipLaunchKernelGGL(sort_rows_kernel, dim3((unsigned)rows), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 

@@ -106,7 +106,7 @@ hipError_t sort_pair_keys(void* temp, size_t temp_bytes, const uint64_t* in, uin
 size_t sort_temp_bytes(int64_t n, int end_bit);
 hipError_t launch_bwd_q(const BwdArgs& a, int64_t nrows, int hg_count, hipStream_t st);
 hipError_t set_q_attributes();
-hipError_t launch_sort_rows(const DenseArgs& a, int64_t rows, int np, hipStream_t st);
+hipError_t launch_sort_rows(const DenseArgs& a, int64_t rows, hipStream_t st);
 hipError_t launch_item_list(const DenseArgs& a, hipStream_t st);
 hipError_t launch_transpose_rows(const DenseArgs& a, int64_t rows, hipStream_t st);
 hipError_t launch_kv_dense(const DenseArgs& a, hipStream_t st);
