@@ -432,6 +432,7 @@ sfag_status sfag_sparse_flash_attention_grad(
     a.dsp = reinterpret_cast<uint16_t*>(ws + p.off_dsp);
     a.zero_row = da.zero_row;
     a.trash = reinterpret_cast<uint16_t*>(ws + p.off_trash);
+    a.bt = reinterpret_cast<uint16_t*>(ws + p.off_bt);
     a.row_begin = 0;
     a.pairs_per_launch = 0;
     SFAG_HIP(sfag::launch_item_list(da, s));
@@ -439,8 +440,6 @@ sfag_status sfag_sparse_flash_attention_grad(
     if (g_ev[0]) SFAG_HIP(hipEventRecord(g_ev[0], s));
     SFAG_HIP(sfag::launch_bwd_q(a, p.rows, p.hg_count, s));
     if (g_ev[1]) SFAG_HIP(hipEventRecord(g_ev[1], s));
-    // after bwd_q, so that its 1.1 GB of writes do not flush what bwd_q finds in the caches
-    SFAG_HIP(sfag::launch_transpose_rows(da, p.rows, s));
     if (g_ev[2]) SFAG_HIP(hipEventRecord(g_ev[2], s));
     SFAG_HIP(sfag::launch_kv_dense(da, s));
     if (g_ev[3]) SFAG_HIP(hipEventRecord(g_ev[3], s));

@@ -5,19 +5,18 @@
 // contributions with fp32 atomics costs one L2 atomic lane-op per value (1088 per pair), far
 // slower than the MFMA work.  Here the accumulation is turned around: a workgroup owns a
 // block of 256 consecutive keys and a slice of the 1088 output columns and walks the query
-// rows of one row segment in order.  For every row that selects keys in the block it builds a
-// dense [256 keys x 64 heads] tile of dS (or P) -- zero where the row did not select the key
-// -- in LDS, and accumulates  tile . Q_row  (or  tile . dO_row) on the 16x16x32 bf16 MFMA into
-// fp32 registers.  Rows with no key in the block cost nothing; rows that select a fraction f
-// of the block cost 1/f of the useful flops.  The per-segment partial sums are then added in
-// segment order, so the result does not depend on scheduling (deterministic by construction).
+// rows of one row segment in order.  For every row that selects keys in the block it multiplies
+// the row's dense [256 keys x 64 heads] dS (or P) -- zero where the row did not select the key,
+// loaded as MFMA fragments straight from the pair records -- by the row's [64 heads x cols]
+// Q (or dO) slice, staged in LDS, on the 16x16x32 bf16 MFMA into fp32 registers.  Rows with no
+// key in the block cost nothing; rows that select a fraction f of the block cost 1/f of the
+// useful flops.  The per-segment partial sums are then added in segment order, so the result
+// does not depend on scheduling (deterministic by construction).
 //
 // Kernels:
 //   sort_rows_kernel   per row: valid key positions sorted ascending, their count, the largest
-//                      multiplicity of a repeated key, and the start of every 256-key block
-//   transpose_rows_kernel  per (row, head group): Q | QRope | dO as [1088 columns][64 heads],
-//                      the layout whose 16-byte pieces are MFMA B fragments of the contraction
-//                      over heads
+//                      multiplicity of a repeated key, the start of every 256-key block and
+//                      the key -> position map
 //   kv_dense_kernel    (item = key block x row segment, column slice, head group) partial sums
 //   kv_reduce_kernel   per key row: sum of the partials in (head group, segment) order -> bf16
 #include "sfag_device.h"
@@ -200,63 +199,6 @@ __global__ void __launch_bounds__(1024) item_list_kernel(DenseArgs a) {
   }
 }
 
-// ------------------------------------------------------------------------------------------
-// One workgroup per (row, head group): the row's 64 heads x 1088 columns (Q 512 | QRope 64 |
-// dO 512) rewritten column-major, bt[row][hg][col][h], heads past N1 zero.  Per 64-column
-// chunk the [64 heads][64 cols] tile goes through LDS (pitch 72) and comes back by
-// transposing reads: lane (g, c) of wave w gets heads 32 s + 8 g .. + 7 of column 16 w + c,
-// one 16-byte store.  The next chunk's loads are in flight during the current chunk's reads.
-constexpr int kTrPitch = 72;
-constexpr int kTrChunks = kDacc / 64;      // 17
-
-__global__ void __launch_bounds__(kThreads) transpose_rows_kernel(DenseArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t tile[2][64 * kTrPitch];
-  const int64_t row = blockIdx.x;
-  const int hg = blockIdx.y;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int g = lane >> 4, c = lane & 15;
-  const int h0 = hg * 64;
-  // this thread's two 16-byte pieces of a chunk: head hh[i], columns 8 cc[i] .. + 7
-  int hh[2], cc[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int P = (int)threadIdx.x + kThreads * i;
-    hh[i] = P >> 3;
-    cc[i] = P & 7;
-  }
-  auto load = [&](u32x4* r, int k) {
-    const int col0 = 64 * k;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int h = h0 + hh[i];
-      const uint16_t* src = a.zero_row;
-      if (h < a.N1) {
-        if (col0 < kDn) src = a.q + (row * a.N1 + h) * kDn + col0;
-        else if (col0 < kDk) src = a.qr + (row * a.N1 + h) * kDr + (col0 - kDn);
-        else src = a.dout + (row * a.N1 + h) * kDn + (col0 - kDk);
-        src += 8 * cc[i];
-      }
-      r[i] = *reinterpret_cast<const u32x4*>(src);
-    }
-  };
-  uint16_t* out = a.bt + (row * a.hgc + hg) * (int64_t)kDacc * 64;
-  u32x4 r[2];
-  load(r, 0);
-#pragma unroll 1
-  for (int k = 0; k < kTrChunks; ++k) {
-    uint16_t* t = tile[k & 1];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) *reinterpret_cast<u32x4*>(t + hh[i] * kTrPitch + 8 * cc[i]) = r[i];
-    if (k + 1 < kTrChunks) load(r, k + 1);
-    lds_barrier();
-#pragma unroll
-    for (int sh = 0; sh < 2; ++sh) {
-      const bf16x8 v = lds_frag_trp(t, 32 * sh, 16 * wave, kTrPitch, lane);
-      *reinterpret_cast<bf16x8*>(out + (64 * k + 16 * wave + c) * 64 + 32 * sh + 8 * g) = v;
-    }
-  }
-}
-
 // Workgroup = (live item, column slice, head group).  Workgroups are dealt to the 8 XCDs
 // round-robin (x = w % 8), so XCD x is given the contiguous run of live items
 // [x n, x n + n) and walks it as  half (dK slices, then dV slices) > item > slice: the
@@ -273,8 +215,8 @@ __global__ void __launch_bounds__(kThreads) transpose_rows_kernel(DenseArgs a) {
 //       memory: lane (g, c) handles keys kb0 + 64 w + 4 c + kt (kt = 0..3) as row c of key
 //       tile kt and needs heads 8 g .. 8 g + 7 (+ 32) of each, found through the row's
 //       key -> position map (one 8-byte load for the 4 keys); unselected keys load nothing.
-//   B = the row's [64 heads x cols] Q (or dO) slice, read from the column-major copy made by
-//       transpose_rows_kernel (one contiguous run of 2 KB per column tile), staged in LDS as
+//   B = the row's [64 heads x cols] Q (or dO) slice, read from the column-major copy written by
+//       the query-major kernel (one contiguous run of 2 KB per column tile), staged in LDS as
 //       [column][8 chunks of 8 heads + 1 pad chunk] and read as whole 16-byte fragments.
 //   acc[keys][cols] += A B  on the 16x16x32 bf16 MFMA, fp32 in registers; accumulator row
 //       4 g + v of key tile kt is key kb0 + 64 w + 4 (4 g + v) + kt.
@@ -594,12 +536,6 @@ hipError_t launch_sort_rows(const DenseArgs& a, int64_t rows, hipStream_t st) {
 hipError_t launch_item_list(const DenseArgs& a, hipStream_t st) {
   if (a.items == 0) return hipSuccess;
   hipLaunchKernelGGL(item_list_kernel, dim3(1), dim3(1024), 0, st, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_transpose_rows(const DenseArgs& a, int64_t rows, hipStream_t st) {
-  if (rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(transpose_rows_kernel, dim3((unsigned)rows, (unsigned)a.hgc), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 

@@ -34,6 +34,7 @@ struct BwdArgs {
   uint16_t* dsp;          // [rows * topk, head groups, 128] bf16 dS | P per pair (key-major mode)
   const uint16_t* zero_row;  // 576 zero bf16 (key-major mode: source of padding slots)
   uint16_t* trash;        // 128 bf16 write-only sink (key-major mode: records of invalid slots)
+  uint16_t* bt;           // [rows, hgc, 1088, 64] heads-innermost Q | QRope | dO (key-major mode)
   Lens lens;
   int64_t S1;             // BSND S1 / TND T1 (statistics head stride)
   int64_t S2;             // BSND S2 / TND T2
@@ -54,7 +55,7 @@ struct DenseArgs {
   int32_t* offs;          // [rows, maxblk + 1]
   int16_t* kpos;          // [rows, kstride] first sorted position of each key, -1: not selected
   const uint16_t* dsp;    // [rows * topk, hgc, 128]
-  uint16_t* bt;           // [rows, hgc, 1088, 64] Q | QRope | dO with the 64 heads of a group innermost
+  const uint16_t* bt;     // [rows, hgc, 1088, 64] Q | QRope | dO with the 64 heads of a group innermost
   float* part;            // [hgc, citems, kBk, 1088]
   int32_t* flag;          // [hgc, citems]
   int32_t* ilist;         // [citems] live item -> item (key block x row segment)
@@ -108,7 +109,6 @@ hipError_t launch_bwd_q(const BwdArgs& a, int64_t nrows, int hg_count, hipStream
 hipError_t set_q_attributes();
 hipError_t launch_sort_rows(const DenseArgs& a, int64_t rows, hipStream_t st);
 hipError_t launch_item_list(const DenseArgs& a, hipStream_t st);
-hipError_t launch_transpose_rows(const DenseArgs& a, int64_t rows, hipStream_t st);
 hipError_t launch_kv_dense(const DenseArgs& a, hipStream_t st);
 hipError_t launch_kv_reduce(const DenseArgs& a, int64_t keys, hipStream_t st);
 hipError_t set_dense_attributes();

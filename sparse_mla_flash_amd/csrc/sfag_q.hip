@@ -263,6 +263,32 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
 
   SFAG_GATHER_ASYNC(Kb0, 0, gsv)
   gsv = srow[min(kKC + gkey, count - 1)];                 // chunk 1
+
+  // The row's Q | QRope | dO with the 64 heads innermost (bt[row][hg][col][h]), the key-major
+  // kernel's B operand, written from the fragments already in registers.  Per 64-column block
+  // (two steps of every wave) the [64 heads][64 cols] tile goes through LDS (pitch 72, the
+  // key buffers 1 and 2 in turn, unused until the loop) and comes back by transposing reads:
+  // lane (g, c) of wave w stores heads 32 s + 8 g .. + 7 of column 64 k + 16 w + c.
+  {
+    uint16_t* bto = a.bt + ((int64_t)row * a.hgc + hg) * (int64_t)kDacc * 64;
+    const int hrow = 16 * wave + c;
+#pragma unroll
+    for (int k = 0; k < kDacc / 64; ++k) {
+      uint16_t* t = (k & 1) ? Kb2 : Kb1;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int ks = 2 * k + j;                         // 32-column step over Q | QRope | dO
+        const bf16x8 v = ks < 18 ? qA[ks] : doA[ks - 18];
+        *reinterpret_cast<bf16x8*>(t + hrow * 72 + 32 * j + 8 * g) = v;
+      }
+      lds_barrier();
+#pragma unroll
+      for (int sh = 0; sh < 2; ++sh) {
+        const bf16x8 v = lds_frag_trp(t, 32 * sh, 16 * wave, 72, lane);
+        *reinterpret_cast<bf16x8*>(bto + (64 * k + 16 * wave + c) * 64 + 32 * sh + 8 * g) = v;
+      }
+    }
+  }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
