@@ -178,9 +178,13 @@ sfag_status make_plan(const sfag_dims* dims, const int32_t* sq, const int32_t* s
   double range_sum = 0, valid_max = 0;
   path_stats(*p, &range_sum, &valid_max);
   p->waste = valid_max > 0 ? range_sum / valid_max : 0.0;
-  p->dense = p->topk <= 16384 && p->waste <= 8.0;
+  int64_t max_lq = 0;
+  for (int64_t b = 0; b < p->B; ++b) max_lq = std::max<int64_t>(max_lq, p->lens.lq[b]);
+  const bool dense_fits = p->topk <= 16384 &&
+      p->hg_count * ((max_lq + sfag::kSegRows - 1) / sfag::kSegRows) <= sfag::kMaxSegs;
+  p->dense = dense_fits && p->waste <= 8.0;
   if (const char* f = std::getenv("SFAG_FORCE_PATH")) {
-    if (std::strcmp(f, "dense") == 0 && p->topk <= 16384) p->dense = 1;
+    if (std::strcmp(f, "dense") == 0 && dense_fits) p->dense = 1;
     if (std::strcmp(f, "scatter") == 0) p->dense = 0;
   }
   uint64_t off = 0;

@@ -487,7 +487,7 @@ __global__ void __launch_bounds__(kThreads) kv_reduce_kernel(DenseArgs a) {
   __shared__ int32_t cum[2 * 257];
   __shared__ int32_t ibase[257];
   __shared__ int32_t s_b;
-  __shared__ int32_t fl[2 * 256];
+  __shared__ int32_t fl[kMaxSegs];
   item_tables(a.lens, a.B, a.layout_tnd, a.S1, a.S2, cum, ibase);
   __syncthreads();
   const int64_t krow = blockIdx.x;

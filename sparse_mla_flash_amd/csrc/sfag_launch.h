@@ -14,6 +14,7 @@ struct Lens {
 
 constexpr int kBk = 256;        // keys per block of the key-major dK / dV kernel
 constexpr int kSegRows = 512;   // query rows per segment of the key-major dK / dV kernel
+constexpr int kMaxSegs = 512;   // (head group, segment) pairs per batch the ordered reduce can hold
 
 struct BwdArgs {
   const uint16_t* q;      // [rows, N1, 512] bf16
