@@ -41,9 +41,10 @@ constexpr int kLdsK = kBlocks * 64 * 16;         // one key tile, chunk-major: [
 constexpr int kLdsDS = kKC * kHtPitch * 2;       // DSt [32 keys][72]
 constexpr int kLdsTotal = 3 * kLdsK + 3 * kLdsDS + 3 * 64 * 4 + 2 * 257 * 4;
 static_assert(kLdsTotal <= 160 * 1024, "LDS budget");
-// s_waitcnt operand: vmcnt(4), expcnt and lgkmcnt at their maximum.  Vector memory operations
-// complete in issue order, so this waits for all but the 4 most recent (the record stores).
-constexpr int kWaitAllButRecords = 0x0f74;
+// s_waitcnt operand: vmcnt(4), lgkmcnt(0), expcnt at its maximum.  Vector memory operations
+// complete in issue order, so this waits for all but the 4 most recent (the record stores),
+// and for this wave's LDS writes.
+constexpr int kWaitAllButRecords = 0x0074;
 }  // namespace
 
 __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
@@ -150,6 +151,10 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
   const uint16_t* kbase = uniform(a.k + geo.kstart * kDn);
   const uint16_t* krbase = uniform(a.kr + geo.kstart * kDr);
   const uint16_t* zrow = uniform(a.zero_row);
+  // The record pointers lose their address space through the scalar round trip; stores through
+  // them are made global explicitly, because a generic (flat) store might hit LDS and would then
+  // wait for every direct-to-LDS gather load in flight.
+  typedef __attribute__((address_space(1))) uint64_t GlobalU64;
   uint16_t* recrow = uniform(a.dsp + ((int64_t)row * a.topk * a.hgc + hg) * 128);   // slot 0 of this row
   uint16_t* trash = uniform(a.trash);
   const int recstride = a.hgc * 128;                                          // elements per slot
@@ -249,8 +254,8 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
       const uint32_t pw[2] = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};               \
       const uint32_t dw[2] = {pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3])};           \
       *reinterpret_cast<uint2*>((DST) + key * kHtPitch + hcol) = make_uint2(dw[0], dw[1]);     \
-      *reinterpret_cast<uint2*>(rec + hcol) = make_uint2(dw[0], dw[1]);                        \
-      *reinterpret_cast<uint2*>(rec + 64 + hcol) = make_uint2(pw[0], pw[1]);                   \
+      *(GlobalU64*)(rec + hcol) = ((uint64_t)dw[1] << 32) | dw[0];                             \
+      *(GlobalU64*)(rec + 64 + hcol) = ((uint64_t)pw[1] << 32) | pw[0];                        \
     }                                                                                          \
   }
 
@@ -307,7 +312,11 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
     /* everything but the 4 record stores just issued (chunk CI + 1 has landed) */            \
     __builtin_amdgcn_s_waitcnt(kWaitAllButRecords);                                            \
     gsv = sv;                                                                                  \
-    __syncthreads();                                                                           \
+    /* a plain barrier: the data exchanged is in LDS, and a release fence would also wait for  \
+       the record stores */                                                                    \
+    asm volatile("" ::: "memory");                                                             \
+    __builtin_amdgcn_s_barrier();                                                              \
+    asm volatile("" ::: "memory");                                                             \
   }
 
   SFAG_CHUNK(0, Kb0, Kb2, Kb1, Db0, Db2, false)
