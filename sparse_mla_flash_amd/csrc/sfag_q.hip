@@ -41,9 +41,11 @@ constexpr int kLdsK = kBlocks * 64 * 16;         // one key tile, chunk-major: [
 constexpr int kLdsDS = kKC * kHtPitch * 2;       // DSt [32 keys][72]
 constexpr int kLdsTotal = 3 * kLdsK + 3 * kLdsDS + 3 * 64 * 4 + 2 * 257 * 4;
 static_assert(kLdsTotal <= 160 * 1024, "LDS budget");
-// s_waitcnt operand: vmcnt(4), lgkmcnt(0), expcnt at its maximum.  Vector memory operations
-// complete in issue order, so this waits for all but the 4 most recent (the record stores),
-// and for this wave's LDS writes.
+// s_waitcnt operands.  kWaitVmem: vmcnt(0), expcnt and lgkmcnt at their maximum (issued just
+// before a chunk's record stores).  kWaitAllButRecords: vmcnt(4), lgkmcnt(0): at the end of a
+// chunk the only vector memory operations that can be in flight are the chunk's 4 record
+// stores, so this leaves them in flight and waits for this wave's LDS writes.
+constexpr int kWaitVmem = 0x0f70;
 constexpr int kWaitAllButRecords = 0x0074;
 }  // namespace
 
@@ -254,6 +256,8 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
       const uint32_t pw[2] = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};               \
       const uint32_t dw[2] = {pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3])};           \
       *reinterpret_cast<uint2*>((DST) + key * kHtPitch + hcol) = make_uint2(dw[0], dw[1]);     \
+      /* the next chunk's gather is in before any record store is issued */                    \
+      if (kt == 0) __builtin_amdgcn_s_waitcnt(kWaitVmem);                                      \
       *(GlobalU64*)(rec + hcol) = ((uint64_t)dw[1] << 32) | dw[0];                             \
       *(GlobalU64*)(rec + 64 + hcol) = ((uint64_t)pw[1] << 32) | pw[0];                        \
     }                                                                                          \
@@ -309,7 +313,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
     SFAG_SCORES(KC)                                                                            \
     if (WITH_DQ) SFAG_DQ(KP, DP)                                                               \
     SFAG_FINISH(ci_, DC)                                                                       \
-    /* everything but the 4 record stores just issued (chunk CI + 1 has landed) */            \
+    /* everything but the 4 record stores just issued */                                      \
     __builtin_amdgcn_s_waitcnt(kWaitAllButRecords);                                            \
     gsv = sv;                                                                                  \
     /* a plain barrier: the data exchanged is in LDS, and a release fence would also wait for  \
