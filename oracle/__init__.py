@@ -43,7 +43,7 @@ class _Problem(ctypes.Structure):
         ("N1", ctypes.c_int64), ("D", ctypes.c_int64), ("Dr", ctypes.c_int64),
         ("topk", ctypes.c_int64), ("layout", ctypes.c_int32), ("sparse_mode", ctypes.c_int32),
         ("seq_q", ctypes.POINTER(ctypes.c_int32)), ("seq_kv", ctypes.POINTER(ctypes.c_int32)),
-        ("scale", ctypes.c_double),
+        ("scale", ctypes.c_double), ("block", ctypes.c_int64),
     ]
 
 
@@ -100,9 +100,10 @@ class Geometry:
 
     def __init__(self, layout: str, B: int, S1: int, S2: int, N1: int, D: int, Dr: int,
                  topk: int, sparse_mode: int, seq_q: Optional[Sequence[int]],
-                 seq_kv: Optional[Sequence[int]], scale: float):
+                 seq_kv: Optional[Sequence[int]], scale: float, block: int = 1):
         self.layout, self.B, self.S1, self.S2 = layout, B, S1, S2
         self.N1, self.D, self.Dr, self.topk = N1, D, Dr, topk
+        self.block = int(block)          # sparseBlockSize: each index names `block` keys
         self.sparse_mode, self.scale = sparse_mode, scale
         self.seq_q = None if seq_q is None else np.ascontiguousarray(seq_q, dtype=np.int32)
         self.seq_kv = None if seq_kv is None else np.ascontiguousarray(seq_kv, dtype=np.int32)
@@ -115,12 +116,12 @@ class Geometry:
     def of(cls, p) -> "Geometry":
         """From a sparse_mla_flash_amd.inputs.Problem (duck-typed)."""
         return cls(p.layout, p.B, p.S1, p.S2, p.N1, p.D, p.Dr, p.topk, p.sparse_mode,
-                   p.seq_q, p.seq_kv, p.scale)
+                   p.seq_q, p.seq_kv, p.scale, getattr(p, "block", 1))
 
     def c(self) -> _Problem:
         s = _Problem(self.B, self.S1, self.S2, self.N1, self.D, self.Dr, self.topk,
                      0 if self.layout == "BSND" else 1, self.sparse_mode, None, None,
-                     float(self.scale))
+                     float(self.scale), self.block)
         if self.seq_q is not None:
             s.seq_q = _ptr(self.seq_q, ctypes.c_int32)
         if self.seq_kv is not None:

@@ -69,12 +69,21 @@ static row_geo geo_of(const sfag_oracle_problem* pb, int64_t g) {
   return r;
 }
 
-/* Key position selected by slot s of row g, or -1 when the slot is skipped. */
+static int64_t block_of(const sfag_oracle_problem* pb) { return pb->block > 1 ? pb->block : 1; }
+
+/* Slots per query row: one per key of every selected block. */
+static int64_t nslots(const sfag_oracle_problem* pb) { return pb->topk * block_of(pb); }
+
+/* Key position selected by slot s of row g, or -1 when the slot is skipped.  Slot s is key
+ * s % bs of the block named by index s / bs of the row. */
 static int64_t slot_key(const sfag_oracle_problem* pb, const row_geo* r, const int32_t* idx,
                         int64_t g, int64_t s) {
   if (!r->active) return -1;
-  int64_t j = idx[g * pb->topk + s];
-  if (j < 0 || j >= r->lkv) return -1;
+  const int64_t bs = block_of(pb);
+  const int64_t jb = idx[g * pb->topk + s / bs];
+  if (jb < 0) return -1;
+  const int64_t j = jb * bs + s % bs;
+  if (j >= r->lkv) return -1;
   if (pb->sparse_mode == 3 && j > r->i + r->lkv - r->lq) return -1;
   return j;
 }
@@ -114,13 +123,13 @@ int sfag_oracle_forward(const sfag_oracle_problem* pb, const double* q, const do
   for (int64_t it = 0; it < n; ++it) {
     const int64_t g = rows ? rows[it] : it;
     const row_geo r = geo_of(pb, g);
-    const int64_t tk = pb->topk > 0 ? pb->topk : 1;
+    const int64_t tk = nslots(pb) > 0 ? nslots(pb) : 1;
     int64_t* key = (int64_t*)malloc(sizeof(int64_t) * (size_t)tk);
     double* z = (double*)malloc(sizeof(double) * (size_t)(tk * pb->N1));  /* z[a*N1 + h] */
     double* mh = (double*)malloc(sizeof(double) * (size_t)pb->N1);
     double* lh = (double*)malloc(sizeof(double) * (size_t)pb->N1);
     int64_t nv = 0;
-    for (int64_t s = 0; s < pb->topk; ++s) {
+    for (int64_t s = 0; s < nslots(pb); ++s) {
       const int64_t j = slot_key(pb, &r, idx, g, s);
       if (j >= 0) key[nv++] = r.kbase + j;
     }
@@ -176,7 +185,7 @@ int sfag_oracle_backward_dq(const sfag_oracle_problem* pb, const double* q, cons
       for (int64_t d = 0; d < pb->D; ++d) dqh[d] = 0.0;
       for (int64_t d = 0; d < pb->Dr; ++d) dqrh[d] = 0.0;
     }
-    for (int64_t s = 0; s < pb->topk; ++s) {
+    for (int64_t s = 0; s < nslots(pb); ++s) {
       const int64_t j = slot_key(pb, &r, idx, g, s);
       if (j < 0) continue;
       const int64_t key_row = r.kbase + j;
@@ -222,7 +231,7 @@ int sfag_oracle_backward_dkv(const sfag_oracle_problem* pb, const double* q, con
   int64_t* cnt = (int64_t*)calloc((size_t)nk + 1, sizeof(int64_t));
   for (int64_t g = row_lo; g < row_hi; ++g) {
     const row_geo r = geo_of(pb, g);
-    for (int64_t s = 0; s < pb->topk; ++s) {
+    for (int64_t s = 0; s < nslots(pb); ++s) {
       const int64_t j = slot_key(pb, &r, idx, g, s);
       if (j >= 0 && where[r.kbase + j] >= 0) cnt[where[r.kbase + j] + 1]++;
     }
@@ -233,9 +242,9 @@ int sfag_oracle_backward_dkv(const sfag_oracle_problem* pb, const double* q, con
   int64_t* pr = (int64_t*)malloc(sizeof(int64_t) * (size_t)(cnt[nk] > 0 ? cnt[nk] : 1));
   for (int64_t g = row_lo; g < row_hi; ++g) {
     const row_geo r = geo_of(pb, g);
-    for (int64_t s = 0; s < pb->topk; ++s) {
+    for (int64_t s = 0; s < nslots(pb); ++s) {
       const int64_t j = slot_key(pb, &r, idx, g, s);
-      if (j >= 0 && where[r.kbase + j] >= 0) pr[fill[where[r.kbase + j]]++] = g * pb->topk + s;
+      if (j >= 0 && where[r.kbase + j] >= 0) pr[fill[where[r.kbase + j]]++] = g * nslots(pb) + s;
     }
   }
 #pragma omp parallel for schedule(dynamic, 1)
@@ -247,7 +256,7 @@ int sfag_oracle_backward_dkv(const sfag_oracle_problem* pb, const double* q, con
     for (int64_t d = 0; d < pb->D; ++d) dka[d] = dva[d] = 0.0;
     for (int64_t d = 0; d < pb->Dr; ++d) dkra[d] = 0.0;
     for (int64_t e = cnt[a]; e < cnt[a + 1]; ++e) {
-      const int64_t g = pr[e] / pb->topk;
+      const int64_t g = pr[e] / nslots(pb);
       const row_geo r = geo_of(pb, g);
       for (int64_t h = 0; h < pb->N1; ++h) {
         const double* doh = dout + (g * pb->N1 + h) * pb->D;

@@ -24,9 +24,13 @@
  *         kr,dkr [B,S2,Dr]; idx [B,S1,topk]; max,sum [B,N1,S1].
  *   TND:  q.. [T1,N1,D]; k.. [T2,D]; idx [T1,topk]; max,sum [N1,T1]; S1=T1,
  *         S2=T2 and seq_q/seq_kv (B entries) are required.
- * A slot of query row i of batch b is valid iff the index j satisfies
+ * A slot of query row i of batch b is valid iff its key position j satisfies
  * 0 <= j < Lkv_b and, for sparse_mode 3, j <= i + Lkv_b - Lq_b.  Rows i >= Lq_b
  * are padding.  Invalid slots are skipped.
+ * Block selection (README "function description": topk blocks of sparseBlockSize
+ * keys each are gathered): with block = bs > 1 a row has topk * bs slots, and
+ * index idx[row][a] >= 0 gives the slots of key positions idx*bs .. idx*bs + bs - 1,
+ * each checked on its own as above; a negative index skips its bs slots.
  */
 #ifndef SFAG_ORACLE_H
 #define SFAG_ORACLE_H
@@ -44,6 +48,7 @@ typedef struct {
   const int32_t* seq_q;   /* B query lengths (NULL: S1 each, BSND only) */
   const int32_t* seq_kv;  /* B key lengths   (NULL: S2 each, BSND only) */
   double scale;
+  int64_t block;          /* sparseBlockSize (<= 1: each index is one key position) */
 } sfag_oracle_problem;
 
 /* Forward for the listed query rows (global row ids, NULL = all rows).

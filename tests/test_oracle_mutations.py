@@ -35,6 +35,10 @@ MUTATIONS = {
                                        "Dt[h] = dot(dout + (g * pb->N1 + h) * pb->D, dout + (g * pb->N1 + h) * pb->D, pb->D);"),
     "dk_transposed_operand": ("dka[d] += c * qh[d];", "dka[d] += c * doh[d];"),
     "tnd_key_offset_zero": ("r.kbase = ckv;", "r.kbase = 0;"),
+    "block_index_as_start": ("const int64_t j = jb * bs + s % bs;", "const int64_t j = jb + s % bs;"),
+    "block_causal_on_start": ("if (pb->sparse_mode == 3 && j > r->i + r->lkv - r->lq) return -1;",
+                              "if (pb->sparse_mode == 3 && jb * bs > r->i + r->lkv - r->lq) return -1;"),
+    "block_uncut_by_length": ("if (j >= r->lkv) return -1;", "if (jb * bs >= r->lkv) return -1;"),
 }
 
 
@@ -47,6 +51,9 @@ def _pins_pass() -> bool:
         lambda: pins.test_dense_reduction_matches_torch_autograd(4),
         pins.test_column_sums,
         pins.test_two_valid_slots_closed_form,
+        lambda: pins.test_every_block_selected_matches_dense_autograd(0),
+        lambda: pins.test_every_block_selected_matches_dense_autograd(1),
+        lambda: pins.test_every_block_selected_matches_dense_autograd(3),
     ]
     for c in checks:
         try:

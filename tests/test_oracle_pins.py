@@ -12,7 +12,10 @@ description" section) defines to an independent fact:
   - closed forms: all-ones inputs, a single valid slot, two valid slots,
     identical key rows (sum of dS over a row is zero);
   - invariants: column sums of dK / dKRope / dV, slot-permutation and padding
-    invariance, invalid indices behaving as -1.
+    invariance, invalid indices behaving as -1;
+  - block selection (sparseBlockSize > 1): every block selected equals dense
+    attention, finite differences with repeated / cut / invalid blocks, and a
+    brute-force single-row forward.
 """
 
 import math
@@ -236,6 +239,90 @@ def test_dense_reduction_matches_torch_autograd(case):
     dq, dk, dv, dqr, dkr = oracle.backward(g, q, k, v, qr, kr, idx, dout, out, m, l)
     for a, b_ in ((dq, t_dq), (dk, t_dk), (dv, t_dv), (dqr, t_dqr), (dkr, t_dkr)):
         np.testing.assert_allclose(a, b_, atol=1e-11, rtol=1e-9)
+
+
+# ---------------------------------------------------------------------------
+# block selection (sparseBlockSize > 1)
+# ---------------------------------------------------------------------------
+
+BLOCK_DENSE_CASES = [
+    ("BSND", 1, 6, 11, 2, 3, None, None, 4),     # causal; the last block is cut by the key length
+    ("BSND", 2, 5, 8, 3, 0, None, [7, 5], 3),    # no mask; padded key lengths cut the last blocks
+    ("BSND", 1, 9, 6, 2, 3, None, None, 5),      # causal, S1 > S2: early rows empty
+    ("TND", 2, 0, 0, 2, 3, [4, 3], [9, 5], 2),   # varlen, causal
+]
+
+
+@pytest.mark.parametrize("case", range(len(BLOCK_DENSE_CASES)))
+def test_every_block_selected_matches_dense_autograd(case):
+    """Indices naming every block of the sequence once (shuffled, with a -1 among them) select
+    every key once, so the result is dense masked attention (torch fp64 autograd).  Pins the
+    block -> key expansion (block j covers keys j*bs .. j*bs + bs - 1), the per-key length and
+    causal checks inside a block, and a -1 skipping only its own block."""
+    layout, B, S1, S2, N1, mode, sq, skv, bs = BLOCK_DENSE_CASES[case]
+    if layout == "TND":
+        S1, S2 = sum(sq), sum(skv)
+    maxkv = S2 if layout == "BSND" else max(skv)
+    nblk = -(-maxkv // bs)
+    g = Geometry(layout, B, S1, S2, N1, 16, 8, nblk + 2, mode, sq, skv, 0.3, block=bs)
+    q, k, v, qr, kr, dout = rnd_inputs(g, 200 + case)
+    r = np.random.default_rng(case)
+    idx = np.full((g.rows, g.topk), -1, dtype=np.int32)
+    for t, (b, i, lq, lkv, koff) in enumerate(row_info(g)):
+        row = np.concatenate([np.arange(-(-lkv // bs)), [-1]])
+        idx[t, :len(row)] = r.permutation(row)
+    out, m, l = oracle.forward(g, q, k, v, qr, kr, idx)
+    t_out, t_m, t_l, t_dq, t_dk, t_dv, t_dqr, t_dkr = torch_dense(g, q, k, v, qr, kr, dout)
+    np.testing.assert_allclose(out, t_out, atol=1e-12, rtol=1e-10)
+    np.testing.assert_allclose(m, t_m, atol=1e-12, rtol=1e-12)
+    np.testing.assert_allclose(l, t_l, atol=1e-12, rtol=1e-10)
+    dq, dk, dv, dqr, dkr = oracle.backward(g, q, k, v, qr, kr, idx, dout, out, m, l)
+    for a, b_ in ((dq, t_dq), (dk, t_dk), (dv, t_dv), (dqr, t_dqr), (dkr, t_dkr)):
+        np.testing.assert_allclose(a, b_, atol=1e-11, rtol=1e-9)
+
+
+def test_finite_differences_block_selection():
+    """All five gradients of sum(dO * out) by central differences with block selection:
+    repeated blocks (their keys count twice), a block cut by the key length, out-of-range and
+    negative block indices."""
+    g = Geometry("BSND", 2, 4, 7, 2, 5, 3, 3, 3, None, None, 0.37, block=3)
+    q, k, v, qr, kr, dout = rnd_inputs(g, 31)
+    idx = np.array([[0, 2, 0], [1, -1, 5], [2, 1, 1], [-3, 0, 2],
+                    [0, 1, 2], [1, 1, -1], [2, 0, 9], [0, 2, 1]], dtype=np.int32)
+    out, m, l = oracle.forward(g, q, k, v, qr, kr, idx)
+    dq, dk, dv, dqr, dkr = oracle.backward(g, q, k, v, qr, kr, idx, dout, out, m, l)
+    h = 1e-6
+    args = dict(q=q, k=k, v=v, qr=qr, kr=kr)
+    grads = dict(q=dq.reshape(q.shape), k=dk, v=dv, qr=dqr.reshape(qr.shape), kr=dkr)
+    for name, base in args.items():
+        fd = np.zeros_like(base)
+        flat = base.reshape(-1)
+        for e in range(flat.size):
+            old = flat[e]
+            flat[e] = old + h
+            lp = loss(g, args["q"], args["k"], args["v"], args["qr"], args["kr"], idx, dout)
+            flat[e] = old - h
+            lm = loss(g, args["q"], args["k"], args["v"], args["qr"], args["kr"], idx, dout)
+            flat[e] = old
+            fd.reshape(-1)[e] = (lp - lm) / (2 * h)
+        err = np.abs(fd - grads[name]).max()
+        assert err < 1e-6 * max(1.0, np.abs(fd).max()), (name, err)
+
+
+def test_block_selection_brute_force_single_row():
+    """One query row, brute force in plain numpy: the keys of the selected blocks (cut at the
+    key length and at the causal bound), softmax over them, out = P V."""
+    g = Geometry("BSND", 1, 3, 10, 1, 4, 2, 2, 3, None, None, 0.5, block=4)
+    q, k, v, qr, kr, dout = rnd_inputs(g, 41)
+    idx = np.array([[2, 0], [1, 2], [0, -1]], dtype=np.int32)
+    out, m, l = oracle.forward(g, q, k, v, qr, kr, idx)
+    for t in range(3):
+        pos = t + 10 - 3
+        keys = [jb * 4 + r for jb in idx[t] if jb >= 0 for r in range(4) if jb * 4 + r < 10 and jb * 4 + r <= pos]
+        z = np.array([0.5 * (q[t, 0] @ k[j] + qr[t, 0] @ kr[j]) for j in keys])
+        p_ = np.exp(z - z.max()) / np.exp(z - z.max()).sum()
+        np.testing.assert_allclose(out[t, 0], p_ @ v[keys], atol=1e-12)
+        assert abs(m[0, 0, t] - z.max()) < 1e-12
 
 
 # ---------------------------------------------------------------------------
