@@ -32,6 +32,11 @@
  *     negative, >= the sequence's key length, or, for sparseMode 3, greater than
  *     i + Lkv - Lq for query position i (causal mask aligned at the bottom-right
  *     vertex).  Query rows at or beyond the sequence's query length are padding.
+ *   - Block selection (sparseBlockSize = bs > 1; the README's "function description"
+ *     selects topk blocks of sparseBlockSize keys): index j names the block of key
+ *     positions j*bs .. j*bs + bs - 1, and each of those keys is a slot of its own,
+ *     skipped by the rules above (so a block may be cut by the key length or the
+ *     causal mask).  A negative index skips its whole block.  topk * bs <= 131072.
  *   - sparseMode 0 (no mask) and 3 (causal, bottom-right) are supported, as the
  *     page's constraint section states; preTokens / nextTokens are accepted and
  *     ignored in both modes.
@@ -64,7 +69,7 @@ typedef enum {
   SFAG_OK = 0,
   SFAG_ERR_PARAM_NULLPTR = 161001, /* a required pointer is NULL */
   SFAG_ERR_PARAM_INVALID = 161002, /* a shape, attribute or layout violates the constraints */
-  SFAG_ERR_UNSUPPORTED = 161901,   /* legal on the page but not built here (fp16, block size > 1, no rope) */
+  SFAG_ERR_UNSUPPORTED = 161901,   /* legal on the page but not built here (fp16, no rope) */
   SFAG_ERR_WORKSPACE = 161902,     /* workspace NULL or smaller than sfag_get_workspace_size() */
   SFAG_ERR_DEVICE = 161903         /* a HIP runtime / launch error */
 } sfag_status;
@@ -77,7 +82,7 @@ typedef struct {
   int64_t N2;     /* key heads: must be 1 */
   int64_t D;      /* head width: must be 512 */
   int64_t Drope;  /* rope width: must be 64 */
-  int64_t topk;   /* selected keys per query token (>= 1; the page lists 1024..8192 step 1024) */
+  int64_t topk;   /* indices per query token (>= 1; the page lists 1024..8192 step 1024) */
 } sfag_dims;
 
 /*
@@ -86,7 +91,8 @@ typedef struct {
  * same status the backward call would return for them.
  *   seq_len_q_host / seq_len_kv_host: B valid lengths (actualSeqLengthsQuery /
  *     actualSeqLengthsKv); NULL means full S1 / S2 (BSND only).
- *   sparse_block_size: must be 1 (sparseBlockSize; larger blocks -> UNSUPPORTED).
+ *   sparse_block_size: sparseBlockSize >= 1, with topk * sparse_block_size <= 131072
+ *     (PARAM_INVALID otherwise).
  *   layout: "BSND" or "TND".
  */
 sfag_status sfag_get_workspace_size(const sfag_dims* dims, const int32_t* seq_len_q_host,

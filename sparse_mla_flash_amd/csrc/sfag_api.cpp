@@ -47,7 +47,8 @@ uint64_t align_up(uint64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Plan {
   int tnd = 0;
-  int64_t B = 0, S1 = 0, S2 = 0, N1 = 0, topk = 0;
+  int64_t B = 0, S1 = 0, S2 = 0, N1 = 0, topk = 0;   // topk: slots per row (indices x block size)
+  int bs = 1;
   int64_t rows = 0, keys = 0;
   int mode3 = 0, det = 0, hg_count = 0;
   float scale = 0.f;
@@ -119,10 +120,12 @@ sfag_status make_plan(const sfag_dims* dims, const int32_t* sq, const int32_t* s
   if (dims->B < 1 || dims->B > 256) return fail(SFAG_ERR_PARAM_INVALID, "B must be in 1..256 (got %lld)", (long long)dims->B);
   if (dims->topk < 1 || dims->topk > kMaxTopk)
     return fail(SFAG_ERR_PARAM_INVALID, "topk must be in 1..%lld (got %lld)", (long long)kMaxTopk, (long long)dims->topk);
+  if (block >= 1 && dims->topk * block > kMaxTopk)
+    return fail(SFAG_ERR_PARAM_INVALID, "topk * sparseBlockSize must be at most %lld (got %lld * %lld)",
+                (long long)kMaxTopk, (long long)dims->topk, (long long)block);
   if (mode != 0 && mode != 3)
     return fail(SFAG_ERR_PARAM_INVALID, "sparseMode must be 0 or 3 (got %lld)", (long long)mode);
   if (block < 1) return fail(SFAG_ERR_PARAM_INVALID, "sparseBlockSize must be >= 1 (got %lld)", (long long)block);
-  if (block != 1) return fail(SFAG_ERR_UNSUPPORTED, "sparseBlockSize > 1 is not built (got %lld)", (long long)block);
   if (!std::isfinite(scale)) return fail(SFAG_ERR_PARAM_INVALID, "scaleValue must be finite");
   if (det != 0 && det != 1) return fail(SFAG_ERR_PARAM_INVALID, "deterministic must be 0 or 1");
 
@@ -130,7 +133,8 @@ sfag_status make_plan(const sfag_dims* dims, const int32_t* sq, const int32_t* s
   p->S1 = dims->S1;
   p->S2 = dims->S2;
   p->N1 = dims->N1;
-  p->topk = dims->topk;
+  p->topk = dims->topk * block;     // slots per row: every index names a block of `block` keys
+  p->bs = (int)block;
   p->mode3 = mode == 3;
   p->det = det;
   p->scale = scale;
@@ -391,6 +395,7 @@ sfag_status sfag_sparse_flash_attention_grad(
   a.B = (int)p.B;
   a.N1 = (int)p.N1;
   a.topk = (int)p.topk;
+  a.bs = p.bs;
   a.mode3 = p.mode3;
   a.layout_tnd = p.tnd;
   a.hgc = p.hg_count;
@@ -422,6 +427,7 @@ sfag_status sfag_sparse_flash_attention_grad(
     da.B = (int)p.B;
     da.N1 = (int)p.N1;
     da.topk = (int)p.topk;
+    da.bs = p.bs;
     da.mode3 = p.mode3;
     da.layout_tnd = p.tnd;
     da.hgc = p.hg_count;
@@ -519,6 +525,7 @@ sfag_status sfag_sparse_flash_attention_forward(const void* query, const void* k
   a.B = (int)p.B;
   a.N1 = (int)p.N1;
   a.topk = (int)p.topk;
+  a.bs = p.bs;
   a.mode3 = p.mode3;
   a.layout_tnd = p.tnd;
   a.scale = scale_value;

@@ -188,7 +188,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_main_kernel(BwdArgs a) {
 #pragma unroll
   for (int ft = 0; ft < 36; ++ft) dqacc[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int32_t* idxrow = a.idx + row * a.topk;
+  const int32_t* idxrow = a.idx + row * (a.topk / a.bs);
   const int64_t pair_base = (row - a.row_begin) * a.topk;
   // key-major mode walks the row's valid key positions in ascending order (sorted beforehand)
   const int nslots = kMode == 2 ? a.count[row] : a.topk;
@@ -201,7 +201,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_main_kernel(BwdArgs a) {
       const int s = c0 + threadIdx.x;
       int64_t kr_ = -1;
       if (s < nslots) {
-        const int j = srow[s];
+        const int j = kMode == 2 ? srow[s] : slot_key(idxrow, s, a.bs);
         if (j >= 0 && j <= geo.hi) kr_ = geo.kstart + j;
       }
       keyrow[threadIdx.x] = kr_;
@@ -390,7 +390,7 @@ __global__ void pair_keys_kernel(BwdArgs a, uint64_t* keys, int64_t nrows) {
        e += (int64_t)gridDim.x * blockDim.x) {
     const int64_t r = a.row_begin + e / a.topk;
     const RowGeo geo = row_geo(a.lens, cum, a.B, a.layout_tnd, a.S1, a.S2, r, a.mode3);
-    const int j = a.idx[r * a.topk + e % a.topk];
+    const int j = slot_key(a.idx + r * (a.topk / a.bs), (int)(e % a.topk), a.bs);
     uint64_t kv = ~0ull;
     if (geo.active && j >= 0 && j <= geo.hi) kv = ((uint64_t)(geo.kstart + j) << 32) | (uint64_t)e;
     keys[e] = kv;

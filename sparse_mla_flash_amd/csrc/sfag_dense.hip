@@ -71,7 +71,7 @@ __global__ void __launch_bounds__(kThreads) sort_rows_kernel(DenseArgs a) {
     for (int i = t; i < kDk; i += kThreads) a.zero_row[i] = 0;
   const RowGeo geo = row_geo(a.lens, cum, a.B, a.layout_tnd, a.S1, a.S2, row, a.mode3);
   const int map_end = (geo.active && geo.hi >= 0) ? min(a.kstride, ((geo.hi + kBk) / kBk) * kBk) : 0;
-  const int32_t* irow = a.idx + row * a.topk;
+  const int32_t* irow = a.idx + row * (a.topk / a.bs);
   int32_t* srow = a.sorted + row * a.topk;
   int16_t* kp = a.kpos + row * a.kstride;
   int32_t* orow = a.offs + row * (a.maxblk + 1);
@@ -85,7 +85,7 @@ __global__ void __launch_bounds__(kThreads) sort_rows_kernel(DenseArgs a) {
     for (int k = t; k < kSortWords; k += kThreads) cw[k] = 0u;
     __syncthreads();
     for (int i = t; i < a.topk; i += kThreads) {
-      const int j = irow[i];
+      const int j = slot_key(irow, i, a.bs);
       if (j >= 0 && j <= geo.hi && j >= w0 && j < w1) {
         const int k = j - w0;
         atomicAdd(&cw[k >> 1], 1u << (16 * (k & 1)));

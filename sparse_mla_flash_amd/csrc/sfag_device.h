@@ -192,4 +192,17 @@ __device__ __forceinline__ RowGeo row_geo(const Lens& L, const int32_t* cum, int
   return r;
 }
 
+// Key position named by slot s of a query row whose sparseIndices row is irow, with block
+// selection (SparseFlashAttentionGrad README, "function description": each index selects a
+// block of sparseBlockSize keys; index j covers key positions j * bs .. j * bs + bs - 1).  The
+// row has topk * bs slots; slot s is key s % bs of block irow[s / bs].  Negative block indices
+// give -1; positions past the key range stay out of range (the caller checks them against the
+// row's valid range).
+__device__ __forceinline__ int slot_key(const int32_t* irow, int s, int bs) {
+  if (bs == 1) return irow[s];
+  const int jb = irow[s / bs];
+  if (jb < 0) return -1;
+  return (int)min((int64_t)jb * bs + s % bs, (int64_t)0x7fffffff);
+}
+
 }  // namespace sfag

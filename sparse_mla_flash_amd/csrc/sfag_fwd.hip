@@ -75,14 +75,14 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
 #pragma unroll
   for (int ft = 0; ft < 32; ++ft) oacc[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int32_t* idxrow = a.idx + row * a.topk;
+  const int32_t* idxrow = a.idx + row * (a.topk / a.bs);
   for (int c0 = 0; c0 < a.topk; c0 += kKC) {
     int any = 0;
     if (threadIdx.x < kKC) {
       const int s = c0 + threadIdx.x;
       int64_t kr_ = -1;
       if (s < a.topk) {
-        const int j = idxrow[s];
+        const int j = slot_key(idxrow, s, a.bs);
         if (j >= 0 && j <= geo.hi) kr_ = geo.kstart + j;
       }
       keyrow[threadIdx.x] = kr_;

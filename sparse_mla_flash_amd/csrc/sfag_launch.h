@@ -23,7 +23,7 @@ struct BwdArgs {
   const uint16_t* kr;     // [keys, 64]
   const uint16_t* dout;   // [rows, N1, 512]
   const uint16_t* out;    // [rows, N1, 512]
-  const int32_t* idx;     // [rows, topk]
+  const int32_t* idx;     // [rows, topk / bs] block indices (bs = 1: key positions)
   const float* smax;      // statistics (BSND [B, N1, S1], TND [N1, T1])
   const float* ssum;
   uint16_t* dq;           // [rows, N1, 512]
@@ -42,6 +42,7 @@ struct BwdArgs {
   int64_t row_begin;      // first query row of this launch
   int64_t pairs_per_launch;
   int B, N1, topk, mode3, layout_tnd, hgc;
+  int bs;                 // sparseBlockSize: topk slots = index count x bs
   float scale;
 };
 
@@ -49,7 +50,7 @@ struct DenseArgs {
   const uint16_t* q;      // [rows, N1, 512]
   const uint16_t* qr;     // [rows, N1, 64]
   const uint16_t* dout;   // [rows, N1, 512]
-  const int32_t* idx;     // [rows, topk]
+  const int32_t* idx;     // [rows, topk / bs]
   int32_t* sorted;        // [rows, topk]
   int32_t* count;         // [rows]
   int32_t* maxdup;        // [rows]
@@ -68,6 +69,7 @@ struct DenseArgs {
   Lens lens;
   int64_t S1, S2;
   int B, N1, topk, mode3, layout_tnd, hgc, maxblk, items, citems, kstride;
+  int bs;                 // sparseBlockSize: topk slots = index count x bs
   float scale;
 };
 
@@ -84,6 +86,7 @@ struct FwdArgs {
   int64_t S1;
   int64_t S2;
   int B, N1, topk, mode3, layout_tnd;
+  int bs;                 // sparseBlockSize: topk slots = index count x bs
   float scale;
 };
 

@@ -62,6 +62,7 @@ class Problem:
     Dr: int = D_ROPE
     deterministic: bool = False
     name: str = ""
+    block: int = 1                   # sparseBlockSize: each index names `block` consecutive keys
     # tensors (filled by generate())
     q: Optional[np.ndarray] = None       # uint16 bf16 bits
     k: Optional[np.ndarray] = None
@@ -152,11 +153,12 @@ def _distinct_rows(rng, n: np.ndarray, k: int, group: int = 32) -> np.ndarray:
 
 
 def _rows_uniform(p: Problem, rng, b: int) -> np.ndarray:
-    """Per query row: distinct uniform keys over the valid range; short ranges take all keys in
-    random order; -1 padded."""
+    """Per query row: distinct uniform keys (with block selection: blocks of p.block keys, the
+    last one possibly reaching past the valid range) over the valid range; short ranges take all
+    candidates in random order; -1 padded."""
     lq = p.lq(b)
     out = np.full((lq, p.topk), -1, dtype=np.int64)
-    n = np.array([_causal_hi(p, b, i) + 1 for i in range(lq)], dtype=np.int64)
+    n = np.array([_causal_hi(p, b, i) // p.block + 1 for i in range(lq)], dtype=np.int64)
     for i in np.nonzero((n > 0) & (n <= p.topk))[0]:
         out[i, :n[i]] = rng.permutation(int(n[i]))
     long_rows = np.nonzero(n > p.topk)[0]
@@ -220,6 +222,8 @@ def _rows_hot_cold(p: Problem, rng, b: int) -> np.ndarray:
 
 
 def _indices(p: Problem, rng: np.random.Generator, kind: str, window: int) -> np.ndarray:
+    if p.block != 1 and kind != "uniform":
+        raise ValueError("block selection inputs are generated with the uniform recipe only")
     idx = np.full((p.rows, p.topk), -1, dtype=np.int64)
     for b in range(p.B):
         base = p.q_offset(b)
@@ -283,7 +287,8 @@ def fp32(x: float) -> float:
 
 
 def problem(layout="BSND", B=1, S1=128, S2=128, N1=8, topk=64, sparse_mode=3, seq_q=None,
-            seq_kv=None, scale=None, D=D_NOPE, Dr=D_ROPE, deterministic=False, name="") -> Problem:
+            seq_kv=None, scale=None, D=D_NOPE, Dr=D_ROPE, deterministic=False, name="",
+            block=1) -> Problem:
     if scale is None:
         scale = 1.0 / math.sqrt(D + Dr)
     if layout == "TND":
@@ -292,7 +297,8 @@ def problem(layout="BSND", B=1, S1=128, S2=128, N1=8, topk=64, sparse_mode=3, se
     return Problem(layout=layout, B=B, S1=S1, S2=S2, N1=N1, topk=topk, sparse_mode=sparse_mode,
                    seq_q=None if seq_q is None else [int(x) for x in seq_q],
                    seq_kv=None if seq_kv is None else [int(x) for x in seq_kv],
-                   scale=fp32(scale), D=D, Dr=Dr, deterministic=deterministic, name=name)
+                   scale=fp32(scale), D=D, Dr=Dr, deterministic=deterministic, name=name,
+                   block=int(block))
 
 
 # The five benchmark workloads (shapes and index structure).  Seed = workload number.

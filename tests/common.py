@@ -73,7 +73,8 @@ class Case:
         return sf.sparse_flash_attention_grad(
             d["query"], d["key"], d["value"], d["sparse_indices"], d["d_out"], d["out"], d["softmax_max"],
             d["softmax_sum"], p.seq_q, p.seq_kv, d["query_rope"], d["key_rope"], scale_value=p.scale,
-            layout=p.layout, sparse_mode=p.sparse_mode, deterministic=deterministic)
+            sparse_block_size=p.block, layout=p.layout, sparse_mode=p.sparse_mode,
+            deterministic=deterministic)
 
 
 def compare(name, got: np.ndarray, ref: np.ndarray, max_abs=MAX_ABS, rel_l2=REL_L2, scaled=True):

@@ -64,7 +64,8 @@ def test_invalid_attributes():
     assert status_of(ws, d, sparse_mode=1) == sf.SFAG_ERR_PARAM_INVALID
     assert status_of(ws, d, layout="BNSD") == sf.SFAG_ERR_PARAM_INVALID
     assert status_of(ws, d, sparse_block_size=0) == sf.SFAG_ERR_PARAM_INVALID
-    assert status_of(ws, d, sparse_block_size=64) == sf.SFAG_ERR_UNSUPPORTED
+    assert status_of(ws, d, sparse_block_size=64) == sf.SFAG_OK           # 1024 x 64 slots
+    assert status_of(ws, d, sparse_block_size=129) == sf.SFAG_ERR_PARAM_INVALID   # > 131072 slots
     assert status_of(ws, d, scale_value=float("nan")) == sf.SFAG_ERR_PARAM_INVALID
     assert status_of(ws, d, seq_len_q=[129]) == sf.SFAG_ERR_PARAM_INVALID
     assert status_of(ws, d, seq_len_kv=[-1]) == sf.SFAG_ERR_PARAM_INVALID

@@ -5,8 +5,9 @@ Every output tensor must satisfy max abs error <= 2e-2 and relative L2 error
 fp32 statistics).  Sizes are small enough for the oracle to finish in seconds
 while spanning several 32-key chunks, several 16-head tiles and a ragged tail;
 edge cases cover padding, empty rows, invalid / duplicate indices, varlen TND
-with an empty sequence, S1 > S2 under the causal mode and every head-group
-shape the kernels special-case (N1 < 16, N1 not a multiple of 16, N1 = 128).
+with an empty sequence, S1 > S2 under the causal mode, every head-group
+shape the kernels special-case (N1 < 16, N1 not a multiple of 16, N1 = 128)
+and block selection (sparseBlockSize 4, 16, 64).
 """
 
 import numpy as np
@@ -119,6 +120,50 @@ def test_forward_matches_oracle(name):
     out, smax, ssum = sf.sparse_flash_attention_forward(
         d["query"], d["key"], d["value"], d["sparse_indices"], p.seq_q, p.seq_kv, d["query_rope"],
         d["key_rope"], scale_value=p.scale, layout=p.layout, sparse_mode=p.sparse_mode)
+    compare(name + "/out", from_dev(out), case.out64)
+    m, l = from_dev(smax), from_dev(ssum)
+    assert np.abs(m - case.m64).max() <= 1e-4 * max(1.0, np.abs(case.m64).max())
+    assert np.abs(l - case.l64).max() <= 1e-4 * max(1.0, np.abs(case.l64).max())
+
+
+BLOCK_CASES = {
+    # name: (problem kwargs, seed); block selection, the last block cut by the key length
+    "bsnd_n16_block4_causal": (dict(layout="BSND", B=1, S1=40, S2=301, N1=16, topk=20, sparse_mode=3,
+                                    block=4), 31),
+    "tnd_n64_block16_varlen": (dict(layout="TND", B=2, seq_q=[30, 17], seq_kv=[200, 95], N1=64, topk=6,
+                                    sparse_mode=3, block=16), 32),
+    "bsnd_n8_block64_nomask": (dict(layout="BSND", B=1, S1=12, S2=700, N1=8, topk=5, sparse_mode=0,
+                                    block=64), 33),
+}
+
+
+def make_block(name):
+    kw, seed = BLOCK_CASES[name]
+    p = inputs.problem(**kw, name=name)
+    inputs.generate(p, seed)
+    return p
+
+
+@pytest.mark.parametrize("name", sorted(BLOCK_CASES))
+@pytest.mark.parametrize("deterministic", [False, True])
+def test_block_selection_matches_oracle(name, deterministic, path):
+    """sparseBlockSize > 1: every index names a block of consecutive keys."""
+    case = Case(make_block(name))
+    outs = case.run_gpu(deterministic=deterministic)
+    res = check_all(case, outs, f"{name}/{path}/det={int(deterministic)}/")
+    print(name, path, deterministic, {k: f"{v[0]:.2e}/{v[1]:.2e}" for k, v in res.items()})
+
+
+@pytest.mark.parametrize("name", sorted(BLOCK_CASES))
+def test_block_selection_forward_matches_oracle(name):
+    import sparse_mla_flash_amd as sf
+    p = make_block(name)
+    case = Case(p)
+    d = case.device_inputs()
+    out, smax, ssum = sf.sparse_flash_attention_forward(
+        d["query"], d["key"], d["value"], d["sparse_indices"], p.seq_q, p.seq_kv, d["query_rope"],
+        d["key_rope"], scale_value=p.scale, sparse_block_size=p.block, layout=p.layout,
+        sparse_mode=p.sparse_mode)
     compare(name + "/out", from_dev(out), case.out64)
     m, l = from_dev(smax), from_dev(ssum)
     assert np.abs(m - case.m64).max() <= 1e-4 * max(1.0, np.abs(case.m64).max())
