@@ -206,8 +206,10 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
         pacc[1] = mfma(doA[ks], kf1[ks], pacc[1]);                                             \
       }                                                                                        \
     }                                                                                          \
-    /* issue order: the first four fragments, then per step one of the next chunk's gather   \
-       loads (steps 0-8), the fragments two steps ahead and the step's MFMAs */               \
+    /* issue order: the first four fragments, then per step the fragments two steps ahead and \
+       the step's MFMAs.  The vector-memory slots of steps 0-8 take the sorted-position load;   \
+       the gather itself sits in its own (conditional) block before the scores: all 9 loads   \
+       issued together measured faster than spread among the MFMAs */                        \
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);                                         \
     _Pragma("unroll") for (int ks = 0; ks < 16; ++ks) {                                        \
       if (ks < 9) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                           \
