@@ -63,6 +63,7 @@ def valid_per_row(p):
     """Number of valid (row, slot) pairs of every query row (host-side bookkeeping)."""
     import numpy as np
     idx = p.idx.reshape(p.rows, p.topk).astype(np.int64)
+    bs = p.block
     counts = np.zeros(p.rows, dtype=np.int64)
     for b in range(p.B):
         r0 = p.q_offset(b)
@@ -70,7 +71,9 @@ def valid_per_row(p):
         rows = idx[r0:r0 + lq]
         i = np.arange(lq)[:, None]
         hi = np.minimum(i + lkv - lq, lkv - 1) if p.sparse_mode == 3 else np.full((lq, 1), lkv - 1)
-        counts[r0:r0 + lq] = ((rows >= 0) & (rows <= hi)).sum(axis=1)
+        # keys j*bs .. j*bs + bs - 1 of every block index j >= 0 that do not pass hi
+        n = np.clip(hi - rows * bs + 1, 0, bs)
+        counts[r0:r0 + lq] = np.where(rows >= 0, n, 0).sum(axis=1)
     return counts
 
 
@@ -179,11 +182,11 @@ def main():
     q, k, v, qr, kr, dout = (dev(x) for x in (p.q, p.k, p.v, p.qr, p.kr, p.dout))
     idx = dev(p.idx, raw=True)
     out, smax, ssum = sf.sparse_flash_attention_forward(q, k, v, idx, p.seq_q, p.seq_kv, qr, kr,
-                                                        scale_value=p.scale, layout=p.layout,
-                                                        sparse_mode=p.sparse_mode)
+                                                        scale_value=p.scale, sparse_block_size=p.block,
+                                                        layout=p.layout, sparse_mode=p.sparse_mode)
     det = bool(args.deterministic or p.deterministic)
     dims = sf._dims_from(q, k, idx, p.layout, p.seq_q, p.seq_kv)
-    ws_bytes = sf.sfag_get_workspace_size(dims, p.seq_q, p.seq_kv, p.scale, 1, p.layout, p.sparse_mode,
+    ws_bytes = sf.sfag_get_workspace_size(dims, p.seq_q, p.seq_kv, p.scale, p.block, p.layout, p.sparse_mode,
                                           2 ** 31 - 1, 2 ** 31 - 1, det)
     ws = torch.empty(max(1, ws_bytes), dtype=torch.uint8, device="cuda")
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(k)
@@ -193,7 +196,7 @@ def main():
     def step():
         st = sf.sfag_sparse_flash_attention_grad(
             q.data_ptr(), k.data_ptr(), v.data_ptr(), idx.data_ptr(), dout.data_ptr(), out.data_ptr(),
-            smax.data_ptr(), ssum.data_ptr(), p.seq_q, p.seq_kv, qr.data_ptr(), kr.data_ptr(), dims, p.scale, 1,
+            smax.data_ptr(), ssum.data_ptr(), p.seq_q, p.seq_kv, qr.data_ptr(), kr.data_ptr(), dims, p.scale, p.block,
             p.layout, p.sparse_mode, 2 ** 31 - 1, 2 ** 31 - 1, det, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
             dqr.data_ptr(), dkr.data_ptr(), ws.data_ptr(), ws.numel(), stream)
         if st != 0:
@@ -224,7 +227,7 @@ def main():
     ms_per_step = (t1 - t0) / args.steps * 1e3
     per_row = valid_per_row(p)
     npairs = int(per_row.sum())
-    nominal = p.rows * p.topk
+    nominal = p.rows * p.topk * p.block
     flops = npairs * p.N1 * FLOP_PER_PAIR_HEAD
     value = flops / (ms_per_step * 1e-3) / 1e12
     if path == "key-major":
@@ -256,7 +259,7 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": p.name, "layout": p.layout, "B": p.B, "S1": p.S1, "S2": p.S2, "N1": p.N1,
-            "topk": p.topk, "sparse_mode": p.sparse_mode, "deterministic": det,
+            "topk": p.topk, "sparse_block_size": p.block, "sparse_mode": p.sparse_mode, "deterministic": det,
             "valid_pairs": npairs, "nominal_pairs": nominal,
             "effective_tflops_nominal": round(nominal * p.N1 * FLOP_PER_PAIR_HEAD / (ms_per_step * 1e-3) / 1e12, 3),
         },

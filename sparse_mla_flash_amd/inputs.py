@@ -315,6 +315,9 @@ WORKLOADS = {
     5: dict(spec=dict(layout="BSND", B=2, S1=4096, S2=32768, N1=48, topk=8192, sparse_mode=0,
                       deterministic=True, name="bsnd_b2_s4096q_32768k_n48_topk8192_hotcold_det"),
             kind="hot_cold"),
+    # block selection: 32 blocks of 64 consecutive keys per token (2048 keys, as workload 2)
+    6: dict(spec=dict(layout="BSND", B=1, S1=8192, S2=8192, N1=64, topk=32, sparse_mode=3, block=64,
+                      name="bsnd_s8192_n64_top32x64blocks_causal"), kind="uniform"),
 }
 
 

@@ -129,6 +129,25 @@ def inputs_to_dev(bits, raw):
     return to_dev(bits, "raw" if raw else "bf16")
 
 
+def test_block_selection_workload_sampled():
+    """BSND S1 = S2 = 8192, N1 = 64, causal, 32 blocks of 64 keys per token (sparseBlockSize
+    64): sampled rows and keys against the oracle, on both dK / dV modes."""
+    p = inputs.workload(6)
+    live = np.arange(p.rows - 128, p.rows)
+    case = Case(p, fwd_rows=live)
+    rng = np.random.default_rng(606)
+    dq_rows = np.sort(rng.choice(live, 16, replace=False))
+    idx0 = p.idx.reshape(p.rows, p.topk)
+    sel = idx0[live[-1]]
+    block_keys = (sel[sel >= 0][:3, None] * p.block + np.arange(p.block)[None, :]).reshape(-1)
+    keys = np.unique(np.concatenate([rng.choice(p.S2, 32, replace=False), block_keys[block_keys < p.S2]]))
+    dev = case.device_inputs()
+    for det in (False, True):
+        outs = case.run_gpu(deterministic=det, dev=dev)
+        _check_sampled(case, outs, live, dq_rows, [(keys, live[0], live[-1] + 1)],
+                       f"{p.name}/det={int(det)}/sampled/")
+
+
 def test_hot_cold_deterministic_workload_sampled():
     """BSND B = 2, S1 = 4096, S2 = 32768, N1 = 48 (a partial head group), topk = 8192, no mask,
     deterministic; every token selects all hot keys plus distinct cold keys."""
