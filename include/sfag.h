@@ -69,7 +69,7 @@ typedef enum {
   SFAG_OK = 0,
   SFAG_ERR_PARAM_NULLPTR = 161001, /* a required pointer is NULL */
   SFAG_ERR_PARAM_INVALID = 161002, /* a shape, attribute or layout violates the constraints */
-  SFAG_ERR_UNSUPPORTED = 161901,   /* legal on the page but not built here (fp16, no rope) */
+  SFAG_ERR_UNSUPPORTED = 161901,   /* legal on the page but not built here (fp16) */
   SFAG_ERR_WORKSPACE = 161902,     /* workspace NULL or smaller than sfag_get_workspace_size() */
   SFAG_ERR_DEVICE = 161903         /* a HIP runtime / launch error */
 } sfag_status;
@@ -110,6 +110,10 @@ sfag_status sfag_get_workspace_size(const sfag_dims* dims, const int32_t* seq_le
  *   softmax_max / softmax_sum: fp32 statistics of the forward pass (layout above).
  *   d_query, d_key, d_value, d_query_rope, d_key_rope: bf16 outputs shaped like
  *   query, key, value, query_rope, key_rope.
+ *   query_rope / key_rope are optional (queryRopeOptional / keyRopeOptional): give
+ *   both, with both rope gradients, or neither; then the logits have no rope term
+ *   and d_query_rope / d_key_rope are ignored.  Exactly one of them NULL, or a rope
+ *   gradient NULL while the rope inputs are given -> PARAM_NULLPTR.
  *   workspace: device buffer of at least sfag_get_workspace_size() bytes, 256-byte
  *   aligned; its contents on entry are ignored.
  */

@@ -354,12 +354,18 @@ sfag_status sfag_sparse_flash_attention_grad(
       {d_query, "d_query"}, {d_key, "d_key"}, {d_value, "d_value"}};
   for (const auto& r : req)
     if ((st = check_ptr(r.p, r.n)) != SFAG_OK) return st;
-  if (!query_rope || !key_rope || !d_query_rope || !d_key_rope)
-    return fail(SFAG_ERR_UNSUPPORTED, "the rope inputs and outputs are required (rope-less MLA is not built)");
-  const struct { const void* p; const char* n; } rope[] = {
-      {query_rope, "query_rope"}, {key_rope, "key_rope"}, {d_query_rope, "d_query_rope"}, {d_key_rope, "d_key_rope"}};
-  for (const auto& r : rope)
-    if ((st = check_ptr(r.p, r.n)) != SFAG_OK) return st;
+  // rope inputs: both given (then both rope gradients are required) or both absent (no rope
+  // terms; the rope gradient pointers are ignored)
+  const bool has_rope = query_rope || key_rope;
+  if (has_rope) {
+    const struct { const void* p; const char* n; } rope[] = {
+        {query_rope, "query_rope"}, {key_rope, "key_rope"}, {d_query_rope, "d_query_rope"}, {d_key_rope, "d_key_rope"}};
+    for (const auto& r : rope)
+      if ((st = check_ptr(r.p, r.n)) != SFAG_OK) return st;
+  } else {
+    d_query_rope = nullptr;
+    d_key_rope = nullptr;
+  }
   Plan p;
   st = make_plan(dims, seq_len_q_host, seq_len_kv_host, scale_value, sparse_block_size, layout, sparse_mode,
                  deterministic, true, &p);
@@ -500,10 +506,10 @@ sfag_status sfag_sparse_flash_attention_forward(const void* query, const void* k
       {out, "out"}, {softmax_max, "softmax_max"}, {softmax_sum, "softmax_sum"}};
   for (const auto& r : req)
     if ((st = check_ptr(r.p, r.n)) != SFAG_OK) return st;
-  if (!query_rope || !key_rope)
-    return fail(SFAG_ERR_UNSUPPORTED, "the rope inputs are required (rope-less MLA is not built)");
-  if ((st = check_ptr(query_rope, "query_rope")) != SFAG_OK) return st;
-  if ((st = check_ptr(key_rope, "key_rope")) != SFAG_OK) return st;
+  if (query_rope || key_rope) {             // both or neither (no rope terms)
+    if ((st = check_ptr(query_rope, "query_rope")) != SFAG_OK) return st;
+    if ((st = check_ptr(key_rope, "key_rope")) != SFAG_OK) return st;
+  }
   Plan p;
   st = make_plan(dims, seq_len_q_host, seq_len_kv_host, scale_value, sparse_block_size, layout, sparse_mode, 0,
                  false, &p);

@@ -50,8 +50,8 @@ __device__ __forceinline__ void load_q_tile(uint16_t* Qs, const uint16_t* q, con
     uint4 v = make_uint4(0, 0, 0, 0);
     if (h < nh) {
       const int64_t hh = row * N1 + h0 + h;
-      v = part < 64 ? *reinterpret_cast<const uint4*>(q + hh * kDn + part * 8)
-                    : *reinterpret_cast<const uint4*>(qr + hh * kDr + (part - 64) * 8);
+      if (part < 64) v = *reinterpret_cast<const uint4*>(q + hh * kDn + part * 8);
+      else if (qr) v = *reinterpret_cast<const uint4*>(qr + hh * kDr + (part - 64) * 8);
     }
     *reinterpret_cast<uint4*>(Qs + swz(h, part * 8, kQChunks)) = v;
   }
@@ -64,9 +64,10 @@ __device__ __forceinline__ void gather_k_tile(uint16_t* Ks, const uint16_t* k, c
     const int key = c / kQChunks, part = c % kQChunks;
     const int64_t kr_ = keyrow[key];
     uint4 v = make_uint4(0, 0, 0, 0);
-    if (kr_ >= 0)
-      v = part < 64 ? *reinterpret_cast<const uint4*>(k + kr_ * kDn + part * 8)
-                    : *reinterpret_cast<const uint4*>(kr + kr_ * kDr + (part - 64) * 8);
+    if (kr_ >= 0) {
+      if (part < 64) v = *reinterpret_cast<const uint4*>(k + kr_ * kDn + part * 8);
+      else if (kr) v = *reinterpret_cast<const uint4*>(kr + kr_ * kDr + (part - 64) * 8);
+    }
     *reinterpret_cast<uint4*>(Ks + swz(key, part * 8, kQChunks)) = v;
   }
 }
@@ -103,7 +104,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_main_kernel(BwdArgs a) {
     for (int e = threadIdx.x; e < nh * kDn; e += kThreads)
       a.dq[(row * a.N1 + h0) * kDn + e] = 0;
     for (int e = threadIdx.x; e < nh * kDr; e += kThreads)
-      a.dqr[(row * a.N1 + h0) * kDr + e] = 0;
+      if (a.dqr) a.dqr[(row * a.N1 + h0) * kDr + e] = 0;
     return;
   }
 
@@ -347,7 +348,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_main_kernel(BwdArgs a) {
         const uint16_t bv = f2bf(dqacc[ft][v] * a.scale);
         const int64_t hh = row * a.N1 + h0 + h;
         if (col < kDn) a.dq[hh * kDn + col] = bv;
-        else a.dqr[hh * kDr + col - kDn] = bv;
+        else if (a.dqr) a.dqr[hh * kDr + col - kDn] = bv;
       }
     }
   }
@@ -373,7 +374,9 @@ __global__ void cast_kernel(const float* acc, uint16_t* dk, uint16_t* dkr, uint1
     const float4 x = *reinterpret_cast<const float4*>(acc + r * kDacc + col);
     const uint2 w = make_uint2(f2bf(x.x) | ((uint32_t)f2bf(x.y) << 16), f2bf(x.z) | ((uint32_t)f2bf(x.w) << 16));
     if (col < kDn) *reinterpret_cast<uint2*>(dk + r * kDn + col) = w;
-    else if (col < kDk) *reinterpret_cast<uint2*>(dkr + r * kDr + col - kDn) = w;
+    else if (col < kDk) {
+      if (dkr) *reinterpret_cast<uint2*>(dkr + r * kDr + col - kDn) = w;
+    }
     else *reinterpret_cast<uint2*>(dv + r * kDn + col - kDk) = w;
   }
 }

@@ -522,7 +522,9 @@ __global__ void __launch_bounds__(kThreads) kv_reduce_kernel(DenseArgs a) {
         }
     const uint16_t v = f2bf(s);
     if (col < kDn) a.dk[krow * kDn + col] = v;
-    else if (col < kDk) a.dkr[krow * kDr + col - kDn] = v;
+    else if (col < kDk) {
+      if (a.dkr) a.dkr[krow * kDr + col - kDn] = v;
+    }
     else a.dv[krow * kDn + col - kDk] = v;
   }
 }

@@ -62,7 +62,7 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
     if (h < nh) {
       const int64_t hh = row * a.N1 + h0 + h;
       v = part < 64 ? *reinterpret_cast<const uint4*>(a.q + hh * kDn + part * 8)
-                    : *reinterpret_cast<const uint4*>(a.qr + hh * kDr + (part - 64) * 8);
+                    : (a.qr ? *reinterpret_cast<const uint4*>(a.qr + hh * kDr + (part - 64) * 8) : uint4{0, 0, 0, 0});
     }
     *reinterpret_cast<uint4*>(Qs + swz(h, part * 8, kQChunks)) = v;
   }
@@ -95,7 +95,7 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
       uint4 v = make_uint4(0, 0, 0, 0);
       if (kr_ >= 0)
         v = part < 64 ? *reinterpret_cast<const uint4*>(a.k + kr_ * kDn + part * 8)
-                      : *reinterpret_cast<const uint4*>(a.kr + kr_ * kDr + (part - 64) * 8);
+                      : (a.kr ? *reinterpret_cast<const uint4*>(a.kr + kr_ * kDr + (part - 64) * 8) : uint4{0, 0, 0, 0});
       *reinterpret_cast<uint4*>(Ks + swz(key, part * 8, kQChunks)) = v;
     }
     __syncthreads();

@@ -74,7 +74,8 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
   const int count = a.count[row];
   if (!geo.active || geo.hi < 0 || count == 0) {
     for (int e = threadIdx.x; e < nh * kDn; e += kThreads) a.dq[(row * a.N1 + h0) * kDn + e] = 0;
-    for (int e = threadIdx.x; e < nh * kDr; e += kThreads) a.dqr[(row * a.N1 + h0) * kDr + e] = 0;
+    if (a.dqr)
+      for (int e = threadIdx.x; e < nh * kDr; e += kThreads) a.dqr[(row * a.N1 + h0) * kDr + e] = 0;
     return;
   }
   const int32_t* srow = a.sorted + row * a.topk;
@@ -135,8 +136,8 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
     }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const bf16x8 rv = *reinterpret_cast<const bf16x8*>(a.qr + hrow * kDr + 32 * ks + 8 * g);
-      qA[16 + ks] = hv ? rv : bf16x8{};
+      qA[16 + ks] = bf16x8{};
+      if (hv && a.qr) qA[16 + ks] = *reinterpret_cast<const bf16x8*>(a.qr + hrow * kDr + 32 * ks + 8 * g);
     }
   }
   __syncthreads();
@@ -151,7 +152,8 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
     return reinterpret_cast<uint16_t*>(((uint64_t)hi << 32) | lo);
   };
   const uint16_t* kbase = uniform(a.k + geo.kstart * kDn);
-  const uint16_t* krbase = uniform(a.kr + geo.kstart * kDr);
+  const bool rope = a.kr != nullptr;                // without rope inputs the rope terms are absent
+  const uint16_t* krbase = uniform(rope ? a.kr + geo.kstart * kDr : a.zero_row);
   const uint16_t* zrow = uniform(a.zero_row);
   // The record pointers lose their address space through the scalar round trip; stores through
   // them are made global explicitly, because a generic (flat) store might hit LDS and would then
@@ -169,7 +171,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
   {                                                                                            \
     const bool ok_ = (CH) * kKC + gkey < count;                                                \
     const uint16_t* pk_ = ok_ ? kbase + (int64_t)(SV) * kDn : zrow;                            \
-    const uint16_t* pr_ = ok_ ? krbase + (int64_t)(SV) * kDr : zrow;                           \
+    const uint16_t* pr_ = ok_ && rope ? krbase + (int64_t)(SV) * kDr : zrow;                   \
     _Pragma("unroll") for (int j = 0; j < kBlocks / 4; ++j) {                                  \
       const int blk = wave + 4 * j;                                                            \
       const uint16_t* src = j < kBlocks / 4 - 1 ? pk_ + (2 * blk + gcol) * 8                   \
@@ -367,7 +369,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
         const int col = 144 * wave + 16 * nt + c;
         const uint16_t bv = f2bf(dqacc[t][nt][v] * a.scale);
         if (col < kDn) a.dq[hh2 * kDn + col] = bv;
-        else a.dqr[hh2 * kDr + col - kDn] = bv;
+        else if (a.dqr) a.dqr[hh2 * kDr + col - kDn] = bv;
       }
     }
   }

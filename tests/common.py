@@ -33,10 +33,13 @@ def from_dev(t) -> np.ndarray:
 class Case:
     """A generated problem plus its oracle forward (op-mode inputs for the backward)."""
 
-    def __init__(self, p: inputs.Problem, fwd_rows=None):
+    def __init__(self, p: inputs.Problem, fwd_rows=None, rope=True):
         self.p = p
+        self.rope = rope                 # False: the call passes no rope inputs (no rope terms)
         self.g = oracle.Geometry.of(p)
         self.q, self.k, self.qr, self.kr = f64(p.q), f64(p.k), f64(p.qr), f64(p.kr)
+        if not rope:
+            self.qr, self.kr = np.zeros_like(self.qr), np.zeros_like(self.kr)
         self.v = f64(p.v)
         self.dout = f64(p.dout)
         self.idx = p.idx
@@ -64,7 +67,8 @@ class Case:
         p = self.p
         return dict(query=to_dev(p.q), key=to_dev(p.k), value=to_dev(p.v), sparse_indices=to_dev(p.idx, "raw"),
                     d_out=to_dev(p.dout), out=to_dev(self.out_bits), softmax_max=to_dev(self.m32, "raw"),
-                    softmax_sum=to_dev(self.l32, "raw"), query_rope=to_dev(p.qr), key_rope=to_dev(p.kr))
+                    softmax_sum=to_dev(self.l32, "raw"), query_rope=to_dev(p.qr) if self.rope else None,
+                    key_rope=to_dev(p.kr) if self.rope else None)
 
     def run_gpu(self, deterministic=False, dev=None):
         import sparse_mla_flash_amd as sf

@@ -122,8 +122,9 @@ def test_grad_null_pointers(name):
 def test_grad_misaligned_and_rope_and_workspace():
     d = dims()
     assert grad_call(d, query=FAKE + 2) == sf.SFAG_ERR_PARAM_INVALID
-    assert grad_call(d, query_rope=None) == sf.SFAG_ERR_UNSUPPORTED
-    assert grad_call(d, d_key_rope=None) == sf.SFAG_ERR_UNSUPPORTED
+    # rope inputs: both or neither; with them both rope gradients are required
+    assert grad_call(d, query_rope=None) == sf.SFAG_ERR_PARAM_NULLPTR
+    assert grad_call(d, d_key_rope=None) == sf.SFAG_ERR_PARAM_NULLPTR
     need = ws(d)
     assert grad_call(d, workspace_size=need - 1) == sf.SFAG_ERR_WORKSPACE
     assert grad_call(d, workspace=None, workspace_size=need) == sf.SFAG_ERR_WORKSPACE
@@ -139,7 +140,7 @@ def test_forward_validation():
                 sparse_mode=3, pre_tokens=0, next_tokens=0, out=FAKE, softmax_max=FAKE, softmax_sum=FAKE,
                 stream=None)
     assert f(**{**base, "out": None}) == sf.SFAG_ERR_PARAM_NULLPTR
-    assert f(**{**base, "key_rope": None}) == sf.SFAG_ERR_UNSUPPORTED
+    assert f(**{**base, "key_rope": None}) == sf.SFAG_ERR_PARAM_NULLPTR
     assert f(**{**base, "sparse_mode": 2}) == sf.SFAG_ERR_PARAM_INVALID
     assert f(**{**base, "dims": dims(D=256)}) == sf.SFAG_ERR_PARAM_INVALID
 

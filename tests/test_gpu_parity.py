@@ -170,6 +170,33 @@ def test_block_selection_forward_matches_oracle(name):
     assert np.abs(l - case.l64).max() <= 1e-4 * max(1.0, np.abs(case.l64).max())
 
 
+@pytest.mark.parametrize("name", ["bsnd_n64_short_prefix", "tnd_n16_varlen_empty_seq"])
+def test_ropeless_matches_oracle(name, path):
+    """No rope inputs (queryRopeOptional / keyRopeOptional absent): the oracle with zero rope
+    tensors is the reference; no rope gradients are returned."""
+    import sparse_mla_flash_amd as sf
+    case = Case(make(name), rope=False)
+    p = case.p
+    d = case.device_inputs()
+    for det in (False, True):
+        dq, dk, dv, dqr, dkr = sf.sparse_flash_attention_grad(
+            d["query"], d["key"], d["value"], d["sparse_indices"], d["d_out"], d["out"], d["softmax_max"],
+            d["softmax_sum"], p.seq_q, p.seq_kv, None, None, scale_value=p.scale, layout=p.layout,
+            sparse_mode=p.sparse_mode, deterministic=det)
+        assert dqr is None and dkr is None
+        rdq, _ = case.ref_dq()
+        rdk, _, rdv = case.ref_dkv()
+        compare(f"{name}/ropeless/{path}/dq", from_dev(dq), rdq)
+        compare(f"{name}/ropeless/{path}/dk", from_dev(dk), rdk)
+        compare(f"{name}/ropeless/{path}/dv", from_dev(dv), rdv)
+    out, smax, ssum = sf.sparse_flash_attention_forward(
+        d["query"], d["key"], d["value"], d["sparse_indices"], p.seq_q, p.seq_kv, None, None,
+        scale_value=p.scale, layout=p.layout, sparse_mode=p.sparse_mode)
+    compare(name + "/ropeless/out", from_dev(out), case.out64)
+    m = from_dev(smax)
+    assert np.abs(m - case.m64).max() <= 1e-4 * max(1.0, np.abs(case.m64).max())
+
+
 def test_heavy_duplicates(path):
     """Rows repeating a few keys many times: more than 256 positions fall in one 256-key block
     and keys repeat dozens of times; every repeat contributes separately."""
