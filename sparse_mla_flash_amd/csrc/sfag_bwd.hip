@@ -166,12 +166,10 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_main_kernel(BwdArgs a) {
 #pragma unroll
       for (int ks = 0; ks < 16; ++ks) doA[ks] = lds_read8(Ks, hr, 32 * ks + 8 * g, kQChunks);
     }
-    if constexpr (kMode != 2) {
 #pragma unroll
-      for (int ft = 0; ft < 8; ++ft) {
-        const bf16x8 f = lds_frag_tr(Ks, 0, 16 * (8 * wave + ft), kQChunks, lane);
-        if (half == 0) doB[ft][0] = f; else doB[ft][1] = f;
-      }
+    for (int ft = 0; ft < 8; ++ft) {
+      const bf16x8 f = lds_frag_tr(Ks, 0, 16 * (8 * wave + ft), kQChunks, lane);
+      if (half == 0) doB[ft][0] = f; else doB[ft][1] = f;
     }
   }
   __syncthreads();
@@ -191,9 +189,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_main_kernel(BwdArgs a) {
 
   const int32_t* idxrow = a.idx + row * (a.topk / a.bs);
   const int64_t pair_base = (row - a.row_begin) * a.topk;
-  // key-major mode walks the row's valid key positions in ascending order (sorted beforehand)
-  const int nslots = kMode == 2 ? a.count[row] : a.topk;
-  const int32_t* srow = kMode == 2 ? a.sorted + row * a.topk : idxrow;
+  const int nslots = a.topk;
 
   for (int c0 = 0; c0 < nslots; c0 += kKC) {
     // ---- indices and validity --------------------------------------------------------
@@ -202,7 +198,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_main_kernel(BwdArgs a) {
       const int s = c0 + threadIdx.x;
       int64_t kr_ = -1;
       if (s < nslots) {
-        const int j = kMode == 2 ? srow[s] : slot_key(idxrow, s, a.bs);
+        const int j = slot_key(idxrow, s, a.bs);
         if (j >= 0 && j <= geo.hi) kr_ = geo.kstart + j;
       }
       keyrow[threadIdx.x] = kr_;
@@ -244,28 +240,14 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_main_kernel(BwdArgs a) {
         const uint2 dw = make_uint2(db[0] | ((uint32_t)db[1] << 16), db[2] | ((uint32_t)db[3] << 16));
         *reinterpret_cast<uint2*>(PSt + swz(key, hcol, kHtChunks)) = pw;
         *reinterpret_cast<uint2*>(DSt + swz(key, hcol, kHtChunks)) = dw;
-        if constexpr (kMode == 2) {
-          if (valid) {
-            uint16_t* rec = a.dsp + (((int64_t)row * a.topk + c0 + key) * a.hgc + hg) * 128;
-            *reinterpret_cast<uint2*>(rec + hcol) = dw;
-            *reinterpret_cast<uint2*>(rec + 64 + hcol) = pw;
-          }
-        }
       }
-    } else if (kMode == 2 || 16 * wave < 32 * kst) {
+    } else if (16 * wave < 32 * kst) {
       // zero-pad head columns that the 32-deep dK / dV contractions read
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
         const int key = 16 * kt + c, hcol = 16 * wave + 4 * g;
         *reinterpret_cast<uint2*>(PSt + swz(key, hcol, kHtChunks)) = make_uint2(0, 0);
         *reinterpret_cast<uint2*>(DSt + swz(key, hcol, kHtChunks)) = make_uint2(0, 0);
-        if constexpr (kMode == 2) {
-          if (keyrow[key] >= 0) {
-            uint16_t* rec = a.dsp + (((int64_t)row * a.topk + c0 + key) * a.hgc + hg) * 128;
-            *reinterpret_cast<uint2*>(rec + hcol) = make_uint2(0, 0);
-            *reinterpret_cast<uint2*>(rec + 64 + hcol) = make_uint2(0, 0);
-          }
-        }
       }
     }
     __syncthreads();
@@ -282,7 +264,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_main_kernel(BwdArgs a) {
 
     // ---- dK = scale dS^T Q, dV = P^T dO for this chunk ----------------------------------------
 #pragma unroll
-    for (int kt = 0; kt < (kMode == 2 ? 0 : 2); ++kt) {
+    for (int kt = 0; kt < 2; ++kt) {
       bf16x8 sa[2], pa[2];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
@@ -441,8 +423,6 @@ hipError_t launch_bwd_main(const BwdArgs& a, int64_t nrows, int hg_count, int mo
   dim3 grid((unsigned)nrows, (unsigned)hg_count);
   if (mode == 1)
     hipLaunchKernelGGL(bwd_main_kernel<1>, grid, dim3(kThreads), kLdsBwd, st, a);
-  else if (mode == 2)
-    hipLaunchKernelGGL(bwd_main_kernel<2>, grid, dim3(kThreads), kLdsBwd, st, a);
   else
     hipLaunchKernelGGL(bwd_main_kernel<0>, grid, dim3(kThreads), kLdsBwd, st, a);
   return hipGetLastError();
@@ -451,9 +431,6 @@ hipError_t launch_bwd_main(const BwdArgs& a, int64_t nrows, int hg_count, int mo
 hipError_t set_bwd_attributes() {
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_main_kernel<0>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBwd);
-  if (e != hipSuccess) return e;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_main_kernel<2>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBwd);
   if (e != hipSuccess) return e;
   return hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_main_kernel<1>),
                              hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBwd);

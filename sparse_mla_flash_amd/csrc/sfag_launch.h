@@ -96,7 +96,7 @@ __host__ __device__ inline int64_t stat_index(int tnd, const Geo& g, int64_t row
   return tnd ? (int64_t)h * S1 + row : ((int64_t)g.b * N1 + h) * S1 + g.i;
 }
 
-// mode 0: fp32 atomic dK/dV, 1: per-pair partials, 2: dS / P pair records for the key-major kernels
+// mode 0: fp32 atomic dK/dV, 1: per-pair partials (deterministic mode)
 hipError_t launch_bwd_main(const BwdArgs& a, int64_t nrows, int hg_count, int mode, hipStream_t st);
 hipError_t launch_fwd(const FwdArgs& a, int64_t nrows, int hg_count, hipStream_t st);
 hipError_t launch_fill_zero(float* p, int64_t nfloats, hipStream_t st);
