@@ -42,6 +42,39 @@ def test_uniform_indices_are_distinct_valid_and_padded(mode):
     assert (idx[p.q_offset(1) + 33:] == -1).all()
 
 
+@pytest.mark.parametrize("mode", [0, 3])
+def test_block_indices_are_distinct_reachable_blocks(mode):
+    """Block selection: distinct block indices, each holding at least one reachable key; rows
+    whose range spans at most topk blocks take all of them."""
+    p = inputs.problem("BSND", B=2, S1=30, S2=70, N1=2, topk=6, sparse_mode=mode, seq_q=[30, 25],
+                       seq_kv=[70, 33], block=8)
+    inputs.generate(p, 5)
+    idx = p.idx.reshape(p.rows, p.topk)
+    for g, b, i in _rows(p):
+        hi = min(i + p.lkv(b) - p.lq(b), p.lkv(b) - 1) if mode == 3 else p.lkv(b) - 1
+        row = idx[g]
+        valid = row[row >= 0]
+        assert len(set(valid.tolist())) == len(valid)
+        assert (valid * p.block <= hi).all()
+        assert len(valid) == min(p.topk, max(hi // p.block + 1, 0) if hi >= 0 else 0)
+
+
+def test_bench_valid_pair_count_with_blocks():
+    """bench.py's valid-pair bookkeeping (the flop count of the metric) against a per-key
+    brute-force count, with blocks cut by the key length and the causal bound."""
+    import bench
+    p = inputs.problem("BSND", B=2, S1=12, S2=30, N1=1, topk=5, sparse_mode=3, seq_q=[12, 9],
+                       seq_kv=[30, 17], block=4)
+    inputs.generate(p, 9)
+    p.idx.reshape(p.rows, p.topk)[0, 0] = -1                  # a skipped block
+    got = bench.valid_per_row(p)
+    idx = p.idx.reshape(p.rows, p.topk)
+    for g, b, i in _rows(p):
+        hi = min(i + p.lkv(b) - p.lq(b), p.lkv(b) - 1)
+        keys = [j * p.block + r for j in idx[g] if j >= 0 for r in range(p.block)]
+        assert got[g] == sum(1 for k in keys if 0 <= k <= hi)
+
+
 def test_window_indices_half_local():
     p = inputs.problem("BSND", B=1, S1=64, S2=4096, N1=1, topk=64, sparse_mode=3)
     inputs.generate(p, 4, index_kind="window", window=256)
