@@ -23,6 +23,14 @@ softmaxSum come from the library's sparse forward (timing inputs only).
 
   python bench.py [--steps K] [--warmup W] [--workload N] [--deterministic]
   python bench.py --copy-calibration     # plain 1 GiB device copies, for counter scaling
+  python bench.py --ceilings             # measured MFMA rate / shader clock, HBM copy, LDS and
+                                         # atomic rates (sparse_mla_flash_amd/microbench)
+
+Timing: `ms_per_step` is the wall-clock mean over the K timed steps (bracketed by device
+synchronisation); `call_ms` gives the median, min and max of the same K calls measured one by
+one with HIP events on the library's stream.  Per-kernel `hbm_gbs` divide the committed
+rocprofv3 FETCH_SIZE + WRITE_SIZE bytes of that kernel (scaled by the same counters on a plain
+copy) by its event-timed duration, and are null once the kernel sources change.
 """
 
 from __future__ import annotations
@@ -99,6 +107,10 @@ class HipEvents:
     def destroy(self, e):
         self.hip.hipEventDestroy(e)
 
+    def record(self, e, stream):
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        assert self.hip.hipEventRecord(e, stream) == 0
+
 
 def copy_calibration():
     import torch
@@ -145,16 +157,126 @@ def cpu_baseline(p, nrows: int, per_row):
                       f"untimed; {dt:.2f} s wall"}
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _ceilings_lib():
+    path = os.path.join(ROOT, "sparse_mla_flash_amd", "microbench", "libceilings.so")
+    if not os.path.exists(path):
+        return None
+    L = ctypes.CDLL(path)
+    vp = ctypes.c_void_p
+    L.ceil_device_info.argtypes = [ctypes.c_char_p, ctypes.c_int, ctypes.POINTER(ctypes.c_int),
+                                   ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)]
+    L.ceil_mfma.restype = ctypes.c_float
+    L.ceil_mfma.argtypes = [vp, ctypes.c_int, ctypes.c_int, vp, vp]
+    L.ceil_copy.restype = ctypes.c_float
+    L.ceil_copy.argtypes = [vp, vp, ctypes.c_size_t, ctypes.c_int, vp]
+    L.ceil_lds.restype = ctypes.c_float
+    L.ceil_lds.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp]
+    L.ceil_atomic.restype = ctypes.c_float
+    L.ceil_atomic.argtypes = [vp, vp, ctypes.c_int, ctypes.c_int, vp]
+    return L
+
+
+def device_info():
+    """Name, compute-unit count and peak shader / memory clocks from hipGetDeviceProperties."""
+    L = _ceilings_lib()
+    if L is None:
+        return None
+    name = ctypes.create_string_buffer(256)
+    cus, clk, mclk = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    if L.ceil_device_info(name, 256, ctypes.byref(cus), ctypes.byref(clk), ctypes.byref(mclk)) != 0:
+        return None
+    return {"name": name.value.decode(), "compute_units": cus.value, "peak_sclk_mhz": clk.value / 1000.0,
+            "mem_clk_mhz": mclk.value / 1000.0}
+
+
+def ceilings():
+    """Measured ceilings: the bf16 MFMA rate with every CU busy and the shader clock it runs at,
+    HBM copy bandwidth, LDS instruction rates (bytes per clock per CU at that clock) and the
+    fp32 global atomic-add rate on random 4352-byte rows."""
+    import torch
+    L = _ceilings_lib()
+    if L is None:
+        raise SystemExit("libceilings.so is missing: run python -m sparse_mla_flash_amd.build")
+    dev = device_info()
+    cus = dev["compute_units"]
+    stream = torch.cuda.current_stream().cuda_stream
+    out = torch.zeros(1 << 16, dtype=torch.float32, device="cuda")
+    clk = torch.zeros(2, dtype=torch.int64, device="cuda")
+    res = {"device": dev}
+    # MFMA: 4 waves per SIMD, 8 independent 16x16x32 bf16 chains per wave
+    blocks, iters = cus * 4, 20000
+    best = None
+    for _ in range(3):
+        ms = L.ceil_mfma(out.data_ptr(), blocks, iters, clk.data_ptr(), stream)
+        torch.cuda.synchronize()
+        ticks, cyc = (int(x) for x in clk.tolist())
+        if ms > 0 and (best is None or ms < best[0]):
+            best = (ms, ticks, cyc)
+    flop = blocks * 4 * iters * 8 * (16 * 16 * 32 * 2)
+    ms, ticks, cyc = best
+    sclk = cyc / ticks * 100.0 if ticks > 0 else None          # s_memrealtime runs at 100 MHz
+    res["mfma_bf16"] = {"tflops": round(flop / (ms * 1e-3) / 1e12, 1), "ms": round(ms, 4),
+                        "sclk_mhz_under_load": None if sclk is None else round(sclk, 1),
+                        "flop_per_clk_per_cu": None if sclk is None else
+                        round(flop / (ms * 1e-3) / (sclk * 1e6) / cus, 1)}
+    # HBM copy, 2 GiB each way
+    n = 2 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    times = [L.ceil_copy(a.data_ptr(), b.data_ptr(), n, cus * 16, stream) for _ in range(5)]
+    torch.cuda.synchronize()
+    t = min(x for x in times if x > 0)
+    res["hbm_copy"] = {"gbs": round(2 * n / (t * 1e-3) / 1e9, 1), "bytes_each_way": n, "ms": round(t, 4)}
+    del a, b
+    # LDS rates at the shader clock measured above
+    names = {0: "ds_add_f32", 1: "ds_write_b32", 2: "ds_read_b32", 3: "ds_write_b128", 4: "ds_read_b128"}
+    width = {0: 4, 1: 4, 2: 4, 3: 16, 4: 16}
+    lds = {}
+    lblocks, liters = cus * 2, 4000
+    for mode in range(5):
+        t = min(L.ceil_lds(mode, lblocks, liters, out.data_ptr(), stream) for _ in range(3))
+        torch.cuda.synchronize()
+        nbytes = lblocks * 256 * liters * 16 * width[mode]
+        lds[names[mode]] = {"bytes_per_clk_per_cu": None if sclk is None else
+                            round(nbytes / (t * 1e-3) / (sclk * 1e6) / cus, 1),
+                            "tb_per_s": round(nbytes / (t * 1e-3) / 1e12, 2)}
+    res["lds"] = lds
+    # fp32 atomics: 65536 workgroups, each adding into one random row of 1088 floats, 4 times
+    g = torch.Generator(device="cpu").manual_seed(7)
+    for rows_total, label in ((131072, "rows_131072"), (8192, "rows_8192")):
+        acc = torch.zeros(rows_total * 1088, dtype=torch.float32, device="cuda")
+        rows = torch.randint(0, rows_total, (65536,), generator=g, dtype=torch.int32).cuda()
+        t = min(L.ceil_atomic(acc.data_ptr(), rows.data_ptr(), 65536, 4, stream) for _ in range(3))
+        torch.cuda.synchronize()
+        ops = 65536 * 1088 * 4
+        res["atomic_add_f32_" + label] = {"g_ops_per_s": round(ops / (t * 1e-3) / 1e9, 1), "ms": round(t, 3)}
+        del acc, rows
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--deterministic", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=768)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--ceilings", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the kernel is measured on a single "
@@ -162,6 +284,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.ceilings:
+        ceilings()
         return
 
     import numpy as np
@@ -208,18 +333,21 @@ def main():
     print("# warmup done", file=sys.stderr, flush=True)
 
     ev = HipEvents()
-    evs = [[ev.create() for _ in range(4)] for _ in range(args.steps)]
+    evs = [[ev.create() for _ in range(6)] for _ in range(args.steps)]   # call begin / end + 4 stage events
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        sf.sfag_set_profile_events(*evs[i])
+        sf.sfag_set_profile_events(*evs[i][2:6])
+        ev.record(evs[i][0], stream)
         step()
+        ev.record(evs[i][1], stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     sf.sfag_set_profile_events()
     path = "key-major" if sf.sfag_last_path() == 0 else "scatter"
-    s1 = sum(ev.elapsed_ms(e[0], e[1]) for e in evs) / args.steps
-    s2 = sum(ev.elapsed_ms(e[2], e[3]) for e in evs) / args.steps if path == "key-major" else 0.0
+    calls = sorted(ev.elapsed_ms(e[0], e[1]) for e in evs)
+    s1 = sum(ev.elapsed_ms(e[2], e[3]) for e in evs) / args.steps
+    s2 = sum(ev.elapsed_ms(e[4], e[5]) for e in evs) / args.steps if path == "key-major" else 0.0
     for e in evs:
         for x in e:
             ev.destroy(x)
@@ -238,12 +366,20 @@ def main():
     kernel = max(stages, key=lambda n: stages[n][0])
     kern_avg, kflop = stages[kernel]
     achieved = npairs * p.N1 * kflop / (kern_avg * 1e-3) / 1e12
-    # logical gather rate (one bf16 key row per valid pair, read by the kernel that forms the
-    # scores) and scatter rate (one fp32 dK | dKRope | dV row per valid pair)
-    gather_ms = s1
-    scatter_ms = s2 if path == "key-major" else s1
-    gather_gbs = npairs * GATHER_BYTES_PER_PAIR / (gather_ms * 1e-3) / 1e9
-    scatter_gbs = npairs * SCATTER_BYTES_PER_PAIR / (scatter_ms * 1e-3) / 1e9
+    stage_rec = {}
+    for n, (ms, fl) in stages.items():
+        tr = traffic_from_profile(n.split("<")[0].split(" ")[0], p.name)
+        stage_rec[n] = {
+            "ms": round(ms, 4),
+            "tflops": round(npairs * p.N1 * fl / (ms * 1e-3) / 1e12, 2),
+            "mfma_frac": round(npairs * p.N1 * fl / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            # HBM bytes moved by this kernel (rocprofv3 counters, copy-calibrated) over its time
+            "hbm_gbs": None if tr is None else round(tr / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac": None if tr is None else round(tr / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        }
+    # logical gather rate: one bf16 key row per valid pair, mostly served by L2 / MALL, so this
+    # is an on-chip rate, not an HBM one
+    gather_gbs = npairs * GATHER_BYTES_PER_PAIR / (s1 * 1e-3) / 1e9
     rec = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -263,25 +399,27 @@ def main():
             "valid_pairs": npairs, "nominal_pairs": nominal,
             "effective_tflops_nominal": round(nominal * p.N1 * FLOP_PER_PAIR_HEAD / (ms_per_step * 1e-3) / 1e12, 3),
         },
+        "call_ms": {"median": round(calls[len(calls) // 2], 4), "min": round(calls[0], 4),
+                    "max": round(calls[-1], 4), "n": len(calls),
+                    "effective_tflops_median": round(flops / (calls[len(calls) // 2] * 1e-3) / 1e12, 3)},
         "roofline": {
             "bound": "mfma", "achieved": round(achieved, 3), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 5),
-            "traffic": traffic_from_profile(kernel.split("<")[0], p.name),
+            "traffic": traffic_from_profile(kernel.split("<")[0].split(" ")[0], p.name),
             "kernel": kernel,
             "kernel_ms": round(kern_avg, 4),
             "kernel_flop_per_pair_head": kflop,
             "path": path,
-            "stages_ms": {n: round(v[0], 4) for n, v in stages.items()},
-            "stages_tflops": {n: round(npairs * p.N1 * v[1] / (v[0] * 1e-3) / 1e12, 2) for n, v in stages.items()},
+            "stages": stage_rec,
             "gather_logical_gbs": round(gather_gbs, 1),
-            "gather_hbm_frac": round(gather_gbs / HBM_PEAK_GBS, 4),
-            "scatter_logical_gbs": round(scatter_gbs, 1),
-            "scatter_hbm_frac": round(scatter_gbs / HBM_PEAK_GBS, 4),
         },
+        "device": device_info(),
+        "host_cpu": cpu_model(),
     }
     if not args.no_cpu_baseline:
         print("# cpu baseline ...", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(p, min(args.cpu_rows, p.rows), per_row)
+        rec["cpu_baseline"]["cpu_model"] = cpu_model()
     print(json.dumps(rec), flush=True)
 
 

@@ -161,7 +161,7 @@ def sfag_sparse_flash_attention_forward(query, key, value, sparse_indices, seq_l
 # tensor-level wrappers (torch for device memory and streams only)
 # ---------------------------------------------------------------------------------------------
 
-def _dims_from(query, key, sparse_indices, layout: str, seq_len_q, seq_len_kv) -> Dims:
+def _dims_from(query, key, sparse_indices, layout: str, seq_len_q, seq_len_kv, query_rope=None) -> Dims:
     if layout == "BSND":
         if query.dim() != 4 or key.dim() != 4 or sparse_indices.dim() != 4:
             raise ValueError("BSND expects query [B,S1,N1,D], key [B,S2,1,D], sparse_indices [B,S1,1,topk]")
@@ -179,7 +179,31 @@ def _dims_from(query, key, sparse_indices, layout: str, seq_len_q, seq_len_kv) -
         topk = sparse_indices.shape[-1]
     else:
         raise ValueError(f"layout must be BSND or TND, got {layout!r}")
+    # the rope width is fixed at 64 by the operator; rope tensors are checked against it
     return Dims(int(B), int(S1), int(S2), int(N1), int(N2), int(D), 64, int(topk))
+
+
+def _check_shapes(dims: Dims, layout: str, **tensors) -> None:
+    """Every tensor's shape against the dims taken from query / key / sparse_indices, so that a
+    mis-shaped tensor is rejected here instead of being read out of bounds by a kernel."""
+    B, S1, S2, N1, N2, D, Dr, topk = (dims.B, dims.S1, dims.S2, dims.N1, dims.N2, dims.D, dims.Drope,
+                                      dims.topk)
+    if layout == "BSND":
+        want = dict(query=(B, S1, N1, D), key=(B, S2, N2, D), value=(B, S2, N2, D),
+                    sparse_indices=(B, S1, N2, topk), d_out=(B, S1, N1, D), out=(B, S1, N1, D),
+                    softmax_max=(B, N1, S1), softmax_sum=(B, N1, S1), query_rope=(B, S1, N1, Dr),
+                    key_rope=(B, S2, N2, Dr))
+    else:
+        want = dict(query=(S1, N1, D), key=(S2, N2, D), value=(S2, N2, D), sparse_indices=(S1, N2, topk),
+                    d_out=(S1, N1, D), out=(S1, N1, D), softmax_max=(N1, S1), softmax_sum=(N1, S1),
+                    query_rope=(S1, N1, Dr), key_rope=(S2, N2, Dr))
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if tuple(t.shape) != want[name]:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {want[name]} for layout {layout}")
+    if (tensors.get("query_rope") is None) != (tensors.get("key_rope") is None):
+        raise ValueError("query_rope and key_rope must be given together or both omitted")
 
 
 def _dev(t, name, dtype):
@@ -215,7 +239,10 @@ def sparse_flash_attention_grad(query, key, value, sparse_indices, d_out, out, s
     import torch
     bf = torch.bfloat16
     sq, skv = _seq(actual_seq_lengths_query), _seq(actual_seq_lengths_kv)
-    dims = _dims_from(query, key, sparse_indices, layout, sq, skv)
+    dims = _dims_from(query, key, sparse_indices, layout, sq, skv, query_rope)
+    _check_shapes(dims, layout, query=query, key=key, value=value, sparse_indices=sparse_indices, d_out=d_out,
+                  out=out, softmax_max=softmax_max, softmax_sum=softmax_sum, query_rope=query_rope,
+                  key_rope=key_rope)
     ws = sfag_get_workspace_size(dims, sq, skv, scale_value, sparse_block_size, layout, sparse_mode,
                                  pre_tokens, next_tokens, deterministic)
     dq = torch.empty_like(query)
@@ -246,7 +273,9 @@ def sparse_flash_attention_forward(query, key, value, sparse_indices, actual_seq
     import torch
     bf = torch.bfloat16
     sq, skv = _seq(actual_seq_lengths_query), _seq(actual_seq_lengths_kv)
-    dims = _dims_from(query, key, sparse_indices, layout, sq, skv)
+    dims = _dims_from(query, key, sparse_indices, layout, sq, skv, query_rope)
+    _check_shapes(dims, layout, query=query, key=key, value=value, sparse_indices=sparse_indices,
+                  query_rope=query_rope, key_rope=key_rope)
     out = torch.empty_like(query)
     if layout == "BSND":
         stat_shape = (dims.B, dims.N1, dims.S1)

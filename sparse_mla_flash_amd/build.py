@@ -18,6 +18,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsfag.so")
+CEIL_SRC = os.path.join(HERE, "microbench", "ceilings.hip")
+CEIL_LIB = os.path.join(HERE, "microbench", "libceilings.so")
 
 SOURCES = ["sfag_bwd.hip", "sfag_q.hip", "sfag_dense.hip", "sfag_fwd.hip", "sfag_sort.hip", "sfag_api.cpp"]
 
@@ -50,9 +52,21 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    build_ceilings()
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", CEIL_LIB)
     return LIB
+
+
+def build_ceilings() -> str:
+    """The stand-alone ceiling microbenchmarks (bench.py --ceilings); not part of the C ABI."""
+    tmp = CEIL_LIB + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, *COMMON, "-shared", CEIL_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for ceilings.hip:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, CEIL_LIB)
+    return CEIL_LIB
 
 
 def clean() -> None:

@@ -243,12 +243,27 @@ def _indices(p: Problem, rng: np.random.Generator, kind: str, window: int) -> np
 # generation
 # ---------------------------------------------------------------------------
 
-def _normal_bf16(rng: np.random.Generator, shape, chunk: int = 1 << 24) -> np.ndarray:
+def _normal_bf16(rng: np.random.Generator, shape, chunk: int = 1 << 22) -> np.ndarray:
+    """N(0, 1) fp32 values rounded to bf16 bits.  The tensor is cut into fixed chunks of
+    ``chunk`` elements; chunk c is drawn from its own generator, seeded by child c of a
+    SeedSequence whose entropy is one draw from ``rng``.  The values therefore depend only on
+    ``rng``'s state (not on the number of threads), and the chunks are drawn in parallel."""
+    from concurrent.futures import ThreadPoolExecutor
     n = int(np.prod(shape))
     out = np.empty(n, dtype=np.uint16)
-    for s in range(0, n, chunk):
-        e = min(n, s + chunk)
-        out[s:e] = f32_to_bf16_bits(rng.standard_normal(e - s, dtype=np.float32))
+    nchunk = (n + chunk - 1) // chunk
+    kids = np.random.SeedSequence(int(rng.integers(0, 2 ** 63 - 1, dtype=np.int64))).spawn(max(nchunk, 1))
+
+    def fill(c: int) -> None:
+        s, e = c * chunk, min(n, (c + 1) * chunk)
+        out[s:e] = f32_to_bf16_bits(np.random.default_rng(kids[c]).standard_normal(e - s, dtype=np.float32))
+
+    if nchunk <= 1:
+        for c in range(nchunk):
+            fill(c)
+    else:
+        with ThreadPoolExecutor(max_workers=min(16, nchunk)) as ex:
+            list(ex.map(fill, range(nchunk)))
     return out.reshape(shape)
 
 

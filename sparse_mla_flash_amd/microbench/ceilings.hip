@@ -1,0 +1,172 @@
+// ceilings.hip -- measured MI355X (gfx950) ceilings for the roofline figures of the
+// SparseFlashAttentionGrad kernels: bf16 MFMA rate and the shader clock under MFMA load, HBM
+// copy bandwidth, LDS instruction rates and the fp32 global atomic-add rate.  Not part of the
+// library's C ABI; bench.py --ceilings loads it and prints the results.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// 8 independent accumulation chains of v_mfma_f32_16x16x32_bf16 per wave, `iters` rounds.
+// Wave 0 of workgroup 0 records the shader-clock counter (s_memtime) and the 100 MHz constant
+// counter (s_memrealtime) around its loop, so that clk[1] / clk[0] cycles per tick give the
+// shader clock while the chip runs MFMA-bound.
+__global__ void __launch_bounds__(256) mfma_rate_kernel(float* out, int iters, unsigned long long* clk) {
+  const int lane = threadIdx.x & 63;
+  bf16x8 a, b;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    a[e] = (__bf16)(0.001f * (lane + e));
+    b[e] = (__bf16)(0.002f * (lane - e));
+  }
+  f32x4 c[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const bool timer = blockIdx.x == 0 && threadIdx.x == 0;
+  unsigned long long t0 = 0, r0 = 0;
+  if (timer) {
+    t0 = __builtin_amdgcn_s_memtime();
+    r0 = __builtin_amdgcn_s_memrealtime();
+  }
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c[i], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s += c[i][0] + c[i][1] + c[i][2] + c[i][3];
+  if (timer) {
+    // wait for the last MFMA results before reading the counters again
+    asm volatile("" ::"v"(s));
+    const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+    const unsigned long long r1 = __builtin_amdgcn_s_memrealtime();
+    clk[0] = r1 - r0;
+    clk[1] = t1 - t0;
+  }
+  if (s == 12345.f) out[blockIdx.x] = s;   // keeps the chains live; never true in practice
+}
+
+__global__ void __launch_bounds__(256) copy_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst, size_t n) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) dst[i] = src[i];
+}
+
+// LDS instruction rate.  mode 0: ds_add_f32 (result unused), 1: ds_write_b32, 2: ds_read_b32,
+// 3: ds_write_b128, 4: ds_read_b128.  Lanes of a wave address consecutive words (conflict-free);
+// each wave works on its own 16 KB region.  `iters` rounds of 16 instructions per lane.
+__global__ void __launch_bounds__(256) lds_rate_kernel(int mode, int iters, float* out) {
+  __shared__ __attribute__((aligned(16))) float buf[4 * 4096];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float* w = buf + wave * 4096;
+  for (int i = lane; i < 4096; i += 64) w[i] = 0.f;
+  __syncthreads();
+  float acc = 0.f;
+  const float v = 1.0f + lane;
+  for (int it = 0; it < iters; ++it) {
+    if (mode == 0) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) atomicAdd(&w[j * 256 + lane], v);
+    } else if (mode == 1) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) w[j * 256 + lane] = v + j;
+    } else if (mode == 2) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc += w[((j + it) & 15) * 256 + lane];
+    } else if (mode == 3) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        reinterpret_cast<float4*>(w)[(j & 3) * 256 + lane] = make_float4(v, v + j, v, v);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float4 x = reinterpret_cast<const float4*>(w)[((j + it) & 3) * 256 + lane];
+        acc += x.x + x.w;
+      }
+    }
+    asm volatile("" ::: "memory");
+  }
+  __syncthreads();
+  acc += w[lane];
+  if (acc == 12345.f) out[blockIdx.x] = acc;
+}
+
+// fp32 global atomic add (result unused): workgroup w adds 1.0 to every element of row
+// rows[w] (1088 floats) `reps` times.  Rows repeat across workgroups as the index list says.
+__global__ void __launch_bounds__(256) atomic_rate_kernel(float* acc, const int32_t* rows, int reps) {
+  float* r = acc + (int64_t)rows[blockIdx.x] * 1088;
+  for (int k = 0; k < reps; ++k)
+    for (int e = threadIdx.x; e < 1088; e += 256) atomicAdd(&r[e], 1.0f);
+}
+
+extern "C" {
+
+int ceil_device_info(char* name, int name_len, int* cus, int* clock_khz, int* mem_clock_khz) {
+  hipDeviceProp_t p;
+  if (hipGetDeviceProperties(&p, 0) != hipSuccess) return -1;
+  int i = 0;
+  for (; i < name_len - 1 && p.name[i]; ++i) name[i] = p.name[i];
+  name[i] = 0;
+  *cus = p.multiProcessorCount;
+  *clock_khz = p.clockRate;
+  *mem_clock_khz = p.memoryClockRate;
+  return 0;
+}
+
+// Each call runs one launch on `stream` and returns its elapsed ms from HIP events (-1: error).
+static float timed(hipStream_t s, void (*launch)(hipStream_t, void*), void* ctx) {
+  hipEvent_t a, b;
+  if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) return -1.f;
+  float ms = -1.f;
+  if (hipEventRecord(a, s) == hipSuccess) {
+    launch(s, ctx);
+    if (hipGetLastError() == hipSuccess && hipEventRecord(b, s) == hipSuccess && hipEventSynchronize(b) == hipSuccess &&
+        hipEventElapsedTime(&ms, a, b) != hipSuccess)
+      ms = -1.f;
+  }
+  (void)hipEventDestroy(a);
+  (void)hipEventDestroy(b);
+  return ms;
+}
+
+struct MfmaCtx { float* out; int blocks, iters; unsigned long long* clk; };
+static void mfma_launch(hipStream_t s, void* c) {
+  MfmaCtx* x = (MfmaCtx*)c;
+  hipLaunchKernelGGL(mfma_rate_kernel, dim3(x->blocks), dim3(256), 0, s, x->out, x->iters, x->clk);
+}
+float ceil_mfma(float* out, int blocks, int iters, unsigned long long* clk_dev, void* stream) {
+  MfmaCtx c{out, blocks, iters, clk_dev};
+  return timed((hipStream_t)stream, mfma_launch, &c);
+}
+
+struct CopyCtx { const void* src; void* dst; size_t n16; int blocks; };
+static void copy_launch(hipStream_t s, void* c) {
+  CopyCtx* x = (CopyCtx*)c;
+  hipLaunchKernelGGL(copy_kernel, dim3(x->blocks), dim3(256), 0, s, (const uint4*)x->src, (uint4*)x->dst, x->n16);
+}
+float ceil_copy(const void* src, void* dst, size_t bytes, int blocks, void* stream) {
+  CopyCtx c{src, dst, bytes / 16, blocks};
+  return timed((hipStream_t)stream, copy_launch, &c);
+}
+
+struct LdsCtx { int mode, iters, blocks; float* out; };
+static void lds_launch(hipStream_t s, void* c) {
+  LdsCtx* x = (LdsCtx*)c;
+  hipLaunchKernelGGL(lds_rate_kernel, dim3(x->blocks), dim3(256), 0, s, x->mode, x->iters, x->out);
+}
+float ceil_lds(int mode, int blocks, int iters, float* out, void* stream) {
+  LdsCtx c{mode, iters, blocks, out};
+  return timed((hipStream_t)stream, lds_launch, &c);
+}
+
+struct AtomCtx { float* acc; const int32_t* rows; int n, reps; };
+static void atom_launch(hipStream_t s, void* c) {
+  AtomCtx* x = (AtomCtx*)c;
+  hipLaunchKernelGGL(atomic_rate_kernel, dim3(x->n), dim3(256), 0, s, x->acc, x->rows, x->reps);
+}
+float ceil_atomic(float* acc, const int32_t* rows, int n, int reps, void* stream) {
+  AtomCtx c{acc, rows, n, reps};
+  return timed((hipStream_t)stream, atom_launch, &c);
+}
+
+}  // extern "C"

@@ -150,3 +150,55 @@ def test_error_string_clears_on_success():
     assert sf.sfag_last_error() != ""
     ws(dims())
     assert sf.sfag_last_error() == ""
+
+
+def _cpu_call_tensors(layout="BSND"):
+    """Correctly shaped CPU tensors of a tiny problem (shapes only matter here)."""
+    import torch
+    bf = torch.bfloat16
+    if layout == "BSND":
+        B, S1, S2, N1, topk = 2, 5, 7, 4, 3
+        t = dict(query=torch.zeros(B, S1, N1, 512, dtype=bf), key=torch.zeros(B, S2, 1, 512, dtype=bf),
+                 value=torch.zeros(B, S2, 1, 512, dtype=bf), sparse_indices=torch.zeros(B, S1, 1, topk, dtype=torch.int32),
+                 d_out=torch.zeros(B, S1, N1, 512, dtype=bf), out=torch.zeros(B, S1, N1, 512, dtype=bf),
+                 softmax_max=torch.zeros(B, N1, S1), softmax_sum=torch.zeros(B, N1, S1),
+                 query_rope=torch.zeros(B, S1, N1, 64, dtype=bf), key_rope=torch.zeros(B, S2, 1, 64, dtype=bf))
+        return t, None, None
+    T1, T2, N1, topk = 9, 11, 4, 3
+    t = dict(query=torch.zeros(T1, N1, 512, dtype=bf), key=torch.zeros(T2, 1, 512, dtype=bf),
+             value=torch.zeros(T2, 1, 512, dtype=bf), sparse_indices=torch.zeros(T1, 1, topk, dtype=torch.int32),
+             d_out=torch.zeros(T1, N1, 512, dtype=bf), out=torch.zeros(T1, N1, 512, dtype=bf),
+             softmax_max=torch.zeros(N1, T1), softmax_sum=torch.zeros(N1, T1),
+             query_rope=torch.zeros(T1, N1, 64, dtype=bf), key_rope=torch.zeros(T2, 1, 64, dtype=bf))
+    return t, [4, 5], [5, 6]
+
+
+@pytest.mark.parametrize("layout", ["BSND", "TND"])
+@pytest.mark.parametrize("name,cut", [("d_out", 1), ("out", 1), ("softmax_max", 0), ("softmax_sum", -1),
+                                      ("query_rope", -1), ("key_rope", 0), ("value", 0), ("key_rope", -1)])
+def test_wrapper_rejects_misshaped_tensors(layout, name, cut):
+    """The tensor wrapper checks every tensor against the shapes implied by query, key and
+    sparse_indices before anything is allocated or launched."""
+    import torch
+    t, sq, skv = _cpu_call_tensors(layout)
+    shape = list(t[name].shape)
+    shape[cut] += 1
+    t[name] = torch.zeros(shape, dtype=t[name].dtype)
+    with pytest.raises(ValueError, match=name):
+        sf.sparse_flash_attention_grad(
+            t["query"], t["key"], t["value"], t["sparse_indices"], t["d_out"], t["out"], t["softmax_max"],
+            t["softmax_sum"], sq, skv, t["query_rope"], t["key_rope"], scale_value=1 / 24, layout=layout)
+
+
+def test_wrapper_rejects_half_rope_and_accepts_good_shapes():
+    import torch
+    t, sq, skv = _cpu_call_tensors("BSND")
+    with pytest.raises(ValueError, match="rope"):
+        sf.sparse_flash_attention_grad(
+            t["query"], t["key"], t["value"], t["sparse_indices"], t["d_out"], t["out"], t["softmax_max"],
+            t["softmax_sum"], sq, skv, t["query_rope"], None, scale_value=1 / 24)
+    # correct shapes pass the shape checks and stop only at the device check (CPU tensors)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        sf.sparse_flash_attention_grad(
+            t["query"], t["key"], t["value"], t["sparse_indices"], t["d_out"], t["out"], t["softmax_max"],
+            t["softmax_sum"], sq, skv, t["query_rope"], t["key_rope"], scale_value=1 / 24)

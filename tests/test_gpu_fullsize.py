@@ -171,3 +171,82 @@ def test_hot_cold_deterministic_workload_sampled():
     for x, y in zip(a, b):
         assert torch.equal(x.view(torch.int16), y.view(torch.int16))
     _check_sampled(case, a, live, dq_rows, key_sets, f"{p.name}/sampled/")
+
+
+def _check_tail(t, outs, dq_pos, keys, label):
+    """Sampled check of a TailCase run: dQ of live rows self.live[dq_pos], dQ = 0 on every other
+    row, dK / dKRope / dV of `keys` against the oracle's sums over all live rows."""
+    from tests.common import TailCase  # noqa: F401  (type of t)
+    p = t.p
+    dq, dk, dv, dqr, dkr = (from_dev(x) for x in outs)
+    for name, x in (("dq", dq), ("dk", dk), ("dv", dv), ("dq_rope", dqr), ("dk_rope", dkr)):
+        assert np.isfinite(x).all(), f"{label}: non-finite {name}"
+    dq2 = dq.reshape(p.rows, p.N1, p.D)
+    dqr2 = dqr.reshape(p.rows, p.N1, p.Dr)
+    dead = np.ones(p.rows, bool)
+    dead[t.live] = False
+    assert not dq2[dead].any() and not dqr2[dead].any(), f"{label}: dQ of rows without probability mass"
+    rdq, rdqr = t.ref_dq(dq_pos)
+    compare(label + "dq", dq2[t.live[dq_pos]], rdq, scaled=False)
+    compare(label + "dq_rope", dqr2[t.live[dq_pos]], rdqr, scaled=False)
+    rdk, rdkr, rdv = t.ref_dkv(keys)
+    compare(label + "dk", dk.reshape(-1, p.D)[keys], rdk, scaled=False)
+    compare(label + "dk_rope", dkr.reshape(-1, p.Dr)[keys], rdkr, scaled=False)
+    compare(label + "dv", dv.reshape(-1, p.D)[keys], rdv, scaled=False)
+
+
+@pytest.mark.timeout(900)
+def test_tnd_varlen_n128_sampled_across_segments():
+    """TND, 4 sequences of 2K / 4K / 8K / 16K tokens, N1 = 128 (two head groups), topk = 2048,
+    causal.  Live rows: the last 1030 rows of the 4K sequence (three 512-row segments of the
+    key-major kernel), the last 64 of the 2K and the last 128 of the 16K sequence.  The sampled
+    keys are each selected by live rows of at least three segments, so the ordered sum over
+    (head group, segment) partials is checked element by element; both deterministic settings."""
+    from tests.common import TailCase
+    p = inputs.workload(3)
+    print(f"# {p.name}: generated", flush=True)
+    t = TailCase(p, [64, 1030, 0, 128])
+    print(f"# {p.name}: oracle forward on {len(t.live)} rows done", flush=True)
+    rng = np.random.default_rng(303)
+    dq_pos = np.sort(rng.choice(len(t.live), 16, replace=False))
+    multi = t.keys_from_segments(rng, 40, seg_rows=512, min_segments=3)
+    assert len(multi) >= 20
+    other = np.concatenate([p.k_offset(0) + rng.choice(p.lkv(0), 8, replace=False),
+                            p.k_offset(3) + rng.choice(p.lkv(3), 8, replace=False),
+                            p.k_offset(2) + rng.choice(p.lkv(2), 4, replace=False)])   # seq 2: no live row
+    keys = np.unique(np.concatenate([multi, other]))
+    dev = t.device_inputs()
+    for det in (False, True):
+        outs = t.run_gpu(dev, deterministic=det)
+        import sparse_mla_flash_amd as sf
+        assert sf.sfag_last_path() == 0, "this workload takes the key-major path"
+        _check_tail(t, outs, dq_pos, keys, f"{p.name}/det={int(det)}/")
+        print(f"# {p.name}: det={int(det)} ok", flush=True)
+
+
+@pytest.mark.timeout(900)
+def test_long_context_window_sampled_both_modes():
+    """BSND B = 1, 16384 queries at the end of 131072 keys, N1 = 128, topk = 2048, half the
+    slots from the local window [pos - 4095, pos] and half uniform: the per-pair (scatter) path
+    at its full 131072-key accumulator, in both deterministic settings.  Live rows: the last
+    200; sampled keys from the window, from the uniform part and unselected ones."""
+    from tests.common import TailCase
+    import sparse_mla_flash_amd as sf
+    p = inputs.workload(4)
+    print(f"# {p.name}: generated", flush=True)
+    t = TailCase(p, [200])
+    print(f"# {p.name}: oracle forward on {len(t.live)} rows done", flush=True)
+    rng = np.random.default_rng(404)
+    dq_pos = np.sort(rng.choice(len(t.live), 16, replace=False))
+    idx = p.idx.reshape(p.rows, p.topk)
+    last = idx[t.live[-1]]
+    win = last[last >= p.S2 - 4096]
+    far = last[last < p.S2 - 4096]
+    keys = np.unique(np.concatenate([rng.choice(win, 24, replace=False), rng.choice(far, 24, replace=False),
+                                     rng.choice(p.S2, 8, replace=False)]))
+    dev = t.device_inputs()
+    for det in (False, True):
+        outs = t.run_gpu(dev, deterministic=det)
+        assert sf.sfag_last_path() == 1, "this workload takes the per-pair path"
+        _check_tail(t, outs, dq_pos, keys, f"{p.name}/det={int(det)}/")
+        print(f"# {p.name}: det={int(det)} ok", flush=True)
