@@ -20,7 +20,9 @@
  *   - All tensors are dense, row-major, contiguous.  Pointers named *_host are
  *     host memory read during the call only; every other pointer is device
  *     memory owned by the caller.  The library allocates no device memory and
- *     keeps no pointer after a call returns.
+ *     keeps no pointer after a call returns; the one exception is the fixed
+ *     scratch array of the no-allocation entry point (SFAG_NOALLOC_SCRATCH_BYTES
+ *     per GPU, created with the library's code on that device).
  *   - bf16 tensors are IEEE bfloat16 bit patterns (uint16).  Statistics are fp32.
  *   - Layout "BSND": query-side [B, S1, N1, W], key-side [B, S2, 1, W],
  *     sparseIndices [B, S1, 1, topk], statistics [B, N1, S1].
@@ -125,6 +127,36 @@ sfag_status sfag_sparse_flash_attention_grad(
     const char* layout, int64_t sparse_mode, int64_t pre_tokens, int64_t next_tokens,
     int32_t deterministic, void* d_query, void* d_key, void* d_value, void* d_query_rope,
     void* d_key_rope, void* workspace, uint64_t workspace_size, void* stream);
+
+/*
+ * Largest workspace (bytes) the no-allocation entry point below can serve from its built-in
+ * scratch.
+ */
+#define SFAG_NOALLOC_SCRATCH_BYTES (256ull << 20)
+
+/*
+ * No-allocation variant of sfag_sparse_flash_attention_grad, for callers that cannot call
+ * hipMalloc or take a caller-sized workspace: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  Arguments and results are those of
+ * sfag_sparse_flash_attention_grad without workspace / workspace_size; inputs and outputs
+ * are still the caller's device buffers.  Instead of a workspace the call uses a scratch array
+ * built into the library (SFAG_NOALLOC_SCRATCH_BYTES per GPU, allocated with the library's
+ * code on each device it runs on and held until the process ends).  Problems whose
+ * sfag_get_workspace_size() exceeds that size are rejected with SFAG_ERR_WORKSPACE before
+ * anything is enqueued.  The call allocates no device or pinned host memory.
+ * Every call on one GPU shares that GPU's scratch and leaves its contents behind (the kernels
+ * clear whatever must start at zero themselves), so calls on one GPU that overlap in time
+ * (different streams or threads without ordering between them) race: order them on one
+ * stream or serialise them.
+ */
+sfag_status sfag_sparse_flash_attention_grad_noalloc(
+    const void* query, const void* key, const void* value, const int32_t* sparse_indices,
+    const void* d_out, const void* out, const float* softmax_max, const float* softmax_sum,
+    const int32_t* seq_len_q_host, const int32_t* seq_len_kv_host, const void* query_rope,
+    const void* key_rope, const sfag_dims* dims, float scale_value, int64_t sparse_block_size,
+    const char* layout, int64_t sparse_mode, int64_t pre_tokens, int64_t next_tokens,
+    int32_t deterministic, void* d_query, void* d_key, void* d_value, void* d_query_rope,
+    void* d_key_rope, void* stream);
 
 /*
  * Sparse forward over the same selection (the step that produces the inputs

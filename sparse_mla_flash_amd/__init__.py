@@ -30,7 +30,9 @@ SFAG_ERR_UNSUPPORTED = 161901
 SFAG_ERR_WORKSPACE = 161902
 SFAG_ERR_DEVICE = 161903
 
-EXPORTED = ("sfag_get_workspace_size", "sfag_sparse_flash_attention_grad",
+NOALLOC_SCRATCH_BYTES = 256 << 20      # SFAG_NOALLOC_SCRATCH_BYTES
+
+EXPORTED = ("sfag_get_workspace_size", "sfag_sparse_flash_attention_grad", "sfag_sparse_flash_attention_grad_noalloc",
             "sfag_sparse_flash_attention_forward", "sfag_set_profile_events", "sfag_last_path", "sfag_last_error",
             "sfag_version")
 
@@ -68,6 +70,11 @@ def lib():
             vp, vp, vp, vp, vp, vp, vp, vp, i32p, i32p, vp, vp, ctypes.POINTER(Dims),
             ctypes.c_float, ctypes.c_int64, ctypes.c_char_p, ctypes.c_int64, ctypes.c_int64,
             ctypes.c_int64, ctypes.c_int32, vp, vp, vp, vp, vp, vp, ctypes.c_uint64, vp]
+        L.sfag_sparse_flash_attention_grad_noalloc.restype = ctypes.c_int
+        L.sfag_sparse_flash_attention_grad_noalloc.argtypes = [
+            vp, vp, vp, vp, vp, vp, vp, vp, i32p, i32p, vp, vp, ctypes.POINTER(Dims),
+            ctypes.c_float, ctypes.c_int64, ctypes.c_char_p, ctypes.c_int64, ctypes.c_int64,
+            ctypes.c_int64, ctypes.c_int32, vp, vp, vp, vp, vp, vp]
         L.sfag_sparse_flash_attention_forward.restype = ctypes.c_int
         L.sfag_sparse_flash_attention_forward.argtypes = [
             vp, vp, vp, vp, i32p, i32p, vp, vp, ctypes.POINTER(Dims), ctypes.c_float,
@@ -143,6 +150,22 @@ def sfag_sparse_flash_attention_grad(query, key, value, sparse_indices, d_out, o
         ctypes.byref(dims), float(scale_value), int(sparse_block_size), layout.encode(), int(sparse_mode),
         int(pre_tokens), int(next_tokens), int(bool(deterministic)), d_query, d_key, d_value, d_query_rope,
         d_key_rope, workspace, int(workspace_size), stream)
+
+
+def sfag_sparse_flash_attention_grad_noalloc(query, key, value, sparse_indices, d_out, out, softmax_max,
+                                             softmax_sum, seq_len_q, seq_len_kv, query_rope, key_rope, dims: Dims,
+                                             scale_value, sparse_block_size, layout, sparse_mode, pre_tokens,
+                                             next_tokens, deterministic, d_query, d_key, d_value, d_query_rope,
+                                             d_key_rope, stream) -> int:
+    """Raw C call of the no-allocation variant (the library's built-in scratch replaces the
+    workspace); every tensor argument is a device address (int) or None; returns the status."""
+    qa, qp = _lens(seq_len_q)
+    ka, kp = _lens(seq_len_kv)
+    return lib().sfag_sparse_flash_attention_grad_noalloc(
+        query, key, value, sparse_indices, d_out, out, softmax_max, softmax_sum, qp, kp, query_rope, key_rope,
+        ctypes.byref(dims), float(scale_value), int(sparse_block_size), layout.encode(), int(sparse_mode),
+        int(pre_tokens), int(next_tokens), int(bool(deterministic)), d_query, d_key, d_value, d_query_rope,
+        d_key_rope, stream)
 
 
 def sfag_sparse_flash_attention_forward(query, key, value, sparse_indices, seq_len_q, seq_len_kv, query_rope,

@@ -304,6 +304,39 @@ sfag_status init_device() {
     if (e_ != hipSuccess) return fail(SFAG_ERR_DEVICE, "%s: %s", #call, hipGetErrorString(e_)); \
   } while (0)
 
+// Scratch of the no-allocation entry point: one array per GPU the library runs on, held until the
+// process ends.  Host code never uses the array's name as an address: the device address of each
+// GPU's copy is taken once per device with hipGetSymbolAddress and kept in g_scratch_ptr.
+constexpr uint64_t kScratchBytes = SFAG_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+sfag_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  SFAG_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return fail(SFAG_ERR_DEVICE, "device %d out of range for the scratch table", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    SFAG_HIP(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)));
+    if (!ptr) return fail(SFAG_ERR_DEVICE, "hipGetSymbolAddress returned NULL for the scratch array");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return SFAG_OK;
+}
+
+sfag_status backward(const void* query, const void* key, const void* value, const int32_t* sparse_indices,
+                     const void* d_out, const void* out, const float* softmax_max, const float* softmax_sum,
+                     const int32_t* seq_len_q_host, const int32_t* seq_len_kv_host, const void* query_rope,
+                     const void* key_rope, const sfag_dims* dims, float scale_value, int64_t sparse_block_size,
+                     const char* layout, int64_t sparse_mode, int32_t deterministic, void* d_query, void* d_key,
+                     void* d_value, void* d_query_rope, void* d_key_rope, void* workspace, uint64_t workspace_size,
+                     bool noalloc, void* stream);
+
 }  // namespace
 
 extern "C" {
@@ -347,6 +380,37 @@ sfag_status sfag_sparse_flash_attention_grad(
     void* d_key_rope, void* workspace, uint64_t workspace_size, void* stream) {
   (void)pre_tokens;
   (void)next_tokens;
+  return backward(query, key, value, sparse_indices, d_out, out, softmax_max, softmax_sum, seq_len_q_host,
+                  seq_len_kv_host, query_rope, key_rope, dims, scale_value, sparse_block_size, layout, sparse_mode,
+                  deterministic, d_query, d_key, d_value, d_query_rope, d_key_rope, workspace, workspace_size,
+                  false, stream);
+}
+
+sfag_status sfag_sparse_flash_attention_grad_noalloc(
+    const void* query, const void* key, const void* value, const int32_t* sparse_indices, const void* d_out,
+    const void* out, const float* softmax_max, const float* softmax_sum, const int32_t* seq_len_q_host,
+    const int32_t* seq_len_kv_host, const void* query_rope, const void* key_rope, const sfag_dims* dims,
+    float scale_value, int64_t sparse_block_size, const char* layout, int64_t sparse_mode, int64_t pre_tokens,
+    int64_t next_tokens, int32_t deterministic, void* d_query, void* d_key, void* d_value, void* d_query_rope,
+    void* d_key_rope, void* stream) {
+  (void)pre_tokens;
+  (void)next_tokens;
+  return backward(query, key, value, sparse_indices, d_out, out, softmax_max, softmax_sum, seq_len_q_host,
+                  seq_len_kv_host, query_rope, key_rope, dims, scale_value, sparse_block_size, layout, sparse_mode,
+                  deterministic, d_query, d_key, d_value, d_query_rope, d_key_rope, nullptr, 0, true, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+sfag_status backward(const void* query, const void* key, const void* value, const int32_t* sparse_indices,
+                     const void* d_out, const void* out, const float* softmax_max, const float* softmax_sum,
+                     const int32_t* seq_len_q_host, const int32_t* seq_len_kv_host, const void* query_rope,
+                     const void* key_rope, const sfag_dims* dims, float scale_value, int64_t sparse_block_size,
+                     const char* layout, int64_t sparse_mode, int32_t deterministic, void* d_query, void* d_key,
+                     void* d_value, void* d_query_rope, void* d_key_rope, void* workspace, uint64_t workspace_size,
+                     bool noalloc, void* stream) {
   sfag_status st;
   const struct { const void* p; const char* n; } req[] = {
       {query, "query"}, {key, "key"}, {value, "value"}, {sparse_indices, "sparse_indices"},
@@ -370,6 +434,14 @@ sfag_status sfag_sparse_flash_attention_grad(
   st = make_plan(dims, seq_len_q_host, seq_len_kv_host, scale_value, sparse_block_size, layout, sparse_mode,
                  deterministic, true, &p);
   if (st != SFAG_OK) return st;
+  if (noalloc) {
+    if (p.bytes > kScratchBytes)
+      return fail(SFAG_ERR_WORKSPACE,
+                  "this problem needs %llu bytes of scratch; the no-allocation entry point holds %llu",
+                  (unsigned long long)p.bytes, (unsigned long long)kScratchBytes);
+    if ((st = scratch_of_current_device(&workspace)) != SFAG_OK) return st;
+    workspace_size = kScratchBytes;
+  }
   if (workspace_size < p.bytes || (p.bytes > 0 && !workspace))
     return fail(SFAG_ERR_WORKSPACE, "workspace of %llu bytes needed, got %llu%s", (unsigned long long)p.bytes,
                 (unsigned long long)workspace_size, workspace ? "" : " (NULL)");
@@ -490,6 +562,10 @@ sfag_status sfag_sparse_flash_attention_grad(
   g_last_path = 1;
   return ok();
 }
+
+}  // namespace
+
+extern "C" {
 
 sfag_status sfag_sparse_flash_attention_forward(const void* query, const void* key, const void* value,
                                                 const int32_t* sparse_indices, const int32_t* seq_len_q_host,

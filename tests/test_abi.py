@@ -202,3 +202,20 @@ def test_wrapper_rejects_half_rope_and_accepts_good_shapes():
         sf.sparse_flash_attention_grad(
             t["query"], t["key"], t["value"], t["sparse_indices"], t["d_out"], t["out"], t["softmax_max"],
             t["softmax_sum"], sq, skv, t["query_rope"], t["key_rope"], scale_value=1 / 24)
+
+
+def test_noalloc_rejects_problems_beyond_its_scratch():
+    """The no-allocation entry point refuses a problem whose workspace exceeds its built-in
+    scratch, before any device call (the pointers below are never dereferenced)."""
+    d = dims(S1=8192, S2=8192, N1=64, topk=2048)
+    need = ws(d)
+    assert need > sf.NOALLOC_SCRATCH_BYTES
+    st = sf.sfag_sparse_flash_attention_grad_noalloc(
+        FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, d, 1 / 24, 1, "BSND", 3,
+        2 ** 31 - 1, 2 ** 31 - 1, False, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert st == sf.SFAG_ERR_WORKSPACE
+    assert "scratch" in sf.sfag_last_error()
+    st = sf.sfag_sparse_flash_attention_grad_noalloc(
+        None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, dims(), 1 / 24, 1, "BSND", 3,
+        2 ** 31 - 1, 2 ** 31 - 1, False, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert st == sf.SFAG_ERR_PARAM_NULLPTR
