@@ -241,11 +241,12 @@ def ceilings():
     res["hbm_copy"] = {"gbs": round(2 * n / (t * 1e-3) / 1e9, 1), "bytes_each_way": n, "ms": round(t, 4)}
     del a, b
     # LDS rates at the shader clock measured above
-    names = {0: "ds_add_f32", 1: "ds_write_b32", 2: "ds_read_b32", 3: "ds_write_b128", 4: "ds_read_b128"}
-    width = {0: 4, 1: 4, 2: 4, 3: 16, 4: 16}
+    names = {0: "ds_add_f32", 1: "ds_write_b32", 2: "ds_read_b32", 3: "ds_write_b128", 4: "ds_read_b128",
+             5: "ds_read_b64_tr_b16"}
+    width = {0: 4, 1: 4, 2: 4, 3: 16, 4: 16, 5: 8}
     lds = {}
     lblocks, liters = cus * 2, 4000
-    for mode in range(5):
+    for mode in range(6):
         t = min(L.ceil_lds(mode, lblocks, liters, out.data_ptr(), stream) for _ in range(3))
         torch.cuda.synchronize()
         nbytes = lblocks * 256 * liters * 16 * width[mode]

@@ -8,10 +8,11 @@
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// 8 independent accumulation chains of v_mfma_f32_16x16x32_bf16 per wave, `iters` rounds.
-// Wave 0 of workgroup 0 records the shader-clock counter (s_memtime) and the 100 MHz constant
-// counter (s_memrealtime) around its loop, so that clk[1] / clk[0] cycles per tick give the
-// shader clock while the chip runs MFMA-bound.
+// 8 independent accumulation chains of v_mfma_f32_16x16x32_bf16 per wave, `iters` rounds.  The
+// MFMAs are written as inline asm with the accumulator tied to the destination so that each
+// chain stays in place (no memory access in the asm).  Wave 0 of workgroup 0 records the
+// shader-clock counter (s_memtime) and the 100 MHz constant counter (s_memrealtime) around its
+// loop, so that clk[1] / clk[0] cycles per tick give the shader clock under MFMA load.
 __global__ void __launch_bounds__(256) mfma_rate_kernel(float* out, int iters, unsigned long long* clk) {
   const int lane = threadIdx.x & 63;
   bf16x8 a, b;
@@ -20,24 +21,24 @@ __global__ void __launch_bounds__(256) mfma_rate_kernel(float* out, int iters, u
     a[e] = (__bf16)(0.001f * (lane + e));
     b[e] = (__bf16)(0.002f * (lane - e));
   }
-  f32x4 c[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) c[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 c0{}, c1{}, c2{}, c3{}, c4{}, c5{}, c6{}, c7{};
   const bool timer = blockIdx.x == 0 && threadIdx.x == 0;
   unsigned long long t0 = 0, r0 = 0;
   if (timer) {
     t0 = __builtin_amdgcn_s_memtime();
     r0 = __builtin_amdgcn_s_memrealtime();
   }
+#define CEIL_MFMA(c) asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b))
   for (int it = 0; it < iters; ++it) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) c[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c[i], 0, 0, 0);
+    CEIL_MFMA(c0); CEIL_MFMA(c1); CEIL_MFMA(c2); CEIL_MFMA(c3);
+    CEIL_MFMA(c4); CEIL_MFMA(c5); CEIL_MFMA(c6); CEIL_MFMA(c7);
   }
-  float s = 0.f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) s += c[i][0] + c[i][1] + c[i][2] + c[i][3];
+#undef CEIL_MFMA
+  // results are read only after this wait-free dependency point; s_nop covers the last MFMAs
+  asm volatile("s_nop 7\n s_nop 7\n s_nop 7" ::);
+  const f32x4 sum = c0 + c1 + c2 + c3 + c4 + c5 + c6 + c7;
+  const float s = sum[0] + sum[1] + sum[2] + sum[3];
   if (timer) {
-    // wait for the last MFMA results before reading the counters again
     asm volatile("" ::"v"(s));
     const unsigned long long t1 = __builtin_amdgcn_s_memtime();
     const unsigned long long r1 = __builtin_amdgcn_s_memrealtime();
@@ -53,8 +54,12 @@ __global__ void __launch_bounds__(256) copy_kernel(const uint4* __restrict__ src
 }
 
 // LDS instruction rate.  mode 0: ds_add_f32 (result unused), 1: ds_write_b32, 2: ds_read_b32,
-// 3: ds_write_b128, 4: ds_read_b128.  Lanes of a wave address consecutive words (conflict-free);
-// each wave works on its own 16 KB region.  `iters` rounds of 16 instructions per lane.
+// 3: ds_write_b128, 4: ds_read_b128, 5: ds_read_b64_tr_b16 (transposing read).  Each wave works
+// on its own 16 KB region; in one round a lane issues 16 instructions at 16 distinct addresses
+// (lanes of a wave address consecutive elements: conflict-free), every loaded element is
+// consumed and every store survives (the round ends with a compiler barrier).
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 __global__ void __launch_bounds__(256) lds_rate_kernel(int mode, int iters, float* out) {
   __shared__ __attribute__((aligned(16))) float buf[4 * 4096];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -62,8 +67,9 @@ __global__ void __launch_bounds__(256) lds_rate_kernel(int mode, int iters, floa
   for (int i = lane; i < 4096; i += 64) w[i] = 0.f;
   __syncthreads();
   float acc = 0.f;
-  const float v = 1.0f + lane;
+  int iacc = 0;
   for (int it = 0; it < iters; ++it) {
+    const float v = 1.0f + lane + it;
     if (mode == 0) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) atomicAdd(&w[j * 256 + lane], v);
@@ -72,22 +78,28 @@ __global__ void __launch_bounds__(256) lds_rate_kernel(int mode, int iters, floa
       for (int j = 0; j < 16; ++j) w[j * 256 + lane] = v + j;
     } else if (mode == 2) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) acc += w[((j + it) & 15) * 256 + lane];
+      for (int j = 0; j < 16; ++j) acc += w[j * 256 + lane];
     } else if (mode == 3) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j)
-        reinterpret_cast<float4*>(w)[(j & 3) * 256 + lane] = make_float4(v, v + j, v, v);
+      for (int j = 0; j < 16; ++j) reinterpret_cast<float4*>(w)[j * 64 + lane] = make_float4(v, v + j, v, v);
+    } else if (mode == 4) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float4 x = reinterpret_cast<const float4*>(w)[j * 64 + lane];
+        acc += (x.x + x.y) + (x.z + x.w);
+      }
     } else {
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const float4 x = reinterpret_cast<const float4*>(w)[((j + it) & 3) * 256 + lane];
-        acc += x.x + x.w;
+        const i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4_t*)(reinterpret_cast<short*>(w) + j * 512 + 4 * lane));
+        iacc += (x[0] ^ x[1]) + (x[2] ^ x[3]);
       }
     }
     asm volatile("" ::: "memory");
   }
   __syncthreads();
-  acc += w[lane];
+  acc += w[lane] + (float)iacc;
   if (acc == 12345.f) out[blockIdx.x] = acc;
 }
 
