@@ -57,10 +57,11 @@ struct Plan {
   int dense = 0;
   double waste = 0.0;              // dense-masked (row, key) entries per valid pair (upper bound)
   int64_t items = 0, citems = 0, maxblk = 0;
+  int64_t rec_chunks = 0;          // record chunks of 32 positions per (row, head group)
   // workspace layout
   uint64_t off_acc = 0, off_partial = 0, off_keys0 = 0, off_keys1 = 0, off_sorttmp = 0;
   uint64_t off_sorted = 0, off_count = 0, off_maxdup = 0, off_offs = 0, off_dsp = 0, off_part = 0, off_flag = 0;
-  uint64_t off_zero = 0, off_ilist = 0, off_imap = 0, off_trash = 0, off_kpos = 0, off_bt = 0;
+  uint64_t off_zero = 0, off_ilist = 0, off_imap = 0, off_kpos = 0, off_bt = 0;
   uint64_t sort_tmp_bytes = 0, bytes = 0;
   int64_t det_rows = 0;            // query rows per deterministic launch
   int end_bit = 64;
@@ -229,8 +230,9 @@ sfag_status make_plan(const sfag_dims* dims, const int32_t* sq, const int32_t* s
     off = align_up(off + (uint64_t)p->rows * (maxblk + 1) * 4);
     p->off_kpos = off;
     off = align_up(off + (uint64_t)p->rows * maxblk * sfag::kBk * 2);
+    p->rec_chunks = (p->topk + 31) / 32;
     p->off_dsp = off;
-    off = align_up(off + pairs * p->hg_count * 128 * 2);
+    off = align_up(off + (uint64_t)p->rows * p->hg_count * p->rec_chunks * sfag::kRecChunk * 2);
     p->off_part = off;
     off = align_up(off + (uint64_t)p->hg_count * citems * sfag::kBk * kDacc * 4);
     p->off_flag = off;
@@ -241,8 +243,6 @@ sfag_status make_plan(const sfag_dims* dims, const int32_t* sq, const int32_t* s
     off = align_up(off + (uint64_t)std::max<int64_t>(items, 1) * 4);
     p->off_zero = off;
     off = align_up(off + 576 * 2);
-    p->off_trash = off;                 // write-only sink for the records of invalid slots
-    off = align_up(off + 128 * 2);
     p->off_bt = off;                    // Q | QRope | dO, heads innermost (key-major B operand)
     off = align_up(off + (uint64_t)p->rows * p->hg_count * kDacc * 64 * 2);
     p->bytes = off;
@@ -515,11 +515,12 @@ sfag_status backward(const void* query, const void* key, const void* value, cons
     da.ilist = reinterpret_cast<int32_t*>(ws + p.off_ilist);
     da.imap = reinterpret_cast<int32_t*>(ws + p.off_imap);
     da.scale = scale_value;
+    da.rec_chunks = (int)p.rec_chunks;
+    a.rec_chunks = (int)p.rec_chunks;
     a.sorted = da.sorted;
     a.count = da.count;
     a.dsp = reinterpret_cast<uint16_t*>(ws + p.off_dsp);
     a.zero_row = da.zero_row;
-    a.trash = reinterpret_cast<uint16_t*>(ws + p.off_trash);
     a.bt = reinterpret_cast<uint16_t*>(ws + p.off_bt);
     a.row_begin = 0;
     a.pairs_per_launch = 0;

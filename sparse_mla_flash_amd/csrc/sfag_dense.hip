@@ -212,14 +212,17 @@ __global__ void __launch_bounds__(1024) item_list_kernel(DenseArgs a) {
 // keys gives one unit per repeat layer L, the L-th occurrence of each key):
 //   A = [256 keys x 64 heads] of dS (dK slices) or P (dV slices), zero where the row did not
 //       select the key.  MFMA A fragments come straight from the pair records in global
-//       memory: lane (g, c) handles keys kb0 + 64 w + 4 c + kt (kt = 0..3) as row c of key
-//       tile kt and needs heads 8 g .. 8 g + 7 (+ 32) of each, found through the row's
-//       key -> position map (one 8-byte load for the 4 keys); unselected keys load nothing.
+//       memory: lane (g, c) handles key kb0 + 64 w + 16 kt + c (kt = 0..3) as row c of key
+//       tile kt, found through the row's key -> position map; unselected keys load nothing.
+//       The heads are contracted in the order that matches the record layout: head step ks of
+//       lane (g, c) covers heads 16 g + 8 ks .. + 7, so the two A fragments of a key are one
+//       32-byte run of head tile g.
 //   B = the row's [64 heads x cols] Q (or dO) slice, read from the column-major copy written by
 //       the query-major kernel (one contiguous run of 2 KB per column tile), staged in LDS as
-//       [column][8 chunks of 8 heads + 1 pad chunk] and read as whole 16-byte fragments.
+//       [column][8 chunks of 8 heads + 1 pad chunk] and read as whole 16-byte fragments (head
+//       chunk 2 g + ks for head step ks).
 //   acc[keys][cols] += A B  on the 16x16x32 bf16 MFMA, fp32 in registers; accumulator row
-//       4 g + v of key tile kt is key kb0 + 64 w + 4 (4 g + v) + kt.
+//       4 g + v of key tile kt is key kb0 + 64 w + 16 kt + 4 g + v.
 // Two workgroups share a CU (at most 256 registers per lane), so each unit is simple: its
 // records are requested and used at once, the map and the B tile of the next unit are
 // requested before its MFMAs, and the other workgroup runs while this one waits.
@@ -261,11 +264,15 @@ __device__ __forceinline__ void kv_dense_units(const DenseArgs& a, const KvCtx& 
   }
   const int64_t bt_row = (int64_t)a.hgc * kDacc * 64;
   const uint16_t* bt_base = a.bt + ((int64_t)x.hg * kDacc + x.colbase) * 64;
-  const uint32_t rstride = (uint32_t)a.hgc * 128u;
-  const int kmap = x.kb0 + 64 * wave + 4 * c;        // first of this lane's 4 keys
+
+  const int kmap = x.kb0 + 64 * wave + c;            // this lane's key of key tile kt: kmap + 16 kt
   const int64_t row0 = x.qstart + x.i0;
-  const int64_t rec_row = (int64_t)a.topk * a.hgc * 128;
-  const uint16_t* rec_base = a.dsp + (int64_t)x.hg * 128 + x.which + 8 * g;
+  // records of (row, hg): chunk-major [chunk][dS | P][head tile of 16][32 positions][16 heads].
+  // The contraction over heads is taken in the order that makes each lane's A fragments one
+  // 32-byte run: head step ks of lane (g, c) covers heads 16 g + 8 ks .. + 7 (head tile g), and
+  // the B fragments read the same heads of Q / dO.
+  const int64_t rec_row = (int64_t)a.hgc * a.rec_chunks * kRecChunk;
+  const uint16_t* rec_base = a.dsp + (int64_t)x.hg * a.rec_chunks * kRecChunk + x.which + g * 512;
 
   f32x4 acc[4][NFT];
 #pragma unroll
@@ -274,7 +281,10 @@ __device__ __forceinline__ void kv_dense_units(const DenseArgs& a, const KvCtx& 
     for (int ft = 0; ft < NFT; ++ft) acc[kt][ft] = f32x4{0.f, 0.f, 0.f, 0.f};
 
 #define KV_MAP_LOAD(MP, ROW)                                                                   \
-  MP = *reinterpret_cast<const i16x4*>(a.kpos + (row0 + (ROW)) * a.kstride + kmap);
+  {                                                                                            \
+    const int16_t* m_ = a.kpos + (row0 + (ROW)) * a.kstride + kmap;                            \
+    _Pragma("unroll") for (int kt = 0; kt < 4; ++kt) MP[kt] = m_[16 * kt];                     \
+  }
 #define KV_B_LOAD(SP, ROW)                                                                     \
   {                                                                                            \
     const char* run_ = reinterpret_cast<const char*>(bt_base + (row0 + (ROW)) * bt_row);       \
@@ -287,7 +297,7 @@ __device__ __forceinline__ void kv_dense_units(const DenseArgs& a, const KvCtx& 
       *reinterpret_cast<u32x4*>((BT) + bdst[i]) = SP[i];                                       \
   }
 #define KV_BFRAG(BT, Q)                                                                        \
-  (*reinterpret_cast<const bf16x8*>((BT) + ((16 * ((Q) >> 1) + c) * kBtColChunks + 4 * ((Q) & 1) + g) * 8))
+  (*reinterpret_cast<const bf16x8*>((BT) + ((16 * ((Q) >> 1) + c) * kBtColChunks + 2 * g + ((Q) & 1)) * 8))
 
   // unit cursor: row index ri (into s_row) and repeat layer L; the next unit's row is rn
   auto advance = [&](int& ri, int& L) {
@@ -325,14 +335,14 @@ __device__ __forceinline__ void kv_dense_units(const DenseArgs& a, const KvCtx& 
       bool ok = e >= 0;
       if (DUPS && L > 0) {
         e += L;
-        ok = ok && e < a.topk && a.sorted[(row0 + r) * a.topk + min(e, a.topk - 1)] == kmap + kt;
+        ok = ok && e < a.topk && a.sorted[(row0 + r) * a.topk + min(e, a.topk - 1)] == kmap + 16 * kt;
       }
       f[kt][0] = bf16x8{};
       f[kt][1] = bf16x8{};
       if (ok) {
-        const uint16_t* src = rb + (uint32_t)e * rstride;
+        const uint16_t* src = rb + (uint32_t)(e >> 5) * (uint32_t)kRecChunk + (uint32_t)(e & 31) * 16u;
         f[kt][0] = *reinterpret_cast<const bf16x8*>(src);
-        f[kt][1] = *reinterpret_cast<const bf16x8*>(src + 32);
+        f[kt][1] = *reinterpret_cast<const bf16x8*>(src + 8);
       }
     }
     i16x4 mn;
@@ -379,7 +389,7 @@ __device__ __forceinline__ void kv_dense_units(const DenseArgs& a, const KvCtx& 
     for (int ft = 0; ft < NFT; ++ft)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int kk = 64 * wave + 4 * (4 * g + v) + kt;
+        const int kk = 64 * wave + 16 * kt + 4 * g + v;
         part[(int64_t)kk * kDacc + x.colbase + 16 * ft + c] = acc[kt][ft][v] * mul;
       }
 }
@@ -468,7 +478,7 @@ __global__ void __launch_bounds__(kThreads, 2) kv_dense_kernel(DenseArgs a) {
   x.isdk = sl < 4;
   x.colbase = x.isdk ? 144 * sl : kDk + 128 * (sl - 4);
   x.hg = hg;
-  x.which = x.isdk ? 0 : 64;
+  x.which = x.isdk ? 0 : kRecHalf;
   x.citem = citem;
   if (x.isdk) {
     if (dups) kv_dense_units<9, true>(a, x, Bt0, Bt1);

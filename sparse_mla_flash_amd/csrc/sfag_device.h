@@ -120,6 +120,16 @@ __device__ __forceinline__ bf16x8 lds_frag_tr_cm(const uint16_t* tile, int n0, i
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// MFMA fragment from two transposing reads at P and P + HI (elements): lane i of each 16-lane
+// group gets the 4 elements of the first read, then the 4 of the second (see the note on
+// ds_read_b64_tr_b16 above).  The caller points every lane at its own base.
+__device__ __forceinline__ bf16x8 tr_frag(const uint16_t* p, int hi) {
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+  const i16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + hi));
+  const i16x8 v = __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
 __device__ __forceinline__ uint16_t f2bf(float f) {
   // round to nearest even; NaN stays NaN
   uint32_t u = __float_as_uint(f);

@@ -15,6 +15,10 @@ struct Lens {
 constexpr int kBk = 256;        // keys per block of the key-major dK / dV kernel
 constexpr int kSegRows = 512;   // query rows per segment of the key-major dK / dV kernel
 constexpr int kMaxSegs = 512;   // (head group, segment) pairs per batch the ordered reduce can hold
+// dS | P records, per (row, head group) and chunk of 32 sorted positions:
+// [dS | P][head tile of 16][32 positions][16 heads] bf16
+constexpr int kRecChunk = 2 * 4 * 32 * 16;   // elements per chunk (8 KB)
+constexpr int kRecHalf = kRecChunk / 2;      // offset of the P half
 
 struct BwdArgs {
   const uint16_t* q;      // [rows, N1, 512] bf16
@@ -32,9 +36,8 @@ struct BwdArgs {
   float* partial;         // [head groups, pairs_per_launch, 1088] (deterministic mode)
   const int32_t* sorted;  // [rows, topk] valid key positions, ascending (key-major mode)
   const int32_t* count;   // [rows] number of valid positions (key-major mode)
-  uint16_t* dsp;          // [rows * topk, head groups, 128] bf16 dS | P per pair (key-major mode)
-  const uint16_t* zero_row;  // 576 zero bf16 (key-major mode: source of padding slots)
-  uint16_t* trash;        // 128 bf16 write-only sink (key-major mode: records of invalid slots)
+  uint16_t* dsp;          // [rows, head groups, rec_chunks, kRecChunk] bf16 dS | P records (key-major mode)
+  const uint16_t* zero_row;  // 576 zero bf16 (key-major mode: rope operand of rope-less calls)
   uint16_t* bt;           // [rows, hgc, 1088, 64] heads-innermost Q | QRope | dO (key-major mode)
   Lens lens;
   int64_t S1;             // BSND S1 / TND T1 (statistics head stride)
@@ -43,6 +46,7 @@ struct BwdArgs {
   int64_t pairs_per_launch;
   int B, N1, topk, mode3, layout_tnd, hgc;
   int bs;                 // sparseBlockSize: topk slots = index count x bs
+  int rec_chunks;         // record chunks per (row, head group): ceil(topk / 32)
   float scale;
 };
 
@@ -56,7 +60,7 @@ struct DenseArgs {
   int32_t* maxdup;        // [rows]
   int32_t* offs;          // [rows, maxblk + 1]
   int16_t* kpos;          // [rows, kstride] first sorted position of each key, -1: not selected
-  const uint16_t* dsp;    // [rows * topk, hgc, 128]
+  const uint16_t* dsp;    // [rows, hgc, rec_chunks, kRecChunk]
   const uint16_t* bt;     // [rows, hgc, 1088, 64] Q | QRope | dO with the 64 heads of a group innermost
   float* part;            // [hgc, citems, kBk, 1088]
   int32_t* flag;          // [hgc, citems]
@@ -70,6 +74,7 @@ struct DenseArgs {
   int64_t S1, S2;
   int B, N1, topk, mode3, layout_tnd, hgc, maxblk, items, citems, kstride;
   int bs;                 // sparseBlockSize: topk slots = index count x bs
+  int rec_chunks;         // record chunks per (row, head group)
   float scale;
 };
 

@@ -10,20 +10,25 @@
 // key-major kernel that forms dK = scale dS^T Q and dV = P^T dO (SparseFlashAttentionGrad
 // README, "function description", stages 1-3).
 //
-// Work split of the 4 waves (an LDS read of up to 16 bytes per lane costs the same LDS time,
-// and a transposing read delivers only 8):
-//   scores: wave w owns head tile w (heads 16 w .. 16 w + 15) over the whole contraction
-//     (512 value + 64 rope dims) for both 16-key tiles of the chunk.  Its Q and dO fragments
-//     stay in registers for the whole row; every 16-byte key fragment read from LDS feeds the
-//     S and dP MFMAs of its key tile, and no partial sums change hands.
-//   dQ: wave w owns output dims 144 w .. 144 w + 143 for all 64 heads, so each gathered key
-//     element is read (transposed) once per workgroup.
-// Key tiles are stored chunk-major in LDS ([72 chunks of 16 B][32 keys]): one direct-to-LDS
-// block (64 lanes x 16 B) is then two chunk columns of all 32 keys, so a gathering lane always
-// handles the same key (lane % 32) and each of its loads is one add to that key's row address.
-// Pipeline: key tiles are triple-buffered in LDS and gathered straight from global memory
-// one chunk ahead (global_load_lds).  The score MFMAs of chunk c and the dQ MFMAs of chunk
-// c - 1 sit in one block so that the scheduler can interleave them; one barrier per chunk.
+// Work split: 8 waves, two per SIMD, in two roles, so that one wave of every SIMD can issue
+// MFMAs while the other waits for LDS, the exponentials or its stores:
+//   score waves (0-3): wave w keeps the Q and dO fragments of heads 16 w .. 16 w + 15 for the
+//     whole contraction (512 value + 64 rope dims) in registers and, for chunk c, computes S
+//     and dP of its head tile for both 16-key tiles (every 16-byte key fragment read from LDS
+//     feeds the S and dP MFMAs of its key tile), then P and dS in registers, the chunk's dS
+//     tile in LDS ([key][head]) and the 256-byte dS | P record of every (row, key) pair.
+//   dQ waves (4-7): wave 4 + w owns output dims 144 w .. 144 w + 143 for all 64 heads (fp32
+//     accumulators across all chunks) and in step c adds dS K of chunk c - 1 (each gathered key
+//     element is read, transposed, once per workgroup); it also gathers chunk c + 2 straight
+//     from global memory into LDS (global_load_lds, 16 bytes per lane).
+// Records are stored chunk-major: per (row, head group) and chunk of 32 sorted positions, 8 KB
+// = [dS | P][head tile of 16][32 positions][16 heads] bf16, so that each record store
+// instruction of a score wave writes 512 contiguous bytes.
+// One barrier per step.  Key tiles are quadruple-buffered and gathered two chunks ahead, so a
+// gather has two steps to land; dS tiles are double-buffered.  Key tiles are stored
+// chunk-major in LDS ([72 chunks of 16 B][32 keys]): one direct-to-LDS block (64 lanes x 16 B)
+// is then two chunk columns of all 32 keys, so a gathering lane always handles the same key
+// (lane % 32) and each of its loads is one add to that key's row address.
 #include "sfag_device.h"
 #include "sfag_launch.h"
 
@@ -31,35 +36,35 @@ namespace sfag {
 
 namespace {
 constexpr int kKC = 32;
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;                    // 4 score waves + 4 dQ waves
 constexpr int kChunks = kDk / 8;                 // 72 16-byte chunks per key row (64 value + 8 rope)
 constexpr int kHtPitch = 64 + 8;                 // DSt row pitch
 constexpr int kBlocks = kChunks / 2;             // 36 direct-to-LDS blocks (2 chunk columns) per tile
-static_assert(kBlocks % 4 == 0, "gather blocks per wave");
+static_assert(kBlocks % 4 == 0, "gather blocks per dQ wave");
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kLdsK = kBlocks * 64 * 16;         // one key tile, chunk-major: [72 chunks][32 keys][16 B]
 constexpr int kLdsDS = kKC * kHtPitch * 2;       // DSt [32 keys][72]
-constexpr int kLdsTotal = 3 * kLdsK + 3 * kLdsDS + 3 * 64 * 4 + 2 * 257 * 4;
+constexpr int kLdsTotal = 4 * kLdsK + 2 * kLdsDS + 3 * 64 * 4 + 2 * 257 * 4;
 static_assert(kLdsTotal <= 160 * 1024, "LDS budget");
-// s_waitcnt operands.  kWaitVmem: vmcnt(0), expcnt and lgkmcnt at their maximum (issued just
-// before a chunk's record stores).  kWaitAllButRecords: vmcnt(4), lgkmcnt(0): at the end of a
-// chunk the only vector memory operations that can be in flight are the chunk's 4 record
-// stores, so this leaves them in flight and waits for this wave's LDS writes.
-constexpr int kWaitVmem = 0x0f70;
-constexpr int kWaitAllButRecords = 0x0074;
+// s_waitcnt operands with expcnt and lgkmcnt at zero: vmcnt(9) (all but the 9 loads of the
+// newest gather) and vmcnt(10) (all but a gather and one position load)
+constexpr int kWaitVm9 = 0x0009;
+constexpr int kWaitVm10 = 0x000a;
 }  // namespace
 
 __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
   // Separate LDS arrays (not one carved buffer): the compiler can then prove that the
   // direct-to-LDS gather into one key buffer does not alias reads of the others, and does not
   // wait for the gather before every LDS read.
-  __shared__ __attribute__((aligned(16))) uint16_t Kb0[kLdsK / 2], Kb1[kLdsK / 2], Kb2[kLdsK / 2];
-  __shared__ __attribute__((aligned(16))) uint16_t Db0[kKC * kHtPitch], Db1[kKC * kHtPitch], Db2[kKC * kHtPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t Kb0[kLdsK / 2], Kb1[kLdsK / 2], Kb2[kLdsK / 2], Kb3[kLdsK / 2];
+  __shared__ __attribute__((aligned(16))) uint16_t Db0[kKC * kHtPitch], Db1[kKC * kHtPitch];
   __shared__ __attribute__((aligned(16))) float sD[64], sM[64], sIL[64];
   __shared__ int32_t cum[2 * 257];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar
+  const bool swave = wave < 4;                      // score wave; otherwise dQ wave
+  const int rw = wave & 3;                          // index within the role
   const int g = lane >> 4, c = lane & 15;
   // longest rows (highest positions under the causal mask) first
   const int64_t row = (int64_t)gridDim.x - 1 - blockIdx.x;
@@ -82,17 +87,15 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
   const int nchunk = (count + kKC - 1) / kKC;
 
   // ---- per-row setup --------------------------------------------------------------------------
-  // gathering lanes: key slot gkey of every chunk, chunk column gcol of every block
-  const int gkey = lane & 31, gcol = lane >> 5;
-  int32_t gsv = srow[min(gkey, count - 1)];               // sorted position of chunk 0's key
-  // D = rowsum(dO * out) and the statistics of every head
+  // D = rowsum(dO * out) and the statistics of every head (8 threads per head, 64 dims each)
   {
-    const int h = threadIdx.x >> 2, part = threadIdx.x & 3;
+    const int h = threadIdx.x >> 3, part = threadIdx.x & 7;
     float d = 0.f;
     if (h < nh) {
-      const uint16_t* dor = a.dout + (row * a.N1 + h0 + h) * kDn + part * 128;
-      const uint16_t* otr = a.out + (row * a.N1 + h0 + h) * kDn + part * 128;
-      for (int e = 0; e < 128; e += 8) {
+      const uint16_t* dor = a.dout + (row * a.N1 + h0 + h) * kDn + part * 64;
+      const uint16_t* otr = a.out + (row * a.N1 + h0 + h) * kDn + part * 64;
+#pragma unroll
+      for (int e = 0; e < 64; e += 8) {
         const u32x4 x = *reinterpret_cast<const u32x4*>(dor + e);
         const u32x4 y = *reinterpret_cast<const u32x4*>(otr + e);
 #pragma unroll
@@ -104,6 +107,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
     }
     d += __shfl_xor(d, 1);
     d += __shfl_xor(d, 2);
+    d += __shfl_xor(d, 4);
     if (part == 0) {
       float m = 0.f, il = 0.f;
       if (h < nh) {
@@ -117,30 +121,6 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
       sIL[h] = il;
     }
   }
-  // Q and dO fragments of this wave, straight from global memory (A operands of S and dP:
-  // lane (g, c) holds head 16 wave + c, dims 32 ks + 8 g .. + 7; steps 16 and 17 are the rope
-  // dims); zero for padded heads
-  bf16x8 qA[18], doA[16];
-  {
-    const int h = 16 * wave + c;
-    const bool hv = h < nh;
-    const int64_t hrow = row * a.N1 + h0 + (hv ? h : 0);
-    const uint16_t* qrow = a.q + hrow * kDn + 8 * g;
-    const uint16_t* drow = a.dout + hrow * kDn + 8 * g;
-#pragma unroll
-    for (int ks = 0; ks < 16; ++ks) {
-      const bf16x8 qv = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
-      const bf16x8 dv = *reinterpret_cast<const bf16x8*>(drow + 32 * ks);
-      qA[ks] = hv ? qv : bf16x8{};
-      doA[ks] = hv ? dv : bf16x8{};
-    }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      qA[16 + ks] = bf16x8{};
-      if (hv && a.qr) qA[16 + ks] = *reinterpret_cast<const bf16x8*>(a.qr + hrow * kDr + 32 * ks + 8 * g);
-    }
-  }
-  __syncthreads();
   const float zscale = a.scale * kLog2e;
   // Loop-invariant bases, held in SGPRs: the empty asm makes them opaque, so the compiler
   // cannot re-load them from the kernel arguments inside the loop (a scalar load in flight
@@ -154,33 +134,41 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
   const uint16_t* kbase = uniform(a.k + geo.kstart * kDn);
   const bool rope = a.kr != nullptr;                // without rope inputs the rope terms are absent
   const uint16_t* krbase = uniform(rope ? a.kr + geo.kstart * kDr : a.zero_row);
-  const uint16_t* zrow = uniform(a.zero_row);
   // The record pointers lose their address space through the scalar round trip; stores through
-  // them are made global explicitly, because a generic (flat) store might hit LDS and would then
-  // wait for every direct-to-LDS gather load in flight.
+  // them are made global explicitly (a generic store might address LDS).
   typedef __attribute__((address_space(1))) uint64_t GlobalU64;
-  uint16_t* recrow = uniform(a.dsp + ((int64_t)row * a.topk * a.hgc + hg) * 128);   // slot 0 of this row
-  uint16_t* trash = uniform(a.trash);
-  const int recstride = a.hgc * 128;                                          // elements per slot
-  asm volatile("" : "+s"(kbase), "+s"(krbase), "+s"(zrow), "+s"(recrow), "+s"(trash));
+  uint16_t* recrow = uniform(a.dsp + ((int64_t)row * a.hgc + hg) * (int64_t)a.rec_chunks * kRecChunk);
+  asm volatile("" : "+s"(kbase), "+s"(krbase), "+s"(recrow));
 
-  // Gather of chunk CH (this lane's key: sorted position SV) into key buffer KS: block b of the
-  // tile holds chunk columns 2 b and 2 b + 1; wave w loads blocks w, w + 4, ..., w + 32 (the
-  // last one: rope chunks).  Slots past the row's valid count read the zero row.
+  // gathering lanes of the dQ waves: key slot gkey of every chunk, chunk column gcol of every block
+  const int gkey = lane & 31, gcol = lane >> 5;
+  // byte bases of this dQ wave's gather: value chunks 2 b, 2 b + 1 of key 0 for its blocks
+  // b = rw + 4 j, and rope chunks 2 rw, 2 rw + 1 (of the zero row without rope inputs); held as
+  // opaque scalars so that every load is one scalar base plus the lane's 32-bit offset
+  const char* kgat[kBlocks / 4 - 1];
+#pragma unroll
+  for (int j = 0; j < kBlocks / 4 - 1; ++j) {
+    kgat[j] = reinterpret_cast<const char*>(uniform(kbase + 16 * rw + 64 * j));
+    asm volatile("" : "+s"(kgat[j]));
+  }
+  const char* rgat = reinterpret_cast<const char*>(uniform(krbase + 16 * rw));
+  asm volatile("" : "+s"(rgat));
+
+  // Gather of chunk CH (this lane's key: sorted position SV) into key buffer KS (dQ waves): block
+  // b of the tile holds chunk columns 2 b and 2 b + 1; dQ wave rw loads blocks rw, rw + 4, ...,
+  // rw + 32 (the last one: rope chunks).  Slots past the row's valid count read the zero row.
 #define SFAG_GATHER_ASYNC(KS, CH, SV)                                                          \
   {                                                                                            \
-    const bool ok_ = (CH) * kKC + gkey < count;                                                \
-    const uint16_t* pk_ = ok_ ? kbase + (int64_t)(SV) * kDn : zrow;                            \
-    const uint16_t* pr_ = ok_ && rope ? krbase + (int64_t)(SV) * kDr : zrow;                   \
+    /* slots past the row's valid count repeat its last valid key (their p is 0) */           \
+    const uint32_t ko_ = (uint32_t)(SV) * (uint32_t)(kDn * 2) + gcol * 16u;                    \
+    const uint32_t ro_ = rope ? (uint32_t)(SV) * (uint32_t)(kDr * 2) + gcol * 16u : gcol * 16u; \
     _Pragma("unroll") for (int j = 0; j < kBlocks / 4; ++j) {                                  \
-      const int blk = wave + 4 * j;                                                            \
-      const uint16_t* src = j < kBlocks / 4 - 1 ? pk_ + (2 * blk + gcol) * 8                   \
-                                                : pr_ + (2 * blk + gcol - 64) * 8;             \
-      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)((KS) + blk * 512), 16, 0, 0); \
+      const char* src = j < kBlocks / 4 - 1 ? kgat[j] + ko_ : rgat + ro_;                      \
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)((KS) + (rw + 4 * j) * 512), 16, 0, 0); \
     }                                                                                          \
   }
 
-// S and dP of this wave's head tile for both key tiles of chunk buffer KS.
+// S and dP of this score wave's head tile for both key tiles of chunk buffer KS.
 #define SFAG_SCORES(KS)                                                                        \
   {                                                                                            \
     _Pragma("unroll") for (int kt = 0; kt < 2; ++kt) {                                         \
@@ -209,12 +197,9 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
       }                                                                                        \
     }                                                                                          \
     /* issue order: the first four fragments, then per step the fragments two steps ahead and \
-       the step's MFMAs.  The vector-memory slots of steps 0-8 take the sorted-position load;   \
-       the gather itself sits in its own (conditional) block before the scores: all 9 loads   \
-       issued together measured faster than spread among the MFMAs */                        \
+       the step's MFMAs */                                                                     \
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);                                         \
     _Pragma("unroll") for (int ks = 0; ks < 16; ++ks) {                                        \
-      if (ks < 9) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                           \
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                                       \
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);                                       \
     }                                                                                          \
@@ -222,34 +207,39 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
     __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                         \
   }
 
-// dQ[64 heads][144 w .. 144 w + 143] += dS[64][32 keys] K[32 keys][dims] of the previous chunk
+// dQ[64 heads][144 rw .. 144 rw + 143] += dS[64][32 keys] K[32 keys][dims] of one chunk.  A
+// operands (dS^T, heads 16 t + c) from the [key][head] tile, B operands (K, dims 144 rw + 16 nt
+// + c) from the chunk-major key tile, both by transposing reads at one per-lane offset plus
+// constants: the B fragment of column tile nt starts 512 elements after that of nt - 1.
 #define SFAG_DQ(KS, DST)                                                                       \
   {                                                                                            \
+    const uint16_t* kq_ = (KS) + kqoff;                                                        \
+    const uint16_t* dq_ = (DST) + dsoff;                                                       \
     bf16x8 dsa[4];                                                                             \
-    _Pragma("unroll") for (int t = 0; t < 4; ++t) dsa[t] = lds_frag_trp((DST), 0, 16 * t, kHtPitch, lane); \
-    bf16x8 kb = lds_frag_tr_cm((KS), 144 * wave, lane);                                        \
+    _Pragma("unroll") for (int t = 0; t < 4; ++t) dsa[t] = tr_frag(dq_ + 16 * t, 4 * kHtPitch); \
+    bf16x8 kb = tr_frag(kq_, 32);                                                              \
     _Pragma("unroll") for (int nt = 0; nt < 9; ++nt) {                                         \
       bf16x8 nb = kb;                                                                          \
-      if (nt < 8) nb = lds_frag_tr_cm((KS), 144 * wave + 16 * (nt + 1), lane);                 \
+      if (nt < 8) nb = tr_frag(kq_ + 512 * (nt + 1), 32);                                      \
       _Pragma("unroll") for (int t = 0; t < 4; ++t) dqacc[t][nt] = mfma(dsa[t], kb, dqacc[t][nt]); \
       kb = nb;                                                                                 \
     }                                                                                          \
   }
 
-// P and dS of this wave's head tile for both key tiles: records and the DSt tile of this
-// chunk.  Every lane issues exactly 4 record stores (invalid slots write to the sink), so that
-// the end-of-chunk wait can leave them in flight.
+// P and dS of this score wave's head tile for both key tiles: the DSt tile of this chunk and the
+// chunk's records (positions past the valid count get p = dS = 0).  Lane (g, c) stores heads
+// 16 rw + 4 g .. + 3 of position 16 kt + c at ((rw * 32 + 16 kt + c) * 16 + 4 g) of each half.
 #define SFAG_FINISH(CI, DST)                                                                   \
   {                                                                                            \
     const int c0 = (CI) * kKC;                                                                 \
-    const int hcol = 16 * wave + 4 * g;          /* heads hcol .. hcol + 3 */                   \
+    const int hcol = 16 * rw + 4 * g;            /* heads hcol .. hcol + 3 */                   \
     const f32x4 mv = *reinterpret_cast<const f32x4*>(sM + hcol);                               \
     const f32x4 iv = *reinterpret_cast<const f32x4*>(sIL + hcol);                              \
     const f32x4 dv = *reinterpret_cast<const f32x4*>(sD + hcol);                               \
+    uint16_t* rec = recrow + (int64_t)(CI) * kRecChunk + (rw * kKC + c) * 16 + 4 * g;          \
     _Pragma("unroll") for (int kt = 0; kt < 2; ++kt) {                                         \
       const int key = 16 * kt + c;                                                             \
       const bool valid = c0 + key < count;                                                     \
-      uint16_t* rec = valid ? recrow + (int64_t)(c0 + key) * recstride : trash;                \
       float p[4], ds[4];                                                                       \
       _Pragma("unroll") for (int v = 0; v < 4; ++v) {                                          \
         /* v_exp_f32: results below 2^-126 flush to 0, far under bf16 resolution here */       \
@@ -260,119 +250,176 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
       const uint32_t pw[2] = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};               \
       const uint32_t dw[2] = {pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3])};           \
       *reinterpret_cast<uint2*>((DST) + key * kHtPitch + hcol) = make_uint2(dw[0], dw[1]);     \
-      /* the next chunk's gather is in before any record store is issued */                    \
-      if (kt == 0) __builtin_amdgcn_s_waitcnt(kWaitVmem);                                      \
-      *(GlobalU64*)(rec + hcol) = ((uint64_t)dw[1] << 32) | dw[0];                             \
-      *(GlobalU64*)(rec + 64 + hcol) = ((uint64_t)pw[1] << 32) | pw[0];                        \
+      *(GlobalU64*)(rec + 16 * 16 * kt) = ((uint64_t)dw[1] << 32) | dw[0];                     \
+      *(GlobalU64*)(rec + kRecHalf + 16 * 16 * kt) = ((uint64_t)pw[1] << 32) | pw[0];          \
     }                                                                                          \
   }
 
-  f32x4 sacc[2], pacc[2];
-  f32x4 dqacc[4][9];
+  // Steps 0 .. nchunk.  In step ci the score waves take chunk ci and the dQ waves gather chunk
+  // ci + 2 and add dQ of chunk ci - 1.  Chunk ci lives in key buffer ci % 4 and dS buffer ci % 2,
+  // so the loops are unrolled by 4 and every access names its buffer.  The two roles run
+  // separate loops (their register sets are never live together) with one barrier per step.
+  if (swave) {
+    // Q and dO fragments straight from global memory (A operands of S and dP: lane (g, c) holds
+    // head 16 rw + c, dims 32 ks + 8 g .. + 7; steps 16 and 17 are the rope dims); zero for
+    // padded heads
+    bf16x8 qA[18], doA[16];
+    {
+      const int h = 16 * rw + c;
+      const bool hv = h < nh;
+      const int64_t hrow = row * a.N1 + h0 + (hv ? h : 0);
+      const uint16_t* qrow = a.q + hrow * kDn + 8 * g;
+      const uint16_t* drow = a.dout + hrow * kDn + 8 * g;
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int nt = 0; nt < 9; ++nt) dqacc[t][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  SFAG_GATHER_ASYNC(Kb0, 0, gsv)
-  gsv = srow[min(kKC + gkey, count - 1)];                 // chunk 1
-
-  // The row's Q | QRope | dO with the 64 heads innermost (bt[row][hg][col][h]), the key-major
-  // kernel's B operand, written from the fragments already in registers.  Per 64-column block
-  // (two steps of every wave) the [64 heads][64 cols] tile goes through LDS (pitch 72, the
-  // key buffers 1 and 2 in turn, unused until the loop) and comes back by transposing reads:
-  // lane (g, c) of wave w stores heads 32 s + 8 g .. + 7 of column 64 k + 16 w + c.
-  {
-    uint16_t* bto = a.bt + ((int64_t)row * a.hgc + hg) * (int64_t)kDacc * 64;
-    const int hrow = 16 * wave + c;
-#pragma unroll
-    for (int k = 0; k < kDacc / 64; ++k) {
-      uint16_t* t = (k & 1) ? Kb2 : Kb1;
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int ks = 2 * k + j;                         // 32-column step over Q | QRope | dO
-        const bf16x8 v = ks < 18 ? qA[ks] : doA[ks - 18];
-        *reinterpret_cast<bf16x8*>(t + hrow * 72 + 32 * j + 8 * g) = v;
+      for (int ks = 0; ks < 16; ++ks) {
+        const bf16x8 qv = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
+        const bf16x8 dv = *reinterpret_cast<const bf16x8*>(drow + 32 * ks);
+        qA[ks] = hv ? qv : bf16x8{};
+        doA[ks] = hv ? dv : bf16x8{};
       }
-      lds_barrier();
 #pragma unroll
-      for (int sh = 0; sh < 2; ++sh) {
-        const bf16x8 v = lds_frag_trp(t, 32 * sh, 16 * wave, 72, lane);
-        *reinterpret_cast<bf16x8*>(bto + (64 * k + 16 * wave + c) * 64 + 32 * sh + 8 * g) = v;
+      for (int ks = 0; ks < 2; ++ks) {
+        qA[16 + ks] = bf16x8{};
+        if (hv && a.qr) qA[16 + ks] = *reinterpret_cast<const bf16x8*>(a.qr + hrow * kDr + 32 * ks + 8 * g);
       }
     }
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-
-// One chunk CI: gather of chunk CI + 1 into KN, scores of chunk CI (buffer KC), dQ of chunk
-// CI - 1 (buffers KP, DP; skipped for chunk 0), finish into DC.  The sorted position
-// of this lane's key of chunk CI + 2 is loaded branch-free and only used after the
-// end-of-chunk wait.
-#define SFAG_CHUNK(CI, KC, KP, KN, DC, DP, WITH_DQ)                                            \
+    // The row's Q | QRope | dO with the 64 heads innermost (bt[row][hg][col][h]), the key-major
+    // kernel's B operand, written from the fragments already in registers.  Per 64-column block
+    // (two steps of every score wave) the [64 heads][64 cols] tile goes through LDS (pitch 72,
+    // key buffers 2 and 3 in turn, unused until the loop) and comes back by transposing reads:
+    // lane (g, c) of score wave w stores heads 32 s + 8 g .. + 7 of column 64 k + 16 w + c.  The
+    // dQ waves pass the same number of barriers meanwhile.  These stores drain during the loop.
+    {
+      uint16_t* bto = a.bt + ((int64_t)row * a.hgc + hg) * (int64_t)kDacc * 64;
+      const int hrow = 16 * rw + c;
+#pragma unroll
+      for (int k = 0; k < kDacc / 64; ++k) {
+        uint16_t* t = (k & 1) ? Kb3 : Kb2;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int ks = 2 * k + j;                       // 32-column step over Q | QRope | dO
+          const bf16x8 v = ks < 18 ? qA[ks] : doA[ks - 18];
+          *reinterpret_cast<bf16x8*>(t + hrow * 72 + 32 * j + 8 * g) = v;
+        }
+        lds_barrier();
+#pragma unroll
+        for (int sh = 0; sh < 2; ++sh) {
+          const bf16x8 v = lds_frag_trp(t, 32 * sh, 16 * rw, 72, lane);
+          *reinterpret_cast<bf16x8*>(bto + (64 * k + 16 * rw + c) * 64 + 32 * sh + 8 * g) = v;
+        }
+      }
+    }
+    lds_barrier();
+    f32x4 sacc[2], pacc[2];
+// Score step CI on key buffer KC and dS buffer DC; ends by waiting for this wave's LDS accesses
+// (the record stores stay in flight).
+#define SFAG_SSTEP(CI, KC, DC)                                                                 \
   {                                                                                            \
-    const int ci_ = (CI);                                                                      \
-    if (ci_ + 1 < nchunk) SFAG_GATHER_ASYNC(KN, ci_ + 1, gsv)                                  \
-    const int32_t sv = srow[min((ci_ + 2) * kKC + gkey, count - 1)];                           \
-    SFAG_SCORES(KC)                                                                            \
-    if (WITH_DQ) SFAG_DQ(KP, DP)                                                               \
-    SFAG_FINISH(ci_, DC)                                                                       \
-    /* everything but the 4 record stores just issued */                                      \
-    __builtin_amdgcn_s_waitcnt(kWaitAllButRecords);                                            \
-    gsv = sv;                                                                                  \
-    /* a plain barrier: the data exchanged is in LDS, and a release fence would also wait for  \
-       the record stores */                                                                    \
+    if ((CI) < nchunk) {                                                                       \
+      SFAG_SCORES(KC)                                                                          \
+      SFAG_FINISH(CI, DC)                                                                      \
+    }                                                                                          \
+    lds_barrier();                                                                             \
+  }
+    int ci = 0;
+    for (; ci + 3 <= nchunk; ci += 4) {
+      SFAG_SSTEP(ci, Kb0, Db0)
+      SFAG_SSTEP(ci + 1, Kb1, Db1)
+      SFAG_SSTEP(ci + 2, Kb2, Db0)
+      SFAG_SSTEP(ci + 3, Kb3, Db1)
+    }
+    if (ci <= nchunk) {
+      SFAG_SSTEP(ci, Kb0, Db0)
+      ++ci;
+    }
+    if (ci <= nchunk) {
+      SFAG_SSTEP(ci, Kb1, Db1)
+      ++ci;
+    }
+    if (ci <= nchunk) SFAG_SSTEP(ci, Kb2, Db0)
+#undef SFAG_SSTEP
+  } else {
+    // chunks 0 and 1 in flight before the score waves' copy of Q | QRope | dO; the position of
+    // chunk 2's key is loaded too.  Loads complete in order, so vmcnt(10) leaves chunk 1's gather
+    // and that position load outstanding.
+    int32_t gsv = srow[min(gkey, count - 1)];
+    SFAG_GATHER_ASYNC(Kb0, 0, gsv)
+    gsv = srow[min(kKC + gkey, count - 1)];
+    if (1 < nchunk) SFAG_GATHER_ASYNC(Kb1, 1, gsv)
+    gsv = srow[min(2 * kKC + gkey, count - 1)];
+    for (int k = 0; k < kDacc / 64; ++k) lds_barrier();   // the score waves' copy of Q | QRope | dO
+    asm volatile("" ::: "memory");
+    if (1 < nchunk) __builtin_amdgcn_s_waitcnt(kWaitVm10);
+    else __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    // transposing-read lane offsets: K tile (chunk-major, element (key k, dim n) at
+    // ((n / 8) * 32 + k) * 8 + n % 8; lane (g, c) of a read pair points at key 8 g + c / 4 and dim
+    // 144 rw + 4 (c % 4)) and dS tile ([key][head], pitch 72; key 8 g + c / 4, head 4 (c % 4))
+    const int kqoff = ((18 * rw + ((c & 3) >> 1)) * kKC + 8 * g + (c >> 2)) * 8 + 4 * (c & 1);
+    const int dsoff = (8 * g + (c >> 2)) * kHtPitch + 4 * (c & 3);
+    f32x4 dqacc[4][9];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int nt = 0; nt < 9; ++nt) dqacc[t][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+// dQ step CI: the position of chunk CI + 3's key, the gather of chunk CI + 2 into KN, dQ of chunk
+// CI - 1 from KP / DP.  Ends by waiting for chunk CI + 1's gather (issued a step earlier) and the
+// position load, leaving this step's gather in flight, and for the LDS reads.
+#define SFAG_QSTEP(CI, KP, KN, DP)                                                             \
+  {                                                                                            \
+    const int32_t sv = srow[min(((CI) + 3) * kKC + gkey, count - 1)];                          \
+    const bool gath = (CI) + 2 < nchunk;                                                       \
+    if (gath) SFAG_GATHER_ASYNC(KN, (CI) + 2, gsv)                                             \
+    if ((CI) >= 1) SFAG_DQ(KP, DP)                                                             \
     asm volatile("" ::: "memory");                                                             \
+    if (gath) __builtin_amdgcn_s_waitcnt(kWaitVm9);                                            \
+    else __builtin_amdgcn_s_waitcnt(0);                                                        \
+    gsv = sv;                                                                                  \
     __builtin_amdgcn_s_barrier();                                                              \
     asm volatile("" ::: "memory");                                                             \
   }
+    int ci = 0;
+    for (; ci + 3 <= nchunk; ci += 4) {
+      SFAG_QSTEP(ci, Kb3, Kb2, Db1)
+      SFAG_QSTEP(ci + 1, Kb0, Kb3, Db0)
+      SFAG_QSTEP(ci + 2, Kb1, Kb0, Db1)
+      SFAG_QSTEP(ci + 3, Kb2, Kb1, Db0)
+    }
+    if (ci <= nchunk) {
+      SFAG_QSTEP(ci, Kb3, Kb2, Db1)
+      ++ci;
+    }
+    if (ci <= nchunk) {
+      SFAG_QSTEP(ci, Kb0, Kb3, Db0)
+      ++ci;
+    }
+    if (ci <= nchunk) SFAG_QSTEP(ci, Kb1, Kb0, Db1)
+#undef SFAG_QSTEP
 
-  SFAG_CHUNK(0, Kb0, Kb2, Kb1, Db0, Db2, false)
-  // chunk ci lives in key / dS buffers ci % 3; unrolled by 3 so every access names its buffer
-  int ci = 1;
-  for (; ci + 2 < nchunk; ci += 3) {
-    SFAG_CHUNK(ci, Kb1, Kb0, Kb2, Db1, Db0, true)
-    SFAG_CHUNK(ci + 1, Kb2, Kb1, Kb0, Db2, Db1, true)
-    SFAG_CHUNK(ci + 2, Kb0, Kb2, Kb1, Db0, Db2, true)
-  }
-  if (ci < nchunk) {
-    SFAG_CHUNK(ci, Kb1, Kb0, Kb2, Db1, Db0, true)
-    ++ci;
-  }
-  if (ci < nchunk) {
-    SFAG_CHUNK(ci, Kb2, Kb1, Kb0, Db2, Db1, true)
-    ++ci;
-  }
-  // dQ of the last chunk
-  switch ((nchunk - 1) % 3) {
-    case 0: SFAG_DQ(Kb0, Db0) break;
-    case 1: SFAG_DQ(Kb1, Db1) break;
-    default: SFAG_DQ(Kb2, Db2) break;
+    // ---- dQ / dQRope out: lane holds heads 16 t + 4 g + v, dims 144 rw + 16 nt + c ----------------
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int h = 16 * t + 4 * g + v;
+        if (h >= nh) continue;
+        const int64_t hh2 = row * a.N1 + h0 + h;
+#pragma unroll
+        for (int nt = 0; nt < 9; ++nt) {
+          const int col = 144 * rw + 16 * nt + c;
+          const uint16_t bv = f2bf(dqacc[t][nt][v] * a.scale);
+          if (col < kDn) a.dq[hh2 * kDn + col] = bv;
+          else if (a.dqr) a.dqr[hh2 * kDr + col - kDn] = bv;
+        }
+      }
+    }
   }
 
 #undef SFAG_GATHER_ASYNC
 #undef SFAG_SCORES
 #undef SFAG_DQ
 #undef SFAG_FINISH
-#undef SFAG_CHUNK
-
-  // ---- dQ / dQRope out: lane holds heads 16 t + 4 g + v, dims 144 w + 16 nt + c ------------------
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int h = 16 * t + 4 * g + v;
-      if (h >= nh) continue;
-      const int64_t hh2 = row * a.N1 + h0 + h;
-#pragma unroll
-      for (int nt = 0; nt < 9; ++nt) {
-        const int col = 144 * wave + 16 * nt + c;
-        const uint16_t bv = f2bf(dqacc[t][nt][v] * a.scale);
-        if (col < kDn) a.dq[hh2 * kDn + col] = bv;
-        else if (a.dqr) a.dqr[hh2 * kDr + col - kDn] = bv;
-      }
-    }
-  }
 }
 
 hipError_t launch_bwd_q(const BwdArgs& a, int64_t nrows, int hg_count, hipStream_t st) {
