@@ -339,18 +339,18 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
     if (ci <= nchunk) SFAG_SSTEP(ci, Kb2, Db0)
 #undef SFAG_SSTEP
   } else {
-    // chunks 0 and 1 in flight before the score waves' copy of Q | QRope | dO; the position of
-    // chunk 2's key is loaded too.  Loads complete in order, so vmcnt(10) leaves chunk 1's gather
-    // and that position load outstanding.
+    // chunks 0 and 1 in flight before the score waves' copy of Q | QRope | dO (chunk 1 repeats
+    // chunk 0's last position when the row has one chunk); the position of chunk 2's key is
+    // loaded too.  Loads complete in order, so vmcnt(10) leaves chunk 1's gather and that position
+    // load outstanding.
     int32_t gsv = srow[min(gkey, count - 1)];
     SFAG_GATHER_ASYNC(Kb0, 0, gsv)
     gsv = srow[min(kKC + gkey, count - 1)];
-    if (1 < nchunk) SFAG_GATHER_ASYNC(Kb1, 1, gsv)
+    SFAG_GATHER_ASYNC(Kb1, 1, gsv)
     gsv = srow[min(2 * kKC + gkey, count - 1)];
     for (int k = 0; k < kDacc / 64; ++k) lds_barrier();   // the score waves' copy of Q | QRope | dO
     asm volatile("" ::: "memory");
-    if (1 < nchunk) __builtin_amdgcn_s_waitcnt(kWaitVm10);
-    else __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_waitcnt(kWaitVm10);
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     // transposing-read lane offsets: K tile (chunk-major, element (key k, dim n) at
@@ -365,16 +365,19 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
       for (int nt = 0; nt < 9; ++nt) dqacc[t][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 // dQ step CI: the position of chunk CI + 3's key, the gather of chunk CI + 2 into KN, dQ of chunk
 // CI - 1 from KP / DP.  Ends by waiting for chunk CI + 1's gather (issued a step earlier) and the
-// position load, leaving this step's gather in flight, and for the LDS reads.
+// position load, leaving this step's gather in flight, and for the LDS reads.  Every step issues
+// the same vector memory operations (past the last chunk the gather repeats the row's last
+// position into the free buffer KN), so that one wait count fits all and the compiler's own
+// wait analysis sees the same pattern on every path.
 #define SFAG_QSTEP(CI, KP, KN, DP)                                                             \
   {                                                                                            \
     const int32_t sv = srow[min(((CI) + 3) * kKC + gkey, count - 1)];                          \
-    const bool gath = (CI) + 2 < nchunk;                                                       \
-    if (gath) SFAG_GATHER_ASYNC(KN, (CI) + 2, gsv)                                             \
+    /* the position load must be issued before the gather for the wait count below */          \
+    asm volatile("" ::: "memory");                                                             \
+    SFAG_GATHER_ASYNC(KN, (CI) + 2, gsv)                                                       \
     if ((CI) >= 1) SFAG_DQ(KP, DP)                                                             \
     asm volatile("" ::: "memory");                                                             \
-    if (gath) __builtin_amdgcn_s_waitcnt(kWaitVm9);                                            \
-    else __builtin_amdgcn_s_waitcnt(0);                                                        \
+    __builtin_amdgcn_s_waitcnt(kWaitVm9);                                                      \
     gsv = sv;                                                                                  \
     __builtin_amdgcn_s_barrier();                                                              \
     asm volatile("" ::: "memory");                                                             \
@@ -396,6 +399,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
     }
     if (ci <= nchunk) SFAG_QSTEP(ci, Kb1, Kb0, Db1)
 #undef SFAG_QSTEP
+    __builtin_amdgcn_s_waitcnt(0);                        // no gather may still write LDS at exit
 
     // ---- dQ / dQRope out: lane holds heads 16 t + 4 g + v, dims 144 rw + 16 nt + c ----------------
 #pragma unroll
