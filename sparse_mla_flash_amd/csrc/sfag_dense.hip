@@ -311,64 +311,71 @@ __device__ __forceinline__ void kv_dense_units(const DenseArgs& a, const KvCtx& 
   int ri = 0, L = 0;
   i16x4 mc;                                          // map of the current unit's row
   u32x4 bs[kBLoads];
+  bf16x8 f[4][2];                                    // A fragments: [key tile][head step]
+  // records of unit (row R, layer LL, map MP), head step KS, into f[*][KS] (zero where the row
+  // did not select the key)
+#define KV_REC_LOAD(R, LL, MP, KS)                                                             \
+  {                                                                                            \
+    const uint16_t* rb_ = rec_base + (row0 + (R)) * rec_row + 8 * (KS);                        \
+    _Pragma("unroll") for (int kt = 0; kt < 4; ++kt) {                                         \
+      int e = MP[kt];                                                                          \
+      bool ok = e >= 0;                                                                        \
+      if (DUPS && (LL) > 0) {                                                                  \
+        e += (LL);                                                                             \
+        ok = ok && e < a.topk && a.sorted[(row0 + (R)) * a.topk + min(e, a.topk - 1)] == kmap + 16 * kt; \
+      }                                                                                        \
+      f[kt][KS] = bf16x8{};                                                                    \
+      if (ok)                                                                                  \
+        f[kt][KS] = *reinterpret_cast<const bf16x8*>(rb_ + (uint32_t)(e >> 5) * (uint32_t)kRecChunk + (uint32_t)(e & 31) * 16u); \
+    }                                                                                          \
+  }
   {
     const int r0 = __builtin_amdgcn_readfirstlane((int)s_row[0]);
     KV_MAP_LOAD(mc, r0)
     KV_B_LOAD(bs, r0)
     KV_B_STORE(Bt0, bs)
+    KV_REC_LOAD(r0, 0, mc, 0)
+    KV_REC_LOAD(r0, 0, mc, 1)
   }
   lds_barrier();
 
+  // Unit loop.  The MFMAs of a unit run head step by head step (all column tiles with the first
+  // head step's A fragments, then all with the second), so that the registers of the first head
+  // step are free halfway: the next unit's first-half records are requested there, its second
+  // half at the end of the unit, each with the other half-unit (and the other workgroup) to land.
   for (int u = 0; ri < nrows; ++u) {
     uint16_t* BC = (u & 1) ? Bt1 : Bt0;
     uint16_t* BN = (u & 1) ? Bt0 : Bt1;
-    const int r = __builtin_amdgcn_readfirstlane((int)s_row[ri]);
     int ri2 = ri, L2 = L;
     advance(ri2, L2);
+    const bool more = ri2 < nrows;
     const int rn = __builtin_amdgcn_readfirstlane((int)s_row[min(ri2, nrows - 1)]);
-    // records of this unit (layer L: the L-th occurrence of each key)
-    const uint16_t* rb = rec_base + (row0 + r) * rec_row;
-    bf16x8 f[4][2];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      int e = mc[kt];
-      bool ok = e >= 0;
-      if (DUPS && L > 0) {
-        e += L;
-        ok = ok && e < a.topk && a.sorted[(row0 + r) * a.topk + min(e, a.topk - 1)] == kmap + 16 * kt;
-      }
-      f[kt][0] = bf16x8{};
-      f[kt][1] = bf16x8{};
-      if (ok) {
-        const uint16_t* src = rb + (uint32_t)(e >> 5) * (uint32_t)kRecChunk + (uint32_t)(e & 31) * 16u;
-        f[kt][0] = *reinterpret_cast<const bf16x8*>(src);
-        f[kt][1] = *reinterpret_cast<const bf16x8*>(src + 8);
-      }
-    }
     i16x4 mn;
     KV_MAP_LOAD(mn, rn)
     KV_B_LOAD(bs, rn)
-    {
-      bf16x8 bq[kQ];
-      bq[0] = KV_BFRAG(BC, 0);
-      bq[1] = KV_BFRAG(BC, 1);
-      bq[2] = KV_BFRAG(BC, 2);
+    bf16x8 bq[NFT];
 #pragma unroll
-      for (int q = 0; q < kQ; ++q) {
-        if (q + 3 < kQ) bq[q + 3] = KV_BFRAG(BC, q + 3);
-        const int ft = q >> 1, ks = q & 1;
+    for (int ks = 0; ks < 2; ++ks) {
+      bq[0] = KV_BFRAG(BC, ks);
+      bq[1] = KV_BFRAG(BC, 2 + ks);
+      bq[2] = KV_BFRAG(BC, 4 + ks);
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) acc[kt][ft] = mfma(f[kt][ks], bq[q], acc[kt][ft]);
+      for (int ft = 0; ft < NFT; ++ft) {
+        if (ft + 3 < NFT) bq[ft + 3] = KV_BFRAG(BC, 2 * (ft + 3) + ks);
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) acc[kt][ft] = mfma(f[kt][ks], bq[ft], acc[kt][ft]);
       }
-      // issue order: the next unit's map and B tile loads, three fragments, then (fragment
-      // three steps ahead, 4 MFMAs) pairs
-      __builtin_amdgcn_sched_group_barrier(0x020, kBLoads + 1, 0);
+      // issue order: (ks 0: the next unit's map and B tile loads), three fragments, then
+      // (fragment three tiles ahead, 4 MFMAs) per column tile
+      if (ks == 0) __builtin_amdgcn_sched_group_barrier(0x020, kBLoads + 4, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
 #pragma unroll
-      for (int q = 0; q < kQ; ++q) {
-        if (q + 3 < kQ) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      for (int ft = 0; ft < NFT; ++ft) {
+        if (ft + 3 < NFT) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
       }
+      // this head step's fragments are consumed: request the next unit's
+      if (more) KV_REC_LOAD(rn, L2, mn, ks)
     }
     KV_B_STORE(BN, bs)
     lds_barrier();
@@ -376,6 +383,7 @@ __device__ __forceinline__ void kv_dense_units(const DenseArgs& a, const KvCtx& 
     ri = ri2;
     L = L2;
   }
+#undef KV_REC_LOAD
 #undef KV_BFRAG
 #undef KV_B_STORE
 #undef KV_B_LOAD
