@@ -39,9 +39,9 @@ constexpr int64_t kMaxSeq = 131072;           // S1, S2 up to 128K
 constexpr int64_t kMaxTopk = 131072;
 constexpr int kDacc = 1088;                   // fp32 accumulator row: dK 512 | dKRope 64 | dV 512
 constexpr uint64_t kAlign = 256;
-// per-launch budget of the deterministic partial buffer; the row chunk it implies depends
-// only on the shape, so the summation order (and the result) is fixed for a given shape
-constexpr uint64_t kPartialBudget = 4ull << 30;
+// per-chunk budget of the per-pair path's fp32 partials; the row chunk it implies depends only
+// on the shape, so the summation order (and the result) is fixed for a given shape
+constexpr uint64_t kPartialBudget = 8ull << 30;
 
 uint64_t align_up(uint64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -53,18 +53,18 @@ struct Plan {
   int mode3 = 0, det = 0, hg_count = 0;
   float scale = 0.f;
   sfag::Lens lens;                 // per-batch valid lengths
-  // path: key-major dense-masked dK / dV (dense = 1) or per-pair scatter (dense = 0)
+  // path: key-major dense-masked dK / dV (dense = 1) or per-pair partials (dense = 0)
   int dense = 0;
   double waste = 0.0;              // dense-masked (row, key) entries per valid pair (upper bound)
   int64_t items = 0, citems = 0, maxblk = 0;
   int64_t rec_chunks = 0;          // record chunks of 32 positions per (row, head group)
   // workspace layout
-  uint64_t off_acc = 0, off_partial = 0, off_keys0 = 0, off_keys1 = 0, off_sorttmp = 0;
+  uint64_t off_acc = 0, off_keyb = 0, off_rowoff = 0, off_btotal = 0, off_bbase = 0;
   uint64_t off_sorted = 0, off_count = 0, off_maxdup = 0, off_offs = 0, off_dsp = 0, off_part = 0, off_flag = 0;
   uint64_t off_zero = 0, off_ilist = 0, off_imap = 0, off_kpos = 0, off_bt = 0;
-  uint64_t sort_tmp_bytes = 0, bytes = 0;
-  int64_t det_rows = 0;            // query rows per deterministic launch
-  int end_bit = 64;
+  uint64_t bytes = 0;
+  int64_t chunk_rows = 0;          // per-pair path: query rows per chunk
+  int64_t pair_blocks = 0;         // per-pair path: key blocks of 256 the reduce covers
 };
 
 // Rows x candidate keys the key-major kernels visit vs. the most pairs the rows can hold:
@@ -193,15 +193,31 @@ sfag_status make_plan(const sfag_dims* dims, const int32_t* sq, const int32_t* s
     if (std::strcmp(f, "scatter") == 0) p->dense = 0;
   }
   uint64_t off = 0;
+  int64_t maxblk = 0;
+  for (int64_t b = 0; b < p->B; ++b) maxblk = std::max<int64_t>(maxblk, (p->lens.lkv[b] + sfag::kBk - 1) / sfag::kBk);
+  p->maxblk = maxblk;
+  p->rec_chunks = (p->topk + 31) / 32;
+  // shared by both paths: sorted positions, counts, repeat counts, block starts, zero row
+  const uint64_t pairs = (uint64_t)p->rows * p->topk;
+  p->off_sorted = off;
+  off = align_up(off + pairs * 4);
+  p->off_count = off;
+  off = align_up(off + (uint64_t)p->rows * 4);
+  p->off_maxdup = off;
+  off = align_up(off + (uint64_t)p->rows * 4);
+  p->off_offs = off;
+  off = align_up(off + (uint64_t)p->rows * (maxblk + 1) * 4);
+  p->off_zero = off;
+  off = align_up(off + 576 * 2);
+  const uint64_t rec_row = (uint64_t)p->hg_count * p->rec_chunks * sfag::kRecChunk * 2;   // records per row
+  const uint64_t bt_row = (uint64_t)p->hg_count * kDacc * 64 * 2;                         // Q | QRope | dO copy
   if (p->dense) {
-    int64_t items = 0, maxblk = 0;
+    int64_t items = 0;
     for (int64_t b = 0; b < p->B; ++b) {
       const int64_t nblk = (p->lens.lkv[b] + sfag::kBk - 1) / sfag::kBk;
       items += nblk * ((p->lens.lq[b] + sfag::kSegRows - 1) / sfag::kSegRows);
-      maxblk = std::max(maxblk, nblk);
     }
     p->items = items;
-    p->maxblk = maxblk;
     // live items: the key blocks of a row segment that the causal mask leaves reachable form a
     // prefix of the segment's blocks (same rule as the device-side list)
     int64_t citems = 0;
@@ -219,20 +235,10 @@ sfag_status make_plan(const sfag_dims* dims, const int32_t* sq, const int32_t* s
       }
     }
     p->citems = citems;
-    const uint64_t pairs = (uint64_t)p->rows * p->topk;
-    p->off_sorted = off;
-    off = align_up(off + pairs * 4);
-    p->off_count = off;
-    off = align_up(off + (uint64_t)p->rows * 4);
-    p->off_maxdup = off;
-    off = align_up(off + (uint64_t)p->rows * 4);
-    p->off_offs = off;
-    off = align_up(off + (uint64_t)p->rows * (maxblk + 1) * 4);
     p->off_kpos = off;
     off = align_up(off + (uint64_t)p->rows * maxblk * sfag::kBk * 2);
-    p->rec_chunks = (p->topk + 31) / 32;
     p->off_dsp = off;
-    off = align_up(off + (uint64_t)p->rows * p->hg_count * p->rec_chunks * sfag::kRecChunk * 2);
+    off = align_up(off + (uint64_t)p->rows * rec_row);
     p->off_part = off;
     off = align_up(off + (uint64_t)p->hg_count * citems * sfag::kBk * kDacc * 4);
     p->off_flag = off;
@@ -241,37 +247,36 @@ sfag_status make_plan(const sfag_dims* dims, const int32_t* sq, const int32_t* s
     off = align_up(off + (uint64_t)std::max<int64_t>(citems, 1) * 4);
     p->off_imap = off;
     off = align_up(off + (uint64_t)std::max<int64_t>(items, 1) * 4);
-    p->off_zero = off;
-    off = align_up(off + 576 * 2);
     p->off_bt = off;                    // Q | QRope | dO, heads innermost (key-major B operand)
-    off = align_up(off + (uint64_t)p->rows * p->hg_count * kDacc * 64 * 2);
+    off = align_up(off + (uint64_t)p->rows * bt_row);
     p->bytes = off;
     return SFAG_OK;
   }
+  // per-pair path: rows in chunks whose fp32 partials fit the budget
+  const uint64_t part_row = (uint64_t)p->topk * kDacc * 4;
+  int64_t r = (int64_t)(kPartialBudget / part_row);
+  r = std::max<int64_t>(1, std::min<int64_t>(r, p->rows));
+  p->chunk_rows = r;
+  int64_t nblocks = 0;
+  for (int64_t b = 0; b < p->B; ++b)
+    nblocks += ((p->tnd ? p->lens.lkv[b] : p->S2) + sfag::kBk - 1) / sfag::kBk;
+  p->pair_blocks = nblocks;
   p->off_acc = off;
-  off = align_up(off + (uint64_t)p->keys * kDacc * sizeof(float));
-  if (det) {
-    const uint64_t per_row = (uint64_t)p->hg_count * p->topk * kDacc * sizeof(float);
-    int64_t r = (int64_t)(kPartialBudget / per_row);
-    if (r < 1) r = 1;
-    if (r > p->rows) r = p->rows;
-    // the sort takes an int item count
-    while (r > 1 && r * p->topk > (int64_t)INT32_MAX / 2) r /= 2;
-    p->det_rows = r;
-    p->off_partial = off;
-    off = align_up(off + (uint64_t)r * per_row);
-    const uint64_t npairs = (uint64_t)r * p->topk;
-    p->off_keys0 = off;
-    off = align_up(off + npairs * sizeof(uint64_t));
-    p->off_keys1 = off;
-    off = align_up(off + npairs * sizeof(uint64_t));
-    int bits = 1;
-    while (((int64_t)1 << bits) < p->keys + 1) ++bits;
-    p->end_bit = 32 + bits;
-    p->sort_tmp_bytes = sfag::sort_temp_bytes((int64_t)npairs, p->end_bit);
-    p->off_sorttmp = off;
-    off = align_up(off + p->sort_tmp_bytes);
-  }
+  off = align_up(off + (uint64_t)p->keys * kDacc * 4);
+  p->off_dsp = off;
+  off = align_up(off + (uint64_t)r * rec_row);
+  p->off_bt = off;
+  off = align_up(off + (uint64_t)r * bt_row);
+  p->off_part = off;
+  off = align_up(off + (uint64_t)r * part_row);
+  p->off_keyb = off;
+  off = align_up(off + (uint64_t)r * p->topk);
+  p->off_rowoff = off;
+  off = align_up(off + (uint64_t)r * std::max<int64_t>(maxblk, 1) * 4);
+  p->off_btotal = off;
+  off = align_up(off + (uint64_t)std::max<int64_t>(nblocks, 1) * 4);
+  p->off_bbase = off;
+  off = align_up(off + (uint64_t)(nblocks + 1) * 4);
   p->bytes = off;
   return SFAG_OK;
 }
@@ -288,8 +293,7 @@ hipError_t g_attr_err = hipSuccess;
 
 sfag_status init_device() {
   std::call_once(g_attr_once, [] {
-    g_attr_err = sfag::set_bwd_attributes();
-    if (g_attr_err == hipSuccess) g_attr_err = sfag::set_fwd_attributes();
+    g_attr_err = sfag::set_fwd_attributes();
     if (g_attr_err == hipSuccess) g_attr_err = sfag::set_dense_attributes();
     if (g_attr_err == hipSuccess) g_attr_err = sfag::set_q_attributes();
   });
@@ -451,8 +455,6 @@ sfag_status backward(const void* query, const void* key, const void* value, cons
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   unsigned char* ws = static_cast<unsigned char*>(workspace);
-  float* acc = reinterpret_cast<float*>(ws + p.off_acc);
-  if (!p.dense) SFAG_HIP(sfag::launch_fill_zero(acc, p.keys * kDacc, s));
 
   sfag::BwdArgs a{};
   a.q = static_cast<const uint16_t*>(query);
@@ -466,7 +468,6 @@ sfag_status backward(const void* query, const void* key, const void* value, cons
   a.ssum = softmax_sum;
   a.dq = static_cast<uint16_t*>(d_query);
   a.dqr = static_cast<uint16_t*>(d_query_rope);
-  a.acc = acc;
   a.lens = p.lens;
   a.S1 = p.S1;
   a.S2 = p.S2;
@@ -477,53 +478,55 @@ sfag_status backward(const void* query, const void* key, const void* value, cons
   a.mode3 = p.mode3;
   a.layout_tnd = p.tnd;
   a.hgc = p.hg_count;
+  a.rec_chunks = (int)p.rec_chunks;
   a.scale = scale_value;
 
+  // index sort (both paths): sorted positions, counts, block starts (and the key -> position map
+  // of the key-major path)
+  sfag::DenseArgs da{};
+  da.q = a.q;
+  da.qr = a.qr;
+  da.dout = a.dout;
+  da.idx = sparse_indices;
+  da.sorted = reinterpret_cast<int32_t*>(ws + p.off_sorted);
+  da.count = reinterpret_cast<int32_t*>(ws + p.off_count);
+  da.maxdup = reinterpret_cast<int32_t*>(ws + p.off_maxdup);
+  da.offs = reinterpret_cast<int32_t*>(ws + p.off_offs);
+  da.kpos = p.dense ? reinterpret_cast<int16_t*>(ws + p.off_kpos) : nullptr;
+  da.kstride = p.dense ? (int)(p.maxblk * sfag::kBk) : 0;
+  da.zero_row = reinterpret_cast<uint16_t*>(ws + p.off_zero);
+  da.dk = static_cast<uint16_t*>(d_key);
+  da.dkr = static_cast<uint16_t*>(d_key_rope);
+  da.dv = static_cast<uint16_t*>(d_value);
+  da.lens = p.lens;
+  da.S1 = p.S1;
+  da.S2 = p.S2;
+  da.B = (int)p.B;
+  da.N1 = (int)p.N1;
+  da.topk = (int)p.topk;
+  da.bs = p.bs;
+  da.mode3 = p.mode3;
+  da.layout_tnd = p.tnd;
+  da.hgc = p.hg_count;
+  da.maxblk = (int)p.maxblk;
+  da.rec_chunks = (int)p.rec_chunks;
+  da.scale = scale_value;
+  a.sorted = da.sorted;
+  a.count = da.count;
+  a.zero_row = da.zero_row;
+
   if (p.dense) {
-    sfag::DenseArgs da{};
-    da.q = a.q;
-    da.qr = a.qr;
-    da.dout = a.dout;
-    da.idx = sparse_indices;
-    da.sorted = reinterpret_cast<int32_t*>(ws + p.off_sorted);
-    da.count = reinterpret_cast<int32_t*>(ws + p.off_count);
-    da.maxdup = reinterpret_cast<int32_t*>(ws + p.off_maxdup);
-    da.offs = reinterpret_cast<int32_t*>(ws + p.off_offs);
-    da.kpos = reinterpret_cast<int16_t*>(ws + p.off_kpos);
-    da.kstride = (int)(p.maxblk * sfag::kBk);
     da.dsp = reinterpret_cast<uint16_t*>(ws + p.off_dsp);
     da.bt = reinterpret_cast<uint16_t*>(ws + p.off_bt);
     da.part = reinterpret_cast<float*>(ws + p.off_part);
     da.flag = reinterpret_cast<int32_t*>(ws + p.off_flag);
-    da.zero_row = reinterpret_cast<uint16_t*>(ws + p.off_zero);
-    da.dk = static_cast<uint16_t*>(d_key);
-    da.dkr = static_cast<uint16_t*>(d_key_rope);
-    da.dv = static_cast<uint16_t*>(d_value);
-    da.lens = p.lens;
-    da.S1 = p.S1;
-    da.S2 = p.S2;
-    da.B = (int)p.B;
-    da.N1 = (int)p.N1;
-    da.topk = (int)p.topk;
-    da.bs = p.bs;
-    da.mode3 = p.mode3;
-    da.layout_tnd = p.tnd;
-    da.hgc = p.hg_count;
-    da.maxblk = (int)p.maxblk;
     da.items = (int)p.items;
     da.citems = (int)p.citems;
     da.ilist = reinterpret_cast<int32_t*>(ws + p.off_ilist);
     da.imap = reinterpret_cast<int32_t*>(ws + p.off_imap);
-    da.scale = scale_value;
-    da.rec_chunks = (int)p.rec_chunks;
-    a.rec_chunks = (int)p.rec_chunks;
-    a.sorted = da.sorted;
-    a.count = da.count;
     a.dsp = reinterpret_cast<uint16_t*>(ws + p.off_dsp);
-    a.zero_row = da.zero_row;
     a.bt = reinterpret_cast<uint16_t*>(ws + p.off_bt);
     a.row_begin = 0;
-    a.pairs_per_launch = 0;
     SFAG_HIP(sfag::launch_item_list(da, s));
     SFAG_HIP(sfag::launch_sort_rows(da, p.rows, s));
     if (g_ev[0]) SFAG_HIP(hipEventRecord(g_ev[0], s));
@@ -537,29 +540,49 @@ sfag_status backward(const void* query, const void* key, const void* value, cons
     return ok();
   }
 
+  // per-pair path, in chunks of query rows: query-major kernel, slot offsets, partials, ordered
+  // reduce (the last chunk writes the bf16 key gradients)
+  SFAG_HIP(sfag::launch_sort_rows(da, p.rows, s));
+  sfag::PairArgs pa{};
+  pa.sorted = da.sorted;
+  pa.count = da.count;
+  pa.offs = da.offs;
+  pa.dsp = reinterpret_cast<uint16_t*>(ws + p.off_dsp);
+  pa.bt = reinterpret_cast<uint16_t*>(ws + p.off_bt);
+  pa.part = reinterpret_cast<float*>(ws + p.off_part);
+  pa.keyb = reinterpret_cast<uint8_t*>(ws + p.off_keyb);
+  pa.rowoff = reinterpret_cast<int32_t*>(ws + p.off_rowoff);
+  pa.btotal = reinterpret_cast<int32_t*>(ws + p.off_btotal);
+  pa.bbase = reinterpret_cast<int32_t*>(ws + p.off_bbase);
+  pa.acc = reinterpret_cast<float*>(ws + p.off_acc);
+  pa.dk = static_cast<uint16_t*>(d_key);
+  pa.dkr = static_cast<uint16_t*>(d_key_rope);
+  pa.dv = static_cast<uint16_t*>(d_value);
+  pa.lens = p.lens;
+  pa.S1 = p.S1;
+  pa.S2 = p.S2;
+  pa.B = (int)p.B;
+  pa.topk = (int)p.topk;
+  pa.layout_tnd = p.tnd;
+  pa.hgc = p.hg_count;
+  pa.maxblk = (int)p.maxblk;
+  pa.rec_chunks = (int)p.rec_chunks;
+  pa.nblocks = (int)p.pair_blocks;
+  pa.scale = scale_value;
+  a.dsp = const_cast<uint16_t*>(pa.dsp);
+  a.bt = const_cast<uint16_t*>(pa.bt);
   if (g_ev[0]) SFAG_HIP(hipEventRecord(g_ev[0], s));
-  if (!p.det) {
-    a.row_begin = 0;
-    a.pairs_per_launch = 0;
-    SFAG_HIP(sfag::launch_bwd_main(a, p.rows, p.hg_count, 0, s));
-  } else {
-    a.partial = reinterpret_cast<float*>(ws + p.off_partial);
-    uint64_t* k0 = reinterpret_cast<uint64_t*>(ws + p.off_keys0);
-    uint64_t* k1 = reinterpret_cast<uint64_t*>(ws + p.off_keys1);
-    void* tmp = ws + p.off_sorttmp;
-    for (int64_t r0 = 0; r0 < p.rows; r0 += p.det_rows) {
-      const int64_t nr = std::min<int64_t>(p.det_rows, p.rows - r0);
-      a.row_begin = r0;
-      a.pairs_per_launch = nr * p.topk;
-      SFAG_HIP(sfag::launch_bwd_main(a, nr, p.hg_count, 1, s));
-      SFAG_HIP(sfag::launch_pair_keys(a, k0, nr, s));
-      SFAG_HIP(sfag::sort_pair_keys(tmp, p.sort_tmp_bytes, k0, k1, nr * p.topk, p.end_bit, s));
-      SFAG_HIP(sfag::launch_det_reduce(k1, nr * p.topk, a.partial, nr * p.topk, p.hg_count, acc, p.keys, s));
-    }
+  for (int64_t r0 = 0; r0 < p.rows; r0 += p.chunk_rows) {
+    const int64_t nr = std::min<int64_t>(p.chunk_rows, p.rows - r0);
+    a.row_begin = r0;
+    SFAG_HIP(sfag::launch_bwd_q(a, nr, p.hg_count, s));
+    pa.row_begin = r0;
+    pa.nrows = (int)nr;
+    pa.first = r0 == 0;
+    pa.last = r0 + nr >= p.rows;
+    SFAG_HIP(sfag::launch_pair_chunk(pa, s));
   }
   if (g_ev[1]) SFAG_HIP(hipEventRecord(g_ev[1], s));
-  SFAG_HIP(sfag::launch_cast(acc, static_cast<uint16_t*>(d_key), static_cast<uint16_t*>(d_key_rope),
-                             static_cast<uint16_t*>(d_value), p.keys, s));
   g_last_path = 1;
   return ok();
 }

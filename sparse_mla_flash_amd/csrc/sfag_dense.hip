@@ -70,7 +70,10 @@ __global__ void __launch_bounds__(kThreads) sort_rows_kernel(DenseArgs a) {
   if (row == 0)
     for (int i = t; i < kDk; i += kThreads) a.zero_row[i] = 0;
   const RowGeo geo = row_geo(a.lens, cum, a.B, a.layout_tnd, a.S1, a.S2, row, a.mode3);
-  const int map_end = (geo.active && geo.hi >= 0) ? min(a.kstride, ((geo.hi + kBk) / kBk) * kBk) : 0;
+  // keys [0, map_end) are sorted (whole 256-key blocks covering [0, hi]); the key -> position map
+  // is written only when the caller keeps one (kstride > 0, which then covers map_end)
+  const int map_end = (geo.active && geo.hi >= 0) ? ((geo.hi + kBk) / kBk) * kBk : 0;
+  const bool keep_map = a.kstride > 0;
   const int32_t* irow = a.idx + row * (a.topk / a.bs);
   int32_t* srow = a.sorted + row * a.topk;
   int16_t* kp = a.kpos + row * a.kstride;
@@ -129,7 +132,7 @@ __global__ void __launch_bounds__(kThreads) sort_rows_kernel(DenseArgs a) {
           pos += n;
           dup = max(dup, n);
         }
-        *reinterpret_cast<i16x8*>(kp + k0 + 8 * q) = m;
+        if (keep_map) *reinterpret_cast<i16x8*>(kp + k0 + 8 * q) = m;
       }
     }
     __syncthreads();

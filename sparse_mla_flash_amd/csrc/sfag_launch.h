@@ -32,18 +32,16 @@ struct BwdArgs {
   const float* ssum;
   uint16_t* dq;           // [rows, N1, 512]
   uint16_t* dqr;          // [rows, N1, 64]
-  float* acc;             // [keys, 1088] fp32 accumulator (atomic mode)
-  float* partial;         // [head groups, pairs_per_launch, 1088] (deterministic mode)
-  const int32_t* sorted;  // [rows, topk] valid key positions, ascending (key-major mode)
-  const int32_t* count;   // [rows] number of valid positions (key-major mode)
-  uint16_t* dsp;          // [rows, head groups, rec_chunks, kRecChunk] bf16 dS | P records (key-major mode)
-  const uint16_t* zero_row;  // 576 zero bf16 (key-major mode: rope operand of rope-less calls)
-  uint16_t* bt;           // [rows, hgc, 1088, 64] heads-innermost Q | QRope | dO (key-major mode)
+  const int32_t* sorted;  // [rows, topk] valid key positions, ascending
+  const int32_t* count;   // [rows] number of valid positions
+  // records and heads-innermost copy of the launch's rows (row - row_begin)
+  uint16_t* dsp;          // [launch rows, head groups, rec_chunks, kRecChunk] bf16 dS | P records
+  const uint16_t* zero_row;  // 576 zero bf16 (rope operand of rope-less calls)
+  uint16_t* bt;           // [launch rows, hgc, 1088, 64] heads-innermost Q | QRope | dO
   Lens lens;
   int64_t S1;             // BSND S1 / TND T1 (statistics head stride)
   int64_t S2;             // BSND S2 / TND T2
   int64_t row_begin;      // first query row of this launch
-  int64_t pairs_per_launch;
   int B, N1, topk, mode3, layout_tnd, hgc;
   int bs;                 // sparseBlockSize: topk slots = index count x bs
   int rec_chunks;         // record chunks per (row, head group): ceil(topk / 32)
@@ -60,6 +58,7 @@ struct DenseArgs {
   int32_t* maxdup;        // [rows]
   int32_t* offs;          // [rows, maxblk + 1]
   int16_t* kpos;          // [rows, kstride] first sorted position of each key, -1: not selected
+                          // (key-major path only; kstride = 0: not written)
   const uint16_t* dsp;    // [rows, hgc, rec_chunks, kRecChunk]
   const uint16_t* bt;     // [rows, hgc, 1088, 64] Q | QRope | dO with the 64 heads of a group innermost
   float* part;            // [hgc, citems, kBk, 1088]
@@ -75,6 +74,30 @@ struct DenseArgs {
   int B, N1, topk, mode3, layout_tnd, hgc, maxblk, items, citems, kstride;
   int bs;                 // sparseBlockSize: topk slots = index count x bs
   int rec_chunks;         // record chunks per (row, head group)
+  float scale;
+};
+
+// Per-pair dK / dV of one chunk of query rows [row_begin, row_begin + nrows).
+struct PairArgs {
+  const int32_t* sorted;  // [rows, topk] valid key positions, ascending
+  const int32_t* count;   // [rows]
+  const int32_t* offs;    // [rows, maxblk + 1] first sorted position of every 256-key block
+  const uint16_t* dsp;    // [nrows, hgc, rec_chunks, kRecChunk] records of the chunk's rows
+  const uint16_t* bt;     // [nrows, hgc, 1088, 64] heads-innermost Q | QRope | dO of the chunk's rows
+  float* part;            // [slots, 1088] fp32 partials, key-block-major slot order
+  uint8_t* keyb;          // [slots] key % 256 of every slot
+  int32_t* rowoff;        // [nrows, maxblk] offset of a row's pairs within each key block
+  int32_t* btotal;        // [nblocks] pairs of each key block in the chunk
+  int32_t* bbase;         // [nblocks + 1] first slot of each key block
+  float* acc;             // [keys, 1088] fp32 accumulator carried between chunks
+  uint16_t* dk;           // [keys, 512]
+  uint16_t* dkr;          // [keys, 64] (NULL: rope-less call)
+  uint16_t* dv;           // [keys, 512]
+  Lens lens;
+  int64_t S1, S2;
+  int64_t row_begin;
+  int nrows, B, topk, layout_tnd, hgc, maxblk, rec_chunks, nblocks;
+  int first, last;        // the chunk is the first / the last one
   float scale;
 };
 
@@ -101,27 +124,15 @@ __host__ __device__ inline int64_t stat_index(int tnd, const Geo& g, int64_t row
   return tnd ? (int64_t)h * S1 + row : ((int64_t)g.b * N1 + h) * S1 + g.i;
 }
 
-// mode 0: fp32 atomic dK/dV, 1: per-pair partials (deterministic mode)
-hipError_t launch_bwd_main(const BwdArgs& a, int64_t nrows, int hg_count, int mode, hipStream_t st);
 hipError_t launch_fwd(const FwdArgs& a, int64_t nrows, int hg_count, hipStream_t st);
-hipError_t launch_fill_zero(float* p, int64_t nfloats, hipStream_t st);
-hipError_t launch_cast(const float* acc, uint16_t* dk, uint16_t* dkr, uint16_t* dv, int64_t keys,
-                       hipStream_t st);
-hipError_t launch_pair_keys(const BwdArgs& a, uint64_t* keys, int64_t nrows, hipStream_t st);
-hipError_t launch_det_reduce(const uint64_t* sorted, int64_t n, const float* partial,
-                             int64_t pairs_per_launch, int hg_count, float* acc, int64_t keys,
-                             hipStream_t st);
-hipError_t sort_pair_keys(void* temp, size_t temp_bytes, const uint64_t* in, uint64_t* out, int64_t n,
-                          int end_bit, hipStream_t st);
-size_t sort_temp_bytes(int64_t n, int end_bit);
 hipError_t launch_bwd_q(const BwdArgs& a, int64_t nrows, int hg_count, hipStream_t st);
+hipError_t launch_pair_chunk(const PairArgs& a, hipStream_t st);
 hipError_t set_q_attributes();
 hipError_t launch_sort_rows(const DenseArgs& a, int64_t rows, hipStream_t st);
 hipError_t launch_item_list(const DenseArgs& a, hipStream_t st);
 hipError_t launch_kv_dense(const DenseArgs& a, hipStream_t st);
 hipError_t launch_kv_reduce(const DenseArgs& a, int64_t keys, hipStream_t st);
 hipError_t set_dense_attributes();
-hipError_t set_bwd_attributes();
 hipError_t set_fwd_attributes();
 
 }  // namespace sfag

@@ -67,7 +67,8 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
   const int rw = wave & 3;                          // index within the role
   const int g = lane >> 4, c = lane & 15;
   // longest rows (highest positions under the causal mask) first
-  const int64_t row = (int64_t)gridDim.x - 1 - blockIdx.x;
+  const int64_t lrow = (int64_t)gridDim.x - 1 - blockIdx.x;     // row within this launch
+  const int64_t row = a.row_begin + lrow;
   const int hg = blockIdx.y;
   const int h0 = hg * 64;
   const int nh = min(64, a.N1 - h0);
@@ -137,7 +138,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
   // The record pointers lose their address space through the scalar round trip; stores through
   // them are made global explicitly (a generic store might address LDS).
   typedef __attribute__((address_space(1))) uint64_t GlobalU64;
-  uint16_t* recrow = uniform(a.dsp + ((int64_t)row * a.hgc + hg) * (int64_t)a.rec_chunks * kRecChunk);
+  uint16_t* recrow = uniform(a.dsp + (lrow * a.hgc + hg) * (int64_t)a.rec_chunks * kRecChunk);
   asm volatile("" : "+s"(kbase), "+s"(krbase), "+s"(recrow));
 
   // gathering lanes of the dQ waves: key slot gkey of every chunk, chunk column gcol of every block
@@ -290,7 +291,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
     // lane (g, c) of score wave w stores heads 32 s + 8 g .. + 7 of column 64 k + 16 w + c.  The
     // dQ waves pass the same number of barriers meanwhile.  These stores drain during the loop.
     {
-      uint16_t* bto = a.bt + ((int64_t)row * a.hgc + hg) * (int64_t)kDacc * 64;
+      uint16_t* bto = a.bt + (lrow * a.hgc + hg) * (int64_t)kDacc * 64;
       const int hrow = 16 * rw + c;
 #pragma unroll
       for (int k = 0; k < kDacc / 64; ++k) {
