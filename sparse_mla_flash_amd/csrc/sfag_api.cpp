@@ -59,7 +59,7 @@ struct Plan {
   int64_t items = 0, citems = 0, maxblk = 0;
   int64_t rec_chunks = 0;          // record chunks of 32 positions per (row, head group)
   // workspace layout
-  uint64_t off_acc = 0, off_keyb = 0, off_rowoff = 0, off_btotal = 0, off_bbase = 0;
+  uint64_t off_acc = 0, off_loc = 0, off_kcnt = 0, off_koff = 0, off_btotal = 0, off_bbase = 0;
   uint64_t off_sorted = 0, off_count = 0, off_maxdup = 0, off_offs = 0, off_dsp = 0, off_part = 0, off_flag = 0;
   uint64_t off_zero = 0, off_ilist = 0, off_imap = 0, off_kpos = 0, off_bt = 0;
   uint64_t bytes = 0;
@@ -256,6 +256,8 @@ sfag_status make_plan(const sfag_dims* dims, const int32_t* sq, const int32_t* s
   const uint64_t part_row = (uint64_t)p->topk * kDacc * 4;
   int64_t r = (int64_t)(kPartialBudget / part_row);
   r = std::max<int64_t>(1, std::min<int64_t>(r, p->rows));
+  const int64_t nchunks = (p->rows + r - 1) / r;
+  r = (p->rows + nchunks - 1) / nchunks;          // chunks of (nearly) equal size
   p->chunk_rows = r;
   int64_t nblocks = 0;
   for (int64_t b = 0; b < p->B; ++b)
@@ -269,10 +271,12 @@ sfag_status make_plan(const sfag_dims* dims, const int32_t* sq, const int32_t* s
   off = align_up(off + (uint64_t)r * bt_row);
   p->off_part = off;
   off = align_up(off + (uint64_t)r * part_row);
-  p->off_keyb = off;
-  off = align_up(off + (uint64_t)r * p->topk);
-  p->off_rowoff = off;
-  off = align_up(off + (uint64_t)r * std::max<int64_t>(maxblk, 1) * 4);
+  p->off_loc = off;
+  off = align_up(off + (uint64_t)r * p->topk * 4);
+  p->off_kcnt = off;
+  off = align_up(off + (uint64_t)std::max<int64_t>(p->keys, 1) * 4);
+  p->off_koff = off;
+  off = align_up(off + (uint64_t)std::max<int64_t>(p->keys, 1) * 4);
   p->off_btotal = off;
   off = align_up(off + (uint64_t)std::max<int64_t>(nblocks, 1) * 4);
   p->off_bbase = off;
@@ -540,8 +544,8 @@ sfag_status backward(const void* query, const void* key, const void* value, cons
     return ok();
   }
 
-  // per-pair path, in chunks of query rows: query-major kernel, slot offsets, partials, ordered
-  // reduce (the last chunk writes the bf16 key gradients)
+  // per-pair path, in chunks of query rows: query-major kernel, slots (counting sort by key),
+  // partials, per-key sums (the last chunk writes the bf16 key gradients)
   SFAG_HIP(sfag::launch_sort_rows(da, p.rows, s));
   sfag::PairArgs pa{};
   pa.sorted = da.sorted;
@@ -550,8 +554,10 @@ sfag_status backward(const void* query, const void* key, const void* value, cons
   pa.dsp = reinterpret_cast<uint16_t*>(ws + p.off_dsp);
   pa.bt = reinterpret_cast<uint16_t*>(ws + p.off_bt);
   pa.part = reinterpret_cast<float*>(ws + p.off_part);
-  pa.keyb = reinterpret_cast<uint8_t*>(ws + p.off_keyb);
-  pa.rowoff = reinterpret_cast<int32_t*>(ws + p.off_rowoff);
+  pa.loc = reinterpret_cast<int32_t*>(ws + p.off_loc);
+  pa.kcnt = reinterpret_cast<int32_t*>(ws + p.off_kcnt);
+  pa.koff = reinterpret_cast<int32_t*>(ws + p.off_koff);
+  pa.keys = p.keys;
   pa.btotal = reinterpret_cast<int32_t*>(ws + p.off_btotal);
   pa.bbase = reinterpret_cast<int32_t*>(ws + p.off_bbase);
   pa.acc = reinterpret_cast<float*>(ws + p.off_acc);

@@ -84,9 +84,10 @@ struct PairArgs {
   const int32_t* offs;    // [rows, maxblk + 1] first sorted position of every 256-key block
   const uint16_t* dsp;    // [nrows, hgc, rec_chunks, kRecChunk] records of the chunk's rows
   const uint16_t* bt;     // [nrows, hgc, 1088, 64] heads-innermost Q | QRope | dO of the chunk's rows
-  float* part;            // [slots, 1088] fp32 partials, key-block-major slot order
-  uint8_t* keyb;          // [slots] key % 256 of every slot
-  int32_t* rowoff;        // [nrows, maxblk] offset of a row's pairs within each key block
+  float* part;            // [slots, 1088] fp32 partials, key-major slot order
+  int32_t* loc;           // [nrows, topk] slot of each (row, position) pair within its key block
+  int32_t* kcnt;          // [keys] pairs of each key in the chunk
+  int32_t* koff;          // [keys] first slot of each key within its key block
   int32_t* btotal;        // [nblocks] pairs of each key block in the chunk
   int32_t* bbase;         // [nblocks + 1] first slot of each key block
   float* acc;             // [keys, 1088] fp32 accumulator carried between chunks
@@ -96,6 +97,7 @@ struct PairArgs {
   Lens lens;
   int64_t S1, S2;
   int64_t row_begin;
+  int64_t keys;           // key rows (B x S2, or the sum of the key lengths)
   int nrows, B, topk, layout_tnd, hgc, maxblk, rec_chunks, nblocks;
   int first, last;        // the chunk is the first / the last one
   float scale;

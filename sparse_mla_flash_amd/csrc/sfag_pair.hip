@@ -5,17 +5,16 @@
 // rows: dV[u] += P^T dO and dK[u] += scale dS^T Q (SparseFlashAttentionGrad README, "function
 // description").  When every row selects a small fraction of the keys it can reach, the
 // key-major kernel would multiply mostly zeros, so here the work follows the pairs:
-//   pair_kv_kernel      per query row, the [positions x heads] dS (or P) records times the row's
-//                       [heads x 1088] Q | QRope (or dO) on the MFMA: one fp32 partial row of
-//                       1088 values per valid (row, position) pair, written to its slot;
-//   pair_reduce_kernel  per 256-key block and 64-column slice, the block's partials added into
-//                       the block's accumulator rows in slot order.
-// Slots are numbered key-block-major: the pairs of key block lb come together, rows ascending,
-// positions (ascending keys) within a row.  A row's pairs of one block are a contiguous run of
-// its sorted positions, so a slot is the block's base + the row's offset within the block (an
-// exclusive scan over rows, block_slots_kernel) + the pair's rank in its run.  The sum of a key
-// therefore runs over its pairs in ascending (row, position) order, and query rows are taken in
-// fixed chunks in order: the result is bit-reproducible, with or without the deterministic flag.
+//   pair_slots_kernel  per 256-key block, a stable counting sort of the chunk's pairs of the block
+//                      by key: every pair gets its slot, every key its run of slots;
+//   pair_kv_kernel     per query row, the [positions x heads] dS (or P) records times the row's
+//                      [heads x 1088] Q | QRope (or dO) on the MFMA: one fp32 partial row of
+//                      1088 values per valid (row, position) pair, written to its slot;
+//   pair_sum_kernel    per key, its run of partial rows added in slot order (one wave per key).
+// Slots are numbered key-major: the pairs of key block 0 first, inside a block key by key, and
+// the pairs of one key in ascending (row, position) order.  A key's sum therefore runs over its
+// pairs in a fixed order, and query rows are taken in fixed chunks in order: the result is
+// bit-reproducible, with or without the deterministic flag.
 #include "sfag_device.h"
 #include "sfag_launch.h"
 
@@ -53,47 +52,142 @@ __device__ __forceinline__ int batch_of_block(const int32_t* bstart, int B, int 
 }  // namespace
 
 // ------------------------------------------------------------------------------------------
-// Slot offsets of one chunk of query rows: for key block gb (batch b, block lb) and every chunk
-// row r of batch b, rowoff[r][lb] = number of the block's pairs in earlier chunk rows; btotal[gb]
-// = the block's pairs in the chunk.  One workgroup per block, 256 rows per scan step.
-__global__ void __launch_bounds__(kThreads) block_slots_kernel(PairArgs a) {
+// Slots of one chunk of query rows, per key block gb (batch b, block lb): the block's pairs, in
+// (row, position) order, counting-sorted by key.  16 waves; wave w takes a contiguous range of
+// the chunk's rows of batch b.  Pass 1 counts every key's pairs per wave; the counts are turned
+// into starting offsets (keys ascending, waves ascending inside a key); pass 2 walks the same
+// pairs again and gives each its offset: a pair's slot is bbase[gb] + loc.  Within a wave, 64
+// consecutive pairs are ranked at once: lanes holding the same key find each other with eight
+// ballots over the key's bits.
+constexpr int kSlotWaves = 16;
+
+// lanes of this wave holding the same key byte (valid lanes only)
+__device__ __forceinline__ uint64_t same_key_lanes(int key, bool valid) {
+  uint64_t m = __ballot(valid);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const bool bit = (key >> i) & 1;
+    const uint64_t on = __ballot(bit);
+    m &= bit ? on : ~on;
+  }
+  return m;
+}
+
+template <bool kRank>
+__device__ __forceinline__ void slot_pass(const PairArgs& a, int32_t* wcnt, int32_t* wpre, int32_t* wo,
+                                          int64_t rbeg, int64_t rend, int lb, int lane) {
+  const uint64_t lt = (1ull << lane) - 1;
+  for (int64_t rt = rbeg; rt < rend; rt += 64) {
+    const int64_t r = rt + lane;
+    int n = 0, o = 0;
+    if (r < rend) {
+      const int32_t* orow = a.offs + r * (a.maxblk + 1) + lb;
+      o = orow[0];
+      n = orow[1] - o;
+    }
+    int incl = n;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(incl, d);
+      if (lane >= d) incl += y;
+    }
+    const int total = __shfl(incl, 63);
+    // wave-private LDS: run starts of the 64 rows (flattened) and their first positions
+    wpre[lane] = incl - n;
+    wo[lane] = o;
+    asm volatile("" ::: "memory");
+    for (int f0 = 0; f0 < total; f0 += 256) {
+      int key[4];
+      int64_t pidx[4];
+      bool ok[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int f = f0 + 64 * u + lane;
+        ok[u] = f < total;
+        int j = 0;                                  // last row whose run starts at or before f
+#pragma unroll
+        for (int st = 32; st; st >>= 1)
+          if (wpre[j + st] <= f) j += st;
+        const int p = wo[j] + (f - wpre[j]);
+        const int64_t row = rt + j;
+        key[u] = ok[u] ? (a.sorted[row * a.topk + p] & (kBk - 1)) : 0;
+        pidx[u] = (row - a.row_begin) * a.topk + p;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint64_t peers = same_key_lanes(key[u], ok[u]);
+        const int before = __popcll(peers & lt);
+        const int c = __popcll(peers);
+        if (kRank) {
+          if (ok[u]) {
+            const int base = wcnt[key[u]];          // read by every lane of the key before the
+            a.loc[pidx[u]] = base + before;         // first of them moves it on
+            if (before == 0) wcnt[key[u]] = base + c;
+          }
+        } else if (ok[u] && before == 0) {
+          wcnt[key[u]] += c;
+        }
+      }
+    }
+    asm volatile("" ::: "memory");
+  }
+}
+
+__global__ void __launch_bounds__(kSlotWaves * 64) pair_slots_kernel(PairArgs a) {
   __shared__ int32_t cum[2 * 257], bstart[257];
-  __shared__ int32_t s_wsum[kThreads / 64];
+  __shared__ int32_t cnt[kSlotWaves][kBk];
+  __shared__ int32_t s_pre[kSlotWaves][65], s_o[kSlotWaves][64];
+  __shared__ int32_t s_wsum[4];
   pair_tables(a, cum, bstart);
+  for (int e = threadIdx.x; e < kSlotWaves * kBk; e += blockDim.x) (&cnt[0][0])[e] = 0;
   __syncthreads();
   const int gb = blockIdx.x;
   const int b = batch_of_block(bstart, a.B, gb);
   const int lb = gb - bstart[b];
   const int lq = a.lens.lq[b], lkv = a.lens.lkv[b];
+  const int nkeys = a.layout_tnd ? lkv : (int)a.S2;
+  const int nvalid = min(kBk, nkeys - lb * kBk);
+  const int64_t kg0 = (int64_t)cum[257 + b] + lb * kBk;
   const int64_t q0 = cum[b];                      // first query row of batch b
   const int64_t r0 = max((int64_t)a.row_begin, q0), r1 = min(a.row_begin + a.nrows, q0 + lq);
-  const bool live = lb * kBk < lkv;               // keys of later blocks cannot be selected
+  const bool live = lb * kBk < lkv && r1 > r0;    // keys of later blocks cannot be selected
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int running = 0;
-  if (live) {
-    for (int64_t p0 = r0; p0 < r1; p0 += kThreads) {
-      const int64_t r = p0 + threadIdx.x;
-      int n = 0;
-      if (r < r1) {
-        const int32_t* o = a.offs + r * (a.maxblk + 1) + lb;
-        n = o[1] - o[0];
-      }
-      int incl = n;
+  const int64_t per = live ? (r1 - r0 + kSlotWaves - 1) / kSlotWaves : 0;
+  const int64_t rbeg = min(r1, r0 + wave * per), rend = min(r1, rbeg + per);
+  if (live) slot_pass<false>(a, cnt[wave], s_pre[wave], s_o[wave], rbeg, rend, lb, lane);
+  __syncthreads();
+  int tot = 0, incl = 0;
+  if (threadIdx.x < kBk) {
+    const int k = threadIdx.x;
 #pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int y = __shfl_up(incl, d);
-        if (lane >= d) incl += y;
-      }
-      if (lane == 63) s_wsum[wave] = incl;
-      __syncthreads();
-      int base = running;
-      for (int v = 0; v < wave; ++v) base += s_wsum[v];
-      if (r < r1) a.rowoff[(r - a.row_begin) * a.maxblk + lb] = base + incl - n;
-      running += s_wsum[0] + s_wsum[1] + s_wsum[2] + s_wsum[3];
-      __syncthreads();
+    for (int w = 0; w < kSlotWaves; ++w) tot += cnt[w][k];
+    incl = tot;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(incl, d);
+      if (lane >= d) incl += y;
     }
+    if (lane == 63) s_wsum[wave] = incl;
   }
-  if (threadIdx.x == 0) a.btotal[gb] = running;
+  __syncthreads();
+  if (threadIdx.x < kBk) {
+    const int k = threadIdx.x;
+    int base = incl - tot;
+    for (int v = 0; v < wave; ++v) base += s_wsum[v];
+    if (k < nvalid) {
+      a.kcnt[kg0 + k] = tot;
+      a.koff[kg0 + k] = base;
+    }
+#pragma unroll
+    for (int w = 0; w < kSlotWaves; ++w) {
+      const int t = cnt[w][k];
+      cnt[w][k] = base;
+      base += t;
+    }
+    if (k == kBk - 1) a.btotal[gb] = base;
+  }
+  __syncthreads();
+  if (live) slot_pass<true>(a, cnt[wave], s_pre[wave], s_o[wave], rbeg, rend, lb, lane);
 }
 
 // Exclusive scan of the block totals: bbase[gb] = first slot of block gb; bbase[nblocks] = all.
@@ -146,8 +240,7 @@ __device__ __forceinline__ void pair_kv_row(const PairArgs& a, uint16_t* Bs, int
   const int count = a.count[row];
   const int nck = (count + 31) >> 5;
   const int32_t* srow = a.sorted + row * a.topk;
-  const int32_t* orow = a.offs + row * (a.maxblk + 1);
-  const int32_t* rrow = a.rowoff + (int64_t)lr * a.maxblk;
+  const int32_t* lrow = a.loc + (int64_t)lr * a.topk;
   const int64_t hgstride = (int64_t)a.rec_chunks * kRecChunk;
   const uint16_t* rec = a.dsp + (int64_t)lr * a.hgc * hgstride + half + g * 512 + c * 16;
   for (int pc = wave; pc < nck; pc += 4) {
@@ -177,16 +270,13 @@ __device__ __forceinline__ void pair_kv_row(const PairArgs& a, uint16_t* Bs, int
     for (int pt = 0; pt < 2; ++pt) {
       const int p = 32 * pc + 16 * pt + c;
       if (p >= count) continue;
-      const int key = srow[p];
-      const int lb = key >> 8;
-      const int64_t slot = (int64_t)a.bbase[bstart[b] + lb] + rrow[lb] + (p - orow[lb]);
+      const int64_t slot = (int64_t)a.bbase[bstart[b] + (srow[p] >> 8)] + lrow[p];
       float* dst = a.part + slot * kDacc + colbase + 4 * g;
 #pragma unroll
       for (int ft = 0; ft < NFT; ++ft) {
         const f32x4 v = acc[ft][pt];
         *reinterpret_cast<float4*>(dst + 16 * ft) = make_float4(v[0] * mul, v[1] * mul, v[2] * mul, v[3] * mul);
       }
-      if (colbase == 0 && g == 0) a.keyb[slot] = (uint8_t)(key & (kBk - 1));
     }
   }
 }
@@ -224,84 +314,101 @@ __global__ void __launch_bounds__(kThreads, 2) pair_kv_kernel(PairArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------
-// Ordered reduce of one chunk.  Workgroup = (key block gb, 64-column slice cs); the block's 256
-// accumulator rows of the slice sit in LDS (starting from zero in the first chunk, from the fp32
-// accumulator otherwise).  The block's slots are streamed in order; wave w adds the pairs of
-// keys 64 w .. 64 w + 63 (lane = column), so the pairs of one key are added by one wave in slot
-// order.  The last chunk writes bf16 dK / dKRope / dV (zeros for keys no row selected).
-__global__ void __launch_bounds__(kThreads, 2) pair_reduce_kernel(PairArgs a) {
-  __shared__ __attribute__((aligned(16))) float accs[kBk * 64];
+// Sum of one chunk, one wave per key: the key's run of partial rows, in slot order, added to the
+// fp32 accumulator row (zero in the first chunk).  Lane l holds columns 4 l + 256 j .. + 3 for
+// j < 4 and column 1024 + l.  Middle chunks skip keys without pairs; the last chunk writes bf16
+// dK / dKRope / dV for every key (zeros for keys no row selected).
+__device__ __forceinline__ void store_bf16x4(uint16_t* p, f32x4 v) {
+  const uint32_t lo = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+  const uint32_t hi = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+  *reinterpret_cast<uint2*>(p) = make_uint2(lo, hi);
+}
+
+__global__ void __launch_bounds__(kThreads) pair_sum_kernel(PairArgs a) {
   __shared__ int32_t cum[2 * 257], bstart[257];
   pair_tables(a, cum, bstart);
   __syncthreads();
-  const int gb = blockIdx.x, cs = blockIdx.y;
-  const int b = batch_of_block(bstart, a.B, gb);
-  const int lb = gb - bstart[b];
-  const int nkeys = a.layout_tnd ? a.lens.lkv[b] : (int)a.S2;
-  const int nvalid = min(kBk, nkeys - lb * kBk);
-  const int64_t krow0 = (int64_t)cum[257 + b] + lb * kBk;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int col = cs * 64 + lane;
-  for (int k = wave; k < kBk; k += 4)
-    accs[k * 64 + lane] = (a.first || k >= nvalid) ? 0.f : a.acc[(krow0 + k) * kDacc + col];
-  __syncthreads();
-  const int64_t lo = a.bbase[gb], hi = a.bbase[gb + 1];
-  const int k0 = 64 * wave;
-  for (int64_t s0 = lo; s0 < hi; s0 += 64) {
-    const int64_t sl = s0 + lane;
-    const int kb = sl < hi ? (int)a.keyb[sl] : -1;
-    uint64_t mine = __ballot(kb >= k0 && kb < k0 + 64);
-    while (mine) {
-      // up to 8 of this wave's pairs at a time: loads first, then the adds in slot order
-      int bit[8], key[8];
-      float val[8];
-      int n = 0;
+  const int64_t kg = (int64_t)blockIdx.x * 4 + wave;
+  if (kg >= a.keys) return;
+  const int n = a.kcnt[kg];
+  if (n == 0 && !a.first && !a.last) return;
+  int b = 0;
+  if (a.layout_tnd) {
+    int lo = 0, hi = a.B - 1;                     // last batch whose first key is <= kg
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (cum[257 + mid] <= kg) lo = mid; else hi = mid - 1;
+    }
+    b = lo;
+  } else {
+    b = (int)(kg / a.S2);
+  }
+  const int lk = (int)(kg - cum[257 + b]);
+  const int64_t s0 = (int64_t)a.bbase[bstart[b] + (lk >> 8)] + a.koff[kg];
+  f32x4 v[4];
+  float t = 0.f;
+  float* accrow = a.acc + kg * kDacc;
+  if (a.first) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        bit[i] = -1;
-        if (mine) {
-          bit[i] = __builtin_ctzll(mine);
-          mine &= mine - 1;
-          ++n;
-        }
-      }
+    for (int j = 0; j < 4; ++j) v[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        key[i] = bit[i] >= 0 ? __shfl(kb, bit[i]) : 0;
-        val[i] = bit[i] >= 0 ? a.part[(s0 + bit[i]) * kDacc + col] : 0.f;
-      }
+    for (int j = 0; j < 4; ++j) v[j] = *reinterpret_cast<const f32x4*>(accrow + 256 * j + 4 * lane);
+    t = accrow[1024 + lane];
+  }
+  const float* src = a.part + s0 * kDacc;
+  int i = 0;
+  for (; i + 4 <= n; i += 4) {
+    f32x4 x[4][4];
+    float y[4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (i < n) accs[key[i] * 64 + lane] += val[i];
+    for (int u = 0; u < 4; ++u) {
+      const float* sp = src + (int64_t)(i + u) * kDacc;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) x[u][j] = *reinterpret_cast<const f32x4*>(sp + 256 * j + 4 * lane);
+      y[u] = sp[1024 + lane];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] += x[u][j];
+      t += y[u];
     }
   }
-  __syncthreads();
-  for (int k = wave; k < nvalid; k += 4) {
-    const float v = accs[k * 64 + lane];
-    const int64_t kr = krow0 + k;
-    if (!a.last) {
-      a.acc[kr * kDacc + col] = v;
-    } else {
-      const uint16_t bv = f2bf(v);
-      if (col < kDn) a.dk[kr * kDn + col] = bv;
-      else if (col < kDk) {
-        if (a.dkr) a.dkr[kr * kDr + col - kDn] = bv;
-      } else {
-        a.dv[kr * kDn + col - kDk] = bv;
-      }
-    }
+  for (; i < n; ++i) {
+    const float* sp = src + (int64_t)i * kDacc;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] += *reinterpret_cast<const f32x4*>(sp + 256 * j + 4 * lane);
+    t += sp[1024 + lane];
   }
+  if (!a.last) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) *reinterpret_cast<f32x4*>(accrow + 256 * j + 4 * lane) = v[j];
+    accrow[1024 + lane] = t;
+    return;
+  }
+  // columns 0..511 dK, 512..575 dKRope, 576..1087 dV
+  store_bf16x4(a.dk + kg * kDn + 4 * lane, v[0]);
+  store_bf16x4(a.dk + kg * kDn + 256 + 4 * lane, v[1]);
+  if (lane < 16) {
+    if (a.dkr) store_bf16x4(a.dkr + kg * kDr + 4 * lane, v[2]);
+  } else {
+    store_bf16x4(a.dv + kg * kDn + 4 * lane - 64, v[2]);
+  }
+  store_bf16x4(a.dv + kg * kDn + 192 + 4 * lane, v[3]);
+  a.dv[kg * kDn + 448 + lane] = f2bf(t);
 }
 
 // ------------------------------------------------------------------------------------------
 hipError_t launch_pair_chunk(const PairArgs& a, hipStream_t st) {
   if (a.nblocks > 0) {
-    hipLaunchKernelGGL(block_slots_kernel, dim3((unsigned)a.nblocks), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL(pair_slots_kernel, dim3((unsigned)a.nblocks), dim3(kSlotWaves * 64), 0, st, a);
     hipLaunchKernelGGL(block_base_kernel, dim3(1), dim3(1024), 0, st, a);
   }
   if (a.nrows > 0) hipLaunchKernelGGL(pair_kv_kernel, dim3((unsigned)a.nrows, 4), dim3(kThreads), 0, st, a);
-  if (a.nblocks > 0)
-    hipLaunchKernelGGL(pair_reduce_kernel, dim3((unsigned)a.nblocks, kDacc / 64), dim3(kThreads), 0, st, a);
+  if (a.keys > 0)
+    hipLaunchKernelGGL(pair_sum_kernel, dim3((unsigned)((a.keys + 3) / 4)), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
