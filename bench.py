@@ -13,7 +13,8 @@ resident in HBM.  Prints one JSON line:
              with HIP events that the library records on its own stream around that
              kernel, against the 2.5 PFLOP/s bf16 dense MFMA peak.  Key-major path: the
              query-major kernel does 3328 flop per (pair, head) (scores, dP, dQ) and the
-             key-major kernel 2176 (dK, dV); scatter path: one kernel does all 5504.
+             key-major kernel 2176 (dK, dV); per-pair path: the chunk loop (query-major
+             kernel, slots, partials, per-key sums) is timed as one stage with all 5504.
              `traffic` comes from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary
              of that kernel when it matches the current kernel sources, else null
   cpu_baseline  the fp64 CPU oracle on a bounded sample of rows of the same workload
@@ -55,14 +56,17 @@ METRIC = "effective TFLOP/s + ms/call, sparse attn bwd (S=8K, topk=2048, N1=64) 
 FLOP_Q_KERNEL = 2 * 576 + 2 * 512 + 2 * 576                                  # 3328: S, dP, dQ
 FLOP_KV_KERNEL = 2 * 576 + 2 * 512                                           # 2176: dK, dV
 CSRC = os.path.join("sparse_mla_flash_amd", "csrc")
-KERNEL_SOURCES = sorted(os.path.join(CSRC, f) for f in os.listdir(os.path.join(ROOT, CSRC))
-                        if f.endswith((".hip", ".h", ".cpp")))
+# the source file of each profiled kernel; with the two shared headers it fixes the kernel's code
+KERNEL_FILES = {"bwd_q_kernel": "sfag_q.hip", "kv_dense_kernel": "sfag_dense.hip", "sort_rows_kernel": "sfag_dense.hip",
+                "kv_reduce_kernel": "sfag_dense.hip", "pair_kv_kernel": "sfag_pair.hip",
+                "pair_sum_kernel": "sfag_pair.hip", "pair_slots_kernel": "sfag_pair.hip", "fwd_kernel": "sfag_fwd.hip"}
 
 
-def kernel_sha() -> str:
+def kernel_sha(kernel: str) -> str:
+    """Hash of a kernel's source file and the shared device / launch headers."""
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
+    for f in (KERNEL_FILES[kernel], "sfag_device.h", "sfag_launch.h"):
+        with open(os.path.join(ROOT, CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
@@ -129,7 +133,7 @@ def traffic_from_profile(kernel: str, workload_name: str):
         return None
     with open(path) as fh:
         t = json.load(fh)
-    if t.get("kernel_sha") != kernel_sha():
+    if kernel not in KERNEL_FILES or t.get("kernel_sha") != kernel_sha(kernel):
         return None
     return t.get("traffic_bytes_per_launch")
 
@@ -345,7 +349,7 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     sf.sfag_set_profile_events()
-    path = "key-major" if sf.sfag_last_path() == 0 else "scatter"
+    path = "key-major" if sf.sfag_last_path() == 0 else "per-pair"
     calls = sorted(ev.elapsed_ms(e[0], e[1]) for e in evs)
     s1 = sum(ev.elapsed_ms(e[2], e[3]) for e in evs) / args.steps
     s2 = sum(ev.elapsed_ms(e[4], e[5]) for e in evs) / args.steps if path == "key-major" else 0.0
@@ -362,8 +366,8 @@ def main():
     if path == "key-major":
         stages = {"bwd_q_kernel": (s1, FLOP_Q_KERNEL), "kv_dense_kernel": (s2, FLOP_KV_KERNEL)}
     else:
-        stages = {("bwd_main_kernel<partial> + sort + reduce" if det else "bwd_main_kernel<atomic>"):
-                  (s1, FLOP_PER_PAIR_HEAD)}
+        # one event pair around the whole chunk loop (query-major kernel, slots, partials, sums)
+        stages = {"per-pair chunk loop": (s1, FLOP_PER_PAIR_HEAD)}
     kernel = max(stages, key=lambda n: stages[n][0])
     kern_avg, kflop = stages[kernel]
     achieved = npairs * p.N1 * kflop / (kern_avg * 1e-3) / 1e12

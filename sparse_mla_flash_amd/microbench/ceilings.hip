@@ -116,8 +116,19 @@ extern "C" {
 int ceil_device_info(char* name, int name_len, int* cus, int* clock_khz, int* mem_clock_khz) {
   hipDeviceProp_t p;
   if (hipGetDeviceProperties(&p, 0) != hipSuccess) return -1;
+  // marketing name, then the architecture name (the former can be empty in containers)
+  const char* src = p.name[0] ? p.name : p.gcnArchName;
   int i = 0;
-  for (; i < name_len - 1 && p.name[i]; ++i) name[i] = p.name[i];
+  for (; i < name_len - 1 && src[i]; ++i) name[i] = src[i];
+  if (p.name[0]) {
+    const char* arch = p.gcnArchName;
+    if (i + 2 < name_len - 1) {
+      name[i++] = ' ';
+      name[i++] = '(';
+      for (; i < name_len - 2 && *arch; ++i) name[i] = *arch++;
+      name[i++] = ')';
+    }
+  }
   name[i] = 0;
   *cus = p.multiProcessorCount;
   *clock_khz = p.clockRate;
