@@ -144,8 +144,8 @@ def cpu_baseline(p, nrows: int, per_row):
     import oracle
     from sparse_mla_flash_amd import inputs
     g = oracle.Geometry.of(p)
-    q, k, qr, kr = (inputs.bf16_bits_to_f64(x) for x in (p.q, p.k, p.qr, p.kr))
-    dout = inputs.bf16_bits_to_f64(p.dout)
+    q, k, qr, kr = (inputs.bits_to_f64(x, p.dtype) for x in (p.q, p.k, p.qr, p.kr))
+    dout = inputs.bits_to_f64(p.dout, p.dtype)
     lo, hi = p.rows - nrows, p.rows
     rows = np.arange(lo, hi)
     out, m, l = oracle.forward(g, q, k, k, qr, kr, p.idx, rows=rows)     # input preparation, untimed
@@ -278,6 +278,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--deterministic", action="store_true")
+    ap.add_argument("--dtype", choices=("bf16", "fp16"), default="bf16",
+                    help="element type of the 16-bit tensors (the workload's values rounded to it)")
     ap.add_argument("--cpu-rows", type=int, default=768)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -300,14 +302,16 @@ def main():
     from sparse_mla_flash_amd import inputs
 
     t_gen = time.perf_counter()
-    p = inputs.workload(args.workload)
+    p = inputs.workload(args.workload, dtype=args.dtype)
     t_gen = time.perf_counter() - t_gen
     print(f"# generated workload {p.name} in {t_gen:.1f} s", file=sys.stderr, flush=True)
+
+    elem = torch.float16 if args.dtype == "fp16" else torch.bfloat16
 
     def dev(bits, raw=False):
         a = np.ascontiguousarray(bits)
         t = torch.from_numpy(a if raw else a.view(np.int16))
-        return (t if raw else t.view(torch.bfloat16)).cuda()
+        return (t if raw else t.view(elem)).cuda()
 
     q, k, v, qr, kr, dout = (dev(x) for x in (p.q, p.k, p.v, p.qr, p.kr, p.dout))
     idx = dev(p.idx, raw=True)
@@ -396,7 +400,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": args.dtype,
         "data": "synthetic",
         "config": {
             "workload": p.name, "layout": p.layout, "B": p.B, "S1": p.S1, "S2": p.S2, "N1": p.N1,

@@ -23,7 +23,12 @@
  *     keeps no pointer after a call returns; the one exception is the fixed
  *     scratch array of the no-allocation entry point (SFAG_NOALLOC_SCRATCH_BYTES
  *     per GPU, created with the library's code on that device).
- *   - bf16 tensors are IEEE bfloat16 bit patterns (uint16).  Statistics are fp32.
+ *   - Every 16-bit tensor of a call (query, key, value, dOut, out, the rope
+ *     tensors and all gradients) has one element type, sfag_dims.dtype: bfloat16
+ *     (SFAG_DTYPE_BF16) or IEEE half (SFAG_DTYPE_FP16), the two dtypes of the
+ *     README's "parameters" table.  Statistics are fp32.  Products run on the
+ *     matching MFMA (bf16 or fp16 operands, fp32 accumulation); the dS / P
+ *     operands of the key-side contractions are rounded to that same type.
  *   - Layout "BSND": query-side [B, S1, N1, W], key-side [B, S2, 1, W],
  *     sparseIndices [B, S1, 1, topk], statistics [B, N1, S1].
  *     Layout "TND": query-side [T1, N1, W], key-side [T2, 1, W],
@@ -52,11 +57,12 @@
  *     the last error of the calling thread is available from sfag_last_error().
  *     Status codes 161001 / 161002 mirror the CANN null-pointer / invalid-
  *     parameter codes (CANN FlashAttention backward page, "return codes").
- *   - Determinism: with deterministic = 0 key gradients are summed with fp32
- *     atomics (run-to-run bit differences are possible, as on the page, which
- *     calls the operator non-deterministic by default, "constraints").  With
- *     deterministic = 1 they are summed in a fixed order and results are
- *     bit-identical across runs for the same inputs, shape and device.
+ *   - Determinism: the page calls the operator non-deterministic by default and
+ *     lets deterministic = 1 ask for reproducible results ("constraints").  Here
+ *     every key gradient is summed in a fixed order in both modes (per-key partial
+ *     sums added in row-segment or (row, position) order; no atomics), so results
+ *     are bit-identical across runs for the same inputs, shape and device whatever
+ *     the flag; it is accepted and validated.
  */
 #ifndef SFAG_H
 #define SFAG_H
@@ -71,7 +77,7 @@ typedef enum {
   SFAG_OK = 0,
   SFAG_ERR_PARAM_NULLPTR = 161001, /* a required pointer is NULL */
   SFAG_ERR_PARAM_INVALID = 161002, /* a shape, attribute or layout violates the constraints */
-  SFAG_ERR_UNSUPPORTED = 161901,   /* legal on the page but not built here (fp16) */
+  SFAG_ERR_UNSUPPORTED = 161901,   /* legal on the page but not built here */
   SFAG_ERR_WORKSPACE = 161902,     /* workspace NULL or smaller than sfag_get_workspace_size() */
   SFAG_ERR_DEVICE = 161903         /* a HIP runtime / launch error */
 } sfag_status;
@@ -85,7 +91,11 @@ typedef struct {
   int64_t D;      /* head width: must be 512 */
   int64_t Drope;  /* rope width: must be 64 */
   int64_t topk;   /* indices per query token (>= 1; the page lists 1024..8192 step 1024) */
+  int64_t dtype;  /* element type of the 16-bit tensors: SFAG_DTYPE_BF16 (0) or SFAG_DTYPE_FP16 (1) */
 } sfag_dims;
+
+#define SFAG_DTYPE_BF16 0
+#define SFAG_DTYPE_FP16 1
 
 /*
  * Bytes of device workspace the backward call needs for these arguments.

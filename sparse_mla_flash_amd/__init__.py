@@ -31,6 +31,8 @@ SFAG_ERR_WORKSPACE = 161902
 SFAG_ERR_DEVICE = 161903
 
 NOALLOC_SCRATCH_BYTES = 256 << 20      # SFAG_NOALLOC_SCRATCH_BYTES
+SFAG_DTYPE_BF16 = 0
+SFAG_DTYPE_FP16 = 1
 
 EXPORTED = ("sfag_get_workspace_size", "sfag_sparse_flash_attention_grad", "sfag_sparse_flash_attention_grad_noalloc",
             "sfag_sparse_flash_attention_forward", "sfag_set_profile_events", "sfag_last_path", "sfag_last_error",
@@ -46,7 +48,7 @@ class SfagError(RuntimeError):
 class Dims(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int64), ("S1", ctypes.c_int64), ("S2", ctypes.c_int64),
                 ("N1", ctypes.c_int64), ("N2", ctypes.c_int64), ("D", ctypes.c_int64),
-                ("Drope", ctypes.c_int64), ("topk", ctypes.c_int64)]
+                ("Drope", ctypes.c_int64), ("topk", ctypes.c_int64), ("dtype", ctypes.c_int64)]
 
 
 _lib = None
@@ -203,7 +205,21 @@ def _dims_from(query, key, sparse_indices, layout: str, seq_len_q, seq_len_kv, q
     else:
         raise ValueError(f"layout must be BSND or TND, got {layout!r}")
     # the rope width is fixed at 64 by the operator; rope tensors are checked against it
-    return Dims(int(B), int(S1), int(S2), int(N1), int(N2), int(D), 64, int(topk))
+    return Dims(int(B), int(S1), int(S2), int(N1), int(N2), int(D), 64, int(topk), _dtype_code(query))
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return SFAG_DTYPE_BF16
+    if t.dtype == torch.float16:
+        return SFAG_DTYPE_FP16
+    raise ValueError(f"query must be bfloat16 or float16, got {t.dtype}")
+
+
+def _elem_dtype(dims: Dims):
+    import torch
+    return torch.float16 if dims.dtype == SFAG_DTYPE_FP16 else torch.bfloat16
 
 
 def _check_shapes(dims: Dims, layout: str, **tensors) -> None:
@@ -258,11 +274,12 @@ def sparse_flash_attention_grad(query, key, value, sparse_indices, d_out, out, s
                                 key_rope=None, *, scale_value: float, sparse_block_size: int = 1,
                                 layout: str = "BSND", sparse_mode: int = 3, pre_tokens: int = 2 ** 31 - 1,
                                 next_tokens: int = 2 ** 31 - 1, deterministic: bool = False, workspace=None):
-    """Backward of sparse MLA attention; returns (dq, dk, dv, dq_rope, dk_rope) as bf16 tensors."""
+    """Backward of sparse MLA attention; returns (dq, dk, dv, dq_rope, dk_rope) in the inputs'
+    element type (bfloat16 or float16: every 16-bit tensor of a call has query's type)."""
     import torch
-    bf = torch.bfloat16
     sq, skv = _seq(actual_seq_lengths_query), _seq(actual_seq_lengths_kv)
     dims = _dims_from(query, key, sparse_indices, layout, sq, skv, query_rope)
+    bf = _elem_dtype(dims)
     _check_shapes(dims, layout, query=query, key=key, value=value, sparse_indices=sparse_indices, d_out=d_out,
                   out=out, softmax_max=softmax_max, softmax_sum=softmax_sum, query_rope=query_rope,
                   key_rope=key_rope)
@@ -292,11 +309,12 @@ def sparse_flash_attention_forward(query, key, value, sparse_indices, actual_seq
                                    scale_value: float, sparse_block_size: int = 1, layout: str = "BSND",
                                    sparse_mode: int = 3, pre_tokens: int = 2 ** 31 - 1,
                                    next_tokens: int = 2 ** 31 - 1):
-    """Sparse forward over the same selection; returns (out bf16, softmax_max fp32, softmax_sum fp32)."""
+    """Sparse forward over the same selection; returns (out in query's element type, softmax_max
+    fp32, softmax_sum fp32)."""
     import torch
-    bf = torch.bfloat16
     sq, skv = _seq(actual_seq_lengths_query), _seq(actual_seq_lengths_kv)
     dims = _dims_from(query, key, sparse_indices, layout, sq, skv, query_rope)
+    bf = _elem_dtype(dims)
     _check_shapes(dims, layout, query=query, key=key, value=value, sparse_indices=sparse_indices,
                   query_rope=query_rope, key_rope=key_rope)
     out = torch.empty_like(query)

@@ -55,6 +55,7 @@ struct Plan {
   sfag::Lens lens;                 // per-batch valid lengths
   // path: key-major dense-masked dK / dV (dense = 1) or per-pair partials (dense = 0)
   int dense = 0;
+  int f16 = 0;                     // 16-bit tensors are fp16 (else bf16)
   double waste = 0.0;              // dense-masked (row, key) entries per valid pair (upper bound)
   int64_t items = 0, citems = 0, maxblk = 0;
   int64_t rec_chunks = 0;          // record chunks of 32 positions per (row, head group)
@@ -129,6 +130,10 @@ sfag_status make_plan(const sfag_dims* dims, const int32_t* sq, const int32_t* s
   if (block < 1) return fail(SFAG_ERR_PARAM_INVALID, "sparseBlockSize must be >= 1 (got %lld)", (long long)block);
   if (!std::isfinite(scale)) return fail(SFAG_ERR_PARAM_INVALID, "scaleValue must be finite");
   if (det != 0 && det != 1) return fail(SFAG_ERR_PARAM_INVALID, "deterministic must be 0 or 1");
+  if (dims->dtype != SFAG_DTYPE_BF16 && dims->dtype != SFAG_DTYPE_FP16)
+    return fail(SFAG_ERR_PARAM_INVALID, "dtype must be SFAG_DTYPE_BF16 (0) or SFAG_DTYPE_FP16 (1) (got %lld)",
+                (long long)dims->dtype);
+  p->f16 = dims->dtype == SFAG_DTYPE_FP16;
 
   p->B = dims->B;
   p->S1 = dims->S1;
@@ -484,6 +489,7 @@ sfag_status backward(const void* query, const void* key, const void* value, cons
   a.hgc = p.hg_count;
   a.rec_chunks = (int)p.rec_chunks;
   a.scale = scale_value;
+  a.f16 = p.f16;
 
   // index sort (both paths): sorted positions, counts, block starts (and the key -> position map
   // of the key-major path)
@@ -515,6 +521,7 @@ sfag_status backward(const void* query, const void* key, const void* value, cons
   da.maxblk = (int)p.maxblk;
   da.rec_chunks = (int)p.rec_chunks;
   da.scale = scale_value;
+  da.f16 = p.f16;
   a.sorted = da.sorted;
   a.count = da.count;
   a.zero_row = da.zero_row;
@@ -575,6 +582,7 @@ sfag_status backward(const void* query, const void* key, const void* value, cons
   pa.rec_chunks = (int)p.rec_chunks;
   pa.nblocks = (int)p.pair_blocks;
   pa.scale = scale_value;
+  pa.f16 = p.f16;
   a.dsp = const_cast<uint16_t*>(pa.dsp);
   a.bt = const_cast<uint16_t*>(pa.bt);
   if (g_ev[0]) SFAG_HIP(hipEventRecord(g_ev[0], s));
@@ -641,6 +649,7 @@ sfag_status sfag_sparse_flash_attention_forward(const void* query, const void* k
   a.mode3 = p.mode3;
   a.layout_tnd = p.tnd;
   a.scale = scale_value;
+  a.f16 = p.f16;
   SFAG_HIP(sfag::launch_fwd(a, p.rows, p.hg_count, s));
   return ok();
 }

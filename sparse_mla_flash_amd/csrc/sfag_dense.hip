@@ -243,7 +243,7 @@ struct KvCtx {
 
 // Main loop of one workgroup with NFT column tiles (9: dK slice, 8: dV slice).  DUPS: some
 // row of the item repeats keys, so units are (row, layer) pairs; otherwise units are rows.
-template <int NFT, bool DUPS>
+template <int NFT, bool DUPS, bool F16>
 __device__ __forceinline__ void kv_dense_units(const DenseArgs& a, const KvCtx& x, uint16_t* Bt0, uint16_t* Bt1) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
@@ -366,7 +366,7 @@ __device__ __forceinline__ void kv_dense_units(const DenseArgs& a, const KvCtx& 
       for (int ft = 0; ft < NFT; ++ft) {
         if (ft + 3 < NFT) bq[ft + 3] = KV_BFRAG(BC, 2 * (ft + 3) + ks);
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) acc[kt][ft] = mfma(f[kt][ks], bq[ft], acc[kt][ft]);
+        for (int kt = 0; kt < 4; ++kt) acc[kt][ft] = mfma_t<F16>(f[kt][ks], bq[ft], acc[kt][ft]);
       }
       // issue order: (ks 0: the next unit's map and B tile loads), three fragments, then
       // (fragment three tiles ahead, 4 MFMAs) per column tile
@@ -405,6 +405,7 @@ __device__ __forceinline__ void kv_dense_units(const DenseArgs& a, const KvCtx& 
       }
 }
 
+template <bool F16>
 __global__ void __launch_bounds__(kThreads, 2) kv_dense_kernel(DenseArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t Bt0[kBtElems], Bt1[kBtElems];
   __shared__ int32_t cum[2 * 257];
@@ -492,11 +493,11 @@ __global__ void __launch_bounds__(kThreads, 2) kv_dense_kernel(DenseArgs a) {
   x.which = x.isdk ? 0 : kRecHalf;
   x.citem = citem;
   if (x.isdk) {
-    if (dups) kv_dense_units<9, true>(a, x, Bt0, Bt1);
-    else kv_dense_units<9, false>(a, x, Bt0, Bt1);
+    if (dups) kv_dense_units<9, true, F16>(a, x, Bt0, Bt1);
+    else kv_dense_units<9, false, F16>(a, x, Bt0, Bt1);
   } else {
-    if (dups) kv_dense_units<8, true>(a, x, Bt0, Bt1);
-    else kv_dense_units<8, false>(a, x, Bt0, Bt1);
+    if (dups) kv_dense_units<8, true, F16>(a, x, Bt0, Bt1);
+    else kv_dense_units<8, false, F16>(a, x, Bt0, Bt1);
   }
   if (threadIdx.x == 0) *flag = 1;
 }
@@ -504,6 +505,7 @@ __global__ void __launch_bounds__(kThreads, 2) kv_dense_kernel(DenseArgs a) {
 // ------------------------------------------------------------------------------------------
 // One workgroup per key row: sum of the partials of its block over (head group, segment) in
 // that fixed order, written as bf16 dK | dKRope | dV.  Padded key rows get zeros.
+template <bool F16>
 __global__ void __launch_bounds__(kThreads) kv_reduce_kernel(DenseArgs a) {
   __shared__ int32_t cum[2 * 257];
   __shared__ int32_t ibase[257];
@@ -541,7 +543,7 @@ __global__ void __launch_bounds__(kThreads) kv_reduce_kernel(DenseArgs a) {
           if (ci < 0) continue;
           s += a.part[(((int64_t)hg * a.citems + ci) * kBk + kr) * kDacc + col];
         }
-    const uint16_t v = f2bf(s);
+    const uint16_t v = f2x<F16>(s);
     if (col < kDn) a.dk[krow * kDn + col] = v;
     else if (col < kDk) {
       if (a.dkr) a.dkr[krow * kDr + col - kDn] = v;
@@ -565,12 +567,18 @@ hipError_t launch_item_list(const DenseArgs& a, hipStream_t st) {
 hipError_t launch_kv_dense(const DenseArgs& a, hipStream_t st) {
   if (a.citems == 0) return hipSuccess;
   const unsigned per_xcd = (unsigned)((a.citems + 7) / 8);   // 8 XCDs x per_xcd items x 8 slices
-  hipLaunchKernelGGL(kv_dense_kernel, dim3(per_xcd * 64, (unsigned)a.hgc), dim3(kThreads), 0, st, a);
+  if (a.f16)
+    hipLaunchKernelGGL(kv_dense_kernel<true>, dim3(per_xcd * 64, (unsigned)a.hgc), dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL(kv_dense_kernel<false>, dim3(per_xcd * 64, (unsigned)a.hgc), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
 hipError_t launch_kv_reduce(const DenseArgs& a, int64_t keys, hipStream_t st) {
-  hipLaunchKernelGGL(kv_reduce_kernel, dim3((unsigned)keys), dim3(kThreads), 0, st, a);
+  if (a.f16)
+    hipLaunchKernelGGL(kv_reduce_kernel<true>, dim3((unsigned)keys), dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL(kv_reduce_kernel<false>, dim3((unsigned)keys), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 

@@ -1,6 +1,6 @@
 // sfag_device.h -- gfx950 device helpers shared by the SparseFlashAttentionGrad kernels.
 //
-// MFMA shape: v_mfma_f32_16x16x32_bf16 (one wave, 64 lanes).  Operand lane layout,
+// MFMA shape: v_mfma_f32_16x16x32_bf16 / _f16 (one wave, 64 lanes).  Operand lane layout,
 // with g = lane / 16 and c = lane % 16:
 //   A (16 x 32, M x K): lane holds A[c][8g + e], e = 0..7
 //   B (32 x 16, K x N): lane holds B[8g + e][c]
@@ -48,6 +48,17 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Element type of the 16-bit tensors: bf16 (F16 = false) or fp16 (F16 = true).  Fragments are
+// carried as bf16x8 bit patterns either way; the MFMA reinterprets them.
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+template <bool F16>
+__device__ __forceinline__ f32x4 mfma_t(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 // element offset of (row, col) in a swizzled tile whose rows hold `row_chunks` 16-byte chunks
@@ -146,6 +157,31 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
   return __builtin_bit_cast(uint32_t, v);
+}
+
+// The same for either element type: fp16 by v_cvt_f16_f32 (nearest even in the default mode;
+// out-of-range values become infinities).
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+template <bool F16>
+__device__ __forceinline__ uint32_t pack_x2(float lo, float hi) {
+  if constexpr (F16) {
+    const f16x2_t v = {(_Float16)lo, (_Float16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+  } else {
+    return pack_bf16x2(lo, hi);
+  }
+}
+
+template <bool F16>
+__device__ __forceinline__ uint16_t f2x(float f) {
+  if constexpr (F16) return __builtin_bit_cast(uint16_t, (_Float16)f);
+  else return f2bf(f);
+}
+
+template <bool F16>
+__device__ __forceinline__ float x2f(uint16_t b) {
+  if constexpr (F16) return (float)__builtin_bit_cast(_Float16, b);
+  else return bf2f(b);
 }
 
 // Geometry of one query row.  BSND: batch b = row / S1, keys of batch b start at b * S2.

@@ -26,6 +26,7 @@ constexpr int kLdsHT = kKC * 64 * 2;
 constexpr int kLdsFwd = kLdsQ + kLdsK + kLdsHT + kKC * 8 + 2 * 257 * 4;
 }  // namespace
 
+template <bool F16>
 __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   uint16_t* Qs = reinterpret_cast<uint16_t*>(smem);
@@ -107,7 +108,7 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
         const bf16x8 qa = lds_read8(Qs, 16 * wave + c, 32 * ks + 8 * g, kQChunks);
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
-          sacc[kt] = mfma(qa, lds_read8(Ks, 16 * kt + c, 32 * ks + 8 * g, kQChunks), sacc[kt]);
+          sacc[kt] = mfma_t<F16>(qa, lds_read8(Ks, 16 * kt + c, 32 * ks + 8 * g, kQChunks), sacc[kt]);
       }
       float z[2][4];
       float cmax[4];
@@ -140,7 +141,7 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
         for (int v = 0; v < 4; ++v) {
           const float p = z[kt][v] == -INFINITY ? 0.f : exp2f(z[kt][v] - mnew[v]);
           psum[v] += p;
-          pb[v] = f2bf(p);
+          pb[v] = f2x<F16>(p);
         }
         const int key = 16 * kt + c, hcol = 16 * wave + 4 * g;
         *reinterpret_cast<uint2*>(PSt + swz(key, hcol, kHtChunks)) =
@@ -161,7 +162,7 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
     if (wave < ntile) {
       const bf16x8 pa = lds_frag_tr(PSt, 0, 16 * wave, kHtChunks, lane);
 #pragma unroll
-      for (int ft = 0; ft < 32; ++ft) oacc[ft] = mfma(pa, lds_frag_tr(Ks, 0, 16 * ft, kQChunks, lane), oacc[ft]);
+      for (int ft = 0; ft < 32; ++ft) oacc[ft] = mfma_t<F16>(pa, lds_frag_tr(Ks, 0, 16 * ft, kQChunks, lane), oacc[ft]);
     }
     __syncthreads();
   }
@@ -174,7 +175,7 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
       const float inv = lrun[v] > 0.f ? 1.f / lrun[v] : 0.f;
       const int64_t hh = row * a.N1 + h0 + h;
 #pragma unroll
-      for (int ft = 0; ft < 32; ++ft) a.out[hh * kDn + 16 * ft + c] = f2bf(oacc[ft][v] * inv);
+      for (int ft = 0; ft < 32; ++ft) a.out[hh * kDn + 16 * ft + c] = f2x<F16>(oacc[ft][v] * inv);
       if (c == 0) {
         const int64_t st = stat_index(a.layout_tnd, geo, row, a.N1, a.S1, h0 + h);
         a.smax[st] = lrun[v] > 0.f ? mrun[v] / kLog2e : 0.f;
@@ -185,12 +186,18 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
 }
 
 hipError_t launch_fwd(const FwdArgs& a, int64_t nrows, int hg_count, hipStream_t st) {
-  hipLaunchKernelGGL(fwd_kernel, dim3((unsigned)nrows, (unsigned)hg_count), dim3(kThreads), kLdsFwd, st, a);
+  if (a.f16)
+    hipLaunchKernelGGL(fwd_kernel<true>, dim3((unsigned)nrows, (unsigned)hg_count), dim3(kThreads), kLdsFwd, st, a);
+  else
+    hipLaunchKernelGGL(fwd_kernel<false>, dim3((unsigned)nrows, (unsigned)hg_count), dim3(kThreads), kLdsFwd, st, a);
   return hipGetLastError();
 }
 
 hipError_t set_fwd_attributes() {
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_kernel),
+  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_kernel<false>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, kLdsFwd);
+  if (e != hipSuccess) return e;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_kernel<true>),
                              hipFuncAttributeMaxDynamicSharedMemorySize, kLdsFwd);
 }
 

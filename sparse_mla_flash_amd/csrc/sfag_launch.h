@@ -46,6 +46,7 @@ struct BwdArgs {
   int bs;                 // sparseBlockSize: topk slots = index count x bs
   int rec_chunks;         // record chunks per (row, head group): ceil(topk / 32)
   float scale;
+  int f16;                // 16-bit tensors are fp16 (else bf16)
 };
 
 struct DenseArgs {
@@ -75,6 +76,7 @@ struct DenseArgs {
   int bs;                 // sparseBlockSize: topk slots = index count x bs
   int rec_chunks;         // record chunks per (row, head group)
   float scale;
+  int f16;                // 16-bit tensors are fp16 (else bf16)
 };
 
 // Per-pair dK / dV of one chunk of query rows [row_begin, row_begin + nrows).
@@ -101,6 +103,7 @@ struct PairArgs {
   int nrows, B, topk, layout_tnd, hgc, maxblk, rec_chunks, nblocks;
   int first, last;        // the chunk is the first / the last one
   float scale;
+  int f16;                // 16-bit tensors are fp16 (else bf16)
 };
 
 struct FwdArgs {
@@ -118,6 +121,7 @@ struct FwdArgs {
   int B, N1, topk, mode3, layout_tnd;
   int bs;                 // sparseBlockSize: topk slots = index count x bs
   float scale;
+  int f16;                // 16-bit tensors are fp16 (else bf16)
 };
 
 // statistics element of head h of a query row (BSND [B, N1, S1], TND [N1, T1])

@@ -232,7 +232,7 @@ __global__ void __launch_bounds__(1024) block_base_kernel(PairArgs a) {
 constexpr int kPairCols = 288;                      // widest slice (18 column tiles)
 constexpr int kPairLds = 2 * kPairCols * 64;        // two head groups, elements
 
-template <int NFT>
+template <int NFT, bool F16>
 __device__ __forceinline__ void pair_kv_row(const PairArgs& a, uint16_t* Bs, int64_t row, int lr, int b,
                                             int colbase, int half, float mul, int lane, int wave,
                                             const int32_t* bstart) {
@@ -261,8 +261,8 @@ __device__ __forceinline__ void pair_kv_row(const PairArgs& a, uint16_t* Bs, int
         for (int ft = 0; ft < NFT; ++ft) {
           const int col = 16 * ft + c;
           const bf16x8 af = *reinterpret_cast<const bf16x8*>(bs + col * 64 + (((2 * g + ks) ^ (col & 7)) << 3));
-          acc[ft][0] = mfma(af, f[0][ks], acc[ft][0]);
-          acc[ft][1] = mfma(af, f[1][ks], acc[ft][1]);
+          acc[ft][0] = mfma_t<F16>(af, f[0][ks], acc[ft][0]);
+          acc[ft][1] = mfma_t<F16>(af, f[1][ks], acc[ft][1]);
         }
     }
     // slots of this lane's two positions (pt = 0, 1)
@@ -281,6 +281,7 @@ __device__ __forceinline__ void pair_kv_row(const PairArgs& a, uint16_t* Bs, int
   }
 }
 
+template <bool F16>
 __global__ void __launch_bounds__(kThreads, 2) pair_kv_kernel(PairArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t Bs[kPairLds];
   __shared__ int32_t cum[2 * 257], bstart[257];
@@ -309,8 +310,8 @@ __global__ void __launch_bounds__(kThreads, 2) pair_kv_kernel(PairArgs a) {
   } else {
     b = (int)(row / a.S1);
   }
-  if (s < 2) pair_kv_row<18>(a, Bs, row, lr, b, colbase, 0, a.scale, lane, wave, bstart);
-  else pair_kv_row<16>(a, Bs, row, lr, b, colbase, kRecHalf, 1.f, lane, wave, bstart);
+  if (s < 2) pair_kv_row<18, F16>(a, Bs, row, lr, b, colbase, 0, a.scale, lane, wave, bstart);
+  else pair_kv_row<16, F16>(a, Bs, row, lr, b, colbase, kRecHalf, 1.f, lane, wave, bstart);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -318,12 +319,14 @@ __global__ void __launch_bounds__(kThreads, 2) pair_kv_kernel(PairArgs a) {
 // fp32 accumulator row (zero in the first chunk).  Lane l holds columns 4 l + 256 j .. + 3 for
 // j < 4 and column 1024 + l.  Middle chunks skip keys without pairs; the last chunk writes bf16
 // dK / dKRope / dV for every key (zeros for keys no row selected).
-__device__ __forceinline__ void store_bf16x4(uint16_t* p, f32x4 v) {
-  const uint32_t lo = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
-  const uint32_t hi = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+template <bool F16>
+__device__ __forceinline__ void store_x4(uint16_t* p, f32x4 v) {
+  const uint32_t lo = (uint32_t)f2x<F16>(v[0]) | ((uint32_t)f2x<F16>(v[1]) << 16);
+  const uint32_t hi = (uint32_t)f2x<F16>(v[2]) | ((uint32_t)f2x<F16>(v[3]) << 16);
   *reinterpret_cast<uint2*>(p) = make_uint2(lo, hi);
 }
 
+template <bool F16>
 __global__ void __launch_bounds__(kThreads) pair_sum_kernel(PairArgs a) {
   __shared__ int32_t cum[2 * 257], bstart[257];
   pair_tables(a, cum, bstart);
@@ -389,15 +392,15 @@ __global__ void __launch_bounds__(kThreads) pair_sum_kernel(PairArgs a) {
     return;
   }
   // columns 0..511 dK, 512..575 dKRope, 576..1087 dV
-  store_bf16x4(a.dk + kg * kDn + 4 * lane, v[0]);
-  store_bf16x4(a.dk + kg * kDn + 256 + 4 * lane, v[1]);
+  store_x4<F16>(a.dk + kg * kDn + 4 * lane, v[0]);
+  store_x4<F16>(a.dk + kg * kDn + 256 + 4 * lane, v[1]);
   if (lane < 16) {
-    if (a.dkr) store_bf16x4(a.dkr + kg * kDr + 4 * lane, v[2]);
+    if (a.dkr) store_x4<F16>(a.dkr + kg * kDr + 4 * lane, v[2]);
   } else {
-    store_bf16x4(a.dv + kg * kDn + 4 * lane - 64, v[2]);
+    store_x4<F16>(a.dv + kg * kDn + 4 * lane - 64, v[2]);
   }
-  store_bf16x4(a.dv + kg * kDn + 192 + 4 * lane, v[3]);
-  a.dv[kg * kDn + 448 + lane] = f2bf(t);
+  store_x4<F16>(a.dv + kg * kDn + 192 + 4 * lane, v[3]);
+  a.dv[kg * kDn + 448 + lane] = f2x<F16>(t);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -406,9 +409,15 @@ hipError_t launch_pair_chunk(const PairArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(pair_slots_kernel, dim3((unsigned)a.nblocks), dim3(kSlotWaves * 64), 0, st, a);
     hipLaunchKernelGGL(block_base_kernel, dim3(1), dim3(1024), 0, st, a);
   }
-  if (a.nrows > 0) hipLaunchKernelGGL(pair_kv_kernel, dim3((unsigned)a.nrows, 4), dim3(kThreads), 0, st, a);
-  if (a.keys > 0)
-    hipLaunchKernelGGL(pair_sum_kernel, dim3((unsigned)((a.keys + 3) / 4)), dim3(kThreads), 0, st, a);
+  if (a.nrows > 0) {
+    if (a.f16) hipLaunchKernelGGL(pair_kv_kernel<true>, dim3((unsigned)a.nrows, 4), dim3(kThreads), 0, st, a);
+    else hipLaunchKernelGGL(pair_kv_kernel<false>, dim3((unsigned)a.nrows, 4), dim3(kThreads), 0, st, a);
+  }
+  if (a.keys > 0) {
+    const dim3 grid((unsigned)((a.keys + 3) / 4));
+    if (a.f16) hipLaunchKernelGGL(pair_sum_kernel<true>, grid, dim3(kThreads), 0, st, a);
+    else hipLaunchKernelGGL(pair_sum_kernel<false>, grid, dim3(kThreads), 0, st, a);
+  }
   return hipGetLastError();
 }
 

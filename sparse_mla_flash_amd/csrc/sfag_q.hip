@@ -52,6 +52,7 @@ constexpr int kWaitVm9 = 0x0009;
 constexpr int kWaitVm10 = 0x000a;
 }  // namespace
 
+template <bool F16>
 __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
   // Separate LDS arrays (not one carved buffer): the compiler can then prove that the
   // direct-to-LDS gather into one key buffer does not alias reads of the others, and does not
@@ -101,8 +102,8 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
         const u32x4 y = *reinterpret_cast<const u32x4*>(otr + e);
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          d += __uint_as_float(x[w] << 16) * __uint_as_float(y[w] << 16);
-          d += __uint_as_float(x[w] & 0xffff0000u) * __uint_as_float(y[w] & 0xffff0000u);
+          d += x2f<F16>((uint16_t)(x[w] & 0xffffu)) * x2f<F16>((uint16_t)(y[w] & 0xffffu));
+          d += x2f<F16>((uint16_t)(x[w] >> 16)) * x2f<F16>((uint16_t)(y[w] >> 16));
         }
       }
     }
@@ -190,11 +191,11 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
         kf0[ks + 2] = *reinterpret_cast<const bf16x8*>(kr0 + 4 * (ks + 2) * kKC * 8);          \
         kf1[ks + 2] = *reinterpret_cast<const bf16x8*>(kr1 + 4 * (ks + 2) * kKC * 8);          \
       }                                                                                        \
-      sacc[0] = mfma(qA[ks], kf0[ks], sacc[0]);                                                \
-      sacc[1] = mfma(qA[ks], kf1[ks], sacc[1]);                                                \
+      sacc[0] = mfma_t<F16>(qA[ks], kf0[ks], sacc[0]);                                                \
+      sacc[1] = mfma_t<F16>(qA[ks], kf1[ks], sacc[1]);                                                \
       if (ks < 16) {                                                                           \
-        pacc[0] = mfma(doA[ks], kf0[ks], pacc[0]);                                             \
-        pacc[1] = mfma(doA[ks], kf1[ks], pacc[1]);                                             \
+        pacc[0] = mfma_t<F16>(doA[ks], kf0[ks], pacc[0]);                                             \
+        pacc[1] = mfma_t<F16>(doA[ks], kf1[ks], pacc[1]);                                             \
       }                                                                                        \
     }                                                                                          \
     /* issue order: the first four fragments, then per step the fragments two steps ahead and \
@@ -222,7 +223,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
     _Pragma("unroll") for (int nt = 0; nt < 9; ++nt) {                                         \
       bf16x8 nb = kb;                                                                          \
       if (nt < 8) nb = tr_frag(kq_ + 512 * (nt + 1), 32);                                      \
-      _Pragma("unroll") for (int t = 0; t < 4; ++t) dqacc[t][nt] = mfma(dsa[t], kb, dqacc[t][nt]); \
+      _Pragma("unroll") for (int t = 0; t < 4; ++t) dqacc[t][nt] = mfma_t<F16>(dsa[t], kb, dqacc[t][nt]); \
       kb = nb;                                                                                 \
     }                                                                                          \
   }
@@ -248,8 +249,8 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
         p[v] = valid ? e_ : 0.f;                                                               \
         ds[v] = p[v] * (pacc[kt][v] - dv[v]);                                                  \
       }                                                                                        \
-      const uint32_t pw[2] = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};               \
-      const uint32_t dw[2] = {pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3])};           \
+      const uint32_t pw[2] = {pack_x2<F16>(p[0], p[1]), pack_x2<F16>(p[2], p[3])};               \
+      const uint32_t dw[2] = {pack_x2<F16>(ds[0], ds[1]), pack_x2<F16>(ds[2], ds[3])};           \
       *reinterpret_cast<uint2*>((DST) + key * kHtPitch + hcol) = make_uint2(dw[0], dw[1]);     \
       *(GlobalU64*)(rec + 16 * 16 * kt) = ((uint64_t)dw[1] << 32) | dw[0];                     \
       *(GlobalU64*)(rec + kRecHalf + 16 * 16 * kt) = ((uint64_t)pw[1] << 32) | pw[0];          \
@@ -413,7 +414,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
 #pragma unroll
         for (int nt = 0; nt < 9; ++nt) {
           const int col = 144 * rw + 16 * nt + c;
-          const uint16_t bv = f2bf(dqacc[t][nt][v] * a.scale);
+          const uint16_t bv = f2x<F16>(dqacc[t][nt][v] * a.scale);
           if (col < kDn) a.dq[hh2 * kDn + col] = bv;
           else if (a.dqr) a.dqr[hh2 * kDr + col - kDn] = bv;
         }
@@ -428,7 +429,10 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
 }
 
 hipError_t launch_bwd_q(const BwdArgs& a, int64_t nrows, int hg_count, hipStream_t st) {
-  hipLaunchKernelGGL(bwd_q_kernel, dim3((unsigned)nrows, (unsigned)hg_count), dim3(kThreads), 0, st, a);
+  if (a.f16)
+    hipLaunchKernelGGL(bwd_q_kernel<true>, dim3((unsigned)nrows, (unsigned)hg_count), dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL(bwd_q_kernel<false>, dim3((unsigned)nrows, (unsigned)hg_count), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 

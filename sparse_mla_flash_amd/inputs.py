@@ -8,8 +8,9 @@ from here, so the two sides always see bit-identical tensors.
 Tensor layouts follow the operator's parameter list (SparseFlashAttentionGrad
 README, "parameters" section): BSND query-side tensors are [B, S1, N1, D], key
 side [B, S2, 1, D]; TND packs tokens as [T, N, D].  Floating-point tensors are
-returned as bfloat16 bit patterns (uint16) drawn as fp32 N(0, 1) and rounded to
-nearest-even; sparseIndices are int32 with -1 marking skipped slots.
+returned as 16-bit patterns (uint16) of the problem's element type, bfloat16 or
+IEEE half (the two dtypes of the parameter table), drawn as fp32 N(0, 1) and
+rounded to nearest-even; sparseIndices are int32 with -1 marking skipped slots.
 
 Random streams: numpy ``SeedSequence(seed).spawn(6)`` in the fixed order
 query, key, queryRope, keyRope, dOut, indices.  ``value`` is a separate copy of
@@ -44,6 +45,34 @@ def bf16_bits_to_f64(b: np.ndarray) -> np.ndarray:
     return bf16_bits_to_f32(b).astype(np.float64)
 
 
+def f32_to_f16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to IEEE half (nearest, ties to even); returns uint16 bits."""
+    return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def f16_bits_to_f64(b: np.ndarray) -> np.ndarray:
+    return np.ascontiguousarray(b, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+DTYPES = ("bf16", "fp16")
+
+
+def f32_to_bits(x: np.ndarray, dtype: str = "bf16") -> np.ndarray:
+    if dtype == "bf16":
+        return f32_to_bf16_bits(x)
+    if dtype == "fp16":
+        return f32_to_f16_bits(x)
+    raise ValueError(f"dtype must be one of {DTYPES}, got {dtype!r}")
+
+
+def bits_to_f64(b: np.ndarray, dtype: str = "bf16") -> np.ndarray:
+    if dtype == "bf16":
+        return bf16_bits_to_f64(b)
+    if dtype == "fp16":
+        return f16_bits_to_f64(b)
+    raise ValueError(f"dtype must be one of {DTYPES}, got {dtype!r}")
+
+
 @dataclasses.dataclass
 class Problem:
     """One synthetic SparseFlashAttentionGrad workload (shapes + seeded tensors)."""
@@ -63,8 +92,9 @@ class Problem:
     deterministic: bool = False
     name: str = ""
     block: int = 1                   # sparseBlockSize: each index names `block` consecutive keys
+    dtype: str = "bf16"              # element type of the 16-bit tensors: "bf16" or "fp16"
     # tensors (filled by generate())
-    q: Optional[np.ndarray] = None       # uint16 bf16 bits
+    q: Optional[np.ndarray] = None       # uint16 bits of the element type
     k: Optional[np.ndarray] = None
     v: Optional[np.ndarray] = None
     qr: Optional[np.ndarray] = None
@@ -243,8 +273,8 @@ def _indices(p: Problem, rng: np.random.Generator, kind: str, window: int) -> np
 # generation
 # ---------------------------------------------------------------------------
 
-def _normal_bf16(rng: np.random.Generator, shape, chunk: int = 1 << 22) -> np.ndarray:
-    """N(0, 1) fp32 values rounded to bf16 bits.  The tensor is cut into fixed chunks of
+def _normal_bits(rng: np.random.Generator, shape, dtype: str = "bf16", chunk: int = 1 << 22) -> np.ndarray:
+    """N(0, 1) fp32 values rounded to the element type's bits.  The tensor is cut into fixed chunks of
     ``chunk`` elements; chunk c is drawn from its own generator, seeded by child c of a
     SeedSequence whose entropy is one draw from ``rng``.  The values therefore depend only on
     ``rng``'s state (not on the number of threads), and the chunks are drawn in parallel."""
@@ -256,7 +286,7 @@ def _normal_bf16(rng: np.random.Generator, shape, chunk: int = 1 << 22) -> np.nd
 
     def fill(c: int) -> None:
         s, e = c * chunk, min(n, (c + 1) * chunk)
-        out[s:e] = f32_to_bf16_bits(np.random.default_rng(kids[c]).standard_normal(e - s, dtype=np.float32))
+        out[s:e] = f32_to_bits(np.random.default_rng(kids[c]).standard_normal(e - s, dtype=np.float32), dtype)
 
     if nchunk <= 1:
         for c in range(nchunk):
@@ -271,20 +301,20 @@ def generate(p: Problem, seed: int, index_kind: str = "uniform", window: int = 4
              fill: str = "normal") -> Problem:
     """Fill p's tensors from ``seed``.
 
-    fill="normal": N(0,1) bf16 values (the benchmark workloads).
+    fill="normal": N(0,1) values in p.dtype (the benchmark workloads).
     fill="ones": every float tensor is 1.0 (the all-ones sample input of the
     dense FlashAttention-grad page), indices still random.
     """
     ss = np.random.SeedSequence(seed).spawn(6)
     rq, rk, rqr, rkr, rdo, ridx = (np.random.default_rng(s) for s in ss)
     if fill == "normal":
-        p.q = _normal_bf16(rq, p.q_shape(p.D))
-        p.k = _normal_bf16(rk, p.k_shape(p.D))
-        p.qr = _normal_bf16(rqr, p.q_shape(p.Dr))
-        p.kr = _normal_bf16(rkr, p.k_shape(p.Dr))
-        p.dout = _normal_bf16(rdo, p.q_shape(p.D))
+        p.q = _normal_bits(rq, p.q_shape(p.D), p.dtype)
+        p.k = _normal_bits(rk, p.k_shape(p.D), p.dtype)
+        p.qr = _normal_bits(rqr, p.q_shape(p.Dr), p.dtype)
+        p.kr = _normal_bits(rkr, p.k_shape(p.Dr), p.dtype)
+        p.dout = _normal_bits(rdo, p.q_shape(p.D), p.dtype)
     elif fill == "ones":
-        one = np.uint16(0x3F80)
+        one = f32_to_bits(np.ones(1, np.float32), p.dtype)[0]
         p.q = np.full(p.q_shape(p.D), one, np.uint16)
         p.k = np.full(p.k_shape(p.D), one, np.uint16)
         p.qr = np.full(p.q_shape(p.Dr), one, np.uint16)
@@ -303,7 +333,9 @@ def fp32(x: float) -> float:
 
 def problem(layout="BSND", B=1, S1=128, S2=128, N1=8, topk=64, sparse_mode=3, seq_q=None,
             seq_kv=None, scale=None, D=D_NOPE, Dr=D_ROPE, deterministic=False, name="",
-            block=1) -> Problem:
+            block=1, dtype="bf16") -> Problem:
+    if dtype not in DTYPES:
+        raise ValueError(f"dtype must be one of {DTYPES}, got {dtype!r}")
     if scale is None:
         scale = 1.0 / math.sqrt(D + Dr)
     if layout == "TND":
@@ -313,7 +345,7 @@ def problem(layout="BSND", B=1, S1=128, S2=128, N1=8, topk=64, sparse_mode=3, se
                    seq_q=None if seq_q is None else [int(x) for x in seq_q],
                    seq_kv=None if seq_kv is None else [int(x) for x in seq_kv],
                    scale=fp32(scale), D=D, Dr=Dr, deterministic=deterministic, name=name,
-                   block=int(block))
+                   block=int(block), dtype=dtype)
 
 
 # The five benchmark workloads (shapes and index structure).  Seed = workload number.
@@ -336,7 +368,7 @@ WORKLOADS = {
 }
 
 
-def workload(n: int, seed: Optional[int] = None) -> Problem:
+def workload(n: int, seed: Optional[int] = None, dtype: str = "bf16") -> Problem:
     w = WORKLOADS[n]
-    p = problem(**w["spec"])
+    p = problem(**w["spec"], dtype=dtype)
     return generate(p, n if seed is None else seed, index_kind=w["kind"])

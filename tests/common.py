@@ -1,5 +1,5 @@
 """Shared helpers of the GPU parity tests: seeded inputs, oracle references in
-"op mode" (the bf16 out and fp32 statistics the GPU receives), device
+"op mode" (the 16-bit out and fp32 statistics the GPU receives), device
 transfer and the tolerance check."""
 
 from __future__ import annotations
@@ -14,14 +14,20 @@ MAX_ABS = 2e-2
 REL_L2 = 5e-3
 
 
-def f64(bits):
-    return inputs.bf16_bits_to_f64(bits)
+def f64(bits, dtype="bf16"):
+    return inputs.bits_to_f64(bits, dtype)
+
+
+# unit roundoff of the 16-bit element types (half an ulp at 1.0)
+UNIT_ROUNDOFF = {"bf16": 2.0 ** -8, "fp16": 2.0 ** -11}
 
 
 def to_dev(bits, dtype="bf16"):
+    """uint16 bits of `dtype` ("bf16" / "fp16") or any other array ("raw") to a GPU tensor."""
     import torch
-    if dtype == "bf16":
-        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+    if dtype in ("bf16", "fp16"):
+        t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+        return t.view(torch.bfloat16 if dtype == "bf16" else torch.float16).cuda()
     return torch.from_numpy(np.ascontiguousarray(bits)).cuda()
 
 
@@ -37,20 +43,22 @@ class Case:
         self.p = p
         self.rope = rope                 # False: the call passes no rope inputs (no rope terms)
         self.g = oracle.Geometry.of(p)
-        self.q, self.k, self.qr, self.kr = f64(p.q), f64(p.k), f64(p.qr), f64(p.kr)
+        self.dtype = p.dtype
+        dt = p.dtype
+        self.q, self.k, self.qr, self.kr = f64(p.q, dt), f64(p.k, dt), f64(p.qr, dt), f64(p.kr, dt)
         if not rope:
             self.qr, self.kr = np.zeros_like(self.qr), np.zeros_like(self.kr)
-        self.v = f64(p.v)
-        self.dout = f64(p.dout)
+        self.v = f64(p.v, dt)
+        self.dout = f64(p.dout, dt)
         self.idx = p.idx
         out64, m64, l64 = oracle.forward(self.g, self.q, self.k, self.v, self.qr, self.kr, self.idx,
                                          rows=fwd_rows)
         self.out64, self.m64, self.l64 = out64, m64, l64
-        # the operator's inputs: out in bf16, statistics in fp32
-        self.out_bits = inputs.f32_to_bf16_bits(out64.astype(np.float32)).reshape(p.q_shape(p.D))
+        # the operator's inputs: out in the element type, statistics in fp32
+        self.out_bits = inputs.f32_to_bits(out64.astype(np.float32), dt).reshape(p.q_shape(p.D))
         self.m32 = m64.astype(np.float32)
         self.l32 = l64.astype(np.float32)
-        self.out_op = f64(self.out_bits)
+        self.out_op = f64(self.out_bits, dt)
 
     # oracle references in op mode
     def ref_dq(self, rows=None):
@@ -64,11 +72,12 @@ class Case:
                                    keys=keys, row_lo=row_lo, row_hi=row_hi)
 
     def device_inputs(self):
-        p = self.p
-        return dict(query=to_dev(p.q), key=to_dev(p.k), value=to_dev(p.v), sparse_indices=to_dev(p.idx, "raw"),
-                    d_out=to_dev(p.dout), out=to_dev(self.out_bits), softmax_max=to_dev(self.m32, "raw"),
-                    softmax_sum=to_dev(self.l32, "raw"), query_rope=to_dev(p.qr) if self.rope else None,
-                    key_rope=to_dev(p.kr) if self.rope else None)
+        p, dt = self.p, self.dtype
+        return dict(query=to_dev(p.q, dt), key=to_dev(p.k, dt), value=to_dev(p.v, dt),
+                    sparse_indices=to_dev(p.idx, "raw"), d_out=to_dev(p.dout, dt), out=to_dev(self.out_bits, dt),
+                    softmax_max=to_dev(self.m32, "raw"), softmax_sum=to_dev(self.l32, "raw"),
+                    query_rope=to_dev(p.qr, dt) if self.rope else None,
+                    key_rope=to_dev(p.kr, dt) if self.rope else None)
 
     def run_gpu(self, deterministic=False, dev=None):
         import sparse_mla_flash_amd as sf
@@ -81,18 +90,18 @@ class Case:
             deterministic=deterministic)
 
 
-def compare(name, got: np.ndarray, ref: np.ndarray, max_abs=MAX_ABS, rel_l2=REL_L2, scaled=True):
+def compare(name, got: np.ndarray, ref: np.ndarray, max_abs=MAX_ABS, rel_l2=REL_L2, scaled=True, u=2.0 ** -8):
     """Tolerance check of one output tensor.
 
     rel-L2 <= 5e-3 always.  The max-abs bar is 2e-2 per element.  With ``scaled`` (the small
     cases) element x of an output row r (a key row of dK / dKRope / dV, a (token, head) row of
     dQ / dQRope: the last axis) may be off by
 
-        2e-2 + 2^-7 |x| + 2^-8 max_r |ref|.
+        2e-2 + 2u |x| + u max_r |ref|,   u = 2^-8 for bf16 (2^-11 for fp16, passed by the caller).
 
-    The second term is one bf16 ulp of the element (the output is rounded to bf16).  The third
-    comes from the bf16 MFMA operands: every product of the sum that forms x carries a relative
-    rounding error of up to 2^-8 (two operands rounded to bf16), so the error of x scales with
+    The second term is one ulp of the element (the output is rounded to the element type).  The
+    third comes from the 16-bit MFMA operands: every product of the sum that forms x carries a
+    relative rounding error of up to 2u (two operands rounded), so the error of x scales with
     the size of the terms summed, not with x after cancellation, and the largest entry of the
     same row is a lower bound of that size.  The small cases draw few slots per key, so a key
     selected by every row (and with p = 1 by the first one) has entries of 10-35 and cancelled
@@ -102,7 +111,7 @@ def compare(name, got: np.ndarray, ref: np.ndarray, max_abs=MAX_ABS, rel_l2=REL_
     diff = np.abs(got - ref)
     if scaled:
         rowmax = np.abs(ref).max(axis=-1, keepdims=True) if ref.ndim and ref.shape[-1] else np.zeros_like(ref)
-        bound = max_abs + (2.0 ** -7) * np.abs(ref) + (2.0 ** -8) * rowmax
+        bound = max_abs + 2 * u * np.abs(ref) + u * rowmax
     else:
         bound = np.full(ref.shape, max_abs)
     ma = float(diff.max()) if diff.size else 0.0
@@ -144,12 +153,13 @@ class TailCase:
         if lay == "BSND":
             sub = inputs.problem("BSND", B=p.B, S1=s1, S2=p.S2, N1=p.N1, topk=p.topk,
                                  sparse_mode=p.sparse_mode, seq_q=self.tail,
-                                 seq_kv=[p.lkv(b) for b in range(p.B)], scale=p.scale, block=p.block)
+                                 seq_kv=[p.lkv(b) for b in range(p.B)], scale=p.scale, block=p.block,
+                                 dtype=p.dtype)
             # sub row of global live row: batch b, position tail-relative
             self.sub_row = np.concatenate([b * s1 + np.arange(self.tail[b]) for b in range(p.B)])
         else:
             sub = inputs.problem("TND", B=p.B, seq_q=self.tail, seq_kv=list(p.seq_kv), N1=p.N1, topk=p.topk,
-                                 sparse_mode=p.sparse_mode, scale=p.scale, block=p.block)
+                                 sparse_mode=p.sparse_mode, scale=p.scale, block=p.block, dtype=p.dtype)
             self.sub_row = np.arange(len(self.live))
         sub.scale = p.scale
         self.sub = sub
@@ -163,14 +173,15 @@ class TailCase:
         self.qr = np.zeros((n, p.N1, p.Dr))
         self.dout = np.zeros((n, p.N1, p.D))
         self.idx = np.full((n, idxf.shape[1]), -1, np.int32)
-        self.q[self.sub_row] = f64(qf[self.live])
-        self.qr[self.sub_row] = f64(qrf[self.live])
-        self.dout[self.sub_row] = f64(dof[self.live])
+        dt = self.dtype = p.dtype
+        self.q[self.sub_row] = f64(qf[self.live], dt)
+        self.qr[self.sub_row] = f64(qrf[self.live], dt)
+        self.dout[self.sub_row] = f64(dof[self.live], dt)
         self.idx[self.sub_row] = idxf[self.live]
-        self.k, self.kr = f64(p.k).reshape(p.keys, p.D), f64(p.kr).reshape(p.keys, p.Dr)
+        self.k, self.kr = f64(p.k, dt).reshape(p.keys, p.D), f64(p.kr, dt).reshape(p.keys, p.Dr)
         out64, m64, l64 = oracle.forward(self.g, self.q, self.k, self.k, self.qr, self.kr, self.idx)
-        self.out_sub_bits = inputs.f32_to_bf16_bits(out64.astype(np.float32))
-        self.out_op = f64(self.out_sub_bits)
+        self.out_sub_bits = inputs.f32_to_bits(out64.astype(np.float32), dt)
+        self.out_op = f64(self.out_sub_bits, dt)
         self.m32 = m64.astype(np.float32)
         self.l32 = l64.astype(np.float32)
         # full-size operator inputs: live rows from the sub-problem, zeros elsewhere
@@ -198,10 +209,11 @@ class TailCase:
             ff[pf(h)] = sf[ps(h)]
 
     def device_inputs(self):
-        p = self.p
-        return dict(query=to_dev(p.q), key=to_dev(p.k), value=to_dev(p.v), sparse_indices=to_dev(p.idx, "raw"),
-                    d_out=to_dev(p.dout), out=to_dev(self.out_bits), softmax_max=to_dev(self.m_full, "raw"),
-                    softmax_sum=to_dev(self.l_full, "raw"), query_rope=to_dev(p.qr), key_rope=to_dev(p.kr))
+        p, dt = self.p, self.dtype
+        return dict(query=to_dev(p.q, dt), key=to_dev(p.k, dt), value=to_dev(p.v, dt),
+                    sparse_indices=to_dev(p.idx, "raw"), d_out=to_dev(p.dout, dt), out=to_dev(self.out_bits, dt),
+                    softmax_max=to_dev(self.m_full, "raw"), softmax_sum=to_dev(self.l_full, "raw"),
+                    query_rope=to_dev(p.qr, dt), key_rope=to_dev(p.kr, dt))
 
     def run_gpu(self, dev, deterministic=False):
         import sparse_mla_flash_amd as sf

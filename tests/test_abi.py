@@ -32,9 +32,9 @@ def test_library_exports_every_declared_function():
 
 
 def dims(**kw):
-    base = dict(B=1, S1=128, S2=4096, N1=8, N2=1, D=512, Drope=64, topk=1024)
+    base = dict(B=1, S1=128, S2=4096, N1=8, N2=1, D=512, Drope=64, topk=1024, dtype=sf.SFAG_DTYPE_BF16)
     base.update(kw)
-    return Dims(*[base[k] for k in ("B", "S1", "S2", "N1", "N2", "D", "Drope", "topk")])
+    return Dims(*[base[k] for k in ("B", "S1", "S2", "N1", "N2", "D", "Drope", "topk", "dtype")])
 
 
 def ws(d, **kw):
@@ -53,7 +53,8 @@ def status_of(fn, *a, **kw):
 
 
 @pytest.mark.parametrize("field,value", [("N2", 2), ("D", 128), ("Drope", 32), ("N1", 5), ("N1", 256),
-                                         ("B", 0), ("B", 257), ("S1", 0), ("S2", 131073), ("topk", 0)])
+                                         ("B", 0), ("B", 257), ("S1", 0), ("S2", 131073), ("topk", 0),
+                                         ("dtype", 2), ("dtype", -1)])
 def test_invalid_shapes(field, value):
     assert status_of(ws, dims(**{field: value})) == sf.SFAG_ERR_PARAM_INVALID
     assert field.lower() in sf.sfag_last_error().lower() or value is not None
@@ -222,3 +223,21 @@ def test_noalloc_rejects_problems_beyond_its_scratch():
         None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, dims(), 1 / 24, 1, "BSND", 3,
         2 ** 31 - 1, 2 ** 31 - 1, False, FAKE, FAKE, FAKE, FAKE, FAKE, None)
     assert st == sf.SFAG_ERR_PARAM_NULLPTR
+
+
+def test_fp16_dims_accepted_and_sized_like_bf16():
+    """Both element types of the page's dtype column are accepted; the workspace does not depend
+    on the element type (records and copies are 16-bit either way)."""
+    for kw in (dict(), dict(S1=8192, S2=8192, N1=64, topk=2048), dict(S1=4096, S2=131072, N1=128, topk=2048)):
+        assert ws(dims(dtype=sf.SFAG_DTYPE_FP16, **kw)) == ws(dims(**kw))
+
+
+def test_wrapper_takes_the_element_type_from_query():
+    import torch
+    q = torch.zeros(1, 4, 8, 512, dtype=torch.float16)
+    k = torch.zeros(1, 16, 1, 512, dtype=torch.float16)
+    idx = torch.zeros(1, 4, 1, 8, dtype=torch.int32)
+    assert sf._dims_from(q, k, idx, "BSND", None, None).dtype == sf.SFAG_DTYPE_FP16
+    assert sf._dims_from(q.bfloat16(), k.bfloat16(), idx, "BSND", None, None).dtype == sf.SFAG_DTYPE_BF16
+    with pytest.raises(ValueError):
+        sf._dims_from(q.float(), k.float(), idx, "BSND", None, None)

@@ -6,8 +6,8 @@ fp32 statistics).  Sizes are small enough for the oracle to finish in seconds
 while spanning several 32-key chunks, several 16-head tiles and a ragged tail;
 edge cases cover padding, empty rows, invalid / duplicate indices, varlen TND
 with an empty sequence, S1 > S2 under the causal mode, every head-group
-shape the kernels special-case (N1 < 16, N1 not a multiple of 16, N1 = 128)
-and block selection (sparseBlockSize 4, 16, 64).
+shape the kernels special-case (N1 < 16, N1 not a multiple of 16, N1 = 128),
+B = 256, block selection (sparseBlockSize 4, 16, 64) and fp16 tensors.
 """
 
 import numpy as np
@@ -34,6 +34,13 @@ CASES = {
     "bsnd_n64_window": (dict(layout="BSND", B=1, S1=48, S2=2048, N1=64, topk=64, sparse_mode=3), "window", 9),
     "bsnd_n48_hotcold_nomask": (dict(layout="BSND", B=2, S1=16, S2=400, N1=48, topk=96, sparse_mode=0),
                                 "hot_cold", 10),
+    # the rest of the head counts the constraints list (6, 24) and the largest batch count (256)
+    "bsnd_n6_causal": (dict(layout="BSND", B=1, S1=30, S2=200, N1=6, topk=40, sparse_mode=3), "uniform", 11),
+    "bsnd_n24_nomask": (dict(layout="BSND", B=1, S1=20, S2=150, N1=24, topk=50, sparse_mode=0), "uniform", 12),
+    "bsnd_b256_n4": (dict(layout="BSND", B=256, S1=2, S2=24, N1=4, topk=8, sparse_mode=3), "uniform", 13),
+    "tnd_b256_n2_varlen": (dict(layout="TND", B=256, seq_q=[(7 * b) % 5 for b in range(256)],
+                                seq_kv=[1 + (11 * b) % 23 for b in range(256)], N1=2, topk=8, sparse_mode=3),
+                           "uniform", 14),
 }
 
 
@@ -206,3 +213,66 @@ def test_heavy_duplicates(path):
     p.idx = r.integers(0, 10, size=p.idx_shape()).astype(np.int32)
     case = Case(p)
     check_all(case, case.run_gpu(), "dups/")
+
+
+FP16_CASES = ["bsnd_n8_causal_tail", "bsnd_n64_short_prefix", "bsnd_n128_nomask", "bsnd_n48_padded_batches",
+              "tnd_n16_varlen_empty_seq", "bsnd_n64_window", "bsnd_n6_causal"]
+
+
+def make_fp16(name):
+    kw, kind, seed = CASES[name]
+    p = inputs.problem(**kw, name=name, dtype="fp16")
+    inputs.generate(p, seed, index_kind=kind, window=256)
+    return p
+
+
+@pytest.mark.parametrize("name", FP16_CASES)
+def test_fp16_backward_matches_oracle(name, path):
+    """fp16 tensors (the page's second dtype) on both dK / dV paths.  fp16 carries 11 significant
+    bits against bf16's 8, so the bound uses fp16's unit roundoff and rel-L2 <= 1e-3: a path that
+    rounded its MFMA operands to bf16 would miss it (about 3e-3 here)."""
+    import torch
+    case = Case(make_fp16(name))
+    outs = case.run_gpu()
+    assert all(t.dtype == torch.float16 for t in outs if t is not None)
+    dq, dk, dv, dqr, dkr = (from_dev(t) for t in outs)
+    rdq, rdqr = case.ref_dq()
+    rdk, rdkr, rdv = case.ref_dkv()
+    u = 2.0 ** -11
+    res = {}
+    for nm, got, ref in (("dq", dq, rdq), ("dq_rope", dqr, rdqr), ("dk", dk, rdk), ("dk_rope", dkr, rdkr),
+                         ("dv", dv, rdv)):
+        res[nm] = compare(f"{name}/{path}/fp16/{nm}", got, ref, rel_l2=1e-3, u=u)
+    print(name, path, "fp16", {k: f"{v[0]:.2e}/{v[1]:.2e}" for k, v in res.items()})
+
+
+@pytest.mark.parametrize("name", ["bsnd_n64_short_prefix", "tnd_n16_varlen_empty_seq"])
+def test_fp16_forward_matches_oracle(name):
+    import sparse_mla_flash_amd as sf
+    import torch
+    p = make_fp16(name)
+    case = Case(p)
+    d = case.device_inputs()
+    out, smax, ssum = sf.sparse_flash_attention_forward(
+        d["query"], d["key"], d["value"], d["sparse_indices"], p.seq_q, p.seq_kv, d["query_rope"],
+        d["key_rope"], scale_value=p.scale, layout=p.layout, sparse_mode=p.sparse_mode)
+    assert out.dtype == torch.float16
+    compare(name + "/fp16/out", from_dev(out), case.out64, rel_l2=1e-3, u=2.0 ** -11)
+    m, l = from_dev(smax), from_dev(ssum)
+    assert np.abs(m - case.m64).max() <= 1e-4 * max(1.0, np.abs(case.m64).max())
+    assert np.abs(l - case.l64).max() <= 1e-4 * max(1.0, np.abs(case.l64).max())
+
+
+def test_fp16_and_bf16_calls_agree_on_the_same_values():
+    """Inputs that both types hold exactly (bf16 values inside fp16's range) give the same
+    gradients up to the output rounding of each type, so neither path reads the other's bits."""
+    import torch
+    name = "bsnd_n64_short_prefix"
+    case = Case(make(name))
+    d16 = {k: (v.to(torch.float16) if v is not None and v.dtype == torch.bfloat16 else v)
+           for k, v in case.device_inputs().items()}
+    a = case.run_gpu()
+    b = case.run_gpu(dev=d16)
+    assert b[0].dtype == torch.float16
+    for nm, x, y in zip(("dq", "dk", "dv", "dq_rope", "dk_rope"), a, b):
+        compare(f"{name}/bf16-vs-fp16/{nm}", from_dev(y), from_dev(x))      # the bf16 bar

@@ -108,3 +108,22 @@ def test_generation_is_seeded():
     assert not np.array_equal(a.q, c.q)
     assert np.array_equal(a.k, a.v) and a.k is not a.v
     assert a.q.shape == (12, 2, 512) and a.k.shape == (16, 1, 512) and a.idx.shape == (12, 1, 8)
+
+
+def test_fp16_rounding_is_nearest_even_and_generation_matches_bf16_draws():
+    x = np.array([1.0, 1.0 + 2 ** -11, 1.0 + 3 * 2 ** -11, -2.5, 6.0e-8, 70000.0], np.float32)
+    back = inputs.f16_bits_to_f64(inputs.f32_to_f16_bits(x))
+    assert back[1] == 1.0                           # tie between 1 and 1 + 2^-10 goes to even
+    assert back[2] == 1.0 + 2 ** -9                 # tie between 1 + 2^-10 and 1 + 2^-9: even is 2^-9
+    assert back[3] == -2.5 and back[4] == 2.0 ** -24 and np.isinf(back[5])
+    # the same seed draws the same fp32 normals for both element types: only the rounding differs
+    pb = inputs.problem("BSND", B=1, S1=8, S2=32, N1=4, topk=8)
+    ph = inputs.problem("BSND", B=1, S1=8, S2=32, N1=4, topk=8, dtype="fp16")
+    inputs.generate(pb, 11)
+    inputs.generate(ph, 11)
+    a, b = inputs.bits_to_f64(pb.q, "bf16"), inputs.bits_to_f64(ph.q, "fp16")
+    assert np.all(np.abs(a - b) <= 2 ** -8 * np.abs(b) + 1e-7)
+    assert not np.array_equal(a, b)
+    assert (pb.idx == ph.idx).all()
+    with pytest.raises(ValueError):
+        inputs.problem("BSND", dtype="fp32")
