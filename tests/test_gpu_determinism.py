@@ -1,12 +1,12 @@
 """Deterministic mode: bit-identical outputs over repeated runs, including under heavy
-dK / dV contention (every query selects the same hot keys), and agreement with the
-default (atomic) mode within the parity tolerance."""
+dK / dV contention (every query selects the same hot keys), on both dK / dV paths.  Both
+paths sum in a fixed order whatever the flag, so the default mode gives the same bits."""
 
 import numpy as np
 import pytest
 
 from sparse_mla_flash_amd import inputs
-from tests.common import Case, compare, from_dev
+from tests.common import Case
 
 pytestmark = pytest.mark.gpu
 
@@ -31,7 +31,6 @@ def test_deterministic_runs_are_bit_identical(kind, kw, path, monkeypatch):
         again = [_bits(t) for t in case.run_gpu(deterministic=True, dev=dev)]
         for a, b in zip(first, again):
             assert np.array_equal(a, b)
-    atomic = [from_dev(t) for t in case.run_gpu(deterministic=False, dev=dev)]
-    det = [from_dev(t) for t in case.run_gpu(deterministic=True, dev=dev)]
-    for x, y in zip(atomic, det):
-        compare("det-vs-atomic", x, y)
+    default = [_bits(t) for t in case.run_gpu(deterministic=False, dev=dev)]
+    for a, b in zip(first, default):
+        assert np.array_equal(a, b)

@@ -66,7 +66,7 @@ def check_all(case: Case, outs, label=""):
 
 @pytest.fixture(params=["dense", "scatter"])
 def path(request, monkeypatch):
-    """dK / dV path: key-major dense-masked kernels, or per-pair scatter (atomic / partials)."""
+    """dK / dV path: key-major dense-masked kernels, or the per-pair partials path."""
     monkeypatch.setenv("SFAG_FORCE_PATH", request.param)
     return request.param
 
