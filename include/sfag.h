@@ -189,8 +189,8 @@ sfag_status sfag_sparse_flash_attention_forward(
  * the given hipEvent_t handles on its stream around its two main stages, so that a caller
  * can time them with hipEventElapsedTime:
  *   stage 1 (`s1_begin`, `s1_end`): key-major path: the query-major kernel (scores, dS, P,
- *     dQ); scatter path: the whole main sequence (main kernel, and in deterministic mode
- *     the partial / sort / ordered-reduce launches);
+ *     dQ); per-pair path: the whole chunk loop (query-major kernel, slot sort, partials and
+ *     per-key sums of every chunk);
  *   stage 2 (`s2_begin`, `s2_end`): key-major path only: the key-major dK / dV kernel.
  * A NULL handle is not recorded.  All NULL (the default) disables recording.  The events
  * stay owned by the caller.  Always returns SFAG_OK.
@@ -199,10 +199,56 @@ sfag_status sfag_set_profile_events(void* s1_begin, void* s1_end, void* s2_begin
 
 /*
  * dK / dV path taken by the calling thread's last successful backward call: 0 = key-major
- * dense-masked kernels, 1 = per-pair scatter (atomic or partials), -1 = no call yet.  The
+ * dense-masked kernels, 1 = per-pair partials, -1 = no call yet.  The
  * path follows from the shapes alone (see sfag_sparse_flash_attention_grad).
  */
 int32_t sfag_last_path(void);
+
+/*
+ * Lightning-indexer backward with KL loss (DenseLightningIndexerGradKLLoss README,
+ * "function description" and "parameters"): per query token t over the keys its mask admits,
+ *   S[g, s] = queryIndex[t, g] . keyIndex[s],  I[s] = sum_g weights[t, g] ReLU(S[g, s]);
+ *   p[s] = sum over the N1 main heads of exp(scale (q . k + qRope . kRope) - softmaxMax) /
+ *          softmaxSum, L1-normalised over s (the head-summed main attention);
+ *   loss = sum_t KL(p || Softmax(I)) with Softmax(I)[s] = exp(I[s] - softmaxMaxIndex[t]) /
+ *          softmaxSumIndex[t];
+ *   dI = Softmax(I) - p;  dWeights[t, g] = sum_s dI[s] ReLU(S[g, s]);
+ *   dS = dI weights [S > 0];  dQueryIndex[t, g] = sum_s dS[g, s] keyIndex[s];
+ *   dKeyIndex[s] = sum_t sum_g dS[g, s] queryIndex[t, g].
+ * Layouts follow the sparse operator: BSND query [B, S1, N1, 512], key [B, S2, 1, 512], rope
+ * [.., 64], queryIndex [B, S1, G, 128], keyIndex [B, S2, 1, 128], weights [B, S1, G], main
+ * statistics [B, N1, S1], index statistics [B, S1]; TND the same without B ([T, ...], main
+ * statistics [N1, T1], index statistics [T1]).  The mask is the sparse operator's (sparseMode 3:
+ * keys s <= t + Lkv - Lq; mode 0: all keys of the sequence); pre/nextTokens are accepted and
+ * ignored.  The 16-bit tensors share sfag_indexer_dims.dtype; statistics and the loss are fp32.
+ * The actual sequence lengths are int64 host arrays (the page's INT64), optional for BSND and
+ * required for TND.  queryRope / keyRope may both be NULL (no rope terms).
+ * Outputs are overwritten completely (tokens or keys without admitted pairs get zeros); `loss`
+ * is one fp32 value on the device.  Summation orders are fixed: results are bit-reproducible.
+ * Errors and asynchrony as for the backward above; workspace from the size query below.
+ */
+typedef struct {
+  int64_t B, S1, S2;   /* as in sfag_dims */
+  int64_t N1;          /* main query heads, 1..128 */
+  int64_t G;           /* index heads of queryIndex / weights, 1..64 */
+  int64_t D;           /* 512 */
+  int64_t Drope;       /* 64 */
+  int64_t Di;          /* index head width: 128 */
+  int64_t dtype;       /* SFAG_DTYPE_BF16 or SFAG_DTYPE_FP16 */
+} sfag_indexer_dims;
+
+sfag_status sfag_lightning_indexer_grad_get_workspace_size(const sfag_indexer_dims* dims,
+                                                         const int64_t* seq_len_q_host,
+                                                         const int64_t* seq_len_kv_host, const char* layout,
+                                                         int64_t sparse_mode, uint64_t* workspace_size);
+
+sfag_status sfag_dense_lightning_indexer_grad_kl_loss(
+    const void* query, const void* key, const void* query_index, const void* key_index, const void* weights,
+    const float* softmax_max, const float* softmax_sum, const float* softmax_max_index,
+    const float* softmax_sum_index, const void* query_rope, const void* key_rope, const int64_t* seq_len_q_host,
+    const int64_t* seq_len_kv_host, const sfag_indexer_dims* dims, double scale_value, const char* layout,
+    int64_t sparse_mode, int64_t pre_tokens, int64_t next_tokens, void* d_query_index, void* d_key_index,
+    void* d_weights, float* loss, void* workspace, uint64_t workspace_size, void* stream);
 
 /* Text of the calling thread's last non-OK status ("" if none). */
 const char* sfag_last_error(void);

@@ -128,6 +128,28 @@ def index_stats(geo: IndexerGeometry, qi, ki, w):
     return m, s
 
 
+def main_stats(geo: IndexerGeometry, q, k, qr, kr):
+    """The main attention's forward statistics over every admitted key (input preparation for the
+    tests): per (token, head) the max of the scaled logits and the sum of exp(logit - max), laid
+    out [B, N1, S1] / [N1, T1]; tokens without keys get max 0, sum 0."""
+    sm = np.zeros(geo.B * geo.N1 * geo.S1 if geo.layout == "BSND" else geo.N1 * geo.S1)
+    ss = np.zeros_like(sm)
+    qf, qrf = _flat(q, geo.rows, geo.D), _flat(qr, geo.rows, geo.Dr)
+    kf, krf = _flat(k, geo.keys, geo.D)[:, 0], _flat(kr, geo.keys, geo.Dr)[:, 0]
+    for row in range(geo.rows):
+        b, i = geo.token(row)
+        hi = geo.hi(b, i)
+        if hi < 0:
+            continue
+        k0 = geo.k0(b)
+        z = geo.scale * (qf[row] @ kf[k0:k0 + hi + 1].T + qrf[row] @ krf[k0:k0 + hi + 1].T)
+        for h in range(geo.N1):
+            j = geo.stat_index(b, i, h)
+            sm[j] = z[h].max()
+            ss[j] = np.exp(z[h] - sm[j]).sum()
+    return sm, ss
+
+
 def target(geo: IndexerGeometry, q, k, qr, kr, smax, ssum, row: int):
     """Step 2 for one query row: the L1-normalised head sum of the main attention's softmax."""
     b, i = geo.token(row)

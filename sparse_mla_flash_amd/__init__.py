@@ -36,7 +36,8 @@ SFAG_DTYPE_FP16 = 1
 
 EXPORTED = ("sfag_get_workspace_size", "sfag_sparse_flash_attention_grad", "sfag_sparse_flash_attention_grad_noalloc",
             "sfag_sparse_flash_attention_forward", "sfag_set_profile_events", "sfag_last_path", "sfag_last_error",
-            "sfag_version")
+            "sfag_version", "sfag_lightning_indexer_grad_get_workspace_size",
+            "sfag_dense_lightning_indexer_grad_kl_loss")
 
 
 class SfagError(RuntimeError):
@@ -49,6 +50,12 @@ class Dims(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int64), ("S1", ctypes.c_int64), ("S2", ctypes.c_int64),
                 ("N1", ctypes.c_int64), ("N2", ctypes.c_int64), ("D", ctypes.c_int64),
                 ("Drope", ctypes.c_int64), ("topk", ctypes.c_int64), ("dtype", ctypes.c_int64)]
+
+
+class IndexerDims(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("S1", ctypes.c_int64), ("S2", ctypes.c_int64), ("N1", ctypes.c_int64),
+                ("G", ctypes.c_int64), ("D", ctypes.c_int64), ("Drope", ctypes.c_int64), ("Di", ctypes.c_int64),
+                ("dtype", ctypes.c_int64)]
 
 
 _lib = None
@@ -82,6 +89,14 @@ def lib():
             vp, vp, vp, vp, i32p, i32p, vp, vp, ctypes.POINTER(Dims), ctypes.c_float,
             ctypes.c_int64, ctypes.c_char_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
             vp, vp, vp, vp]
+        i64p = ctypes.POINTER(ctypes.c_int64)
+        L.sfag_lightning_indexer_grad_get_workspace_size.restype = ctypes.c_int
+        L.sfag_lightning_indexer_grad_get_workspace_size.argtypes = [
+            ctypes.POINTER(IndexerDims), i64p, i64p, ctypes.c_char_p, ctypes.c_int64, ctypes.POINTER(ctypes.c_uint64)]
+        L.sfag_dense_lightning_indexer_grad_kl_loss.restype = ctypes.c_int
+        L.sfag_dense_lightning_indexer_grad_kl_loss.argtypes = [
+            vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64p, i64p, ctypes.POINTER(IndexerDims), ctypes.c_double,
+            ctypes.c_char_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, vp, vp, vp, vp, vp, ctypes.c_uint64, vp]
         L.sfag_set_profile_events.restype = ctypes.c_int
         L.sfag_set_profile_events.argtypes = [vp, vp, vp, vp]
         L.sfag_last_path.restype = ctypes.c_int32
@@ -331,3 +346,110 @@ def sparse_flash_attention_forward(query, key, value, sparse_indices, actual_seq
         next_tokens, out.data_ptr(), smax.data_ptr(), ssum.data_ptr(), _stream())
     _check(st)
     return out, smax, ssum
+
+
+# ---- lightning-indexer backward with KL loss ------------------------------------------------------
+
+def _lens64(x: Optional[Sequence[int]]):
+    if x is None:
+        return None, None
+    arr = (ctypes.c_int64 * len(x))(*[int(v) for v in x])
+    return arr, ctypes.cast(arr, ctypes.POINTER(ctypes.c_int64))
+
+
+def sfag_lightning_indexer_grad_get_workspace_size(dims: IndexerDims, seq_len_q=None, seq_len_kv=None,
+                                                   layout: str = "BSND", sparse_mode: int = 3) -> int:
+    a, q = _lens64(seq_len_q)
+    b, kv = _lens64(seq_len_kv)
+    out = ctypes.c_uint64(0)
+    _check(lib().sfag_lightning_indexer_grad_get_workspace_size(ctypes.byref(dims), q, kv, layout.encode(),
+                                                                int(sparse_mode), ctypes.byref(out)))
+    del a, b
+    return int(out.value)
+
+
+def sfag_dense_lightning_indexer_grad_kl_loss(query, key, query_index, key_index, weights, softmax_max,
+                                              softmax_sum, softmax_max_index, softmax_sum_index, query_rope,
+                                              key_rope, seq_len_q, seq_len_kv, dims: IndexerDims, scale_value,
+                                              layout, sparse_mode, pre_tokens, next_tokens, d_query_index,
+                                              d_key_index, d_weights, loss, workspace, workspace_size,
+                                              stream) -> int:
+    """Raw C call: every tensor argument is a device address (int) or None; returns the status."""
+    a, q = _lens64(seq_len_q)
+    b, kv = _lens64(seq_len_kv)
+    st = lib().sfag_dense_lightning_indexer_grad_kl_loss(
+        query, key, query_index, key_index, weights, softmax_max, softmax_sum, softmax_max_index,
+        softmax_sum_index, query_rope, key_rope, q, kv, ctypes.byref(dims), float(scale_value), layout.encode(),
+        int(sparse_mode), int(pre_tokens), int(next_tokens), d_query_index, d_key_index, d_weights, loss,
+        workspace, int(workspace_size), stream)
+    del a, b
+    return st
+
+
+def _indexer_dims(query, key, query_index, weights, layout: str, seq_len_q) -> IndexerDims:
+    if layout == "BSND":
+        if query.dim() != 4 or key.dim() != 4 or query_index.dim() != 4 or weights.dim() != 3:
+            raise ValueError("BSND expects query [B,S1,N1,512], key [B,S2,1,512], query_index [B,S1,G,128], "
+                             "weights [B,S1,G]")
+        B, S1, N1, D = query.shape
+        S2 = key.shape[1]
+        G, Di = query_index.shape[2], query_index.shape[3]
+    elif layout == "TND":
+        if query.dim() != 3 or key.dim() != 3 or query_index.dim() != 3 or weights.dim() != 2:
+            raise ValueError("TND expects query [T1,N1,512], key [T2,1,512], query_index [T1,G,128], weights [T1,G]")
+        if seq_len_q is None:
+            raise ValueError("TND needs actual_seq_lengths_query and actual_seq_lengths_kv")
+        S1, N1, D = query.shape
+        S2 = key.shape[0]
+        B = len(seq_len_q)
+        G, Di = query_index.shape[1], query_index.shape[2]
+    else:
+        raise ValueError(f"layout must be BSND or TND, got {layout!r}")
+    return IndexerDims(int(B), int(S1), int(S2), int(N1), int(G), int(D), 64, int(Di), _dtype_code(query))
+
+
+def lightning_indexer_grad_kl_loss(query, key, query_index, key_index, weights, softmax_max, softmax_sum,
+                                   softmax_max_index, softmax_sum_index, actual_seq_lengths_query=None,
+                                   actual_seq_lengths_kv=None, query_rope=None, key_rope=None, *,
+                                   scale_value: float, layout: str = "BSND", sparse_mode: int = 3,
+                                   pre_tokens: int = 2 ** 31 - 1, next_tokens: int = 2 ** 31 - 1, workspace=None):
+    """Backward of the lightning indexer with its KL loss; returns (d_query_index, d_key_index,
+    d_weights, loss): gradients in the inputs' element type, loss a one-element fp32 tensor."""
+    import torch
+    sq, skv = _seq(actual_seq_lengths_query), _seq(actual_seq_lengths_kv)
+    dims = _indexer_dims(query, key, query_index, weights, layout, sq)
+    B, S1, S2, N1, G = dims.B, dims.S1, dims.S2, dims.N1, dims.G
+    if layout == "BSND":
+        want = dict(query=(B, S1, N1, 512), key=(B, S2, 1, 512), query_index=(B, S1, G, 128),
+                    key_index=(B, S2, 1, 128), weights=(B, S1, G), softmax_max=(B, N1, S1), softmax_sum=(B, N1, S1),
+                    softmax_max_index=(B, S1), softmax_sum_index=(B, S1), query_rope=(B, S1, N1, 64),
+                    key_rope=(B, S2, 1, 64))
+    else:
+        want = dict(query=(S1, N1, 512), key=(S2, 1, 512), query_index=(S1, G, 128), key_index=(S2, 1, 128),
+                    weights=(S1, G), softmax_max=(N1, S1), softmax_sum=(N1, S1), softmax_max_index=(S1,),
+                    softmax_sum_index=(S1,), query_rope=(S1, N1, 64), key_rope=(S2, 1, 64))
+    given = dict(query=query, key=key, query_index=query_index, key_index=key_index, weights=weights,
+                 softmax_max=softmax_max, softmax_sum=softmax_sum, softmax_max_index=softmax_max_index,
+                 softmax_sum_index=softmax_sum_index, query_rope=query_rope, key_rope=key_rope)
+    for name, t in given.items():
+        if t is not None and tuple(t.shape) != want[name]:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {want[name]} for layout {layout}")
+    el = _elem_dtype(dims)
+    f32 = torch.float32
+    ws = sfag_lightning_indexer_grad_get_workspace_size(dims, sq, skv, layout, sparse_mode)
+    if workspace is None or workspace.numel() < ws:
+        workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=query.device)
+    dqi = torch.empty_like(query_index)
+    dki = torch.empty_like(key_index)
+    dw = torch.empty_like(weights)
+    loss = torch.empty(1, dtype=f32, device=query.device)
+    st = sfag_dense_lightning_indexer_grad_kl_loss(
+        _dev(query, "query", el), _dev(key, "key", el), _dev(query_index, "query_index", el),
+        _dev(key_index, "key_index", el), _dev(weights, "weights", el), _dev(softmax_max, "softmax_max", f32),
+        _dev(softmax_sum, "softmax_sum", f32), _dev(softmax_max_index, "softmax_max_index", f32),
+        _dev(softmax_sum_index, "softmax_sum_index", f32), _dev(query_rope, "query_rope", el),
+        _dev(key_rope, "key_rope", el), sq, skv, dims, scale_value, layout, sparse_mode, pre_tokens, next_tokens,
+        dqi.data_ptr(), dki.data_ptr(), dw.data_ptr(), loss.data_ptr(), workspace.data_ptr(), workspace.numel(),
+        _stream())
+    _check(st)
+    return dqi, dki, dw, loss

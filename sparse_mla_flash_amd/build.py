@@ -21,7 +21,7 @@ LIB = os.path.join(HERE, "libsfag.so")
 CEIL_SRC = os.path.join(HERE, "microbench", "ceilings.hip")
 CEIL_LIB = os.path.join(HERE, "microbench", "libceilings.so")
 
-SOURCES = ["sfag_pair.hip", "sfag_q.hip", "sfag_dense.hip", "sfag_fwd.hip", "sfag_api.cpp"]
+SOURCES = ["sfag_pair.hip", "sfag_q.hip", "sfag_dense.hip", "sfag_fwd.hip", "sfag_indexer.hip", "sfag_api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = [

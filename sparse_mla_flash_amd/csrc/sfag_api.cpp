@@ -601,6 +601,98 @@ sfag_status backward(const void* query, const void* key, const void* value, cons
   return ok();
 }
 
+// ---- lightning-indexer backward --------------------------------------------------------------
+struct IxPlan {
+  int tnd = 0, mode3 = 0;
+  int64_t B = 0, S1 = 0, S2 = 0, N1 = 0, G = 0, rows = 0, keys = 0, kstride = 0, key_tiles = 0;
+  int parts = 1;
+  sfag::Lens lens;
+  uint64_t off_tot = 0, off_norm = 0, off_lrow = 0, off_dkp = 0, bytes = 0;
+};
+
+constexpr int kIxKeyTile = 64;
+
+sfag_status make_ix_plan(const sfag_indexer_dims* d, const int64_t* sq, const int64_t* skv, const char* layout,
+                         int64_t mode, IxPlan* p) {
+  if (!d) return fail(SFAG_ERR_PARAM_NULLPTR, "dims is NULL");
+  if (!layout) return fail(SFAG_ERR_PARAM_NULLPTR, "layout is NULL");
+  if (std::strcmp(layout, "BSND") == 0) p->tnd = 0;
+  else if (std::strcmp(layout, "TND") == 0) p->tnd = 1;
+  else return fail(SFAG_ERR_PARAM_INVALID, "layout must be \"BSND\" or \"TND\", got \"%s\"", layout);
+  if (d->D != 512) return fail(SFAG_ERR_PARAM_INVALID, "D must be 512 (got %lld)", (long long)d->D);
+  if (d->Drope != 64) return fail(SFAG_ERR_PARAM_INVALID, "Drope must be 64 (got %lld)", (long long)d->Drope);
+  if (d->Di != sfag::kIxDi) return fail(SFAG_ERR_PARAM_INVALID, "Di must be 128 (got %lld)", (long long)d->Di);
+  if (d->N1 < 1 || d->N1 > 128) return fail(SFAG_ERR_PARAM_INVALID, "N1 must be in 1..128 (got %lld)", (long long)d->N1);
+  if (d->G < 1 || d->G > 64) return fail(SFAG_ERR_PARAM_INVALID, "G must be in 1..64 (got %lld)", (long long)d->G);
+  if (d->B < 1 || d->B > 256) return fail(SFAG_ERR_PARAM_INVALID, "B must be in 1..256 (got %lld)", (long long)d->B);
+  if (d->dtype != SFAG_DTYPE_BF16 && d->dtype != SFAG_DTYPE_FP16)
+    return fail(SFAG_ERR_PARAM_INVALID, "dtype must be SFAG_DTYPE_BF16 (0) or SFAG_DTYPE_FP16 (1) (got %lld)",
+                (long long)d->dtype);
+  if (mode != 0 && mode != 3) return fail(SFAG_ERR_PARAM_INVALID, "sparseMode must be 0 or 3 (got %lld)", (long long)mode);
+  p->mode3 = mode == 3;
+  p->B = d->B;
+  p->S1 = d->S1;
+  p->S2 = d->S2;
+  p->N1 = d->N1;
+  p->G = d->G;
+  std::memset(&p->lens, 0, sizeof(p->lens));
+  int64_t maxkv = 0;
+  if (!p->tnd) {
+    if (p->S1 < 1 || p->S1 > kMaxSeq || p->S2 < 1 || p->S2 > kMaxSeq)
+      return fail(SFAG_ERR_PARAM_INVALID, "S1 and S2 must be in 1..131072 (got %lld, %lld)", (long long)p->S1,
+                  (long long)p->S2);
+    for (int64_t b = 0; b < p->B; ++b) {
+      const int64_t lq = sq ? sq[b] : p->S1, lkv = skv ? skv[b] : p->S2;
+      if (lq < 0 || lq > p->S1 || lkv < 0 || lkv > p->S2)
+        return fail(SFAG_ERR_PARAM_INVALID, "actual sequence lengths of batch %lld out of range (%lld, %lld)",
+                    (long long)b, (long long)lq, (long long)lkv);
+      p->lens.lq[b] = (int32_t)lq;
+      p->lens.lkv[b] = (int32_t)lkv;
+    }
+    p->rows = p->B * p->S1;
+    p->keys = p->B * p->S2;
+    maxkv = p->S2;
+  } else {
+    if (!sq || !skv) return fail(SFAG_ERR_PARAM_NULLPTR, "TND layout needs both actual sequence length arrays");
+    int64_t cq = 0, ckv = 0;
+    for (int64_t b = 0; b < p->B; ++b) {
+      if (sq[b] < 0 || sq[b] > kMaxSeq || skv[b] < 0 || skv[b] > kMaxSeq)
+        return fail(SFAG_ERR_PARAM_INVALID, "sequence %lld lengths out of range (%lld, %lld)", (long long)b,
+                    (long long)sq[b], (long long)skv[b]);
+      p->lens.lq[b] = (int32_t)sq[b];
+      p->lens.lkv[b] = (int32_t)skv[b];
+      cq += sq[b];
+      ckv += skv[b];
+      maxkv = std::max<int64_t>(maxkv, skv[b]);
+    }
+    if (cq != p->S1 || ckv != p->S2)
+      return fail(SFAG_ERR_PARAM_INVALID, "TND: query / key lengths sum to %lld / %lld but dims give T1=%lld T2=%lld",
+                  (long long)cq, (long long)ckv, (long long)p->S1, (long long)p->S2);
+    if (cq < 1 || ckv < 1) return fail(SFAG_ERR_PARAM_INVALID, "TND: no query or key tokens");
+    p->rows = cq;
+    p->keys = ckv;
+  }
+  p->kstride = std::max<int64_t>(maxkv, 1);
+  int64_t tiles = 0;
+  for (int64_t b = 0; b < p->B; ++b)
+    tiles += ((p->tnd ? p->lens.lkv[b] : p->S2) + kIxKeyTile - 1) / kIxKeyTile;
+  p->key_tiles = tiles;
+  // split every key tile's query rows so that the key kernel has about 1024 workgroups
+  const int64_t t1 = std::max<int64_t>(tiles, 1);
+  p->parts = (int)std::max<int64_t>(1, std::min<int64_t>(32, (1024 + t1 - 1) / t1));
+  uint64_t off = 0;
+  p->off_tot = off;
+  off = align_up(off + (uint64_t)p->rows * p->kstride * 4);
+  p->off_norm = off;
+  off = align_up(off + (uint64_t)p->rows * 4);
+  p->off_lrow = off;
+  off = align_up(off + (uint64_t)p->rows * 4);
+  p->off_dkp = off;
+  off = align_up(off + (uint64_t)p->parts * p->keys * sfag::kIxDi * 4);
+  p->bytes = off;
+  return SFAG_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -651,6 +743,94 @@ sfag_status sfag_sparse_flash_attention_forward(const void* query, const void* k
   a.scale = scale_value;
   a.f16 = p.f16;
   SFAG_HIP(sfag::launch_fwd(a, p.rows, p.hg_count, s));
+  return ok();
+}
+
+sfag_status sfag_lightning_indexer_grad_get_workspace_size(const sfag_indexer_dims* dims,
+                                                         const int64_t* seq_len_q_host,
+                                                         const int64_t* seq_len_kv_host, const char* layout,
+                                                         int64_t sparse_mode, uint64_t* workspace_size) {
+  if (!workspace_size) return fail(SFAG_ERR_PARAM_NULLPTR, "workspace_size is NULL");
+  IxPlan p;
+  const sfag_status st = make_ix_plan(dims, seq_len_q_host, seq_len_kv_host, layout, sparse_mode, &p);
+  if (st != SFAG_OK) return st;
+  *workspace_size = p.bytes;
+  return ok();
+}
+
+sfag_status sfag_dense_lightning_indexer_grad_kl_loss(
+    const void* query, const void* key, const void* query_index, const void* key_index, const void* weights,
+    const float* softmax_max, const float* softmax_sum, const float* softmax_max_index,
+    const float* softmax_sum_index, const void* query_rope, const void* key_rope, const int64_t* seq_len_q_host,
+    const int64_t* seq_len_kv_host, const sfag_indexer_dims* dims, double scale_value, const char* layout,
+    int64_t sparse_mode, int64_t pre_tokens, int64_t next_tokens, void* d_query_index, void* d_key_index,
+    void* d_weights, float* loss, void* workspace, uint64_t workspace_size, void* stream) {
+  (void)pre_tokens;
+  (void)next_tokens;
+  sfag_status st;
+  // 16-byte rows are read as whole pieces: these need 16-byte alignment; the others are read
+  // element by element
+  const struct { const void* p; const char* n; bool al; } req[] = {
+      {query, "query", true}, {key, "key", true}, {query_index, "query_index", true},
+      {key_index, "key_index", true}, {weights, "weights", false}, {softmax_max, "softmax_max", false},
+      {softmax_sum, "softmax_sum", false}, {softmax_max_index, "softmax_max_index", false},
+      {softmax_sum_index, "softmax_sum_index", false}, {d_query_index, "d_query_index", false},
+      {d_key_index, "d_key_index", false}, {d_weights, "d_weights", false}, {loss, "loss", false}};
+  for (const auto& r : req) {
+    if (!r.p) return fail(SFAG_ERR_PARAM_NULLPTR, "%s is NULL", r.n);
+    if (r.al && (st = check_ptr(r.p, r.n)) != SFAG_OK) return st;
+  }
+  if ((query_rope == nullptr) != (key_rope == nullptr))
+    return fail(SFAG_ERR_PARAM_INVALID, "query_rope and key_rope must both be given or both be NULL");
+  if (query_rope) {
+    if ((st = check_ptr(query_rope, "query_rope")) != SFAG_OK) return st;
+    if ((st = check_ptr(key_rope, "key_rope")) != SFAG_OK) return st;
+  }
+  if (!std::isfinite(scale_value)) return fail(SFAG_ERR_PARAM_INVALID, "scaleValue must be finite");
+  IxPlan p;
+  if ((st = make_ix_plan(dims, seq_len_q_host, seq_len_kv_host, layout, sparse_mode, &p)) != SFAG_OK) return st;
+  if (workspace_size < p.bytes || (p.bytes > 0 && !workspace))
+    return fail(SFAG_ERR_WORKSPACE, "workspace of %llu bytes needed, got %llu%s", (unsigned long long)p.bytes,
+                (unsigned long long)workspace_size, workspace ? "" : " (NULL)");
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign)
+    return fail(SFAG_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if ((st = init_device()) != SFAG_OK) return st;
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  sfag::IxArgs a{};
+  a.q = static_cast<const uint16_t*>(query);
+  a.qr = static_cast<const uint16_t*>(query_rope);
+  a.k = static_cast<const uint16_t*>(key);
+  a.kr = static_cast<const uint16_t*>(key_rope);
+  a.qi = static_cast<const uint16_t*>(query_index);
+  a.ki = static_cast<const uint16_t*>(key_index);
+  a.w = static_cast<const uint16_t*>(weights);
+  a.smax = softmax_max;
+  a.ssum = softmax_sum;
+  a.smax_i = softmax_max_index;
+  a.ssum_i = softmax_sum_index;
+  a.dqi = static_cast<uint16_t*>(d_query_index);
+  a.dki = static_cast<uint16_t*>(d_key_index);
+  a.dw = static_cast<uint16_t*>(d_weights);
+  a.loss = loss;
+  a.tot = reinterpret_cast<float*>(ws + p.off_tot);
+  a.norm = reinterpret_cast<float*>(ws + p.off_norm);
+  a.lrow = reinterpret_cast<float*>(ws + p.off_lrow);
+  a.dkp = reinterpret_cast<float*>(ws + p.off_dkp);
+  a.lens = p.lens;
+  a.S1 = p.S1;
+  a.S2 = p.S2;
+  a.kstride = p.kstride;
+  a.rows = p.rows;
+  a.keys = p.keys;
+  a.B = (int)p.B;
+  a.N1 = (int)p.N1;
+  a.G = (int)p.G;
+  a.mode3 = p.mode3;
+  a.layout_tnd = p.tnd;
+  a.parts = p.parts;
+  a.scale = (float)scale_value;
+  a.f16 = dims->dtype == SFAG_DTYPE_FP16;
+  SFAG_HIP(sfag::launch_indexer(a, p.key_tiles, reinterpret_cast<hipStream_t>(stream)));
   return ok();
 }
 

@@ -1,0 +1,539 @@
+// sfag_indexer.hip -- backward of the lightning indexer with its KL loss (gfx950).
+//
+// DenseLightningIndexerGradKLLoss README, "function description": per query token t and the keys
+// s its mask admits,
+//   index scores  S[g, s] = q~[t, g] . K~[s],   I[s] = sum_g W[t, g] ReLU(S[g, s])
+//   target        p[s] = head-summed main-attention softmax, L1-normalised over s
+//   loss          sum_t KL(p || Softmax(I))
+//   gradients     dI = Softmax(I) - p,  dW[t, g] = sum_s dI[s] ReLU(S[g, s]),
+//                 dS = dI W [S > 0],  dq~[t, g] = sum_s dS[g, s] K~[s],  dK~[s] += dS^T q~[t].
+// The main softmax is rebuilt from the forward's statistics on the MLA logits q . k + qRope .
+// kRope (times scaleValue), and Softmax(I) from the indexer forward's statistics.
+//
+// Kernels:
+//   ix_query_kernel  one workgroup of 8 waves per query row, keys in chunks of 32 (key rows
+//                    staged in LDS, next chunk loaded while this one is computed).  Main waves
+//                    0-3 (head tiles w, w + 4) form the main scores on the MFMA and the chunk's
+//                    head-summed softmax; index waves 4-7 (index-head tile w - 4) form S and
+//                    their part of I.  After a barrier the index waves form Softmax(I) and the
+//                    gradient terms, and add dq~ on the MFMA.  The head sum's L1 norm is known
+//                    only after the last chunk, so the chunk terms use 1 / (heads) and a second
+//                    accumulator carries the correction (1 / heads - 1 / norm), applied at the
+//                    end: exact for any statistics, and without cancellation in 16-bit operands
+//                    (the main term is the small difference itself).  Writes dq~, dW, the row's
+//                    loss and norm, and the head sum of every (row, key) for the key kernel.
+//   ix_key_kernel    workgroup = (64 keys, part of the query rows): per query row, S for its
+//                    keys (recomputed on the MFMA), Softmax(I), dI = Softmax(I) - sum / norm,
+//                    dS, and dK~ += dS^T q~ on the MFMA into registers; fp32 partials per part.
+//   ix_finish_kernel dK~ = sum of the parts in part order, and the loss = sum of the rows' losses
+//                    in row order (one workgroup); deterministic.
+#include "sfag_device.h"
+#include "sfag_launch.h"
+
+namespace sfag {
+
+namespace {
+constexpr int kIxThreads = 512;                   // query kernel: 8 waves
+constexpr int kIxKC = 32;                         // keys per chunk
+constexpr int kKPitch = kDk + 8;                  // 584: main key rows (512 + 64 rope) in LDS
+constexpr int kIPitch = kIxDi + 8;                // 136: index rows in LDS
+constexpr int kDsPitch = kIxKC + 8;               // 40: [16 heads][32 keys] gradient tiles
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kKeyThreads = 256;                  // key kernel: 4 waves of 16 keys
+constexpr int kKeyTile = 64;
+constexpr int kDkPitch = 64 + 8;                  // [16 keys][64 index heads] dS tile per wave
+
+__device__ __forceinline__ float wsum16(float v) {  // sum over the 16 lanes c of a 16-lane group
+  v += __shfl_xor(v, 1);
+  v += __shfl_xor(v, 2);
+  v += __shfl_xor(v, 4);
+  v += __shfl_xor(v, 8);
+  return v;
+}
+}  // namespace
+
+// ------------------------------------------------------------------------------------------
+template <bool F16>
+__global__ void __launch_bounds__(kIxThreads, 1) ix_query_kernel(IxArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t Kt[2][kIxKC * kKPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t Ki[2][kIxKC * kIPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t Dt[4][2][16 * kDsPitch];   // per index wave: dS', T
+  __shared__ float sP[4][kIxKC];                 // per main wave: softmax summed over its heads
+  __shared__ float sI[4][kIxKC];                 // per index wave: its part of I
+  __shared__ float sM[128], sIL[128];            // main statistics (log2 domain), 1 / sum
+  __shared__ float sRed[4];
+  __shared__ int32_t cum[2 * 257];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4, c = lane & 15;
+  const int64_t row = (int64_t)gridDim.x - 1 - blockIdx.x;     // long rows first
+  if (a.layout_tnd) {
+    cum_lengths(a.lens, a.B, cum);
+    __syncthreads();
+  }
+  const RowGeo geo = row_geo(a.lens, cum, a.B, a.layout_tnd, a.S1, a.S2, row, a.mode3);
+  const int G = a.G;
+  const int nit = (G + 15) >> 4;                  // index-head tiles (<= 4)
+  const int nmt = (a.N1 + 15) >> 4;               // main-head tiles (<= 8)
+  const bool live = geo.active && geo.hi >= 0 && a.ssum_i[row] > 0.f;
+  if (!live) {
+    for (int e = threadIdx.x; e < G * kIxDi; e += kIxThreads) a.dqi[row * G * kIxDi + e] = 0;
+    for (int e = threadIdx.x; e < G; e += kIxThreads) a.dw[row * G + e] = 0;
+    if (threadIdx.x == 0) {
+      a.lrow[row] = 0.f;
+      a.norm[row] = 0.f;
+    }
+    return;
+  }
+  const int nkeys = geo.hi + 1;
+  const int nchunk = (nkeys + kIxKC - 1) / kIxKC;
+  const float zscale = a.scale * kLog2e;
+  // main statistics; heads with an empty sum take no part (their softmax is zero)
+  for (int h = threadIdx.x; h < 128; h += kIxThreads) {
+    float m = 0.f, il = 0.f;
+    if (h < a.N1) {
+      const int64_t j = stat_index(a.layout_tnd, geo, row, a.N1, a.S1, h);
+      const float l = a.ssum[j];
+      if (l > 0.f) {
+        m = a.smax[j] * kLog2e;
+        il = 1.f / l;
+      }
+    }
+    sM[h] = m;
+    sIL[h] = il;
+  }
+  __syncthreads();
+  int heads = 0;
+  for (int h = 0; h < a.N1; ++h) heads += sIL[h] > 0.f ? 1 : 0;
+  const float inv_heads = heads > 0 ? 1.f / (float)heads : 0.f;
+  const float max_i = a.smax_i[row], lsum_i = __logf(a.ssum_i[row]);
+
+  // chunk staging: key row r of chunk ci is key ci * 32 + r (rows past the last admitted key,
+  // and the rope pieces of a rope-less call, are zeros); 72 + 16 sixteen-byte pieces per row
+  const uint16_t* kbase = a.k + geo.kstart * kDn;
+  const bool has_rope = a.kr != nullptr;
+  const uint16_t* krbase = has_rope ? a.kr + geo.kstart * kDr : kbase;   // not read without rope
+  const uint16_t* kibase = a.ki + geo.kstart * kIxDi;
+  constexpr int kPieces = kIxKC * (kDk / 8 + kIxDi / 8);       // 2816
+  constexpr int kPer = (kPieces + kIxThreads - 1) / kIxThreads;  // 6
+  u32x4 stage[kPer];
+  auto load_chunk = [&](int ci) {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int e = (int)threadIdx.x + kIxThreads * u;
+      if (e < kPieces) {
+        const int r = e / 88, j = e % 88;
+        const int key = ci * kIxKC + r;
+        const bool ok = key < nkeys && (j < 64 || j >= 72 || has_rope);
+        const uint16_t* src = j < 64 ? kbase + (int64_t)key * kDn + 8 * j
+                              : j < 72 ? krbase + (int64_t)key * kDr + 8 * (j - 64)
+                                       : kibase + (int64_t)key * kIxDi + 8 * (j - 72);
+        stage[u] = ok ? *reinterpret_cast<const u32x4*>(src) : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  auto store_chunk = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int e = (int)threadIdx.x + kIxThreads * u;
+      if (e < kPieces) {
+        const int r = e / 88, j = e % 88;
+        uint16_t* dst = j < 72 ? &Kt[buf][r * kKPitch + 8 * j] : &Ki[buf][r * kIPitch + 8 * (j - 72)];
+        *reinterpret_cast<u32x4*>(dst) = stage[u];
+      }
+    }
+  };
+
+  // Two roles with separate loops (their registers are never live together) and the same two
+  // barriers per chunk.  Main waves 0-3: head tiles w and w + 4.  Index waves 4-7: index-head
+  // tile w - 4.
+  if (wave < 4) {
+    // A operands: Q of head 16 t + c (dims 32 ks + 8 g; steps 16, 17: rope), for t = w, w + 4
+    bf16x8 qA[2][18];
+    bool has[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int t = wave + 4 * u;
+      has[u] = t < nmt;
+      const int h = 16 * t + c;
+      const bool okh = has[u] && h < a.N1;
+      const uint16_t* qrow = a.q + (row * a.N1 + min(h, a.N1 - 1)) * kDn;
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks)
+        qA[u][ks] = okh ? *reinterpret_cast<const bf16x8*>(qrow + 32 * ks + 8 * g) : bf16x8{};
+#pragma unroll
+      for (int ks = 16; ks < 18; ++ks)
+        qA[u][ks] = (okh && a.qr)
+                        ? *reinterpret_cast<const bf16x8*>(a.qr + (row * a.N1 + h) * kDr + 32 * (ks - 16) + 8 * g)
+                        : bf16x8{};
+    }
+    load_chunk(0);
+    store_chunk(0);
+    __syncthreads();
+    for (int ci = 0; ci < nchunk; ++ci) {
+      const int buf = ci & 1;
+      if (ci + 1 < nchunk) load_chunk(ci + 1);
+      const int s0 = ci * kIxKC;
+      float ps[2] = {0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        if (!has[u]) continue;
+        const int t = wave + 4 * u;
+        f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int ks = 0; ks < 18; ++ks)
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
+            sacc[kt] = mfma_t<F16>(qA[u][ks], lds_read8p(Kt[buf], 16 * kt + c, 32 * ks + 8 * g, kKPitch), sacc[kt]);
+        const f32x4 mv = *reinterpret_cast<const f32x4*>(sM + 16 * t + 4 * g);
+        const f32x4 iv = *reinterpret_cast<const f32x4*>(sIL + 16 * t + 4 * g);
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) ps[kt] += __builtin_amdgcn_exp2f(sacc[kt][v] * zscale - mv[v]) * iv[v];
+      }
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        float p = ps[kt];
+        p += __shfl_xor(p, 16);
+        p += __shfl_xor(p, 32);
+        if (g == 0) sP[wave][16 * kt + c] = s0 + 16 * kt + c < nkeys ? p : 0.f;
+      }
+      lds_barrier();
+      if (ci + 1 < nchunk) store_chunk(buf ^ 1);
+      lds_barrier();
+    }
+    __syncthreads();                              // the index waves' row results
+    return;
+  }
+
+  const int it = wave - 4;
+  const bool hasi = it < nit;
+  bf16x8 qiA[4];
+  float wv[4];                                    // W of this lane's C rows (index heads 16 it + 4 g + v)
+  {
+    const int h = 16 * it + c;
+    const bool okh = hasi && h < G;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      qiA[ks] = okh ? *reinterpret_cast<const bf16x8*>(a.qi + (row * G + h) * kIxDi + 32 * ks + 8 * g) : bf16x8{};
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int hh = 16 * it + 4 * g + v;
+      wv[v] = (hasi && hh < G) ? x2f<F16>(a.w[row * G + hh]) : 0.f;
+    }
+  }
+  // accumulators: dq~ (main term and correction term), dW terms, loss terms
+  f32x4 qacc[8], tacc[8];
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt) qacc[nt] = tacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float aw[4] = {0.f, 0.f, 0.f, 0.f}, bw[4] = {0.f, 0.f, 0.f, 0.f};
+  float l1 = 0.f, nrm = 0.f;
+
+  load_chunk(0);
+  store_chunk(0);
+  __syncthreads();
+  for (int ci = 0; ci < nchunk; ++ci) {
+    const int buf = ci & 1;
+    if (ci + 1 < nchunk) load_chunk(ci + 1);
+    const int s0 = ci * kIxKC;
+    // index scores and this tile's part of I
+    f32x4 iacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    if (hasi) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+          iacc[kt] = mfma_t<F16>(qiA[ks], lds_read8p(Ki[buf], 16 * kt + c, 32 * ks + 8 * g, kIPitch), iacc[kt]);
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        float is = 0.f;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) is += wv[v] * fmaxf(iacc[kt][v], 0.f);
+        is += __shfl_xor(is, 16);
+        is += __shfl_xor(is, 32);
+        if (g == 0) sI[it][16 * kt + c] = is;
+      }
+    }
+    lds_barrier();
+    // gradient terms of the chunk
+    if (hasi) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const int key = 16 * kt + c;
+        const bool valid = s0 + key < nkeys;
+        const float tot = valid ? sP[0][key] + sP[1][key] + sP[2][key] + sP[3][key] : 0.f;
+        float ival = 0.f;
+        for (int u = 0; u < nit; ++u) ival += sI[u][key];
+        const float lsm = ival - max_i - lsum_i;   // log Softmax(I)
+        const float sm = valid ? __expf(lsm) : 0.f;
+        const float dip = sm - tot * inv_heads;   // dI with the provisional norm
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float s = iacc[kt][v];
+          const float relu = fmaxf(s, 0.f);
+          aw[v] += dip * relu;
+          bw[v] += tot * relu;
+          Dt[it][0][(4 * g + v) * kDsPitch + key] = f2x<F16>(s > 0.f ? dip : 0.f);
+          Dt[it][1][(4 * g + v) * kDsPitch + key] = f2x<F16>(s > 0.f ? tot : 0.f);
+        }
+        if (it == 0 && g == 0 && valid) {
+          if (tot > 0.f) l1 += tot * (__logf(tot) - lsm);
+          nrm += tot;
+          a.tot[row * a.kstride + s0 + key] = tot;
+        }
+      }
+    }
+    if (ci + 1 < nchunk) store_chunk(buf ^ 1);
+    lds_barrier();
+    // dq~ += dS' K~ and the correction term T K~
+    if (hasi) {
+      const bf16x8 da = *reinterpret_cast<const bf16x8*>(&Dt[it][0][c * kDsPitch + 8 * g]);
+      const bf16x8 ta = *reinterpret_cast<const bf16x8*>(&Dt[it][1][c * kDsPitch + 8 * g]);
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) {
+        const bf16x8 kb = lds_frag_trp(Ki[buf], 0, 16 * nt, kIPitch, lane);
+        qacc[nt] = mfma_t<F16>(da, kb, qacc[nt]);
+        tacc[nt] = mfma_t<F16>(ta, kb, tacc[nt]);
+      }
+    }
+  }
+
+  // ---- row results ----
+  if (it == 0) {
+    l1 = wsum16(l1);
+    nrm = wsum16(nrm);
+    if (lane == 0) {
+      sRed[0] = l1;
+      sRed[1] = nrm;
+    }
+  }
+  __syncthreads();
+  const float norm = sRed[1];
+  const float corr = norm > 0.f ? inv_heads - 1.f / norm : 0.f;
+  if (wave == 4 && lane == 0) {
+    a.norm[row] = norm;
+    a.lrow[row] = norm > 0.f ? sRed[0] / norm - __logf(norm) : 0.f;
+  }
+  if (hasi) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const float d = wsum16(aw[v]) + corr * wsum16(bw[v]);
+      const int hh = 16 * it + 4 * g + v;
+      if (c == 0 && hh < G) a.dw[row * G + hh] = f2x<F16>(d);
+    }
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int hh = 16 * it + 4 * g + v;
+        if (hh < G)
+          a.dqi[(row * G + hh) * kIxDi + 16 * nt + c] = f2x<F16>(wv[v] * (qacc[nt][v] + corr * tacc[nt][v]));
+      }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// dK~ partials: workgroup = (64 keys of one batch, part of that batch's query rows); wave w owns
+// keys 16 w .. 16 w + 15 of the tile.  Per query row: S'[key][head] = K~[key] . q~[head] (A =
+// this wave's K~ rows, held in registers; B = the row's q~ tile in LDS), I, Softmax(I),
+// dI = Softmax(I) - sum / norm, dS'[key][head] = dI W [S' > 0] (through a per-wave LDS tile),
+// and dK~[key][dims] += dS' q~ on the MFMA.
+template <bool F16>
+__global__ void __launch_bounds__(kKeyThreads, 2) ix_key_kernel(IxArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t Qt[2][64 * kIPitch];     // [index head][dims]
+  __shared__ __attribute__((aligned(16))) uint16_t Dk[4][16 * kDkPitch];    // per wave [key][head]
+  __shared__ float sW[2][64];
+  __shared__ int32_t cum[2 * 257], kbase_tile[257];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4, c = lane & 15;
+  const int G = a.G;
+  // tile -> batch: tiles of 64 keys per batch, numbered batch by batch
+  for (int t = threadIdx.x; t <= a.B; t += blockDim.x) {
+    int32_t sq = 0, skv = 0, nt = 0;
+    for (int b = 0; b < t; ++b) {
+      const int lq = a.layout_tnd ? a.lens.lq[b] : (int)a.S1;
+      const int lk = a.layout_tnd ? a.lens.lkv[b] : (int)a.S2;
+      sq += lq;
+      skv += lk;
+      nt += (lk + kKeyTile - 1) / kKeyTile;
+    }
+    cum[t] = sq;
+    cum[257 + t] = skv;
+    kbase_tile[t] = nt;
+  }
+  __syncthreads();
+  const int tile = blockIdx.x, part = blockIdx.y;
+  int b = 0;
+  {
+    int lo = 0, hi = a.B - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (kbase_tile[mid] <= tile) lo = mid; else hi = mid - 1;
+    }
+    b = lo;
+  }
+  const int lq = a.lens.lq[b], lkv = a.lens.lkv[b];
+  const int nk = a.layout_tnd ? lkv : (int)a.S2;     // key rows of the batch (BSND: padded too)
+  const int kt0 = (tile - kbase_tile[b]) * kKeyTile;
+  const int64_t q0 = cum[b], k0 = cum[257 + b];
+  // query rows that admit a key of the tile: i >= kt0 - (lkv - lq) under the causal mode
+  int ilo = 0;
+  if (a.mode3) ilo = max(0, kt0 - (lkv - lq));
+  if (kt0 >= lkv) ilo = lq;                           // padded keys: no row admits them
+  const int span = max(0, lq - ilo);
+  const int per = (span + a.parts - 1) / a.parts;
+  const int i0 = min(lq, ilo + part * per), i1 = min(lq, i0 + per);
+
+  // this wave's keys: rows of the A operand (K~, dims 32 ks + 8 g), zero past the batch's keys
+  const int mykey = kt0 + 16 * wave + c;
+  bf16x8 kA[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+    kA[ks] = mykey < lkv ? *reinterpret_cast<const bf16x8*>(a.ki + (k0 + mykey) * kIxDi + 32 * ks + 8 * g)
+                         : bf16x8{};
+  f32x4 dacc[8];
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt) dacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int nit = (G + 15) >> 4;
+
+  // q~ tile staging: 64 heads x 16 pieces of 16 bytes, 4 per thread (heads past G read zeros)
+  u32x4 st[4];
+  float stw = 0.f;
+  auto load_row = [&](int i) {
+    const int64_t r = q0 + i;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = (int)threadIdx.x + kKeyThreads * u;
+      const int h = e >> 4, j = e & 15;
+      st[u] = h < G ? *reinterpret_cast<const u32x4*>(a.qi + (r * G + h) * kIxDi + 8 * j) : u32x4{0u, 0u, 0u, 0u};
+    }
+    stw = threadIdx.x < 64 && (int)threadIdx.x < G ? x2f<F16>(a.w[r * G + threadIdx.x]) : 0.f;
+  };
+  auto store_row = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = (int)threadIdx.x + kKeyThreads * u;
+      const int h = e >> 4, j = e & 15;
+      *reinterpret_cast<u32x4*>(&Qt[buf][h * kIPitch + 8 * j]) = st[u];
+    }
+    if (threadIdx.x < 64) sW[buf][threadIdx.x] = stw;
+  };
+
+  if (i0 < i1) {
+    load_row(i0);
+    store_row(0);
+  }
+  __syncthreads();
+  for (int i = i0; i < i1; ++i) {
+    const int buf = (i - i0) & 1;
+    if (i + 1 < i1) load_row(i + 1);
+    const int64_t r = q0 + i;
+    // keys this row admits: positions <= hi
+    const int hi = a.mode3 ? min(lkv - 1, i + lkv - lq) : lkv - 1;
+    const float norm = a.norm[r];
+    const float inv_norm = norm > 0.f ? 1.f / norm : 0.f;
+    const float max_i = a.smax_i[r];
+    const float sum_i = a.ssum_i[r];
+    const float lsum_i = sum_i > 0.f ? __logf(sum_i) : 0.f;
+    // S'[key 4 g + v][head 16 nt + c]
+    f32x4 sacc[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      sacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (nt < nit)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          sacc[nt] = mfma_t<F16>(kA[ks], lds_read8p(Qt[buf], 16 * nt + c, 32 * ks + 8 * g, kIPitch), sacc[nt]);
+    }
+    float wl[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) wl[nt] = sW[buf][16 * nt + c];
+    const int kb = kt0 + 16 * wave + 4 * g;       // first key of this lane's C rows
+    float tot4[4];
+    {
+      const float* tp = a.tot + r * a.kstride;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) tot4[v] = (kb + v <= hi && sum_i > 0.f) ? tp[kb + v] : 0.f;
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      float is = 0.f;
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) is += wl[nt] * fmaxf(sacc[nt][v], 0.f);
+      is = wsum16(is);
+      const bool valid = kb + v <= hi && sum_i > 0.f;
+      const float sm = valid ? __expf(is - max_i - lsum_i) : 0.f;
+      const float di = sm - tot4[v] * inv_norm;
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+        Dk[wave][(4 * g + v) * kDkPitch + 16 * nt + c] = f2x<F16>(sacc[nt][v] > 0.f ? di * wl[nt] : 0.f);
+    }
+    // the tile is read by other lanes of this wave only
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    bf16x8 dA[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) dA[ks] = *reinterpret_cast<const bf16x8*>(&Dk[wave][c * kDkPitch + 32 * ks + 8 * g]);
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        dacc[nt] = mfma_t<F16>(dA[ks], lds_frag_trp(Qt[buf], 32 * ks, 16 * nt, kIPitch, lane), dacc[nt]);
+    if (i + 1 < i1) store_row(buf ^ 1);
+    lds_barrier();
+  }
+  // partial rows (all 64 keys of the tile that exist in the batch's key rows)
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int key = kt0 + 16 * wave + 4 * g + v;
+    if (key < nk)
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt)
+        a.dkp[((int64_t)part * a.keys + k0 + key) * kIxDi + 16 * nt + c] = dacc[nt][v];
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// blockIdx.x < keys: one key row, dK~ = sum of the parts in part order.  The last workgroup
+// (blockIdx.x == keys) sums the rows' losses in row order.
+template <bool F16>
+__global__ void __launch_bounds__(kIxDi) ix_finish_kernel(IxArgs a) {
+  const int64_t key = blockIdx.x;
+  if (key < a.keys) {
+    float s = 0.f;
+    for (int p = 0; p < a.parts; ++p) s += a.dkp[((int64_t)p * a.keys + key) * kIxDi + threadIdx.x];
+    a.dki[key * kIxDi + threadIdx.x] = f2x<F16>(s);
+    return;
+  }
+  __shared__ float part[kIxDi];
+  float s = 0.f;
+  for (int64_t r = threadIdx.x; r < a.rows; r += kIxDi) s += a.lrow[r];
+  part[threadIdx.x] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float t = 0.f;
+    for (int j = 0; j < kIxDi; ++j) t += part[j];
+    a.loss[0] = t;
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+hipError_t launch_indexer(const IxArgs& a, int64_t key_tiles, hipStream_t st) {
+  if (a.rows > 0) {
+    if (a.f16) hipLaunchKernelGGL(ix_query_kernel<true>, dim3((unsigned)a.rows), dim3(kIxThreads), 0, st, a);
+    else hipLaunchKernelGGL(ix_query_kernel<false>, dim3((unsigned)a.rows), dim3(kIxThreads), 0, st, a);
+  }
+  if (key_tiles > 0) {
+    const dim3 grid((unsigned)key_tiles, (unsigned)a.parts);
+    if (a.f16) hipLaunchKernelGGL(ix_key_kernel<true>, grid, dim3(kKeyThreads), 0, st, a);
+    else hipLaunchKernelGGL(ix_key_kernel<false>, grid, dim3(kKeyThreads), 0, st, a);
+  }
+  if (a.f16) hipLaunchKernelGGL(ix_finish_kernel<true>, dim3((unsigned)(a.keys + 1)), dim3(kIxDi), 0, st, a);
+  else hipLaunchKernelGGL(ix_finish_kernel<false>, dim3((unsigned)(a.keys + 1)), dim3(kIxDi), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace sfag

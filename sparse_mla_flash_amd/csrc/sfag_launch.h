@@ -124,6 +124,35 @@ struct FwdArgs {
   int f16;                // 16-bit tensors are fp16 (else bf16)
 };
 
+// Lightning-indexer backward with KL loss (index head width fixed at 128).
+constexpr int kIxDi = 128;
+struct IxArgs {
+  const uint16_t* q;      // [rows, N1, 512] main query
+  const uint16_t* qr;     // [rows, N1, 64] (NULL: no rope terms)
+  const uint16_t* k;      // [keys, 512] main key
+  const uint16_t* kr;     // [keys, 64] (NULL with qr)
+  const uint16_t* qi;     // [rows, G, 128] queryIndex
+  const uint16_t* ki;     // [keys, 128] keyIndex
+  const uint16_t* w;      // [rows, G] weights
+  const float* smax;      // main statistics ([B, N1, S1] / [N1, T1])
+  const float* ssum;
+  const float* smax_i;    // index statistics [rows]
+  const float* ssum_i;
+  uint16_t* dqi;          // [rows, G, 128]
+  uint16_t* dki;          // [keys, 128]
+  uint16_t* dw;           // [rows, G]
+  float* loss;            // [1]
+  float* tot;             // [rows, kstride] head-summed main softmax of every admitted (row, key)
+  float* norm;            // [rows] its sum over the row's keys
+  float* lrow;            // [rows] loss of every row
+  float* dkp;             // [parts, keys, 128] fp32 dK~ partials
+  Lens lens;
+  int64_t S1, S2, kstride, rows, keys;
+  int B, N1, G, mode3, layout_tnd, parts;
+  float scale;
+  int f16;
+};
+
 // statistics element of head h of a query row (BSND [B, N1, S1], TND [N1, T1])
 template <typename Geo>
 __host__ __device__ inline int64_t stat_index(int tnd, const Geo& g, int64_t row, int N1, int64_t S1, int h) {
@@ -140,5 +169,6 @@ hipError_t launch_kv_dense(const DenseArgs& a, hipStream_t st);
 hipError_t launch_kv_reduce(const DenseArgs& a, int64_t keys, hipStream_t st);
 hipError_t set_dense_attributes();
 hipError_t set_fwd_attributes();
+hipError_t launch_indexer(const IxArgs& a, int64_t key_tiles, hipStream_t st);
 
 }  // namespace sfag

@@ -372,3 +372,83 @@ def workload(n: int, seed: Optional[int] = None, dtype: str = "bf16") -> Problem
     w = WORKLOADS[n]
     p = problem(**w["spec"], dtype=dtype)
     return generate(p, n if seed is None else seed, index_kind=w["kind"])
+
+
+# ---------------------------------------------------------------------------
+# lightning-indexer backward inputs
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class IndexerProblem:
+    """Shapes and seeded tensors of one lightning-indexer backward call (the sparse operator's
+    layouts; index heads G of width Di = 128)."""
+
+    layout: str
+    B: int
+    S1: int
+    S2: int
+    N1: int
+    G: int
+    sparse_mode: int
+    seq_q: Optional[List[int]]
+    seq_kv: Optional[List[int]]
+    scale: float
+    Di: int = 128
+    D: int = D_NOPE
+    Dr: int = D_ROPE
+    dtype: str = "bf16"
+    name: str = ""
+    q: Optional[np.ndarray] = None       # [rows, N1, 512] bits
+    qr: Optional[np.ndarray] = None      # [rows, N1, 64]
+    k: Optional[np.ndarray] = None       # [keys, 1, 512]
+    kr: Optional[np.ndarray] = None      # [keys, 1, 64]
+    qi: Optional[np.ndarray] = None      # [rows, G, 128]
+    ki: Optional[np.ndarray] = None      # [keys, 1, 128]
+    w: Optional[np.ndarray] = None       # [rows, G]
+
+    @property
+    def rows(self) -> int:
+        return self.B * self.S1 if self.layout == "BSND" else self.S1
+
+    @property
+    def keys(self) -> int:
+        return self.B * self.S2 if self.layout == "BSND" else self.S2
+
+    def shape(self, n: int, w: int, side: str = "q"):
+        """Tensor shape of n heads of width w on the query (or key) side in this layout."""
+        if self.layout == "BSND":
+            return (self.B, self.S1 if side == "q" else self.S2, n, w)
+        return (self.S1 if side == "q" else self.S2, n, w)
+
+
+def indexer_problem(layout="BSND", B=1, S1=128, S2=128, N1=16, G=16, sparse_mode=3, seq_q=None, seq_kv=None,
+                    scale=None, dtype="bf16", name="") -> IndexerProblem:
+    if dtype not in DTYPES:
+        raise ValueError(f"dtype must be one of {DTYPES}, got {dtype!r}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D_NOPE + D_ROPE)
+    if layout == "TND":
+        assert seq_q is not None and seq_kv is not None
+        S1, S2 = int(sum(seq_q)), int(sum(seq_kv))
+    return IndexerProblem(layout=layout, B=B, S1=S1, S2=S2, N1=N1, G=G, sparse_mode=sparse_mode,
+                          seq_q=None if seq_q is None else [int(x) for x in seq_q],
+                          seq_kv=None if seq_kv is None else [int(x) for x in seq_kv],
+                          scale=fp32(scale), dtype=dtype, name=name)
+
+
+def indexer_generate(p: IndexerProblem, seed: int) -> IndexerProblem:
+    """Fill p from ``seed``: streams in the order query, queryRope, key, keyRope, queryIndex,
+    keyIndex, weights.  Every value is N(0, 1) in fp32 rounded to p.dtype, except the weights,
+    drawn N(0, 1 / (G Di)) so that the index scores W . ReLU(q~ K~) have a spread of order one."""
+    ss = np.random.SeedSequence(seed).spawn(7)
+    rq, rqr, rk, rkr, rqi, rki, rw = (np.random.default_rng(s) for s in ss)
+    p.q = _normal_bits(rq, p.shape(p.N1, p.D), p.dtype)
+    p.qr = _normal_bits(rqr, p.shape(p.N1, p.Dr), p.dtype)
+    p.k = _normal_bits(rk, p.shape(1, p.D, "k"), p.dtype)
+    p.kr = _normal_bits(rkr, p.shape(1, p.Dr, "k"), p.dtype)
+    p.qi = _normal_bits(rqi, p.shape(p.G, p.Di), p.dtype)
+    p.ki = _normal_bits(rki, p.shape(1, p.Di, "k"), p.dtype)
+    wshape = p.shape(p.G, 1)[:-1]
+    p.w = f32_to_bits(rw.standard_normal(int(np.prod(wshape)), dtype=np.float32)
+                      / np.float32(math.sqrt(p.G * p.Di)), p.dtype).reshape(wshape)
+    return p

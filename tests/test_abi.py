@@ -241,3 +241,51 @@ def test_wrapper_takes_the_element_type_from_query():
     assert sf._dims_from(q.bfloat16(), k.bfloat16(), idx, "BSND", None, None).dtype == sf.SFAG_DTYPE_BF16
     with pytest.raises(ValueError):
         sf._dims_from(q.float(), k.float(), idx, "BSND", None, None)
+
+
+def ix_dims(**kw):
+    base = dict(B=1, S1=256, S2=256, N1=64, G=64, D=512, Drope=64, Di=128, dtype=sf.SFAG_DTYPE_BF16)
+    base.update(kw)
+    return sf.IndexerDims(*[base[k] for k in ("B", "S1", "S2", "N1", "G", "D", "Drope", "Di", "dtype")])
+
+
+@pytest.mark.parametrize("field,value", [("G", 0), ("G", 65), ("Di", 64), ("N1", 0), ("N1", 129), ("D", 256),
+                                         ("Drope", 0), ("B", 257), ("S2", 0), ("S1", 131073), ("dtype", 2)])
+def test_indexer_invalid_shapes(field, value):
+    assert status_of(sf.sfag_lightning_indexer_grad_get_workspace_size, ix_dims(**{field: value})) == \
+        sf.SFAG_ERR_PARAM_INVALID
+
+
+def test_indexer_workspace_and_attributes():
+    ws = sf.sfag_lightning_indexer_grad_get_workspace_size(ix_dims())
+    # the head sums of every (row, key) in fp32 are the largest part
+    assert ws >= 256 * 256 * 4
+    assert sf.sfag_lightning_indexer_grad_get_workspace_size(ix_dims(dtype=sf.SFAG_DTYPE_FP16)) == ws
+    assert status_of(sf.sfag_lightning_indexer_grad_get_workspace_size, ix_dims(), layout="BNSD") == \
+        sf.SFAG_ERR_PARAM_INVALID
+    assert status_of(sf.sfag_lightning_indexer_grad_get_workspace_size, ix_dims(), sparse_mode=2) == \
+        sf.SFAG_ERR_PARAM_INVALID
+    # TND: lengths must sum to the token counts
+    d = ix_dims(B=2, S1=10, S2=12)
+    assert sf.sfag_lightning_indexer_grad_get_workspace_size(d, [4, 6], [5, 7], layout="TND") > 0
+    assert status_of(sf.sfag_lightning_indexer_grad_get_workspace_size, d, [4, 5], [5, 7], layout="TND") == \
+        sf.SFAG_ERR_PARAM_INVALID
+    assert status_of(sf.sfag_lightning_indexer_grad_get_workspace_size, d, None, None, layout="TND") == \
+        sf.SFAG_ERR_PARAM_NULLPTR
+
+
+def test_indexer_null_pointers_are_rejected_before_launch():
+    d = ix_dims()
+    args = dict(query=16, key=16, query_index=16, key_index=16, weights=16, softmax_max=16, softmax_sum=16,
+                softmax_max_index=16, softmax_sum_index=16, query_rope=None, key_rope=None, seq_len_q=None,
+                seq_len_kv=None, dims=d, scale_value=1 / 24, layout="BSND", sparse_mode=3, pre_tokens=0,
+                next_tokens=0, d_query_index=16, d_key_index=16, d_weights=16, loss=16, workspace=None,
+                workspace_size=0, stream=None)
+    for name in ("query", "key_index", "weights", "softmax_sum_index", "d_weights", "loss"):
+        a = dict(args)
+        a[name] = None
+        assert sf.sfag_dense_lightning_indexer_grad_kl_loss(**a) == sf.SFAG_ERR_PARAM_NULLPTR, name
+    a = dict(args)
+    a["query_rope"] = 16                          # key_rope missing
+    assert sf.sfag_dense_lightning_indexer_grad_kl_loss(**a) == sf.SFAG_ERR_PARAM_INVALID
+    assert sf.sfag_dense_lightning_indexer_grad_kl_loss(**args) == sf.SFAG_ERR_WORKSPACE

@@ -8,8 +8,8 @@
 - central finite differences of the oracle's own loss (fed exact statistics) against its
   gradients;
 - closed forms: W = 0 (uniform Softmax(I)), one admitted key (loss and gradients zero);
-- invariants: KL >= 0, and the loss is unchanged by adding a constant to every index score of a
-  row only through the statistics (the softmax is shift-invariant);
+- the forward statistics the tests feed in (main and index) against torch's;
+- invariants: KL >= 0 on every case;
 - planted mistakes in a copy of the oracle's source, each caught by one of the pins above.
 """
 
@@ -112,6 +112,16 @@ def test_matches_torch_autograd(name):
     np.testing.assert_allclose(dki, ref["dki"], atol=1e-11, rtol=1e-9)
     np.testing.assert_allclose(dw, ref["dw"], atol=1e-11, rtol=1e-9)
     assert loss > 0
+
+
+def test_main_stats_match_torch():
+    for name in ("bsnd_nomask_b2", "tnd_varlen_empty"):
+        geo, t = make(**CASES[name])
+        ref = torch_reference(geo, t)
+        m, l = ix.main_stats(geo, t["q"], t["k"], t["qr"], t["kr"])
+        n = len(m)
+        np.testing.assert_allclose(m, ref["smax"][:n], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(l, ref["ssum"][:n], rtol=1e-12, atol=1e-12)
 
 
 def test_index_stats_match_torch():
