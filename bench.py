@@ -161,6 +161,129 @@ def cpu_baseline(p, nrows: int, per_row):
                       f"untimed; {dt:.2f} s wall"}
 
 
+INDEXER_WORKLOADS = {
+    # name: (indexer_problem kwargs, seed); index heads 64 x 128 wide, causal
+    "ix_bsnd_s4096_n64_g64_causal": (dict(layout="BSND", B=1, S1=4096, S2=4096, N1=64, G=64, sparse_mode=3), 101),
+    "ix_bsnd_s8192_n128_g64_causal": (dict(layout="BSND", B=1, S1=8192, S2=8192, N1=128, G=64, sparse_mode=3), 102),
+}
+
+
+def indexer_bench(args):
+    """Lightning-indexer backward (KL loss): one call per step on a seeded workload.  Inputs and
+    both sets of forward statistics are prepared on the GPU with torch (fp32 products of the
+    16-bit inputs); the timed region is the library call only."""
+    import numpy as np
+    import torch
+    import sparse_mla_flash_amd as sf
+    from sparse_mla_flash_amd import inputs
+    name = args.indexer
+    kw, seed = INDEXER_WORKLOADS[name]
+    p = inputs.indexer_generate(inputs.indexer_problem(**kw, dtype=args.dtype, name=name), seed)
+    elem = torch.float16 if args.dtype == "fp16" else torch.bfloat16
+
+    def dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(elem).cuda()
+
+    q, qr, k, kr, qi, ki, w = (dev(x) for x in (p.q, p.qr, p.k, p.kr, p.qi, p.ki, p.w))
+    S1, S2, N1 = p.S1, p.S2, p.N1
+    smax = torch.zeros(1, N1, S1, device="cuda")
+    ssum = torch.zeros_like(smax)
+    mi = torch.zeros(1, S1, device="cuda")
+    si = torch.zeros_like(mi)
+    kf = torch.cat([k[0, :, 0].float(), kr[0, :, 0].float()], 1)            # [S2, 576]
+    kif = ki[0, :, 0].float()                                                # [S2, 128]
+    pos = torch.arange(S2, device="cuda")
+    for r0 in range(0, S1, 256):
+        r1 = min(S1, r0 + 256)
+        qf = torch.cat([q[0, r0:r1].float(), qr[0, r0:r1].float()], 2)      # [R, N1, 576]
+        hi = torch.arange(r0, r1, device="cuda")[:, None] + (S2 - S1)        # causal bound
+        mask = pos[None, :] <= hi                                            # [R, S2]
+        z = p.scale * torch.matmul(qf, kf.t().contiguous())                  # [R, N1, S2]
+        z = z.masked_fill(~mask[:, None, :], float("-inf"))
+        m = z.amax(2)
+        smax[0, :, r0:r1] = m.t()
+        ssum[0, :, r0:r1] = torch.exp(z - m[:, :, None]).sum(2).t()
+        sc = torch.matmul(qi[0, r0:r1].float(), kif.t().contiguous())        # [R, G, S2]
+        iv = (w[0, r0:r1].float()[:, :, None] * torch.relu(sc)).sum(1).masked_fill(~mask, float("-inf"))
+        im = iv.amax(1)
+        mi[0, r0:r1] = im
+        si[0, r0:r1] = torch.exp(iv - im[:, None]).sum(1)
+        del z, sc, iv
+    torch.cuda.synchronize()
+    dims = sf._indexer_dims(q, k, qi, w, "BSND", None)
+    ws_bytes = sf.sfag_lightning_indexer_grad_get_workspace_size(dims, None, None, "BSND", p.sparse_mode)
+    ws = torch.empty(max(1, ws_bytes), dtype=torch.uint8, device="cuda")
+    dqi, dki, dw = torch.empty_like(qi), torch.empty_like(ki), torch.empty_like(w)
+    loss = torch.empty(1, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def step():
+        st = sf.sfag_dense_lightning_indexer_grad_kl_loss(
+            q.data_ptr(), k.data_ptr(), qi.data_ptr(), ki.data_ptr(), w.data_ptr(), smax.data_ptr(),
+            ssum.data_ptr(), mi.data_ptr(), si.data_ptr(), qr.data_ptr(), kr.data_ptr(), None, None, dims, p.scale,
+            "BSND", p.sparse_mode, 2 ** 31 - 1, 2 ** 31 - 1, dqi.data_ptr(), dki.data_ptr(), dw.data_ptr(),
+            loss.data_ptr(), ws.data_ptr(), ws.numel(), stream)
+        if st != 0:
+            raise sf.SfagError(st, sf.sfag_last_error())
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = HipEvents()
+    evs = [(ev.create(), ev.create()) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        ev.record(e0, stream)
+        step()
+        ev.record(e1, stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    calls = sorted(ev.elapsed_ms(a, b) for a, b in evs)
+    for a, b in evs:
+        ev.destroy(a)
+        ev.destroy(b)
+    pairs = sum(min(S2, i + 1 + (S2 - S1)) for i in range(S1) if i + (S2 - S1) >= 0)
+    flop_pair = 2 * 576 * N1 + 3 * 2 * p.Di * p.G       # main scores; index scores, dq~, dK~
+    med = calls[len(calls) // 2]
+    tf = pairs * flop_pair / (med * 1e-3) / 1e12
+    rec = {"metric": "lightning-indexer backward (KL loss) TFLOP/s on 1 MI355X", "value": round(tf, 3),
+           "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round((t1 - t0) / args.steps * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": args.dtype, "data": "synthetic",
+           "config": {"workload": name, "layout": "BSND", "S1": S1, "S2": S2, "N1": N1, "G": p.G, "Di": p.Di,
+                      "sparse_mode": p.sparse_mode, "admitted_pairs": pairs, "flop_per_pair": flop_pair},
+           "call_ms": {"median": round(med, 4), "min": round(calls[0], 4), "max": round(calls[-1], 4),
+                       "n": len(calls)},
+           "roofline": {"bound": "mfma", "achieved": round(tf, 3), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 5), "traffic": None,
+                        "kernel": "whole call (ix_query_kernel + ix_key_kernel + ix_finish_kernel)"},
+           "loss": float(loss.item()), "device": device_info()}
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = indexer_cpu_baseline(p, flop_pair, smax, ssum, mi, si)
+    print(json.dumps(rec), flush=True)
+
+
+def indexer_cpu_baseline(p, flop_pair, smax, ssum, mi, si, nrows: int = 512):
+    """The fp64 indexer oracle on the last `nrows` query rows of the same workload."""
+    import numpy as np
+    from oracle import indexer as ix
+    from sparse_mla_flash_amd import inputs
+    geo = ix.IndexerGeometry(p.layout, p.B, p.S1, p.S2, p.N1, p.G, p.Di, p.D, p.Dr, p.seq_q, p.seq_kv,
+                             p.sparse_mode, p.scale)
+    f = lambda x: inputs.bits_to_f64(x, p.dtype)
+    rows = list(range(p.rows - nrows, p.rows))
+    cpu = lambda t: t.detach().double().cpu().numpy()
+    t0 = time.perf_counter()
+    ix.indexer_grad(geo, f(p.q), f(p.k), f(p.qr), f(p.kr), cpu(smax), cpu(ssum), f(p.qi), f(p.ki), f(p.w),
+                    cpu(mi), cpu(si), rows=rows)
+    dt = time.perf_counter() - t0
+    pairs = sum(min(p.S2, i + 1 + (p.S2 - p.S1)) for i in range(p.S1 - nrows, p.S1))
+    import os as _os
+    return {"value": pairs * flop_pair / dt / 1e12, "unit": "TFLOP/s", "cores": _os.cpu_count(), "kind": "oracle",
+            "sample": f"fp64 numpy indexer oracle over query rows {rows[0]}..{rows[-1]} ({pairs} admitted pairs); "
+                      f"{dt:.2f} s wall"}
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as fh:
@@ -284,6 +407,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--ceilings", action="store_true")
+    ap.add_argument("--indexer", choices=sorted(INDEXER_WORKLOADS), default=None,
+                    help="time the lightning-indexer backward on this workload instead")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the kernel is measured on a single "
@@ -294,6 +419,9 @@ def main():
         return
     if args.ceilings:
         ceilings()
+        return
+    if args.indexer:
+        indexer_bench(args)
         return
 
     import numpy as np
