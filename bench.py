@@ -263,6 +263,48 @@ def indexer_bench(args):
     print(json.dumps(rec), flush=True)
 
 
+def forward_bench(args, p, q, k, v, idx, qr, kr):
+    """The sparse forward on the same workload: one call per step, HIP events per call."""
+    import torch
+    import sparse_mla_flash_amd as sf
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def step():
+        return sf.sparse_flash_attention_forward(q, k, v, idx, p.seq_q, p.seq_kv, qr, kr, scale_value=p.scale,
+                                                 sparse_block_size=p.block, layout=p.layout,
+                                                 sparse_mode=p.sparse_mode)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = HipEvents()
+    evs = [(ev.create(), ev.create()) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        ev.record(e0, stream)
+        step()
+        ev.record(e1, stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    calls = sorted(ev.elapsed_ms(a, b) for a, b in evs)
+    for a, b in evs:
+        ev.destroy(a)
+        ev.destroy(b)
+    npairs = int(valid_per_row(p).sum())
+    flop = 2 * 576 + 2 * 512                              # S and P V per (pair, head)
+    med = calls[len(calls) // 2]
+    tf = npairs * p.N1 * flop / (med * 1e-3) / 1e12
+    print(json.dumps({
+        "metric": "sparse forward TFLOP/s on 1 MI355X", "value": round(tf, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round((t1 - t0) / args.steps * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": args.dtype, "data": "synthetic",
+        "config": {"workload": p.name, "valid_pairs": npairs, "N1": p.N1, "flop_per_pair_head": flop},
+        "call_ms": {"median": round(med, 4), "min": round(calls[0], 4), "max": round(calls[-1], 4), "n": len(calls)},
+        "roofline": {"bound": "mfma", "achieved": round(tf, 3), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 5), "traffic": None, "kernel": "fwd_kernel"},
+        "device": device_info()}), flush=True)
+
+
 def indexer_cpu_baseline(p, flop_pair, smax, ssum, mi, si, nrows: int = 512):
     """The fp64 indexer oracle on the last `nrows` query rows of the same workload."""
     import numpy as np
@@ -407,6 +449,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--ceilings", action="store_true")
+    ap.add_argument("--forward", action="store_true",
+                    help="time the sparse forward (out, softmaxMax, softmaxSum) on the workload instead")
     ap.add_argument("--indexer", choices=sorted(INDEXER_WORKLOADS), default=None,
                     help="time the lightning-indexer backward on this workload instead")
     args = ap.parse_args()
@@ -446,6 +490,9 @@ def main():
     out, smax, ssum = sf.sparse_flash_attention_forward(q, k, v, idx, p.seq_q, p.seq_kv, qr, kr,
                                                         scale_value=p.scale, sparse_block_size=p.block,
                                                         layout=p.layout, sparse_mode=p.sparse_mode)
+    if args.forward:
+        forward_bench(args, p, q, k, v, idx, qr, kr)
+        return
     det = bool(args.deterministic or p.deterministic)
     dims = sf._dims_from(q, k, idx, p.layout, p.seq_q, p.seq_kv)
     ws_bytes = sf.sfag_get_workspace_size(dims, p.seq_q, p.seq_kv, p.scale, p.block, p.layout, p.sparse_mode,

@@ -1,14 +1,26 @@
 // sfag_fwd.hip -- sparse attention forward over the selected keys (gfx950).
 //
-// Produces the backward's inputs out, softmaxMax and softmaxSum: per query row and head,
-// over the valid selected slots, z = scale (q.k + qRope.kRope), softmaxMax = max z,
-// softmaxSum = sum exp(z - max), out = sum softmax(z) v with v = k[:512] (SparseAttnSharedkv
-// README, "function description": O = softmax(Q K~^T scale) V~ with K~ = V~; the statistics
-// are the forward intermediates the SparseFlashAttentionGrad page names).
+// Produces the backward's inputs out, softmaxMax and softmaxSum: per query row and head, over
+// the valid selected slots, z = scale (q.k + qRope.kRope), softmaxMax = max z, softmaxSum =
+// sum exp(z - max), out = sum softmax(z) v with v = k[:512] (SparseAttnSharedkv README,
+// "function description": O = softmax(Q K~^T scale) V~ with K~ = V~; the statistics are the
+// forward intermediates the SparseFlashAttentionGrad page names).
 //
-// Same decomposition as the backward: one workgroup per (row, <= 64 heads), Q in LDS, 32-key
-// chunks gathered into LDS, S = Q K^T on 16x16x32 bf16 MFMA, an online softmax with running
-// max / sum per head, and O += P V with P passed through LDS and V read with transpose loads.
+// One workgroup of 8 waves per (row, group of <= 64 heads), over the row's slots in chunks of
+// 32 (slots past the row's last valid one are not visited; invalid slots inside are masked):
+//   score waves (0-3): wave w keeps Q | QRope of heads 16 w .. + 15 in registers, forms S for
+//     both 16-key tiles of the chunk on the 16x16x32 MFMA, and runs the online softmax per
+//     head: chunk max, new running max m, rescale factor alpha = exp(m_old - m), P = exp(S - m)
+//     (zero for invalid slots), running sum l = alpha l + sum P.  P goes to LDS as a [key][head]
+//     tile, alpha as 64 floats.
+//   output waves (4-7): wave 4 + w owns output dims 128 w .. + 127 of all 64 heads (fp32
+//     accumulators across all chunks); in step c it rescales them by alpha of chunk c - 1 and
+//     adds P V of that chunk (transposing LDS reads of P and of the key tile's value dims); it
+//     also gathers the key rows of chunk c + 2 straight from global memory into LDS
+//     (global_load_lds, 16 bytes per lane) and marks which of that chunk's slots are valid.
+// One barrier per step; key tiles quadruple-buffered (a gather has two steps to land), P tiles
+// and alpha double-buffered.  Key tiles are chunk-major in LDS ([72 chunks of 16 B][32 keys]),
+// so each gathering lane handles one key and each of its loads is one add to that key's row.
 #include "sfag_device.h"
 #include "sfag_launch.h"
 
@@ -16,170 +28,307 @@ namespace sfag {
 
 namespace {
 constexpr int kKC = 32;
-constexpr int kThreads = 256;
-constexpr int kQChunks = kDk / 8;
-constexpr int kHtChunks = 64 / 8;
+constexpr int kThreads = 512;                    // 4 score waves + 4 output waves
+constexpr int kChunks = kDk / 8;                 // 72 16-byte chunks per key row (64 value + 8 rope)
+constexpr int kHtPitch = 64 + 8;                 // P tile row pitch
+constexpr int kBlocks = kChunks / 2;             // 36 direct-to-LDS blocks (2 chunk columns) per tile
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kLdsQ = 64 * kDk * 2;
-constexpr int kLdsK = kKC * kDk * 2;
-constexpr int kLdsHT = kKC * 64 * 2;
-constexpr int kLdsFwd = kLdsQ + kLdsK + kLdsHT + kKC * 8 + 2 * 257 * 4;
+constexpr int kLdsK = kBlocks * 64 * 16;         // one key tile, chunk-major
+// s_waitcnt operands with expcnt and lgkmcnt at zero: vmcnt(9) (all but the 9 loads of the
+// newest gather) and vmcnt(10) (all but a gather and one position load)
+constexpr int kWaitVm9 = 0x0009;
+constexpr int kWaitVm10 = 0x000a;
 }  // namespace
 
 template <bool F16>
 __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  uint16_t* Qs = reinterpret_cast<uint16_t*>(smem);
-  uint16_t* Ks = reinterpret_cast<uint16_t*>(smem + kLdsQ);
-  uint16_t* PSt = reinterpret_cast<uint16_t*>(smem + kLdsQ + kLdsK);
-  int64_t* keyrow = reinterpret_cast<int64_t*>(smem + kLdsQ + kLdsK + kLdsHT);
-  int32_t* cum = reinterpret_cast<int32_t*>(smem + kLdsQ + kLdsK + kLdsHT + kKC * 8);
+  __shared__ __attribute__((aligned(16))) uint16_t Kb0[kLdsK / 2], Kb1[kLdsK / 2], Kb2[kLdsK / 2], Kb3[kLdsK / 2];
+  __shared__ __attribute__((aligned(16))) uint16_t Pb0[kKC * kHtPitch], Pb1[kKC * kHtPitch];
+  __shared__ __attribute__((aligned(16))) float sA0[64], sA1[64], sIL[64];
+  __shared__ int32_t sVal[4][kKC];
+  __shared__ int32_t cum[2 * 257];
+  __shared__ int32_t s_last;
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool swave = wave < 4;
+  const int rw = wave & 3;
   const int g = lane >> 4, c = lane & 15;
-  const int64_t row = blockIdx.x;
-  const int h0 = blockIdx.y * 64;
+  const int64_t row = (int64_t)gridDim.x - 1 - blockIdx.x;     // long rows first
+  const int hg = blockIdx.y;
+  const int h0 = hg * 64;
   const int nh = min(64, a.N1 - h0);
-  const int ntile = (nh + 15) >> 4;
   if (a.layout_tnd) {
     cum_lengths(a.lens, a.B, cum);
     __syncthreads();
   }
   const RowGeo geo = row_geo(a.lens, cum, a.B, a.layout_tnd, a.S1, a.S2, row, a.mode3);
-
-  if (!geo.active || geo.hi < 0) {
+  const int32_t* irow = a.idx + row * (a.topk / a.bs);
+  // slots past the last valid one are never visited
+  if (threadIdx.x == 0) s_last = -1;
+  __syncthreads();
+  if (geo.active && geo.hi >= 0) {
+    int last = -1;
+    for (int s = threadIdx.x; s < a.topk; s += kThreads) {
+      const int j = slot_key(irow, s, a.bs);
+      if (j >= 0 && j <= geo.hi) last = s;
+    }
+    if (last >= 0) atomicMax(&s_last, last);
+  }
+  __syncthreads();
+  const int nslots = s_last + 1;
+  if (nslots == 0) {
     for (int e = threadIdx.x; e < nh * kDn; e += kThreads) a.out[(row * a.N1 + h0) * kDn + e] = 0;
     for (int h = threadIdx.x; h < nh; h += kThreads) {
-        const int64_t st = stat_index(a.layout_tnd, geo, row, a.N1, a.S1, h0 + h);
-        a.smax[st] = 0.f;
-        a.ssum[st] = 0.f;
+      const int64_t st = stat_index(a.layout_tnd, geo, row, a.N1, a.S1, h0 + h);
+      a.smax[st] = 0.f;
+      a.ssum[st] = 0.f;
     }
     return;
   }
-
-  for (int cc = threadIdx.x; cc < 64 * kQChunks; cc += kThreads) {
-    const int h = cc / kQChunks, part = cc % kQChunks;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (h < nh) {
-      const int64_t hh = row * a.N1 + h0 + h;
-      v = part < 64 ? *reinterpret_cast<const uint4*>(a.q + hh * kDn + part * 8)
-                    : (a.qr ? *reinterpret_cast<const uint4*>(a.qr + hh * kDr + (part - 64) * 8) : uint4{0, 0, 0, 0});
-    }
-    *reinterpret_cast<uint4*>(Qs + swz(h, part * 8, kQChunks)) = v;
-  }
-
+  const int nchunk = (nslots + kKC - 1) / kKC;
   const float zscale = a.scale * kLog2e;
-  float mrun[4], lrun[4];
-#pragma unroll
-  for (int v = 0; v < 4; ++v) { mrun[v] = -INFINITY; lrun[v] = 0.f; }
-  f32x4 oacc[32];
-#pragma unroll
-  for (int ft = 0; ft < 32; ++ft) oacc[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int32_t* idxrow = a.idx + row * (a.topk / a.bs);
-  for (int c0 = 0; c0 < a.topk; c0 += kKC) {
-    int any = 0;
-    if (threadIdx.x < kKC) {
-      const int s = c0 + threadIdx.x;
-      int64_t kr_ = -1;
-      if (s < a.topk) {
-        const int j = slot_key(idxrow, s, a.bs);
-        if (j >= 0 && j <= geo.hi) kr_ = geo.kstart + j;
-      }
-      keyrow[threadIdx.x] = kr_;
-      any = kr_ >= 0;
-    }
-    if (!__syncthreads_or(any)) continue;
-    for (int cc = threadIdx.x; cc < kKC * kQChunks; cc += kThreads) {
-      const int key = cc / kQChunks, part = cc % kQChunks;
-      const int64_t kr_ = keyrow[key];
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (kr_ >= 0)
-        v = part < 64 ? *reinterpret_cast<const uint4*>(a.k + kr_ * kDn + part * 8)
-                      : (a.kr ? *reinterpret_cast<const uint4*>(a.kr + kr_ * kDr + (part - 64) * 8) : uint4{0, 0, 0, 0});
-      *reinterpret_cast<uint4*>(Ks + swz(key, part * 8, kQChunks)) = v;
-    }
-    __syncthreads();
+  auto uniform = [](const void* p) {               // a workgroup-uniform pointer, made scalar
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return reinterpret_cast<uint16_t*>(((uint64_t)hi << 32) | lo);
+  };
+  const uint16_t* kbase = uniform(a.k + geo.kstart * kDn);
+  const bool rope = a.kr != nullptr;
+  // without rope inputs the rope chunks are read from the key's value row (their Q is zero)
+  const uint16_t* krbase = uniform(rope ? a.kr + geo.kstart * kDr : a.k + geo.kstart * kDn);
+  asm volatile("" : "+s"(kbase), "+s"(krbase));
 
-    if (wave < ntile) {
-      f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  if (swave) {
+    // Q | QRope fragments (A operands of S: lane (g, c) holds head 16 rw + c, dims 32 ks + 8 g)
+    bf16x8 qA[18];
+    {
+      const int h = 16 * rw + c;
+      const bool hv = h < nh;
+      const int64_t hrow = row * a.N1 + h0 + (hv ? h : 0);
+      const uint16_t* qrow = a.q + hrow * kDn + 8 * g;
 #pragma unroll
-      for (int ks = 0; ks < kDk / 32; ++ks) {
-        const bf16x8 qa = lds_read8(Qs, 16 * wave + c, 32 * ks + 8 * g, kQChunks);
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-          sacc[kt] = mfma_t<F16>(qa, lds_read8(Ks, 16 * kt + c, 32 * ks + 8 * g, kQChunks), sacc[kt]);
-      }
-      float z[2][4];
-      float cmax[4];
-#pragma unroll
-      for (int v = 0; v < 4; ++v) cmax[v] = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const bool valid = keyrow[16 * kt + c] >= 0;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          z[kt][v] = valid ? sacc[kt][v] * zscale : -INFINITY;
-          cmax[v] = fmaxf(cmax[v], z[kt][v]);
-        }
-      }
-      // max over the 16 lanes that hold the other keys of the same heads
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-        for (int o = 1; o < 16; o <<= 1) cmax[v] = fmaxf(cmax[v], __shfl_xor(cmax[v], o));
-      float alpha[4], mnew[4], psum[4];
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        mnew[v] = fmaxf(mrun[v], cmax[v]);
-        alpha[v] = mrun[v] == -INFINITY ? 0.f : exp2f(mrun[v] - mnew[v]);
-        psum[v] = 0.f;
+      for (int ks = 0; ks < 16; ++ks) {
+        const bf16x8 qv = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
+        qA[ks] = hv ? qv : bf16x8{};
       }
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        uint16_t pb[4];
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float p = z[kt][v] == -INFINITY ? 0.f : exp2f(z[kt][v] - mnew[v]);
-          psum[v] += p;
-          pb[v] = f2x<F16>(p);
-        }
-        const int key = 16 * kt + c, hcol = 16 * wave + 4 * g;
-        *reinterpret_cast<uint2*>(PSt + swz(key, hcol, kHtChunks)) =
-            make_uint2(pb[0] | ((uint32_t)pb[1] << 16), pb[2] | ((uint32_t)pb[3] << 16));
+      for (int ks = 0; ks < 2; ++ks) {
+        qA[16 + ks] = bf16x8{};
+        if (hv && a.qr) qA[16 + ks] = *reinterpret_cast<const bf16x8*>(a.qr + hrow * kDr + 32 * ks + 8 * g);
       }
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        for (int o = 1; o < 16; o <<= 1) psum[v] += __shfl_xor(psum[v], o);
-        lrun[v] = lrun[v] * alpha[v] + psum[v];
-        mrun[v] = mnew[v];
-      }
-#pragma unroll
-      for (int ft = 0; ft < 32; ++ft)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) oacc[ft][v] *= alpha[v];
     }
-    __syncthreads();
-    if (wave < ntile) {
-      const bf16x8 pa = lds_frag_tr(PSt, 0, 16 * wave, kHtChunks, lane);
-#pragma unroll
-      for (int ft = 0; ft < 32; ++ft) oacc[ft] = mfma_t<F16>(pa, lds_frag_tr(Ks, 0, 16 * ft, kQChunks, lane), oacc[ft]);
-    }
-    __syncthreads();
-  }
-
-  if (wave < ntile) {
+    // online softmax state of heads 16 rw + 4 g + v (log2 domain of the scaled logits)
+    float m[4], l[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const int h = 16 * wave + 4 * g + v;
-      if (h >= nh) continue;
-      const float inv = lrun[v] > 0.f ? 1.f / lrun[v] : 0.f;
-      const int64_t hh = row * a.N1 + h0 + h;
+      m[v] = -INFINITY;
+      l[v] = 0.f;
+    }
+    lds_barrier();                                  // chunks 0, 1 gathered, their slots marked
+    f32x4 sacc[2];
+// Scores and online softmax of chunk CI on key buffer KS, P buffer PD, alpha buffer AD.
+#define SFAG_FSTEP(CI, KS, PD, AD)                                                             \
+  {                                                                                            \
+    if ((CI) < nchunk) {                                                                       \
+      sacc[0] = sacc[1] = f32x4{0.f, 0.f, 0.f, 0.f};                                           \
+      const uint16_t* kr0 = (KS) + (g * kKC + c) * 8;                                          \
+      const uint16_t* kr1 = (KS) + (g * kKC + 16 + c) * 8;                                     \
+      bf16x8 kf0[18], kf1[18];                                                                 \
+      _Pragma("unroll") for (int ks = 0; ks < 2; ++ks) {                                       \
+        kf0[ks] = *reinterpret_cast<const bf16x8*>(kr0 + 4 * ks * kKC * 8);                    \
+        kf1[ks] = *reinterpret_cast<const bf16x8*>(kr1 + 4 * ks * kKC * 8);                    \
+      }                                                                                        \
+      _Pragma("unroll") for (int ks = 0; ks < 18; ++ks) {                                      \
+        if (ks + 2 < 18) {                                                                     \
+          kf0[ks + 2] = *reinterpret_cast<const bf16x8*>(kr0 + 4 * (ks + 2) * kKC * 8);        \
+          kf1[ks + 2] = *reinterpret_cast<const bf16x8*>(kr1 + 4 * (ks + 2) * kKC * 8);        \
+        }                                                                                      \
+        sacc[0] = mfma_t<F16>(qA[ks], kf0[ks], sacc[0]);                                       \
+        sacc[1] = mfma_t<F16>(qA[ks], kf1[ks], sacc[1]);                                       \
+      }                                                                                        \
+      const bool ok0 = sVal[(CI) & 3][c] != 0, ok1 = sVal[(CI) & 3][16 + c] != 0;              \
+      float mc[4];                                                                             \
+      _Pragma("unroll") for (int v = 0; v < 4; ++v) {                                          \
+        sacc[0][v] = ok0 ? sacc[0][v] * zscale : -INFINITY;                                    \
+        sacc[1][v] = ok1 ? sacc[1][v] * zscale : -INFINITY;                                    \
+        float x = fmaxf(sacc[0][v], sacc[1][v]);                                               \
+        x = fmaxf(x, __shfl_xor(x, 1));                                                        \
+        x = fmaxf(x, __shfl_xor(x, 2));                                                        \
+        x = fmaxf(x, __shfl_xor(x, 4));                                                        \
+        x = fmaxf(x, __shfl_xor(x, 8));                                                        \
+        mc[v] = fmaxf(m[v], x);                                                                \
+      }                                                                                        \
+      const int hcol = 16 * rw + 4 * g;                                                        \
+      float p[2][4];                                                                           \
+      _Pragma("unroll") for (int v = 0; v < 4; ++v) {                                          \
+        /* mc is finite once any slot so far was valid; before that nothing is accumulated */  \
+        const bool fin = mc[v] != -INFINITY;                                                   \
+        const float al = fin ? __builtin_amdgcn_exp2f(m[v] - mc[v]) : 1.f;                     \
+        p[0][v] = fin ? __builtin_amdgcn_exp2f(sacc[0][v] - mc[v]) : 0.f;                      \
+        p[1][v] = fin ? __builtin_amdgcn_exp2f(sacc[1][v] - mc[v]) : 0.f;                      \
+        float ps = p[0][v] + p[1][v];                                                          \
+        ps += __shfl_xor(ps, 1);                                                               \
+        ps += __shfl_xor(ps, 2);                                                               \
+        ps += __shfl_xor(ps, 4);                                                               \
+        ps += __shfl_xor(ps, 8);                                                               \
+        l[v] = l[v] * al + ps;                                                                 \
+        m[v] = mc[v];                                                                          \
+        if (c == 0) (AD)[hcol + v] = al;                                                       \
+      }                                                                                        \
+      _Pragma("unroll") for (int kt = 0; kt < 2; ++kt) {                                       \
+        const uint32_t pw0 = pack_x2<F16>(p[kt][0], p[kt][1]), pw1 = pack_x2<F16>(p[kt][2], p[kt][3]); \
+        *reinterpret_cast<uint2*>((PD) + (16 * kt + c) * kHtPitch + hcol) = make_uint2(pw0, pw1); \
+      }                                                                                        \
+    }                                                                                          \
+    lds_barrier();                                                                             \
+  }
+    int ci = 0;
+    for (; ci + 3 <= nchunk; ci += 4) {
+      SFAG_FSTEP(ci, Kb0, Pb0, sA0)
+      SFAG_FSTEP(ci + 1, Kb1, Pb1, sA1)
+      SFAG_FSTEP(ci + 2, Kb2, Pb0, sA0)
+      SFAG_FSTEP(ci + 3, Kb3, Pb1, sA1)
+    }
+    if (ci <= nchunk) {
+      SFAG_FSTEP(ci, Kb0, Pb0, sA0)
+      ++ci;
+    }
+    if (ci <= nchunk) {
+      SFAG_FSTEP(ci, Kb1, Pb1, sA1)
+      ++ci;
+    }
+    if (ci <= nchunk) SFAG_FSTEP(ci, Kb2, Pb0, sA0)
+#undef SFAG_FSTEP
+    // statistics out (natural-log domain) and 1 / l for the output waves
 #pragma unroll
-      for (int ft = 0; ft < 32; ++ft) a.out[hh * kDn + 16 * ft + c] = f2x<F16>(oacc[ft][v] * inv);
+    for (int v = 0; v < 4; ++v) {
+      const int h = 16 * rw + 4 * g + v;
       if (c == 0) {
-        const int64_t st = stat_index(a.layout_tnd, geo, row, a.N1, a.S1, h0 + h);
-        a.smax[st] = lrun[v] > 0.f ? mrun[v] / kLog2e : 0.f;
-        a.ssum[st] = lrun[v];
+        sIL[h] = l[v] > 0.f ? 1.f / l[v] : 0.f;
+        if (h < nh) {
+          const int64_t st = stat_index(a.layout_tnd, geo, row, a.N1, a.S1, h0 + h);
+          a.smax[st] = l[v] > 0.f ? m[v] / kLog2e : 0.f;
+          a.ssum[st] = l[v];
+        }
+      }
+    }
+    lds_barrier();
+  } else {
+    const int gkey = lane & 31, gcol = lane >> 5;
+    const char* kgat[kBlocks / 4 - 1];
+#pragma unroll
+    for (int j = 0; j < kBlocks / 4 - 1; ++j) {
+      kgat[j] = reinterpret_cast<const char*>(uniform(kbase + 16 * rw + 64 * j));
+      asm volatile("" : "+s"(kgat[j]));
+    }
+    const char* rgat = reinterpret_cast<const char*>(uniform(krbase + 16 * rw));
+    asm volatile("" : "+s"(rgat));
+    // key position of slot s (clamped to the last visited slot); invalid slots read key 0
+    auto slot_pos = [&](int s) { return slot_key(irow, min(s, nslots - 1), a.bs); };
+    auto gather_pos = [&](int j) { return (j >= 0 && j <= geo.hi) ? j : 0; };
+#define SFAG_GATHER_ASYNC(KS, SV)                                                              \
+  {                                                                                            \
+    const uint32_t ko_ = (uint32_t)(SV) * (uint32_t)(kDn * 2) + gcol * 16u;                    \
+    const uint32_t ro_ = (uint32_t)(SV) * (uint32_t)((rope ? kDr : kDn) * 2) + gcol * 16u;     \
+    _Pragma("unroll") for (int j = 0; j < kBlocks / 4; ++j) {                                  \
+      const char* src = j < kBlocks / 4 - 1 ? kgat[j] + ko_ : rgat + ro_;                      \
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)((KS) + (rw + 4 * j) * 512), 16, 0, 0); \
+    }                                                                                          \
+  }
+    // slot validity of chunk CH from the raw position J (written by one output wave)
+#define SFAG_MARK(CH, J)                                                                       \
+  {                                                                                            \
+    if (rw == 0 && gcol == 0)                                                                  \
+      sVal[(CH) & 3][gkey] = ((CH) * kKC + gkey < nslots && (J) >= 0 && (J) <= geo.hi) ? 1 : 0; \
+  }
+    int32_t raw = slot_pos(gkey);
+    SFAG_MARK(0, raw)
+    SFAG_GATHER_ASYNC(Kb0, gather_pos(raw))
+    raw = slot_pos(kKC + gkey);
+    SFAG_MARK(1, raw)
+    SFAG_GATHER_ASYNC(Kb1, gather_pos(raw))
+    int32_t gsv = slot_pos(2 * kKC + gkey);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(kWaitVm10);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    // transposing-read lane offsets: key tile (chunk-major; lane (g, c) points at key 8 g + c / 4
+    // and dim 128 rw + 4 (c % 4)) and P tile ([key][head]; key 8 g + c / 4, head 4 (c % 4))
+    const int kqoff = ((16 * rw + ((c & 3) >> 1)) * kKC + 8 * g + (c >> 2)) * 8 + 4 * (c & 1);
+    const int psoff = (8 * g + (c >> 2)) * kHtPitch + 4 * (c & 3);
+    f32x4 oacc[4][8];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) oacc[t][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+// Output step CI: the position of chunk CI + 3's slot, the gather of chunk CI + 2 into KN (and
+// its slot marks), then O = alpha O + P V of chunk CI - 1 from KP / PP / AP.  Ends by waiting
+// for chunk CI + 1's gather and the position load, leaving this step's gather in flight.
+#define SFAG_OSTEP(CI, KP, KN, PP, AP)                                                         \
+  {                                                                                            \
+    const int32_t sv = slot_pos(((CI) + 3) * kKC + gkey);                                      \
+    asm volatile("" ::: "memory");                                                             \
+    SFAG_MARK((CI) + 2, gsv)                                                                   \
+    SFAG_GATHER_ASYNC(KN, gather_pos(gsv))                                                     \
+    if ((CI) >= 1) {                                                                           \
+      _Pragma("unroll") for (int t = 0; t < 4; ++t) {                                          \
+        const f32x4 al = *reinterpret_cast<const f32x4*>((AP) + 16 * t + 4 * g);               \
+        _Pragma("unroll") for (int nt = 0; nt < 8; ++nt)                                       \
+          _Pragma("unroll") for (int v = 0; v < 4; ++v) oacc[t][nt][v] *= al[v];               \
+      }                                                                                        \
+      const uint16_t* kq_ = (KP) + kqoff;                                                      \
+      const uint16_t* pq_ = (PP) + psoff;                                                      \
+      bf16x8 pa[4];                                                                            \
+      _Pragma("unroll") for (int t = 0; t < 4; ++t) pa[t] = tr_frag(pq_ + 16 * t, 4 * kHtPitch); \
+      bf16x8 kb = tr_frag(kq_, 32);                                                            \
+      _Pragma("unroll") for (int nt = 0; nt < 8; ++nt) {                                       \
+        bf16x8 nb = kb;                                                                        \
+        if (nt < 7) nb = tr_frag(kq_ + 512 * (nt + 1), 32);                                    \
+        _Pragma("unroll") for (int t = 0; t < 4; ++t) oacc[t][nt] = mfma_t<F16>(pa[t], kb, oacc[t][nt]); \
+        kb = nb;                                                                               \
+      }                                                                                        \
+    }                                                                                          \
+    asm volatile("" ::: "memory");                                                             \
+    __builtin_amdgcn_s_waitcnt(kWaitVm9);                                                      \
+    gsv = sv;                                                                                  \
+    __builtin_amdgcn_s_barrier();                                                              \
+    asm volatile("" ::: "memory");                                                             \
+  }
+    int ci = 0;
+    for (; ci + 3 <= nchunk; ci += 4) {
+      SFAG_OSTEP(ci, Kb3, Kb2, Pb1, sA1)
+      SFAG_OSTEP(ci + 1, Kb0, Kb3, Pb0, sA0)
+      SFAG_OSTEP(ci + 2, Kb1, Kb0, Pb1, sA1)
+      SFAG_OSTEP(ci + 3, Kb2, Kb1, Pb0, sA0)
+    }
+    if (ci <= nchunk) {
+      SFAG_OSTEP(ci, Kb3, Kb2, Pb1, sA1)
+      ++ci;
+    }
+    if (ci <= nchunk) {
+      SFAG_OSTEP(ci, Kb0, Kb3, Pb0, sA0)
+      ++ci;
+    }
+    if (ci <= nchunk) SFAG_OSTEP(ci, Kb1, Kb0, Pb1, sA1)
+#undef SFAG_OSTEP
+#undef SFAG_MARK
+#undef SFAG_GATHER_ASYNC
+    __builtin_amdgcn_s_waitcnt(0);                        // no gather may still write LDS at exit
+    lds_barrier();                                        // sIL from the score waves
+    // out: lane holds heads 16 t + 4 g + v, dims 128 rw + 16 nt + c
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const f32x4 il = *reinterpret_cast<const f32x4*>(sIL + 16 * t + 4 * g);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int h = 16 * t + 4 * g + v;
+        if (h >= nh) continue;
+        uint16_t* orow = a.out + (row * a.N1 + h0 + h) * kDn + 128 * rw + c;
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) orow[16 * nt] = f2x<F16>(oacc[t][nt][v] * il[v]);
       }
     }
   }
@@ -187,18 +336,12 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
 
 hipError_t launch_fwd(const FwdArgs& a, int64_t nrows, int hg_count, hipStream_t st) {
   if (a.f16)
-    hipLaunchKernelGGL(fwd_kernel<true>, dim3((unsigned)nrows, (unsigned)hg_count), dim3(kThreads), kLdsFwd, st, a);
+    hipLaunchKernelGGL(fwd_kernel<true>, dim3((unsigned)nrows, (unsigned)hg_count), dim3(kThreads), 0, st, a);
   else
-    hipLaunchKernelGGL(fwd_kernel<false>, dim3((unsigned)nrows, (unsigned)hg_count), dim3(kThreads), kLdsFwd, st, a);
+    hipLaunchKernelGGL(fwd_kernel<false>, dim3((unsigned)nrows, (unsigned)hg_count), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
-hipError_t set_fwd_attributes() {
-  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_kernel<false>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, kLdsFwd);
-  if (e != hipSuccess) return e;
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_kernel<true>),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, kLdsFwd);
-}
+hipError_t set_fwd_attributes() { return hipSuccess; }
 
 }  // namespace sfag
