@@ -55,8 +55,10 @@ __device__ __forceinline__ float wsum16(float v) {  // sum over the 16 lanes c o
 // ------------------------------------------------------------------------------------------
 template <bool F16>
 __global__ void __launch_bounds__(kIxThreads, 1) ix_query_kernel(IxArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t Kt[2][kIxKC * kKPitch];
-  __shared__ __attribute__((aligned(16))) uint16_t Ki[2][kIxKC * kIPitch];
+  // three chunk buffers (separate arrays, so that the compiler can tell a direct-to-LDS load
+  // into one from reads of the others): main key rows and index key rows, chunk-major
+  __shared__ __attribute__((aligned(16))) uint16_t Kt0[kIxKC * kDk], Kt1[kIxKC * kDk], Kt2[kIxKC * kDk];
+  __shared__ __attribute__((aligned(16))) uint16_t Ki0[kIxKC * kIxDi], Ki1[kIxKC * kIxDi], Ki2[kIxKC * kIxDi];
   __shared__ __attribute__((aligned(16))) uint16_t Dt[4][2][16 * kDsPitch];   // per index wave: dS', T
   __shared__ float sP[4][kIxKC];                 // per main wave: softmax summed over its heads
   __shared__ float sI[4][kIxKC];                 // per index wave: its part of I
@@ -109,45 +111,47 @@ __global__ void __launch_bounds__(kIxThreads, 1) ix_query_kernel(IxArgs a) {
   const float inv_heads = heads > 0 ? 1.f / (float)heads : 0.f;
   const float max_i = a.smax_i[row], lsum_i = __logf(a.ssum_i[row]);
 
-  // chunk staging: key row r of chunk ci is key ci * 32 + r (rows past the last admitted key,
-  // and the rope pieces of a rope-less call, are zeros); 72 + 16 sixteen-byte pieces per row
-  const uint16_t* kbase = a.k + geo.kstart * kDn;
+  // Gathers: the keys of a chunk are consecutive rows, clamped to the last admitted key (the
+  // clamped copies are masked).  A direct-to-LDS block (64 lanes x 16 bytes) is chunk columns
+  // 2 b, 2 b + 1 of all 32 keys: lane l takes key l % 32.  Main waves load the 36 blocks of the
+  // main rows (value columns 0..63, rope 64..71; a rope-less call reads value columns instead,
+  // whose Q is zero), 9 each; index waves the 8 blocks of the index rows, 2 each.
+  const int gkey = lane & 31, gcol = lane >> 5;
   const bool has_rope = a.kr != nullptr;
-  const uint16_t* krbase = has_rope ? a.kr + geo.kstart * kDr : kbase;   // not read without rope
-  const uint16_t* kibase = a.ki + geo.kstart * kIxDi;
-  constexpr int kPieces = kIxKC * (kDk / 8 + kIxDi / 8);       // 2816
-  constexpr int kPer = (kPieces + kIxThreads - 1) / kIxThreads;  // 6
-  u32x4 stage[kPer];
-  auto load_chunk = [&](int ci) {
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int e = (int)threadIdx.x + kIxThreads * u;
-      if (e < kPieces) {
-        const int r = e / 88, j = e % 88;
-        const int key = ci * kIxKC + r;
-        const bool ok = key < nkeys && (j < 64 || j >= 72 || has_rope);
-        const uint16_t* src = j < 64 ? kbase + (int64_t)key * kDn + 8 * j
-                              : j < 72 ? krbase + (int64_t)key * kDr + 8 * (j - 64)
-                                       : kibase + (int64_t)key * kIxDi + 8 * (j - 72);
-        stage[u] = ok ? *reinterpret_cast<const u32x4*>(src) : u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-  };
-  auto store_chunk = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int e = (int)threadIdx.x + kIxThreads * u;
-      if (e < kPieces) {
-        const int r = e / 88, j = e % 88;
-        uint16_t* dst = j < 72 ? &Kt[buf][r * kKPitch + 8 * j] : &Ki[buf][r * kIPitch + 8 * (j - 72)];
-        *reinterpret_cast<u32x4*>(dst) = stage[u];
-      }
-    }
-  };
+  const char* kb8 = reinterpret_cast<const char*>(a.k + geo.kstart * kDn);
+  const char* kr8 = has_rope ? reinterpret_cast<const char*>(a.kr + geo.kstart * kDr) : kb8;
+  const char* ki8 = reinterpret_cast<const char*>(a.ki + geo.kstart * kIxDi);
+  typedef __attribute__((address_space(3))) void LdsVoid;
+#define IX_GATHER_MAIN(KT, CH)                                                                  \
+  {                                                                                            \
+    const uint32_t key_ = (uint32_t)min((CH) * kIxKC + gkey, nkeys - 1);                       \
+    _Pragma("unroll") for (int j = 0; j < 9; ++j) {                                            \
+      const int b_ = wave + 4 * j;                   /* blocks 0..31: value, 32..35: rope */   \
+      const int col_ = 2 * b_ + gcol;                                                          \
+      const char* src_ = b_ < 32 ? kb8 + key_ * (uint32_t)(kDn * 2) + col_ * 16                \
+                                 : (has_rope ? kr8 + key_ * (uint32_t)(kDr * 2) + (col_ - 64) * 16 \
+                                             : kb8 + key_ * (uint32_t)(kDn * 2) + (col_ - 64) * 16); \
+      __builtin_amdgcn_global_load_lds(src_, (LdsVoid*)((KT) + b_ * 512), 16, 0, 0);          \
+    }                                                                                          \
+  }
+#define IX_GATHER_INDEX(KI, CH)                                                                 \
+  {                                                                                            \
+    const uint32_t key_ = (uint32_t)min((CH) * kIxKC + gkey, nkeys - 1);                       \
+    _Pragma("unroll") for (int j = 0; j < 2; ++j) {                                            \
+      const int b_ = (wave - 4) + 4 * j;              /* blocks 0..7 */                        \
+      __builtin_amdgcn_global_load_lds(ki8 + key_ * (uint32_t)(kIxDi * 2) + (2 * b_ + gcol) * 16, \
+                                       (LdsVoid*)((KI) + b_ * 512), 16, 0, 0);                 \
+    }                                                                                          \
+  }
+  // s_waitcnt operands with expcnt and lgkmcnt at zero: vmcnt(9) / vmcnt(2): all but the newest
+  // gather of a main / an index wave
+  constexpr int kWaitMain = 0x0009, kWaitIndex = 0x0002;
 
-  // Two roles with separate loops (their registers are never live together) and the same two
-  // barriers per chunk.  Main waves 0-3: head tiles w and w + 4.  Index waves 4-7: index-head
-  // tile w - 4.
+  // Two roles with separate loops (their registers are never live together) and the same
+  // barriers: one before step 0, two per step.  Step c: main waves form the scores of chunk c;
+  // index waves add dq~ of chunk c - 1 and form the index scores of chunk c; barrier A; every
+  // wave gathers its part of chunk c + 2 into the buffer chunk c - 1 used (the index waves
+  // first form the gradient terms of chunk c); wait for chunk c + 1; barrier B.
   if (wave < 4) {
     // A operands: Q of head 16 t + c (dims 32 ks + 8 g; steps 16, 17: rope), for t = w, w + 4
     bf16x8 qA[2][18];
@@ -168,42 +172,58 @@ __global__ void __launch_bounds__(kIxThreads, 1) ix_query_kernel(IxArgs a) {
                         ? *reinterpret_cast<const bf16x8*>(a.qr + (row * a.N1 + h) * kDr + 32 * (ks - 16) + 8 * g)
                         : bf16x8{};
     }
-    load_chunk(0);
-    store_chunk(0);
-    __syncthreads();
-    for (int ci = 0; ci < nchunk; ++ci) {
-      const int buf = ci & 1;
-      if (ci + 1 < nchunk) load_chunk(ci + 1);
-      const int s0 = ci * kIxKC;
-      float ps[2] = {0.f, 0.f};
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        if (!has[u]) continue;
-        const int t = wave + 4 * u;
-        f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-        for (int ks = 0; ks < 18; ++ks)
-#pragma unroll
-          for (int kt = 0; kt < 2; ++kt)
-            sacc[kt] = mfma_t<F16>(qA[u][ks], lds_read8p(Kt[buf], 16 * kt + c, 32 * ks + 8 * g, kKPitch), sacc[kt]);
-        const f32x4 mv = *reinterpret_cast<const f32x4*>(sM + 16 * t + 4 * g);
-        const f32x4 iv = *reinterpret_cast<const f32x4*>(sIL + 16 * t + 4 * g);
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) ps[kt] += __builtin_amdgcn_exp2f(sacc[kt][v] * zscale - mv[v]) * iv[v];
-      }
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        float p = ps[kt];
-        p += __shfl_xor(p, 16);
-        p += __shfl_xor(p, 32);
-        if (g == 0) sP[wave][16 * kt + c] = s0 + 16 * kt + c < nkeys ? p : 0.f;
-      }
-      lds_barrier();
-      if (ci + 1 < nchunk) store_chunk(buf ^ 1);
-      lds_barrier();
+    IX_GATHER_MAIN(Kt0, 0)
+    IX_GATHER_MAIN(Kt1, 1)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(kWaitMain);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+#define IX_MSTEP(CI, KC, KN)                                                                   \
+  {                                                                                            \
+    if ((CI) < nchunk) {                                                                       \
+      float ps[2] = {0.f, 0.f};                                                                \
+      _Pragma("unroll") for (int u = 0; u < 2; ++u) {                                          \
+        if (!has[u]) continue;                                                                 \
+        const int t = wave + 4 * u;                                                            \
+        f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};                \
+        _Pragma("unroll") for (int ks = 0; ks < 18; ++ks)                                      \
+          _Pragma("unroll") for (int kt = 0; kt < 2; ++kt)                                     \
+            sacc[kt] = mfma_t<F16>(qA[u][ks],                                                  \
+                                   *reinterpret_cast<const bf16x8*>((KC) + ((4 * ks + g) * kIxKC + 16 * kt + c) * 8), \
+                                   sacc[kt]);                                                  \
+        const f32x4 mv = *reinterpret_cast<const f32x4*>(sM + 16 * t + 4 * g);                 \
+        const f32x4 iv = *reinterpret_cast<const f32x4*>(sIL + 16 * t + 4 * g);                \
+        _Pragma("unroll") for (int kt = 0; kt < 2; ++kt)                                       \
+          _Pragma("unroll") for (int v = 0; v < 4; ++v)                                        \
+            ps[kt] += __builtin_amdgcn_exp2f(sacc[kt][v] * zscale - mv[v]) * iv[v];            \
+      }                                                                                        \
+      _Pragma("unroll") for (int kt = 0; kt < 2; ++kt) {                                       \
+        float p_ = ps[kt];                                                                     \
+        p_ += __shfl_xor(p_, 16);                                                              \
+        p_ += __shfl_xor(p_, 32);                                                              \
+        if (g == 0) sP[wave][16 * kt + c] = (CI) * kIxKC + 16 * kt + c < nkeys ? p_ : 0.f;     \
+      }                                                                                        \
+    }                                                                                          \
+    lds_barrier();                                                                             \
+    IX_GATHER_MAIN(KN, min((CI) + 2, nchunk - 1))                                              \
+    asm volatile("" ::: "memory");                                                             \
+    __builtin_amdgcn_s_waitcnt(kWaitMain);                                                     \
+    __builtin_amdgcn_s_barrier();                                                              \
+    asm volatile("" ::: "memory");                                                             \
+  }
+    int ci = 0;
+    for (; ci + 3 <= nchunk + 1; ci += 3) {
+      IX_MSTEP(ci, Kt0, Kt2)
+      IX_MSTEP(ci + 1, Kt1, Kt0)
+      IX_MSTEP(ci + 2, Kt2, Kt1)
     }
+    if (ci <= nchunk) {
+      IX_MSTEP(ci, Kt0, Kt2)
+      ++ci;
+    }
+    if (ci <= nchunk) IX_MSTEP(ci, Kt1, Kt0)
+#undef IX_MSTEP
+    __builtin_amdgcn_s_waitcnt(0);                // no gather may still write LDS at exit
     __syncthreads();                              // the index waves' row results
     return;
   }
@@ -230,75 +250,102 @@ __global__ void __launch_bounds__(kIxThreads, 1) ix_query_kernel(IxArgs a) {
   for (int nt = 0; nt < 8; ++nt) qacc[nt] = tacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float aw[4] = {0.f, 0.f, 0.f, 0.f}, bw[4] = {0.f, 0.f, 0.f, 0.f};
   float l1 = 0.f, nrm = 0.f;
+  // head sums of the previous chunk, stored at the start of the next step so that the stores
+  // are older than that step's gather (stores count in vmcnt too)
+  float tot_prev[2] = {0.f, 0.f};
+  int key_prev = -1;
 
-  load_chunk(0);
-  store_chunk(0);
-  __syncthreads();
-  for (int ci = 0; ci < nchunk; ++ci) {
-    const int buf = ci & 1;
-    if (ci + 1 < nchunk) load_chunk(ci + 1);
-    const int s0 = ci * kIxKC;
-    // index scores and this tile's part of I
-    f32x4 iacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-    if (hasi) {
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-          iacc[kt] = mfma_t<F16>(qiA[ks], lds_read8p(Ki[buf], 16 * kt + c, 32 * ks + 8 * g, kIPitch), iacc[kt]);
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        float is = 0.f;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) is += wv[v] * fmaxf(iacc[kt][v], 0.f);
-        is += __shfl_xor(is, 16);
-        is += __shfl_xor(is, 32);
-        if (g == 0) sI[it][16 * kt + c] = is;
-      }
-    }
-    lds_barrier();
-    // gradient terms of the chunk
-    if (hasi) {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const int key = 16 * kt + c;
-        const bool valid = s0 + key < nkeys;
-        const float tot = valid ? sP[0][key] + sP[1][key] + sP[2][key] + sP[3][key] : 0.f;
-        float ival = 0.f;
-        for (int u = 0; u < nit; ++u) ival += sI[u][key];
-        const float lsm = ival - max_i - lsum_i;   // log Softmax(I)
-        const float sm = valid ? __expf(lsm) : 0.f;
-        const float dip = sm - tot * inv_heads;   // dI with the provisional norm
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float s = iacc[kt][v];
-          const float relu = fmaxf(s, 0.f);
-          aw[v] += dip * relu;
-          bw[v] += tot * relu;
-          Dt[it][0][(4 * g + v) * kDsPitch + key] = f2x<F16>(s > 0.f ? dip : 0.f);
-          Dt[it][1][(4 * g + v) * kDsPitch + key] = f2x<F16>(s > 0.f ? tot : 0.f);
-        }
-        if (it == 0 && g == 0 && valid) {
-          if (tot > 0.f) l1 += tot * (__logf(tot) - lsm);
-          nrm += tot;
-          a.tot[row * a.kstride + s0 + key] = tot;
-        }
-      }
-    }
-    if (ci + 1 < nchunk) store_chunk(buf ^ 1);
-    lds_barrier();
-    // dq~ += dS' K~ and the correction term T K~
-    if (hasi) {
-      const bf16x8 da = *reinterpret_cast<const bf16x8*>(&Dt[it][0][c * kDsPitch + 8 * g]);
-      const bf16x8 ta = *reinterpret_cast<const bf16x8*>(&Dt[it][1][c * kDsPitch + 8 * g]);
-#pragma unroll
-      for (int nt = 0; nt < 8; ++nt) {
-        const bf16x8 kb = lds_frag_trp(Ki[buf], 0, 16 * nt, kIPitch, lane);
-        qacc[nt] = mfma_t<F16>(da, kb, qacc[nt]);
-        tacc[nt] = mfma_t<F16>(ta, kb, tacc[nt]);
-      }
-    }
+  IX_GATHER_INDEX(Ki0, 0)
+  IX_GATHER_INDEX(Ki1, 1)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(kWaitIndex);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+#define IX_ISTEP(CI, KC, KP)                                                                   \
+  {                                                                                            \
+    if (it == 0 && g == 0 && key_prev >= 0) {                                                  \
+      float* tp_ = a.tot + row * a.kstride + key_prev;                                         \
+      if (key_prev + c < nkeys) tp_[c] = tot_prev[0];                                          \
+      if (key_prev + 16 + c < nkeys) tp_[16 + c] = tot_prev[1];                                \
+    }                                                                                          \
+    key_prev = -1;                                                                             \
+    /* dq~ += dS' K~ and the correction term T K~ of chunk CI - 1 */                            \
+    if (hasi && (CI) >= 1) {                                                                   \
+      const bf16x8 da = *reinterpret_cast<const bf16x8*>(&Dt[it][0][c * kDsPitch + 8 * g]);    \
+      const bf16x8 ta = *reinterpret_cast<const bf16x8*>(&Dt[it][1][c * kDsPitch + 8 * g]);    \
+      _Pragma("unroll") for (int nt = 0; nt < 8; ++nt) {                                       \
+        const bf16x8 kb_ = lds_frag_tr_cm((KP), 16 * nt, lane);                                \
+        qacc[nt] = mfma_t<F16>(da, kb_, qacc[nt]);                                             \
+        tacc[nt] = mfma_t<F16>(ta, kb_, tacc[nt]);                                             \
+      }                                                                                        \
+    }                                                                                          \
+    f32x4 iacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};                    \
+    if (hasi && (CI) < nchunk) {                                                               \
+      _Pragma("unroll") for (int ks = 0; ks < 4; ++ks)                                         \
+        _Pragma("unroll") for (int kt = 0; kt < 2; ++kt)                                       \
+          iacc[kt] = mfma_t<F16>(qiA[ks],                                                      \
+                                 *reinterpret_cast<const bf16x8*>((KC) + ((4 * ks + g) * kIxKC + 16 * kt + c) * 8), \
+                                 iacc[kt]);                                                    \
+      _Pragma("unroll") for (int kt = 0; kt < 2; ++kt) {                                       \
+        float is = 0.f;                                                                        \
+        _Pragma("unroll") for (int v = 0; v < 4; ++v) is += wv[v] * fmaxf(iacc[kt][v], 0.f);   \
+        is += __shfl_xor(is, 16);                                                              \
+        is += __shfl_xor(is, 32);                                                              \
+        if (g == 0) sI[it][16 * kt + c] = is;                                                  \
+      }                                                                                        \
+    }                                                                                          \
+    lds_barrier();                                                                             \
+    /* gradient terms of chunk CI */                                                           \
+    if (hasi && (CI) < nchunk) {                                                               \
+      const int s0 = (CI) * kIxKC;                                                             \
+      _Pragma("unroll") for (int kt = 0; kt < 2; ++kt) {                                       \
+        const int key = 16 * kt + c;                                                           \
+        const bool valid = s0 + key < nkeys;                                                   \
+        const float tot = valid ? sP[0][key] + sP[1][key] + sP[2][key] + sP[3][key] : 0.f;     \
+        float ival = 0.f;                                                                      \
+        for (int u = 0; u < nit; ++u) ival += sI[u][key];                                      \
+        const float lsm = ival - max_i - lsum_i;   /* log Softmax(I) */                        \
+        const float sm = valid ? __expf(lsm) : 0.f;                                            \
+        const float dip = sm - tot * inv_heads;    /* dI with the provisional norm */          \
+        _Pragma("unroll") for (int v = 0; v < 4; ++v) {                                        \
+          const float sv_ = iacc[kt][v];                                                       \
+          const float relu = fmaxf(sv_, 0.f);                                                  \
+          aw[v] += dip * relu;                                                                 \
+          bw[v] += tot * relu;                                                                 \
+          Dt[it][0][(4 * g + v) * kDsPitch + key] = f2x<F16>(sv_ > 0.f ? dip : 0.f);            \
+          Dt[it][1][(4 * g + v) * kDsPitch + key] = f2x<F16>(sv_ > 0.f ? tot : 0.f);            \
+        }                                                                                      \
+        if (it == 0 && g == 0 && valid) {                                                      \
+          if (tot > 0.f) l1 += tot * (__logf(tot) - lsm);                                      \
+          nrm += tot;                                                                          \
+        }                                                                                      \
+        tot_prev[kt] = tot;                                                                    \
+      }                                                                                        \
+      key_prev = s0;                                                                           \
+    }                                                                                          \
+    IX_GATHER_INDEX(KP, min((CI) + 2, nchunk - 1))                                             \
+    asm volatile("" ::: "memory");                                                             \
+    __builtin_amdgcn_s_waitcnt(kWaitIndex);                                                    \
+    __builtin_amdgcn_s_barrier();                                                              \
+    asm volatile("" ::: "memory");                                                             \
   }
+  {
+    int ci = 0;
+    for (; ci + 3 <= nchunk + 1; ci += 3) {
+      IX_ISTEP(ci, Ki0, Ki2)
+      IX_ISTEP(ci + 1, Ki1, Ki0)
+      IX_ISTEP(ci + 2, Ki2, Ki1)
+    }
+    if (ci <= nchunk) {
+      IX_ISTEP(ci, Ki0, Ki2)
+      ++ci;
+    }
+    if (ci <= nchunk) IX_ISTEP(ci, Ki1, Ki0)
+  }
+#undef IX_ISTEP
+#undef IX_GATHER_MAIN
+#undef IX_GATHER_INDEX
+  __builtin_amdgcn_s_waitcnt(0);                  // no gather may still write LDS at exit
 
   // ---- row results ----
   if (it == 0) {
