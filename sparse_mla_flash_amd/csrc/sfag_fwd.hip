@@ -38,6 +38,30 @@ constexpr int kLdsK = kBlocks * 64 * 16;         // one key tile, chunk-major
 // newest gather) and vmcnt(10) (all but a gather and one position load)
 constexpr int kWaitVm9 = 0x0009;
 constexpr int kWaitVm10 = 0x000a;
+
+// Max and sum over the 16 lanes of a row (lanes 16 r .. 16 r + 15) by DPP moves, which stay in
+// the vector ALU (cross-lane shuffles through ds_bpermute would occupy the LDS pipe): swap in
+// pairs, in quads, mirror the half rows, mirror the rows; every lane ends with the total.
+template <int Ctrl>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), Ctrl, 0xf, 0xf, false));
+}
+constexpr int kDppXor1 = 0xB1;          // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;          // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141;   // row_half_mirror
+constexpr int kDppMirror = 0x140;       // row_mirror
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp_f<kDppXor1>(x));
+  x = fmaxf(x, dpp_f<kDppXor2>(x));
+  x = fmaxf(x, dpp_f<kDppHalfMirror>(x));
+  return fmaxf(x, dpp_f<kDppMirror>(x));
+}
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_f<kDppXor1>(x);
+  x += dpp_f<kDppXor2>(x);
+  x += dpp_f<kDppHalfMirror>(x);
+  return x + dpp_f<kDppMirror>(x);
+}
 }  // namespace
 
 template <bool F16>
@@ -154,12 +178,7 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
       _Pragma("unroll") for (int v = 0; v < 4; ++v) {                                          \
         sacc[0][v] = ok0 ? sacc[0][v] * zscale : -INFINITY;                                    \
         sacc[1][v] = ok1 ? sacc[1][v] * zscale : -INFINITY;                                    \
-        float x = fmaxf(sacc[0][v], sacc[1][v]);                                               \
-        x = fmaxf(x, __shfl_xor(x, 1));                                                        \
-        x = fmaxf(x, __shfl_xor(x, 2));                                                        \
-        x = fmaxf(x, __shfl_xor(x, 4));                                                        \
-        x = fmaxf(x, __shfl_xor(x, 8));                                                        \
-        mc[v] = fmaxf(m[v], x);                                                                \
+        mc[v] = fmaxf(m[v], row16_max(fmaxf(sacc[0][v], sacc[1][v])));                        \
       }                                                                                        \
       const int hcol = 16 * rw + 4 * g;                                                        \
       float p[2][4];                                                                           \
@@ -169,12 +188,7 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
         const float al = fin ? __builtin_amdgcn_exp2f(m[v] - mc[v]) : 1.f;                     \
         p[0][v] = fin ? __builtin_amdgcn_exp2f(sacc[0][v] - mc[v]) : 0.f;                      \
         p[1][v] = fin ? __builtin_amdgcn_exp2f(sacc[1][v] - mc[v]) : 0.f;                      \
-        float ps = p[0][v] + p[1][v];                                                          \
-        ps += __shfl_xor(ps, 1);                                                               \
-        ps += __shfl_xor(ps, 2);                                                               \
-        ps += __shfl_xor(ps, 4);                                                               \
-        ps += __shfl_xor(ps, 8);                                                               \
-        l[v] = l[v] * al + ps;                                                                 \
+        l[v] = l[v] * al + row16_sum(p[0][v] + p[1][v]);                                       \
         m[v] = mc[v];                                                                          \
         if (c == 0) (AD)[hcol + v] = al;                                                       \
       }                                                                                        \
