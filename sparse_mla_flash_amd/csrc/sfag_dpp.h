@@ -1,0 +1,35 @@
+// sfag_dpp.h -- reductions over the 16 lanes of a row by DPP moves (gfx950).
+//
+// Cross-lane shuffles (__shfl_xor) compile to ds_bpermute / ds_swizzle, which occupy the LDS pipe
+// and wait for its latency; DPP moves stay in the vector ALU.  A row of 16 lanes is reduced by
+// swapping in pairs and in quads, mirroring the half rows and mirroring the row: every lane of
+// the row ends with the total.
+#pragma once
+#include <hip/hip_runtime.h>
+
+namespace sfag {
+
+template <int Ctrl>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), Ctrl, 0xf, 0xf, false));
+}
+constexpr int kDppXor1 = 0xB1;          // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;          // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141;   // row_half_mirror
+constexpr int kDppMirror = 0x140;       // row_mirror
+
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp_f<kDppXor1>(x));
+  x = fmaxf(x, dpp_f<kDppXor2>(x));
+  x = fmaxf(x, dpp_f<kDppHalfMirror>(x));
+  return fmaxf(x, dpp_f<kDppMirror>(x));
+}
+
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_f<kDppXor1>(x);
+  x += dpp_f<kDppXor2>(x);
+  x += dpp_f<kDppHalfMirror>(x);
+  return x + dpp_f<kDppMirror>(x);
+}
+
+}  // namespace sfag

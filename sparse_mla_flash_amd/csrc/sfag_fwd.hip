@@ -22,6 +22,7 @@
 // and alpha double-buffered.  Key tiles are chunk-major in LDS ([72 chunks of 16 B][32 keys]),
 // so each gathering lane handles one key and each of its loads is one add to that key's row.
 #include "sfag_device.h"
+#include "sfag_dpp.h"
 #include "sfag_launch.h"
 
 namespace sfag {
@@ -38,30 +39,6 @@ constexpr int kLdsK = kBlocks * 64 * 16;         // one key tile, chunk-major
 // newest gather) and vmcnt(10) (all but a gather and one position load)
 constexpr int kWaitVm9 = 0x0009;
 constexpr int kWaitVm10 = 0x000a;
-
-// Max and sum over the 16 lanes of a row (lanes 16 r .. 16 r + 15) by DPP moves, which stay in
-// the vector ALU (cross-lane shuffles through ds_bpermute would occupy the LDS pipe): swap in
-// pairs, in quads, mirror the half rows, mirror the rows; every lane ends with the total.
-template <int Ctrl>
-__device__ __forceinline__ float dpp_f(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), Ctrl, 0xf, 0xf, false));
-}
-constexpr int kDppXor1 = 0xB1;          // quad_perm [1, 0, 3, 2]
-constexpr int kDppXor2 = 0x4E;          // quad_perm [2, 3, 0, 1]
-constexpr int kDppHalfMirror = 0x141;   // row_half_mirror
-constexpr int kDppMirror = 0x140;       // row_mirror
-__device__ __forceinline__ float row16_max(float x) {
-  x = fmaxf(x, dpp_f<kDppXor1>(x));
-  x = fmaxf(x, dpp_f<kDppXor2>(x));
-  x = fmaxf(x, dpp_f<kDppHalfMirror>(x));
-  return fmaxf(x, dpp_f<kDppMirror>(x));
-}
-__device__ __forceinline__ float row16_sum(float x) {
-  x += dpp_f<kDppXor1>(x);
-  x += dpp_f<kDppXor2>(x);
-  x += dpp_f<kDppHalfMirror>(x);
-  return x + dpp_f<kDppMirror>(x);
-}
 }  // namespace
 
 template <bool F16>

@@ -28,6 +28,7 @@
 //   ix_finish_kernel dK~ = sum of the parts in part order, and the loss = sum of the rows' losses
 //                    in row order (one workgroup); deterministic.
 #include "sfag_device.h"
+#include "sfag_dpp.h"
 #include "sfag_launch.h"
 
 namespace sfag {
@@ -44,11 +45,7 @@ constexpr int kKeyTile = 64;
 constexpr int kDkPitch = 64 + 8;                  // [16 keys][64 index heads] dS tile per wave
 
 __device__ __forceinline__ float wsum16(float v) {  // sum over the 16 lanes c of a 16-lane group
-  v += __shfl_xor(v, 1);
-  v += __shfl_xor(v, 2);
-  v += __shfl_xor(v, 4);
-  v += __shfl_xor(v, 8);
-  return v;
+  return row16_sum(v);
 }
 }  // namespace
 
