@@ -133,6 +133,40 @@ def test_forward_matches_oracle(name):
     assert np.abs(l - case.l64).max() <= 1e-4 * max(1.0, np.abs(case.l64).max())
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_forward_max_rising_far_after_the_first_chunk(dtype):
+    """One key, selected by row r only after its first 32 slots, is a multiple of r's head-0 query:
+    that head's logit for it lies about 100 nats above everything in the row's first chunk.  The
+    forward's reference max comes from the first chunk, so its probabilities would overflow
+    (exp of about 144 in log2 units) unless the row is recomputed against the true max."""
+    import sparse_mla_flash_amd as sf
+    p = inputs.problem(layout="BSND", B=1, S1=16, S2=256, N1=16, topk=128, sparse_mode=0,
+                       name=f"rising_max_{dtype}", dtype=dtype)
+    inputs.generate(p, 41)
+    idx = p.idx.reshape(p.rows, p.topk)
+    r = 5
+    first = set(int(j) for j in idx[r, :32])
+    j = next(int(x) for x in idx[r, 40:] if x >= 0 and int(x) not in first)
+    qh = inputs.bits_to_f64(p.q, dtype).reshape(p.rows, p.N1, p.D)[r, 0]
+    factor = 100.0 / (p.scale * float(qh @ qh))
+    k = p.k.reshape(p.S2, p.D)
+    k[j] = inputs.f32_to_bits((factor * qh).astype(np.float32), dtype)
+    p.v = p.k.copy()
+    case = Case(p)
+    assert case.m64.max() > 90.0                  # the planted logit is the row's maximum
+    d = case.device_inputs()
+    out, smax, ssum = sf.sparse_flash_attention_forward(
+        d["query"], d["key"], d["value"], d["sparse_indices"], p.seq_q, p.seq_kv, d["query_rope"],
+        d["key_rope"], scale_value=p.scale, layout=p.layout, sparse_mode=p.sparse_mode)
+    u = 2.0 ** -11 if dtype == "fp16" else 2.0 ** -8
+    got = from_dev(out)
+    assert np.isfinite(got).all()
+    compare(p.name + "/out", got, case.out64, u=u)
+    m, l = from_dev(smax), from_dev(ssum)
+    assert np.abs(m - case.m64).max() <= 1e-4 * max(1.0, np.abs(case.m64).max())
+    assert np.abs(l - case.l64).max() <= 1e-4 * max(1.0, np.abs(case.l64).max())
+
+
 BLOCK_CASES = {
     # name: (problem kwargs, seed); block selection, the last block cut by the key length
     "bsnd_n16_block4_causal": (dict(layout="BSND", B=1, S1=40, S2=301, N1=16, topk=20, sparse_mode=3,
