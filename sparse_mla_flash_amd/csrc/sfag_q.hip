@@ -17,19 +17,20 @@
 //     and dP of its head tile for both 16-key tiles (every 16-byte key fragment read from LDS
 //     feeds the S and dP MFMAs of its key tile), then P and dS in registers, the chunk's dS
 //     tile in LDS ([key][head]) and the 256-byte dS | P record of every (row, key) pair.
-//   dQ waves (4-7): wave 4 + w owns output dims 144 w .. 144 w + 143 for all 64 heads (fp32
-//     accumulators across all chunks) and in step c adds dS K of chunk c - 1 (each gathered key
-//     element is read, transposed, once per workgroup); it also gathers chunk c + 2 straight
-//     from global memory into LDS (global_load_lds, 16 bytes per lane).
+//   dQ waves (4-7): wave 4 + w owns the output dims of 16-dim column tiles w, w + 4, .., w + 32
+//     (144 dims) for all 64 heads (fp32 accumulators across all chunks) and in step c adds dS K
+//     of chunk c - 1 (each gathered key element is read, transposed, once per workgroup); it also
+//     gathers keys 8 w .. 8 w + 7 of chunk c + 2 straight from global memory into LDS
+//     (global_load_lds, 16 bytes per lane).
 // Records are stored chunk-major: per (row, head group) and chunk of 32 sorted positions, 8 KB
 // = [dS | P][head tile of 16][32 positions][16 heads] bf16, so that each record store
 // instruction of a score wave writes 512 contiguous bytes.
 // One barrier per step.  Key tiles are quadruple-buffered and gathered two chunks ahead, so a
-// gather has two steps to land; dS tiles are double-buffered.  Key tiles are stored
-// chunk-major in LDS ([72 chunks of 16 B][32 keys]): one direct-to-LDS block (64 lanes x 16 B)
-// is then two chunk columns of all 32 keys, so a gathering lane always handles the same key
-// (lane % 32) and each of its loads is one add to that key's row address.
+// gather has two steps to land; dS tiles are double-buffered.  Key tiles use the swizzled
+// [chunk group][key][slot] layout of sfag_ktile.h: each direct-to-LDS load reads eight whole
+// 128-byte runs of key rows, and a gathering lane always handles the same key.
 #include "sfag_device.h"
+#include "sfag_ktile.h"
 #include "sfag_launch.h"
 
 namespace sfag {
@@ -39,10 +40,11 @@ constexpr int kKC = 32;
 constexpr int kThreads = 512;                    // 4 score waves + 4 dQ waves
 constexpr int kChunks = kDk / 8;                 // 72 16-byte chunks per key row (64 value + 8 rope)
 constexpr int kHtPitch = 64 + 8;                 // DSt row pitch
-constexpr int kBlocks = kChunks / 2;             // 36 direct-to-LDS blocks (2 chunk columns) per tile
+constexpr int kBlocks = kChunks / 2;             // 36 direct-to-LDS blocks of 1 KB per tile
 static_assert(kBlocks % 4 == 0, "gather blocks per dQ wave");
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kLdsK = kBlocks * 64 * 16;         // one key tile, chunk-major: [72 chunks][32 keys][16 B]
+constexpr int kLdsK = kBlocks * 64 * 16;         // one key tile
+static_assert(kLdsK == kTileBytes, "key tile size");
 constexpr int kLdsDS = kKC * kHtPitch * 2;       // DSt [32 keys][72]
 constexpr int kLdsTotal = 4 * kLdsK + 2 * kLdsDS + 3 * 64 * 4 + 2 * 257 * 4;
 static_assert(kLdsTotal <= 160 * 1024, "LDS budget");
@@ -142,31 +144,33 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
   uint16_t* recrow = uniform(a.dsp + (lrow * a.hgc + hg) * (int64_t)a.rec_chunks * kRecChunk);
   asm volatile("" : "+s"(kbase), "+s"(krbase), "+s"(recrow));
 
-  // gathering lanes of the dQ waves: key slot gkey of every chunk, chunk column gcol of every block
-  const int gkey = lane & 31, gcol = lane >> 5;
-  // byte bases of this dQ wave's gather: value chunks 2 b, 2 b + 1 of key 0 for its blocks
-  // b = rw + 4 j, and rope chunks 2 rw, 2 rw + 1 (of the zero row without rope inputs); held as
-  // opaque scalars so that every load is one scalar base plus the lane's 32-bit offset
+  // gathering lanes of the dQ waves: key gkey of every chunk, the 16 bytes at gcol of each
+  // 128-byte run of its row
+  const int gkey = ktile_gather_key(rw, lane);
+  const uint32_t gcol = ktile_gather_col(rw, lane);
+  // byte bases of the gather: value chunk group j of key 0, and the rope row (the zero row
+  // without rope inputs); held as opaque scalars so that every load is one scalar base plus the
+  // lane's 32-bit offset
   const char* kgat[kBlocks / 4 - 1];
 #pragma unroll
   for (int j = 0; j < kBlocks / 4 - 1; ++j) {
-    kgat[j] = reinterpret_cast<const char*>(uniform(kbase + 16 * rw + 64 * j));
+    kgat[j] = reinterpret_cast<const char*>(uniform(kbase + 64 * j));
     asm volatile("" : "+s"(kgat[j]));
   }
-  const char* rgat = reinterpret_cast<const char*>(uniform(krbase + 16 * rw));
+  const char* rgat = reinterpret_cast<const char*>(uniform(krbase));
   asm volatile("" : "+s"(rgat));
 
-  // Gather of chunk CH (this lane's key: sorted position SV) into key buffer KS (dQ waves): block
-  // b of the tile holds chunk columns 2 b and 2 b + 1; dQ wave rw loads blocks rw, rw + 4, ...,
-  // rw + 32 (the last one: rope chunks).  Slots past the row's valid count read the zero row.
+  // Gather of chunk CH (this lane's key: sorted position SV) into key buffer KS (dQ waves): dQ
+  // wave rw loads keys 8 rw .. 8 rw + 7 of chunk groups 0 .. 8 (the last one: the rope row) into
+  // blocks 4 j + rw.
 #define SFAG_GATHER_ASYNC(KS, CH, SV)                                                          \
   {                                                                                            \
     /* slots past the row's valid count repeat its last valid key (their p is 0) */           \
-    const uint32_t ko_ = (uint32_t)(SV) * (uint32_t)(kDn * 2) + gcol * 16u;                    \
-    const uint32_t ro_ = rope ? (uint32_t)(SV) * (uint32_t)(kDr * 2) + gcol * 16u : gcol * 16u; \
+    const uint32_t ko_ = (uint32_t)(SV) * (uint32_t)(kDn * 2) + gcol;                          \
+    const uint32_t ro_ = rope ? (uint32_t)(SV) * (uint32_t)(kDr * 2) + gcol : gcol;            \
     _Pragma("unroll") for (int j = 0; j < kBlocks / 4; ++j) {                                  \
       const char* src = j < kBlocks / 4 - 1 ? kgat[j] + ko_ : rgat + ro_;                      \
-      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)((KS) + (rw + 4 * j) * 512), 16, 0, 0); \
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)((KS) + (4 * j + rw) * 512), 16, 0, 0); \
     }                                                                                          \
   }
 
@@ -177,19 +181,21 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
       sacc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};                                                    \
       pacc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};                                                    \
     }                                                                                          \
-    /* chunk-major tile: element (chunk, key) at (chunk * 32 + key) * 8; lane (g, c) of step  \
-       ks reads chunk 4 ks + g of key 16 kt + c */                                             \
-    const uint16_t* kr0 = (KS) + (g * kKC + c) * 8;                                            \
-    const uint16_t* kr1 = (KS) + (g * kKC + 16 + c) * 8;                                       \
+    /* lane (g, c) of step ks reads chunk 4 ks + g of keys c and 16 + c: chunk group ks / 2,   \
+       slot bit 2 = ks % 2 (key 16 + c is 1024 elements after key c) */                        \
+    const uint16_t* kre = (KS) + kse;                                                          \
+    const uint16_t* kro = (KS) + (kse ^ 32);                                                   \
     bf16x8 kf0[18], kf1[18];                /* key fragments, read two steps ahead */         \
     _Pragma("unroll") for (int ks = 0; ks < 2; ++ks) {                                         \
-      kf0[ks] = *reinterpret_cast<const bf16x8*>(kr0 + 4 * ks * kKC * 8);                      \
-      kf1[ks] = *reinterpret_cast<const bf16x8*>(kr1 + 4 * ks * kKC * 8);                      \
+      const uint16_t* kr_ = (ks & 1) ? kro : kre;                                              \
+      kf0[ks] = *reinterpret_cast<const bf16x8*>(kr_ + (ks >> 1) * 2048);                      \
+      kf1[ks] = *reinterpret_cast<const bf16x8*>(kr_ + (ks >> 1) * 2048 + 1024);               \
     }                                                                                          \
     _Pragma("unroll") for (int ks = 0; ks < 18; ++ks) {                                        \
       if (ks + 2 < 18) {                                                                       \
-        kf0[ks + 2] = *reinterpret_cast<const bf16x8*>(kr0 + 4 * (ks + 2) * kKC * 8);          \
-        kf1[ks + 2] = *reinterpret_cast<const bf16x8*>(kr1 + 4 * (ks + 2) * kKC * 8);          \
+        const uint16_t* kr_ = ((ks + 2) & 1) ? kro : kre;                                      \
+        kf0[ks + 2] = *reinterpret_cast<const bf16x8*>(kr_ + ((ks + 2) >> 1) * 2048);          \
+        kf1[ks + 2] = *reinterpret_cast<const bf16x8*>(kr_ + ((ks + 2) >> 1) * 2048 + 1024);   \
       }                                                                                        \
       sacc[0] = mfma_t<F16>(qA[ks], kf0[ks], sacc[0]);                                                \
       sacc[1] = mfma_t<F16>(qA[ks], kf1[ks], sacc[1]);                                                \
@@ -209,20 +215,21 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
     __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                         \
   }
 
-// dQ[64 heads][144 rw .. 144 rw + 143] += dS[64][32 keys] K[32 keys][dims] of one chunk.  A
-// operands (dS^T, heads 16 t + c) from the [key][head] tile, B operands (K, dims 144 rw + 16 nt
-// + c) from the chunk-major key tile, both by transposing reads at one per-lane offset plus
-// constants: the B fragment of column tile nt starts 512 elements after that of nt - 1.
+// dQ[64 heads][column tiles rw + 4 nt] += dS[64][32 keys] K[32 keys][dims] of one chunk.  A
+// operands (dS^T, heads 16 t + c) from the [key][head] tile, B operands (K, dims 16 (rw + 4 nt)
+// + c: chunk group nt, slot pair rw) from the key tile, both by transposing reads at one
+// per-lane offset plus constants (2048 elements per column tile).  The contraction takes the
+// chunk's keys in the order 4 g + j, 4 g + 16 + j (j = 0..3) for lane group g in both operands.
 #define SFAG_DQ(KS, DST)                                                                       \
   {                                                                                            \
     const uint16_t* kq_ = (KS) + kqoff;                                                        \
     const uint16_t* dq_ = (DST) + dsoff;                                                       \
     bf16x8 dsa[4];                                                                             \
-    _Pragma("unroll") for (int t = 0; t < 4; ++t) dsa[t] = tr_frag(dq_ + 16 * t, 4 * kHtPitch); \
-    bf16x8 kb = tr_frag(kq_, 32);                                                              \
+    _Pragma("unroll") for (int t = 0; t < 4; ++t) dsa[t] = tr_frag(dq_ + 16 * t, 16 * kHtPitch); \
+    bf16x8 kb = tr_frag(kq_, 1024);                                                            \
     _Pragma("unroll") for (int nt = 0; nt < 9; ++nt) {                                         \
       bf16x8 nb = kb;                                                                          \
-      if (nt < 8) nb = tr_frag(kq_ + 512 * (nt + 1), 32);                                      \
+      if (nt < 8) nb = tr_frag(kq_ + 2048 * (nt + 1), 1024);                                   \
       _Pragma("unroll") for (int t = 0; t < 4; ++t) dqacc[t][nt] = mfma_t<F16>(dsa[t], kb, dqacc[t][nt]); \
       kb = nb;                                                                                 \
     }                                                                                          \
@@ -313,6 +320,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
     }
     lds_barrier();
     f32x4 sacc[2], pacc[2];
+    const int kse = ktile_off(g, c);                // chunk g of key c
 // Score step CI on key buffer KC and dS buffer DC; ends by waiting for this wave's LDS accesses
 // (the record stores stay in flight).
 #define SFAG_SSTEP(CI, KC, DC)                                                                 \
@@ -355,11 +363,12 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
     __builtin_amdgcn_s_waitcnt(kWaitVm10);
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    // transposing-read lane offsets: K tile (chunk-major, element (key k, dim n) at
-    // ((n / 8) * 32 + k) * 8 + n % 8; lane (g, c) of a read pair points at key 8 g + c / 4 and dim
-    // 144 rw + 4 (c % 4)) and dS tile ([key][head], pitch 72; key 8 g + c / 4, head 4 (c % 4))
-    const int kqoff = ((18 * rw + ((c & 3) >> 1)) * kKC + 8 * g + (c >> 2)) * 8 + 4 * (c & 1);
-    const int dsoff = (8 * g + (c >> 2)) * kHtPitch + 4 * (c & 3);
+    // transposing-read lane offsets (keys 4 g + c / 4 and, at the second read, + 16): K tile
+    // (dims 16 rw + 4 (c % 4) of chunk group 0, i.e. chunk 2 rw + (c % 4) / 2) and dS tile
+    // ([key][head], pitch 72; head 4 (c % 4))
+    const int tk = 4 * g + (c >> 2);
+    const int kqoff = tk * 64 + (((2 * rw + ((c & 3) >> 1)) ^ ktile_swz(tk)) << 3) + 4 * (c & 1);
+    const int dsoff = tk * kHtPitch + 4 * (c & 3);
     f32x4 dqacc[4][9];
 #pragma unroll
     for (int t = 0; t < 4; ++t)
@@ -403,7 +412,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
 #undef SFAG_QSTEP
     __builtin_amdgcn_s_waitcnt(0);                        // no gather may still write LDS at exit
 
-    // ---- dQ / dQRope out: lane holds heads 16 t + 4 g + v, dims 144 rw + 16 nt + c ----------------
+    // ---- dQ / dQRope out: lane holds heads 16 t + 4 g + v, dims 16 (rw + 4 nt) + c -------------
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
 #pragma unroll
@@ -413,7 +422,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
         const int64_t hh2 = row * a.N1 + h0 + h;
 #pragma unroll
         for (int nt = 0; nt < 9; ++nt) {
-          const int col = 144 * rw + 16 * nt + c;
+          const int col = 16 * (rw + 4 * nt) + c;
           const uint16_t bv = f2x<F16>(dqacc[t][nt][v] * a.scale);
           if (col < kDn) a.dq[hh2 * kDn + col] = bv;
           else if (a.dqr) a.dqr[hh2 * kDr + col - kDn] = bv;
