@@ -119,20 +119,29 @@ __global__ void __launch_bounds__(kThreads) sort_rows_kernel(DenseArgs a) {
     // w1 - w0 is a multiple of 256, so a thread's 64 keys are all inside or all outside
     if (k0 < w1) {
       if ((k0 & (kBk - 1)) == 0) orow[k0 / kBk] = pos;                   // block start
+      short mv[64];                                                       // map of keys k0 + i
 #pragma unroll
       for (int q = 0; q < 8; ++q) {                                       // 8 keys per step
         const u32x4 v = *reinterpret_cast<const u32x4*>(mine + 4 * q);
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-        i16x8 m;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int n = (int)((w[e >> 1] >> (16 * (e & 1))) & 0xffffu);
-          m[e] = n > 0 ? (short)pos : (short)-1;
+          mv[8 * q + e] = n > 0 ? (short)pos : (short)-1;
           for (int r = 0; r < n; ++r) srow[pos + r] = k0 + 8 * q + e;
           pos += n;
           dup = max(dup, n);
         }
-        if (keep_map) *reinterpret_cast<i16x8*>(kp + k0 + 8 * q) = m;
+      }
+      // stored permuted inside the 64-key group: key 16 kt + c at 4 c + kt
+      if (keep_map) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          i16x8 m;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) m[e] = mv[16 * (e & 3) + 2 * q + (e >> 2)];
+          *reinterpret_cast<i16x8*>(kp + k0 + 8 * q) = m;
+        }
       }
     }
     __syncthreads();
@@ -218,12 +227,12 @@ __global__ void __launch_bounds__(1024) item_list_kernel(DenseArgs a) {
 //       memory: lane (g, c) handles key kb0 + 64 w + 16 kt + c (kt = 0..3) as row c of key
 //       tile kt, found through the row's key -> position map; unselected keys load nothing.
 //       The heads are contracted in the order that matches the record layout: head step ks of
-//       lane (g, c) covers heads 16 g + 8 ks .. + 7, so the two A fragments of a key are one
-//       32-byte run of head tile g.
+//       lane (g, c) covers heads 32 ks + 8 g .. + 7, so the lanes of one head step read both
+//       16-byte halves of head tiles 2 ks and 2 ks + 1 of every position (whole 32-byte runs).
 //   B = the row's [64 heads x cols] Q (or dO) slice, read from the column-major copy written by
 //       the query-major kernel (one contiguous run of 2 KB per column tile), staged in LDS as
 //       [column][8 chunks of 8 heads + 1 pad chunk] and read as whole 16-byte fragments (head
-//       chunk 2 g + ks for head step ks).
+//       chunk 4 ks + g for head step ks).
 //   acc[keys][cols] += A B  on the 16x16x32 bf16 MFMA, fp32 in registers; accumulator row
 //       4 g + v of key tile kt is key kb0 + 64 w + 16 kt + 4 g + v.
 // Two workgroups share a CU (at most 256 registers per lane), so each unit is simple: its
@@ -269,13 +278,17 @@ __device__ __forceinline__ void kv_dense_units(const DenseArgs& a, const KvCtx& 
   const uint16_t* bt_base = a.bt + ((int64_t)x.hg * kDacc + x.colbase) * 64;
 
   const int kmap = x.kb0 + 64 * wave + c;            // this lane's key of key tile kt: kmap + 16 kt
+  const int kb0w = x.kb0 + 64 * wave;                 // first key of this wave's 64-key group
   const int64_t row0 = x.qstart + x.i0;
   // records of (row, hg): chunk-major [chunk][dS | P][head tile of 16][32 positions][16 heads].
-  // The contraction over heads is taken in the order that makes each lane's A fragments one
-  // 32-byte run: head step ks of lane (g, c) covers heads 16 g + 8 ks .. + 7 (head tile g), and
-  // the B fragments read the same heads of Q / dO.
+  // The contraction over heads is taken in the order that makes each record load read whole
+  // 32-byte runs: head step ks of lane (g, c) covers heads 32 ks + 8 g .. + 7 (half g % 2 of head
+  // tile 2 ks + g / 2), so one load instruction reads both halves of every position of two head
+  // tiles; the B fragments read the same heads of Q / dO.
   const int64_t rec_row = (int64_t)a.hgc * a.rec_chunks * kRecChunk;
-  const uint16_t* rec_base = a.dsp + (int64_t)x.hg * a.rec_chunks * kRecChunk + x.which + g * 512;
+  const uint16_t* rec_base = a.dsp + (int64_t)x.hg * a.rec_chunks * kRecChunk + x.which;
+  const uint32_t rec_lane = (uint32_t)((g >> 1) * 512 + 8 * (g & 1));
+  const uint16_t* zrow = a.zero_row;                 // 576 zero elements
 
   f32x4 acc[4][NFT];
 #pragma unroll
@@ -285,22 +298,22 @@ __device__ __forceinline__ void kv_dense_units(const DenseArgs& a, const KvCtx& 
 
 #define KV_MAP_LOAD(MP, ROW)                                                                   \
   {                                                                                            \
-    const int16_t* m_ = a.kpos + (row0 + (ROW)) * a.kstride + kmap;                            \
-    _Pragma("unroll") for (int kt = 0; kt < 4; ++kt) MP[kt] = m_[16 * kt];                     \
+    /* the map stores key 16 kt + c of each 64-key group at 4 c + kt: one 8-byte load */       \
+    MP = *reinterpret_cast<const i16x4*>(a.kpos + (row0 + (ROW)) * a.kstride + kb0w + 4 * c); \
   }
-#define KV_B_LOAD(SP, ROW)                                                                     \
+#define KV_B_LOAD(SP, ROW, I0, I1)                                                             \
   {                                                                                            \
     const char* run_ = reinterpret_cast<const char*>(bt_base + (row0 + (ROW)) * bt_row);       \
-    _Pragma("unroll") for (int i = 0; i < kBLoads; ++i)                                        \
-      SP[i] = *reinterpret_cast<const u32x4*>(run_ + bsrc[i]);                                 \
+    _Pragma("unroll") for (int i = (I0); i < (I1); ++i)                                        \
+      SP[i - (I0)] = *reinterpret_cast<const u32x4*>(run_ + bsrc[i]);                          \
   }
-#define KV_B_STORE(BT, SP)                                                                     \
+#define KV_B_STORE(BT, SP, I0, I1)                                                             \
   {                                                                                            \
-    _Pragma("unroll") for (int i = 0; i < kBLoads; ++i)                                        \
-      *reinterpret_cast<u32x4*>((BT) + bdst[i]) = SP[i];                                       \
+    _Pragma("unroll") for (int i = (I0); i < (I1); ++i)                                        \
+      *reinterpret_cast<u32x4*>((BT) + bdst[i]) = SP[i - (I0)];                                \
   }
 #define KV_BFRAG(BT, Q)                                                                        \
-  (*reinterpret_cast<const bf16x8*>((BT) + ((16 * ((Q) >> 1) + c) * kBtColChunks + 2 * g + ((Q) & 1)) * 8))
+  (*reinterpret_cast<const bf16x8*>((BT) + ((16 * ((Q) >> 1) + c) * kBtColChunks + 4 * ((Q) & 1) + g) * 8))
 
   // unit cursor: row index ri (into s_row) and repeat layer L; the next unit's row is rn
   auto advance = [&](int& ri, int& L) {
@@ -313,30 +326,36 @@ __device__ __forceinline__ void kv_dense_units(const DenseArgs& a, const KvCtx& 
   };
   int ri = 0, L = 0;
   i16x4 mc;                                          // map of the current unit's row
-  u32x4 bs[kBLoads];
+  constexpr int kBHalf = (kBLoads + 1) / 2;          // B loads staged in the first half-unit
+  u32x4 bs[kBHalf];
   bf16x8 f[4][2];                                    // A fragments: [key tile][head step]
   // records of unit (row R, layer LL, map MP), head step KS, into f[*][KS] (zero where the row
   // did not select the key)
 #define KV_REC_LOAD(R, LL, MP, KS)                                                             \
   {                                                                                            \
-    const uint16_t* rb_ = rec_base + (row0 + (R)) * rec_row + 8 * (KS);                        \
+    const uint16_t* rb_ = rec_base + (row0 + (R)) * rec_row;                                   \
+    /* opaque here, so that nothing derived from the map is computed (and waited for) earlier */ \
+    i16x4 mp_ = (MP);                                                                          \
+    asm volatile("" : "+v"(mp_));                                                              \
     _Pragma("unroll") for (int kt = 0; kt < 4; ++kt) {                                         \
-      int e = MP[kt];                                                                          \
+      int e = mp_[kt];                                                                         \
       bool ok = e >= 0;                                                                        \
       if (DUPS && (LL) > 0) {                                                                  \
         e += (LL);                                                                             \
         ok = ok && e < a.topk && a.sorted[(row0 + (R)) * a.topk + min(e, a.topk - 1)] == kmap + 16 * kt; \
       }                                                                                        \
-      f[kt][KS] = bf16x8{};                                                                    \
-      if (ok)                                                                                  \
-        f[kt][KS] = *reinterpret_cast<const bf16x8*>(rb_ + (uint32_t)(e >> 5) * (uint32_t)kRecChunk + (uint32_t)(e & 31) * 16u); \
+      /* unselected keys read 16 zero bytes: every unit issues the same loads */               \
+      const uint16_t* src_ = ok ? rb_ + (rec_lane + 1024u * (KS) + (uint32_t)(e >> 5) * (uint32_t)kRecChunk + (uint32_t)(e & 31) * 16u) : zrow; \
+      f[kt][KS] = *reinterpret_cast<const bf16x8*>(src_);                                      \
     }                                                                                          \
   }
   {
     const int r0 = __builtin_amdgcn_readfirstlane((int)s_row[0]);
     KV_MAP_LOAD(mc, r0)
-    KV_B_LOAD(bs, r0)
-    KV_B_STORE(Bt0, bs)
+    KV_B_LOAD(bs, r0, 0, kBHalf)
+    KV_B_STORE(Bt0, bs, 0, kBHalf)
+    KV_B_LOAD(bs, r0, kBHalf, kBLoads)
+    KV_B_STORE(Bt0, bs, kBHalf, kBLoads)
     KV_REC_LOAD(r0, 0, mc, 0)
     KV_REC_LOAD(r0, 0, mc, 1)
   }
@@ -355,7 +374,10 @@ __device__ __forceinline__ void kv_dense_units(const DenseArgs& a, const KvCtx& 
     const int rn = __builtin_amdgcn_readfirstlane((int)s_row[min(ri2, nrows - 1)]);
     i16x4 mn;
     KV_MAP_LOAD(mn, rn)
-    KV_B_LOAD(bs, rn)
+    KV_B_LOAD(bs, rn, 0, kBHalf)
+    // fixed phase order (nothing is moved across these): the loads above, per head step its
+    // MFMAs, then its record loads for the next unit (and the B tile halves)
+    __builtin_amdgcn_sched_barrier(0);
     bf16x8 bq[NFT];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -368,19 +390,24 @@ __device__ __forceinline__ void kv_dense_units(const DenseArgs& a, const KvCtx& 
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) acc[kt][ft] = mfma_t<F16>(f[kt][ks], bq[ft], acc[kt][ft]);
       }
-      // issue order: (ks 0: the next unit's map and B tile loads), three fragments, then
-      // (fragment three tiles ahead, 4 MFMAs) per column tile
-      if (ks == 0) __builtin_amdgcn_sched_group_barrier(0x020, kBLoads + 4, 0);
+      // issue order: three fragments, then (fragment three tiles ahead, 4 MFMAs) per column tile
       __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
 #pragma unroll
       for (int ft = 0; ft < NFT; ++ft) {
         if (ft + 3 < NFT) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
       }
-      // this head step's fragments are consumed: request the next unit's
-      if (more) KV_REC_LOAD(rn, L2, mn, ks)
+      // this head step's fragments are consumed: request the next unit's; the next unit's B tile
+      // goes to LDS in two halves, the second loaded while the second head step runs
+      __builtin_amdgcn_sched_barrier(0);
+      KV_REC_LOAD(rn, L2, mn, ks)      /* past the last unit: the last row again, unused */
+      if (ks == 0) {
+        KV_B_STORE(BN, bs, 0, kBHalf)
+        KV_B_LOAD(bs, rn, kBHalf, kBLoads)
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    KV_B_STORE(BN, bs)
+    KV_B_STORE(BN, bs, kBHalf, kBLoads)
     lds_barrier();
     mc = mn;
     ri = ri2;

@@ -58,7 +58,8 @@ struct DenseArgs {
   int32_t* count;         // [rows]
   int32_t* maxdup;        // [rows]
   int32_t* offs;          // [rows, maxblk + 1]
-  int16_t* kpos;          // [rows, kstride] first sorted position of each key, -1: not selected
+  int16_t* kpos;          // [rows, kstride] first sorted position of each key, -1: not selected;
+                          // inside each 64-key group key 16 t + c is stored at 4 c + t
                           // (key-major path only; kstride = 0: not written)
   const uint16_t* dsp;    // [rows, hgc, rec_chunks, kRecChunk]
   const uint16_t* bt;     // [rows, hgc, 1088, 64] Q | QRope | dO with the 64 heads of a group innermost
