@@ -12,14 +12,16 @@
 // of 32 different rows.  A gathering wave that owns key octet q keeps one key per lane
 // (8 q + lane / 8) for all 9 groups, so each of its loads is one add to that key's row address.
 //
-// Reading: the swizzle keeps both readers free of LDS bank conflicts:
-//   - 16-byte reads of MFMA operand fragments, 16 lanes reading one chunk of 16 different keys:
-//     for keys of equal parity ktile_swz is a bijection onto the 8 slots;
-//   - transposing reads (ds_read_b64_tr_b16), 16 lanes reading two adjacent chunks (one 32-byte
-//     slot pair) of 4 consecutive keys 4 g .. 4 g + 3: keys of equal parity among 8 consecutive
-//     ones fall into four different slot pairs.
-// ktile_swz ignores key bit 4, so key k + 16 sits exactly 2 KB after key k: a contraction over
-// the tile's keys can read keys 4 g + j and 4 g + 16 + j as one MFMA fragment (any key order
+// Reading: LDS has 32 banks of 4 bytes; a 16-byte read is served 8 lanes per cycle, an 8-byte
+// read 16 lanes per cycle.  A key row of a chunk group is 128 bytes, so every key starts at bank
+// 0 and only the slot swizzle spreads them:
+//   - 16-byte reads of MFMA operand fragments (8 lanes: one chunk of 8 consecutive keys):
+//     ktile_swz is a bijection on each run of 8 keys;
+//   - transposing reads (ds_read_b64_tr_b16; 16 lanes: two adjacent chunks, i.e. one 32-byte
+//     slot pair, of 4 consecutive keys 4 g .. 4 g + 3): the slot-pair bits of ktile_swz are
+//     key bits 0-1, different for the 4 keys.
+// ktile_swz ignores key bits 3 and up, so key k + 16 sits exactly 2 KB after key k: a contraction
+// over the tile's keys can read keys 4 g + j and 4 g + 16 + j as one MFMA fragment (any key order
 // serves, as long as both operands use the same one).
 #pragma once
 #include <stdint.h>
@@ -30,8 +32,8 @@ constexpr int kTileKeys = 32;
 constexpr int kTileGroups = 9;                         // 8 value groups + 1 rope group
 constexpr int kTileBytes = kTileGroups * kTileKeys * 128;
 
-// slot swizzle of key k: slot bits 1, 2 <- key bits 1, 2; slot bit 0 <- key bit 3
-__device__ __forceinline__ int ktile_swz(int k) { return (k & 6) | ((k >> 3) & 1); }
+// slot swizzle of key k: slot bits 1, 2 <- key bits 0, 1; slot bit 0 <- key bit 2
+__device__ __forceinline__ int ktile_swz(int k) { return ((k & 3) << 1) | ((k >> 2) & 1); }
 
 // Element offset (16-bit units) of chunk ch of key k.
 __device__ __forceinline__ int ktile_off(int ch, int k) {
