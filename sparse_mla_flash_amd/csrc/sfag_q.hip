@@ -235,6 +235,31 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
     }                                                                                          \
   }
 
+// The same with the gather of chunk CH (sorted position SV) into key buffer KN issued one block
+// per column tile, so that the gather queues behind the MFMAs instead of ahead of them.
+#define SFAG_DQ_GATHER(KS, DST, KN, SV)                                                        \
+  {                                                                                            \
+    const uint32_t ko_ = (uint32_t)(SV) * (uint32_t)(kDn * 2) + gcol;                          \
+    const uint32_t ro_ = rope ? (uint32_t)(SV) * (uint32_t)(kDr * 2) + gcol : gcol;            \
+    const uint16_t* kq_ = (KS) + kqoff;                                                        \
+    const uint16_t* dq_ = (DST) + dsoff;                                                       \
+    bf16x8 dsa[4];                                                                             \
+    _Pragma("unroll") for (int t = 0; t < 4; ++t) dsa[t] = tr_frag(dq_ + 16 * t, 16 * kHtPitch); \
+    bf16x8 kb = tr_frag(kq_, 1024);                                                            \
+    _Pragma("unroll") for (int nt = 0; nt < 9; ++nt) {                                         \
+      __builtin_amdgcn_sched_barrier(0);                                                       \
+      {                                                                                        \
+        const char* src = nt < kBlocks / 4 - 1 ? kgat[nt] + ko_ : rgat + ro_;                  \
+        __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)((KN) + (4 * nt + rw) * 512), 16, 0, 0); \
+      }                                                                                        \
+      bf16x8 nb = kb;                                                                          \
+      if (nt < 8) nb = tr_frag(kq_ + 2048 * (nt + 1), 1024);                                   \
+      _Pragma("unroll") for (int t = 0; t < 4; ++t) dqacc[t][nt] = mfma_t<F16>(dsa[t], kb, dqacc[t][nt]); \
+      kb = nb;                                                                                 \
+    }                                                                                          \
+    __builtin_amdgcn_sched_barrier(0);                                                         \
+  }
+
 // P and dS of this score wave's head tile for both key tiles: the DSt tile of this chunk and the
 // chunk's records (positions past the valid count get p = dS = 0).  Lane (g, c) stores heads
 // 16 rw + 4 g .. + 3 of position 16 kt + c at ((rw * 32 + 16 kt + c) * 16 + 4 g) of each half.
@@ -385,30 +410,41 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
     const int32_t sv = srow[min(((CI) + 3) * kKC + gkey, count - 1)];                          \
     /* the position load must be issued before the gather for the wait count below */          \
     asm volatile("" ::: "memory");                                                             \
-    SFAG_GATHER_ASYNC(KN, (CI) + 2, gsv)                                                       \
-    if ((CI) >= 1) SFAG_DQ(KP, DP)                                                             \
+    SFAG_DQ_GATHER(KP, DP, KN, gsv)                                                            \
     asm volatile("" ::: "memory");                                                             \
     __builtin_amdgcn_s_waitcnt(kWaitVm9);                                                      \
     gsv = sv;                                                                                  \
     __builtin_amdgcn_s_barrier();                                                              \
     asm volatile("" ::: "memory");                                                             \
   }
-    int ci = 0;
-    for (; ci + 3 <= nchunk; ci += 4) {
-      SFAG_QSTEP(ci, Kb3, Kb2, Db1)
-      SFAG_QSTEP(ci + 1, Kb0, Kb3, Db0)
-      SFAG_QSTEP(ci + 2, Kb1, Kb0, Db1)
-      SFAG_QSTEP(ci + 3, Kb2, Kb1, Db0)
+    // step 0: no dQ yet (chunk 0 is being scored), only the position of chunk 3 and the gather
+    // of chunk 2
+    {
+      const int32_t sv = srow[min(3 * kKC + gkey, count - 1)];
+      asm volatile("" ::: "memory");
+      SFAG_GATHER_ASYNC(Kb2, 2, gsv)
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(kWaitVm9);
+      gsv = sv;
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
     }
-    if (ci <= nchunk) {
-      SFAG_QSTEP(ci, Kb3, Kb2, Db1)
-      ++ci;
+    int ci = 1;
+    for (; ci + 3 <= nchunk; ci += 4) {
+      SFAG_QSTEP(ci, Kb0, Kb3, Db0)
+      SFAG_QSTEP(ci + 1, Kb1, Kb0, Db1)
+      SFAG_QSTEP(ci + 2, Kb2, Kb1, Db0)
+      SFAG_QSTEP(ci + 3, Kb3, Kb2, Db1)
     }
     if (ci <= nchunk) {
       SFAG_QSTEP(ci, Kb0, Kb3, Db0)
       ++ci;
     }
-    if (ci <= nchunk) SFAG_QSTEP(ci, Kb1, Kb0, Db1)
+    if (ci <= nchunk) {
+      SFAG_QSTEP(ci, Kb1, Kb0, Db1)
+      ++ci;
+    }
+    if (ci <= nchunk) SFAG_QSTEP(ci, Kb2, Kb1, Db0)
 #undef SFAG_QSTEP
     __builtin_amdgcn_s_waitcnt(0);                        // no gather may still write LDS at exit
 
@@ -434,6 +470,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
 #undef SFAG_GATHER_ASYNC
 #undef SFAG_SCORES
 #undef SFAG_DQ
+#undef SFAG_DQ_GATHER
 #undef SFAG_FINISH
 }
 
