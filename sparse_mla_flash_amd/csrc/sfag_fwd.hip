@@ -296,52 +296,73 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
       __builtin_amdgcn_s_waitcnt(kWaitVm10);
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
-// Output step CI: the position of chunk CI + 3's slot, the gather of chunk CI + 2 into KN (and
-// its slot marks), then O += P V of chunk CI - 1 from KP / PP.  Ends by waiting for chunk
+// Output step CI (>= 1): the position of chunk CI + 3's slot, the slot marks of chunk CI + 2,
+// then O += P V of chunk CI - 1 from KP / PP with the gather of chunk CI + 2 into KN issued one
+// 1 KB load per column tile between the MFMAs (the loads queue on the vector memory path behind
+// the other waves'; ahead of the MFMAs they would hold them up).  Ends by waiting for chunk
 // CI + 1's gather and the position load, leaving this step's gather in flight.
 #define SFAG_OSTEP(CI, KP, KN, PP)                                                             \
   {                                                                                            \
     const int32_t sv = slot_pos(((CI) + 3) * kKC + gkey);                                      \
     asm volatile("" ::: "memory");                                                             \
     SFAG_MARK((CI) + 2, gsv)                                                                   \
-    SFAG_GATHER_ASYNC(KN, gather_pos(gsv))                                                     \
-    if ((CI) >= 1) {                                                                           \
-      const uint16_t* pq_ = (PP) + psoff;                                                      \
-      bf16x8 pa[4];                                                                            \
-      _Pragma("unroll") for (int t = 0; t < 4; ++t) pa[t] = tr_frag(pq_ + 16 * t, 16 * kHtPitch); \
-      /* the lane offset is made opaque per step so that its per-buffer sums are not hoisted */ \
-      int kq_ = kq0;                                                                           \
-      asm volatile("" : "+v"(kq_));                                                            \
-      bf16x8 kb = tr_frag((KP) + kq_, 1024);                                                   \
-      _Pragma("unroll") for (int nt = 0; nt < 8; ++nt) {                                       \
-        bf16x8 nb = kb;                                                                        \
-        if (nt < 7) nb = tr_frag((KP) + (kq_ ^ (16 * ((nt + 1) & 3))) + 2048 * ((nt + 1) >> 2), 1024); \
-        _Pragma("unroll") for (int t = 0; t < 4; ++t) oacc[t][nt] = mfma_t<F16>(pa[t], kb, oacc[t][nt]); \
-        kb = nb;                                                                               \
+    const int32_t gp_ = gather_pos(gsv);                                                       \
+    const uint32_t ko_ = (uint32_t)gp_ * (uint32_t)(kDn * 2) + gcol;                           \
+    const uint32_t ro_ = (uint32_t)gp_ * (uint32_t)((rope ? kDr : kDn) * 2) + gcol;            \
+    const uint16_t* pq_ = (PP) + psoff;                                                        \
+    bf16x8 pa[4];                                                                              \
+    _Pragma("unroll") for (int t = 0; t < 4; ++t) pa[t] = tr_frag(pq_ + 16 * t, 16 * kHtPitch); \
+    /* the lane offset is made opaque per step so that its per-buffer sums are not hoisted */   \
+    int kq_ = kq0;                                                                             \
+    asm volatile("" : "+v"(kq_));                                                              \
+    bf16x8 kb = tr_frag((KP) + kq_, 1024);                                                     \
+    _Pragma("unroll") for (int nt = 0; nt < 8; ++nt) {                                         \
+      __builtin_amdgcn_sched_barrier(0);                                                       \
+      _Pragma("unroll") for (int j = nt; j < (nt == 7 ? 9 : nt + 1); ++j) {                   \
+        const char* src = j < kBlocks / 4 - 1 ? kgat[j] + ko_ : rgat + ro_;                    \
+        __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)((KN) + (4 * j + rw) * 512), 16, 0, 0); \
       }                                                                                        \
+      bf16x8 nb = kb;                                                                          \
+      if (nt < 7) nb = tr_frag((KP) + (kq_ ^ (16 * ((nt + 1) & 3))) + 2048 * ((nt + 1) >> 2), 1024); \
+      _Pragma("unroll") for (int t = 0; t < 4; ++t) oacc[t][nt] = mfma_t<F16>(pa[t], kb, oacc[t][nt]); \
+      kb = nb;                                                                                 \
     }                                                                                          \
+    __builtin_amdgcn_sched_barrier(0);                                                         \
     asm volatile("" ::: "memory");                                                             \
     __builtin_amdgcn_s_waitcnt(kWaitVm9);                                                      \
     gsv = sv;                                                                                  \
     __builtin_amdgcn_s_barrier();                                                              \
     asm volatile("" ::: "memory");                                                             \
   }
-      int ci = 0;
-      for (; ci + 3 <= nchunk; ci += 4) {
-        SFAG_OSTEP(ci, Kb3, Kb2, Pb1)
-        SFAG_OSTEP(ci + 1, Kb0, Kb3, Pb0)
-        SFAG_OSTEP(ci + 2, Kb1, Kb0, Pb1)
-        SFAG_OSTEP(ci + 3, Kb2, Kb1, Pb0)
+      // step 0: no P V yet (chunk 0 is being scored), only the position of chunk 3's slot and
+      // the gather of chunk 2
+      {
+        const int32_t sv = slot_pos(3 * kKC + gkey);
+        asm volatile("" ::: "memory");
+        SFAG_MARK(2, gsv)
+        SFAG_GATHER_ASYNC(Kb2, gather_pos(gsv))
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(kWaitVm9);
+        gsv = sv;
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
       }
-      if (ci <= nchunk) {
-        SFAG_OSTEP(ci, Kb3, Kb2, Pb1)
-        ++ci;
+      int ci = 1;
+      for (; ci + 3 <= nchunk; ci += 4) {
+        SFAG_OSTEP(ci, Kb0, Kb3, Pb0)
+        SFAG_OSTEP(ci + 1, Kb1, Kb0, Pb1)
+        SFAG_OSTEP(ci + 2, Kb2, Kb1, Pb0)
+        SFAG_OSTEP(ci + 3, Kb3, Kb2, Pb1)
       }
       if (ci <= nchunk) {
         SFAG_OSTEP(ci, Kb0, Kb3, Pb0)
         ++ci;
       }
-      if (ci <= nchunk) SFAG_OSTEP(ci, Kb1, Kb0, Pb1)
+      if (ci <= nchunk) {
+        SFAG_OSTEP(ci, Kb1, Kb0, Pb1)
+        ++ci;
+      }
+      if (ci <= nchunk) SFAG_OSTEP(ci, Kb2, Kb1, Pb0)
 #undef SFAG_OSTEP
       __builtin_amdgcn_s_waitcnt(0);                    // no gather may still write LDS
       lds_barrier();                                    // the score waves' verdict in s_over
