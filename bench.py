@@ -353,6 +353,8 @@ def _ceilings_lib():
     L.ceil_lds.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp]
     L.ceil_atomic.restype = ctypes.c_float
     L.ceil_atomic.argtypes = [vp, vp, ctypes.c_int, ctypes.c_int, vp]
+    L.ceil_gather.restype = ctypes.c_float
+    L.ceil_gather.argtypes = [ctypes.c_int, vp, vp, vp, ctypes.c_int, ctypes.c_int, vp, vp]
     return L
 
 
@@ -433,6 +435,24 @@ def ceilings():
         ops = 65536 * 1088 * 4
         res["atomic_add_f32_" + label] = {"g_ops_per_s": round(ops / (t * 1e-3) / 1e9, 1), "ms": round(t, 3)}
         del acc, rows
+    # direct-to-LDS gather of 32 random key rows (1152 B each) per chunk, 2048 workgroups x 128
+    # chunks, two lane mappings: 32 B of 32 keys per 1 KB load, or whole 128-byte runs of 8 keys
+    nkeys, gblocks, nch = 8192, 2048, 128
+    kv = torch.ones(nkeys * 1024, dtype=torch.uint8, device="cuda")
+    kr = torch.ones(nkeys * 128, dtype=torch.uint8, device="cuda")
+    gi = torch.randint(0, nkeys, (gblocks * nch, 32), generator=g, dtype=torch.int32).sort(dim=1).values
+    gi = gi.contiguous().cuda()
+    gather = {}
+    for mode, label in ((0, "32_keys_x_32B_per_load"), (1, "8_keys_x_128B_per_load")):
+        t = min(L.ceil_gather(mode, kv.data_ptr(), kr.data_ptr(), gi.data_ptr(), gblocks, nch, out.data_ptr(), stream)
+                for _ in range(5))
+        torch.cuda.synchronize()
+        nbytes = gblocks * nch * 36 * 1024
+        gather[label] = {"gb_per_s": round(nbytes / (t * 1e-3) / 1e9, 1),
+                         "bytes_per_clk_per_cu": None if sclk is None else
+                         round(nbytes / (t * 1e-3) / (sclk * 1e6) / cus, 1), "ms": round(t, 4)}
+    res["key_row_gather"] = gather
+    del kv, kr, gi
     print(json.dumps(res), flush=True)
 
 

@@ -1,6 +1,7 @@
 // ceilings.hip -- measured MI355X (gfx950) ceilings for the roofline figures of the
 // SparseFlashAttentionGrad kernels: bf16 MFMA rate and the shader clock under MFMA load, HBM
-// copy bandwidth, LDS instruction rates and the fp32 global atomic-add rate.  Not part of the
+// copy bandwidth, LDS instruction rates, the fp32 global atomic-add rate and the rate of the
+// direct-to-LDS key-row gather in two lane mappings.  Not part of the
 // library's C ABI; bench.py --ceilings loads it and prints the results.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -111,6 +112,62 @@ __global__ void __launch_bounds__(256) atomic_rate_kernel(float* acc, const int3
     for (int e = threadIdx.x; e < 1088; e += 256) atomicAdd(&r[e], 1.0f);
 }
 
+// Direct-to-LDS gather of 32 key rows (a 1024-byte value row and a 128-byte rope row each) per
+// chunk: the query-major kernels' key-tile fill.  Waves 4-7 of a 512-thread workgroup issue the
+// 36 loads of 1 KB per chunk (9 each) into one of 4 LDS buffers, two chunks in flight; waves 0-3
+// only pass the barriers.  mode 0: each load covers 32 bytes of 32 different keys (lane l: key
+// l % 32, 16-byte piece 2 b + l / 32 of block b); mode 1: each load covers the whole 128-byte
+// runs of 8 keys (lane l: key 8 q + l / 8, piece l % 8 of run g for load (g, q)).  idx holds nch
+// chunks of 32 key numbers per workgroup, each below nkeys.
+constexpr int kGatherChunkBytes = 36 * 1024;
+__global__ void __launch_bounds__(512, 1) gather_rate_kernel(int mode, const char* kv, const char* kr,
+                                                             const int32_t* idx, int nch, float* out) {
+  __shared__ __attribute__((aligned(16))) char b0[kGatherChunkBytes], b1[kGatherChunkBytes],
+      b2[kGatherChunkBytes], b3[kGatherChunkBytes];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int32_t* wg = idx + (size_t)blockIdx.x * nch * 32;
+  const bool gw = wave >= 4;
+  const int q = wave - 4;
+  auto issue = [&](int ch) {
+    if (!gw || ch >= nch) return;
+    const int32_t* keys = wg + ch * 32;
+    char* dst = (ch & 3) == 0 ? b0 : (ch & 3) == 1 ? b1 : (ch & 3) == 2 ? b2 : b3;
+#pragma unroll
+    for (int j = 0; j < 9; ++j) {
+      const int i = q + 4 * j;                 // load index 0 .. 35 (32 .. 35: rope)
+      int key, off;
+      bool rope;
+      if (mode == 0) {
+        key = lane & 31;
+        const int piece = 2 * i + (lane >> 5);
+        rope = piece >= 64;
+        off = (rope ? piece - 64 : piece) * 16;
+      } else {
+        rope = i >= 32;
+        key = 8 * (i & 3) + (lane >> 3);
+        off = ((rope ? 0 : (i >> 2) * 8) + (lane & 7)) * 16;
+      }
+      const int k = keys[key];
+      const char* src = rope ? kr + (size_t)k * 128 + off : kv + (size_t)k * 1024 + off;
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(dst + i * 1024), 16, 0, 0);
+    }
+  };
+  issue(0);
+  issue(1);
+  float acc = 0.f;
+  for (int ch = 0; ch < nch; ++ch) {
+    issue(ch + 2);
+    // this wave's loads of chunk ch done: chunks ch + 1 and ch + 2 (18 loads) may remain
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((18 & 15) | ((18 >> 4) << 14) | (0x7 << 4));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    const char* rb = (ch & 3) == 0 ? b0 : (ch & 3) == 1 ? b1 : (ch & 3) == 2 ? b2 : b3;
+    acc += (float)rb[threadIdx.x * 16];
+  }
+  if (acc == 12345.f) out[blockIdx.x] = acc;
+}
+
 extern "C" {
 
 int ceil_device_info(char* name, int name_len, int* cus, int* clock_khz, int* mem_clock_khz) {
@@ -190,6 +247,17 @@ static void atom_launch(hipStream_t s, void* c) {
 float ceil_atomic(float* acc, const int32_t* rows, int n, int reps, void* stream) {
   AtomCtx c{acc, rows, n, reps};
   return timed((hipStream_t)stream, atom_launch, &c);
+}
+
+struct GatherCtx { int mode; const char* kv; const char* kr; const int32_t* idx; int blocks, nch; float* out; };
+static void gather_launch(hipStream_t s, void* c) {
+  GatherCtx* x = (GatherCtx*)c;
+  hipLaunchKernelGGL(gather_rate_kernel, dim3(x->blocks), dim3(512), 0, s, x->mode, x->kv, x->kr, x->idx, x->nch, x->out);
+}
+float ceil_gather(int mode, const void* kv, const void* kr, const int32_t* idx, int blocks, int nch, float* out,
+                  void* stream) {
+  GatherCtx c{mode, (const char*)kv, (const char*)kr, idx, blocks, nch, out};
+  return timed((hipStream_t)stream, gather_launch, &c);
 }
 
 }  // extern "C"
