@@ -32,4 +32,17 @@ __device__ __forceinline__ float row16_sum(float x) {
   return x + dpp_f<kDppMirror>(x);
 }
 
+// Sum over the four 16-lane rows at the same position (lanes l, l ^ 16, l ^ 32, l ^ 48), by the
+// row swaps of v_permlane16_swap (odd rows of one operand with even rows of the other) and
+// v_permlane32_swap (upper half with lower half), both VALU: with both operands x, the two
+// results of a swap hold the two rows of each pair, and their sum is the pair's sum in every lane.
+__device__ __forceinline__ float col4_sum(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const uint32_t v = __float_as_uint(y);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 }  // namespace sfag

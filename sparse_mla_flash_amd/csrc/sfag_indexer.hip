@@ -29,6 +29,7 @@
 //                    in row order (one workgroup); deterministic.
 #include "sfag_device.h"
 #include "sfag_dpp.h"
+#include "sfag_ktile.h"
 #include "sfag_launch.h"
 
 namespace sfag {
@@ -53,7 +54,8 @@ __device__ __forceinline__ float wsum16(float v) {  // sum over the 16 lanes c o
 template <bool F16>
 __global__ void __launch_bounds__(kIxThreads, 1) ix_query_kernel(IxArgs a) {
   // three chunk buffers (separate arrays, so that the compiler can tell a direct-to-LDS load
-  // into one from reads of the others): main key rows and index key rows, chunk-major
+  // into one from reads of the others): main key rows (9 chunk groups) and index key rows (2
+  // chunk groups), both in the swizzled [chunk group][key][slot] layout of sfag_ktile.h
   __shared__ __attribute__((aligned(16))) uint16_t Kt0[kIxKC * kDk], Kt1[kIxKC * kDk], Kt2[kIxKC * kDk];
   __shared__ __attribute__((aligned(16))) uint16_t Ki0[kIxKC * kIxDi], Ki1[kIxKC * kIxDi], Ki2[kIxKC * kIxDi];
   __shared__ __attribute__((aligned(16))) uint16_t Dt[4][2][16 * kDsPitch];   // per index wave: dS', T
@@ -109,11 +111,13 @@ __global__ void __launch_bounds__(kIxThreads, 1) ix_query_kernel(IxArgs a) {
   const float max_i = a.smax_i[row], lsum_i = __logf(a.ssum_i[row]);
 
   // Gathers: the keys of a chunk are consecutive rows, clamped to the last admitted key (the
-  // clamped copies are masked).  A direct-to-LDS block (64 lanes x 16 bytes) is chunk columns
-  // 2 b, 2 b + 1 of all 32 keys: lane l takes key l % 32.  Main waves load the 36 blocks of the
-  // main rows (value columns 0..63, rope 64..71; a rope-less call reads value columns instead,
-  // whose Q is zero), 9 each; index waves the 8 blocks of the index rows, 2 each.
-  const int gkey = lane & 31, gcol = lane >> 5;
+  // clamped copies are masked).  A direct-to-LDS block (64 lanes x 16 bytes) is one 128-byte run
+  // (chunk group) of 8 keys: main wave w loads keys 8 w .. 8 w + 7 of the 9 groups of the main
+  // rows (value groups 0..7, rope group 8; a rope-less call reads value columns instead, whose Q
+  // is zero); index wave 4 + w the same keys of the 2 groups of the index rows.
+  const int gkey = ktile_gather_key(wave & 3, lane);
+  const uint32_t gcol = ktile_gather_col(wave & 3, lane);
+  const int kse = ktile_off(g, c);               // fragment reads: chunk g of key c
   const bool has_rope = a.kr != nullptr;
   const char* kb8 = reinterpret_cast<const char*>(a.k + geo.kstart * kDn);
   const char* kr8 = has_rope ? reinterpret_cast<const char*>(a.kr + geo.kstart * kDr) : kb8;
@@ -123,23 +127,23 @@ __global__ void __launch_bounds__(kIxThreads, 1) ix_query_kernel(IxArgs a) {
   {                                                                                            \
     const uint32_t key_ = (uint32_t)min((CH) * kIxKC + gkey, nkeys - 1);                       \
     _Pragma("unroll") for (int j = 0; j < 9; ++j) {                                            \
-      const int b_ = wave + 4 * j;                   /* blocks 0..31: value, 32..35: rope */   \
-      const int col_ = 2 * b_ + gcol;                                                          \
-      const char* src_ = b_ < 32 ? kb8 + key_ * (uint32_t)(kDn * 2) + col_ * 16                \
-                                 : (has_rope ? kr8 + key_ * (uint32_t)(kDr * 2) + (col_ - 64) * 16 \
-                                             : kb8 + key_ * (uint32_t)(kDn * 2) + (col_ - 64) * 16); \
-      __builtin_amdgcn_global_load_lds(src_, (LdsVoid*)((KT) + b_ * 512), 16, 0, 0);          \
+      const char* src_ = j < 8 ? kb8 + key_ * (uint32_t)(kDn * 2) + j * 128 + gcol             \
+                               : (has_rope ? kr8 + key_ * (uint32_t)(kDr * 2) + gcol           \
+                                           : kb8 + key_ * (uint32_t)(kDn * 2) + gcol);          \
+      __builtin_amdgcn_global_load_lds(src_, (LdsVoid*)((KT) + (4 * j + wave) * 512), 16, 0, 0); \
     }                                                                                          \
   }
 #define IX_GATHER_INDEX(KI, CH)                                                                 \
   {                                                                                            \
     const uint32_t key_ = (uint32_t)min((CH) * kIxKC + gkey, nkeys - 1);                       \
-    _Pragma("unroll") for (int j = 0; j < 2; ++j) {                                            \
-      const int b_ = (wave - 4) + 4 * j;              /* blocks 0..7 */                        \
-      __builtin_amdgcn_global_load_lds(ki8 + key_ * (uint32_t)(kIxDi * 2) + (2 * b_ + gcol) * 16, \
-                                       (LdsVoid*)((KI) + b_ * 512), 16, 0, 0);                 \
-    }                                                                                          \
+    _Pragma("unroll") for (int j = 0; j < 2; ++j)                                              \
+      __builtin_amdgcn_global_load_lds(ki8 + key_ * (uint32_t)(kIxDi * 2) + j * 128 + gcol,    \
+                                       (LdsVoid*)((KI) + (4 * j + (wave - 4)) * 512), 16, 0, 0); \
   }
+  // fragment read of step ks (chunk 4 ks + g) of key tile kt (keys 16 kt + c): chunk group ks / 2,
+  // slot bit 2 = ks % 2, key 16 + c 1024 elements after key c
+#define IX_KFRAG(KC, KS, KT) \
+  (*reinterpret_cast<const bf16x8*>((KC) + (((KS) & 1) ? (kse ^ 32) : kse) + ((KS) >> 1) * 2048 + (KT) * 1024))
   // s_waitcnt operands with expcnt and lgkmcnt at zero: vmcnt(9) / vmcnt(2): all but the newest
   // gather of a main / an index wave
   constexpr int kWaitMain = 0x0009, kWaitIndex = 0x0002;
@@ -185,9 +189,7 @@ __global__ void __launch_bounds__(kIxThreads, 1) ix_query_kernel(IxArgs a) {
         f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};                \
         _Pragma("unroll") for (int ks = 0; ks < 18; ++ks)                                      \
           _Pragma("unroll") for (int kt = 0; kt < 2; ++kt)                                     \
-            sacc[kt] = mfma_t<F16>(qA[u][ks],                                                  \
-                                   *reinterpret_cast<const bf16x8*>((KC) + ((4 * ks + g) * kIxKC + 16 * kt + c) * 8), \
-                                   sacc[kt]);                                                  \
+            sacc[kt] = mfma_t<F16>(qA[u][ks], IX_KFRAG(KC, ks, kt), sacc[kt]);                 \
         const f32x4 mv = *reinterpret_cast<const f32x4*>(sM + 16 * t + 4 * g);                 \
         const f32x4 iv = *reinterpret_cast<const f32x4*>(sIL + 16 * t + 4 * g);                \
         _Pragma("unroll") for (int kt = 0; kt < 2; ++kt)                                       \
@@ -195,9 +197,7 @@ __global__ void __launch_bounds__(kIxThreads, 1) ix_query_kernel(IxArgs a) {
             ps[kt] += __builtin_amdgcn_exp2f(sacc[kt][v] * zscale - mv[v]) * iv[v];            \
       }                                                                                        \
       _Pragma("unroll") for (int kt = 0; kt < 2; ++kt) {                                       \
-        float p_ = ps[kt];                                                                     \
-        p_ += __shfl_xor(p_, 16);                                                              \
-        p_ += __shfl_xor(p_, 32);                                                              \
+        const float p_ = col4_sum(ps[kt]);                                                     \
         if (g == 0) sP[wave][16 * kt + c] = (CI) * kIxKC + 16 * kt + c < nkeys ? p_ : 0.f;     \
       }                                                                                        \
     }                                                                                          \
@@ -241,6 +241,13 @@ __global__ void __launch_bounds__(kIxThreads, 1) ix_query_kernel(IxArgs a) {
       wv[v] = (hasi && hh < G) ? x2f<F16>(a.w[row * G + hh]) : 0.f;
     }
   }
+  // dq~ contraction over the chunk's keys in the order 4 g + j, 4 g + 16 + j (j = 0..3) for lane
+  // group g, in both operands: the dS' / T tiles hold key 16 kt + c at 8 (c / 4) + c % 4 + 4 kt;
+  // the transposing reads of the index key tile point lane (g, c) at key 4 g + c / 4 and dims
+  // 16 nt + 4 (c % 4) (chunk group nt / 4, slot (2 (nt % 4) + (c % 4) / 2) ^ swz), keys + 16 at
+  // 1024 elements on
+  const int tk = 4 * g + (c >> 2);
+  const int kq0 = tk * 64 + 4 * (c & 1) + ((((c & 3) >> 1) ^ ktile_swz(tk)) << 3);
   // accumulators: dq~ (main term and correction term), dW terms, loss terms
   f32x4 qacc[8], tacc[8];
 #pragma unroll
@@ -271,7 +278,7 @@ __global__ void __launch_bounds__(kIxThreads, 1) ix_query_kernel(IxArgs a) {
       const bf16x8 da = *reinterpret_cast<const bf16x8*>(&Dt[it][0][c * kDsPitch + 8 * g]);    \
       const bf16x8 ta = *reinterpret_cast<const bf16x8*>(&Dt[it][1][c * kDsPitch + 8 * g]);    \
       _Pragma("unroll") for (int nt = 0; nt < 8; ++nt) {                                       \
-        const bf16x8 kb_ = lds_frag_tr_cm((KP), 16 * nt, lane);                                \
+        const bf16x8 kb_ = tr_frag((KP) + ((kq0 ^ (16 * (nt & 3))) + 2048 * (nt >> 2)), 1024);   \
         qacc[nt] = mfma_t<F16>(da, kb_, qacc[nt]);                                             \
         tacc[nt] = mfma_t<F16>(ta, kb_, tacc[nt]);                                             \
       }                                                                                        \
@@ -280,14 +287,11 @@ __global__ void __launch_bounds__(kIxThreads, 1) ix_query_kernel(IxArgs a) {
     if (hasi && (CI) < nchunk) {                                                               \
       _Pragma("unroll") for (int ks = 0; ks < 4; ++ks)                                         \
         _Pragma("unroll") for (int kt = 0; kt < 2; ++kt)                                       \
-          iacc[kt] = mfma_t<F16>(qiA[ks],                                                      \
-                                 *reinterpret_cast<const bf16x8*>((KC) + ((4 * ks + g) * kIxKC + 16 * kt + c) * 8), \
-                                 iacc[kt]);                                                    \
+          iacc[kt] = mfma_t<F16>(qiA[ks], IX_KFRAG(KC, ks, kt), iacc[kt]);                     \
       _Pragma("unroll") for (int kt = 0; kt < 2; ++kt) {                                       \
         float is = 0.f;                                                                        \
         _Pragma("unroll") for (int v = 0; v < 4; ++v) is += wv[v] * fmaxf(iacc[kt][v], 0.f);   \
-        is += __shfl_xor(is, 16);                                                              \
-        is += __shfl_xor(is, 32);                                                              \
+        is = col4_sum(is);                                                                     \
         if (g == 0) sI[it][16 * kt + c] = is;                                                  \
       }                                                                                        \
     }                                                                                          \
@@ -297,6 +301,7 @@ __global__ void __launch_bounds__(kIxThreads, 1) ix_query_kernel(IxArgs a) {
       const int s0 = (CI) * kIxKC;                                                             \
       _Pragma("unroll") for (int kt = 0; kt < 2; ++kt) {                                       \
         const int key = 16 * kt + c;                                                           \
+        const int kpos = 8 * (c >> 2) + (c & 3) + 4 * kt;   /* key's place in the dq~ key order */ \
         const bool valid = s0 + key < nkeys;                                                   \
         const float tot = valid ? sP[0][key] + sP[1][key] + sP[2][key] + sP[3][key] : 0.f;     \
         float ival = 0.f;                                                                      \
@@ -309,8 +314,8 @@ __global__ void __launch_bounds__(kIxThreads, 1) ix_query_kernel(IxArgs a) {
           const float relu = fmaxf(sv_, 0.f);                                                  \
           aw[v] += dip * relu;                                                                 \
           bw[v] += tot * relu;                                                                 \
-          Dt[it][0][(4 * g + v) * kDsPitch + key] = f2x<F16>(sv_ > 0.f ? dip : 0.f);            \
-          Dt[it][1][(4 * g + v) * kDsPitch + key] = f2x<F16>(sv_ > 0.f ? tot : 0.f);            \
+          Dt[it][0][(4 * g + v) * kDsPitch + kpos] = f2x<F16>(sv_ > 0.f ? dip : 0.f);           \
+          Dt[it][1][(4 * g + v) * kDsPitch + kpos] = f2x<F16>(sv_ > 0.f ? tot : 0.f);           \
         }                                                                                      \
         if (it == 0 && g == 0 && valid) {                                                      \
           if (tot > 0.f) l1 += tot * (__logf(tot) - lsm);                                      \
@@ -342,6 +347,7 @@ __global__ void __launch_bounds__(kIxThreads, 1) ix_query_kernel(IxArgs a) {
 #undef IX_ISTEP
 #undef IX_GATHER_MAIN
 #undef IX_GATHER_INDEX
+#undef IX_KFRAG
   __builtin_amdgcn_s_waitcnt(0);                  // no gather may still write LDS at exit
 
   // ---- row results ----
