@@ -114,7 +114,9 @@ __global__ void __launch_bounds__(kIxThreads, 1) ix_query_kernel(IxArgs a) {
   // clamped copies are masked).  A direct-to-LDS block (64 lanes x 16 bytes) is one 128-byte run
   // (chunk group) of 8 keys: main wave w loads keys 8 w .. 8 w + 7 of the 9 groups of the main
   // rows (value groups 0..7, rope group 8; a rope-less call reads value columns instead, whose Q
-  // is zero); index wave 4 + w the same keys of the 2 groups of the index rows.
+  // is zero) and of the 2 groups of the index rows.  The index waves issue no direct-to-LDS
+  // loads: while one is in flight the compiler makes a wave's ordinary LDS accesses wait for all
+  // its loads, and the index waves read and write LDS through ordinary accesses every step.
   const int gkey = ktile_gather_key(wave & 3, lane);
   const uint32_t gcol = ktile_gather_col(wave & 3, lane);
   const int kse = ktile_off(g, c);               // fragment reads: chunk g of key c
@@ -138,15 +140,15 @@ __global__ void __launch_bounds__(kIxThreads, 1) ix_query_kernel(IxArgs a) {
     const uint32_t key_ = (uint32_t)min((CH) * kIxKC + gkey, nkeys - 1);                       \
     _Pragma("unroll") for (int j = 0; j < 2; ++j)                                              \
       __builtin_amdgcn_global_load_lds(ki8 + key_ * (uint32_t)(kIxDi * 2) + j * 128 + gcol,    \
-                                       (LdsVoid*)((KI) + (4 * j + (wave - 4)) * 512), 16, 0, 0); \
+                                       (LdsVoid*)((KI) + (4 * j + wave) * 512), 16, 0, 0);     \
   }
   // fragment read of step ks (chunk 4 ks + g) of key tile kt (keys 16 kt + c): chunk group ks / 2,
   // slot bit 2 = ks % 2, key 16 + c 1024 elements after key c
 #define IX_KFRAG(KC, KS, KT) \
   (*reinterpret_cast<const bf16x8*>((KC) + (((KS) & 1) ? (kse ^ 32) : kse) + ((KS) >> 1) * 2048 + (KT) * 1024))
-  // s_waitcnt operands with expcnt and lgkmcnt at zero: vmcnt(9) / vmcnt(2): all but the newest
-  // gather of a main / an index wave
-  constexpr int kWaitMain = 0x0009, kWaitIndex = 0x0002;
+  // s_waitcnt operand with expcnt and lgkmcnt at zero: vmcnt(11): all but a main wave's newest
+  // gather (9 main-row and 2 index-row loads)
+  constexpr int kWaitMain = 0x000b;
 
   // Two roles with separate loops (their registers are never live together) and the same
   // barriers: one before step 0, two per step.  Step c: main waves form the scores of chunk c;
@@ -174,12 +176,14 @@ __global__ void __launch_bounds__(kIxThreads, 1) ix_query_kernel(IxArgs a) {
                         : bf16x8{};
     }
     IX_GATHER_MAIN(Kt0, 0)
+    IX_GATHER_INDEX(Ki0, 0)
     IX_GATHER_MAIN(Kt1, 1)
+    IX_GATHER_INDEX(Ki1, 1)
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(kWaitMain);
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-#define IX_MSTEP(CI, KC, KN)                                                                   \
+#define IX_MSTEP(CI, KC, KN, KIN)                                                              \
   {                                                                                            \
     if ((CI) < nchunk) {                                                                       \
       float ps[2] = {0.f, 0.f};                                                                \
@@ -203,6 +207,7 @@ __global__ void __launch_bounds__(kIxThreads, 1) ix_query_kernel(IxArgs a) {
     }                                                                                          \
     lds_barrier();                                                                             \
     IX_GATHER_MAIN(KN, min((CI) + 2, nchunk - 1))                                              \
+    IX_GATHER_INDEX(KIN, min((CI) + 2, nchunk - 1))                                            \
     asm volatile("" ::: "memory");                                                             \
     __builtin_amdgcn_s_waitcnt(kWaitMain);                                                     \
     __builtin_amdgcn_s_barrier();                                                              \
@@ -210,15 +215,15 @@ __global__ void __launch_bounds__(kIxThreads, 1) ix_query_kernel(IxArgs a) {
   }
     int ci = 0;
     for (; ci + 3 <= nchunk + 1; ci += 3) {
-      IX_MSTEP(ci, Kt0, Kt2)
-      IX_MSTEP(ci + 1, Kt1, Kt0)
-      IX_MSTEP(ci + 2, Kt2, Kt1)
+      IX_MSTEP(ci, Kt0, Kt2, Ki2)
+      IX_MSTEP(ci + 1, Kt1, Kt0, Ki0)
+      IX_MSTEP(ci + 2, Kt2, Kt1, Ki1)
     }
     if (ci <= nchunk) {
-      IX_MSTEP(ci, Kt0, Kt2)
+      IX_MSTEP(ci, Kt0, Kt2, Ki2)
       ++ci;
     }
-    if (ci <= nchunk) IX_MSTEP(ci, Kt1, Kt0)
+    if (ci <= nchunk) IX_MSTEP(ci, Kt1, Kt0, Ki0)
 #undef IX_MSTEP
     __builtin_amdgcn_s_waitcnt(0);                // no gather may still write LDS at exit
     __syncthreads();                              // the index waves' row results
@@ -259,10 +264,8 @@ __global__ void __launch_bounds__(kIxThreads, 1) ix_query_kernel(IxArgs a) {
   float tot_prev[2] = {0.f, 0.f};
   int key_prev = -1;
 
-  IX_GATHER_INDEX(Ki0, 0)
-  IX_GATHER_INDEX(Ki1, 1)
+  // chunks 0 and 1 are gathered by the main waves
   asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(kWaitIndex);
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 #define IX_ISTEP(CI, KC, KP)                                                                   \
@@ -325,9 +328,8 @@ __global__ void __launch_bounds__(kIxThreads, 1) ix_query_kernel(IxArgs a) {
       }                                                                                        \
       key_prev = s0;                                                                           \
     }                                                                                          \
-    IX_GATHER_INDEX(KP, min((CI) + 2, nchunk - 1))                                             \
+    /* chunk CI + 2 goes into KP, gathered by the main waves */                                 \
     asm volatile("" ::: "memory");                                                             \
-    __builtin_amdgcn_s_waitcnt(kWaitIndex);                                                    \
     __builtin_amdgcn_s_barrier();                                                              \
     asm volatile("" ::: "memory");                                                             \
   }
