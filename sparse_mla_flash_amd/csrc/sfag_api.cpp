@@ -122,7 +122,7 @@ sfag_status make_plan(const sfag_dims* dims, const int32_t* sq, const int32_t* s
   if (dims->B < 1 || dims->B > 256) return fail(SFAG_ERR_PARAM_INVALID, "B must be in 1..256 (got %lld)", (long long)dims->B);
   if (dims->topk < 1 || dims->topk > kMaxTopk)
     return fail(SFAG_ERR_PARAM_INVALID, "topk must be in 1..%lld (got %lld)", (long long)kMaxTopk, (long long)dims->topk);
-  if (block >= 1 && dims->topk * block > kMaxTopk)
+  if (block >= 1 && block > kMaxTopk / dims->topk)     // topk * block > kMaxTopk, without overflow
     return fail(SFAG_ERR_PARAM_INVALID, "topk * sparseBlockSize must be at most %lld (got %lld * %lld)",
                 (long long)kMaxTopk, (long long)dims->topk, (long long)block);
   if (mode != 0 && mode != 3)
