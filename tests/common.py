@@ -125,6 +125,7 @@ def compare(name, got: np.ndarray, ref: np.ndarray, max_abs=MAX_ABS, rel_l2=REL_
            f"rel-L2 {rel:.3e} (bound {rel_l2})")
     assert np.isfinite(got).all(), f"{name}: non-finite values"
     assert excess <= 0.0 and rel <= rel_l2, msg
+    print(f"# compare {name}: max abs {ma:.3e}, rel-L2 {rel:.3e}, max|ref| {peak:.3f}")
     return ma, rel
 
 
