@@ -62,6 +62,7 @@ struct Plan {
   // workspace layout
   uint64_t off_acc = 0, off_loc = 0, off_kcnt = 0, off_koff = 0, off_btotal = 0, off_bbase = 0;
   uint64_t off_sorted = 0, off_count = 0, off_maxdup = 0, off_offs = 0, off_dsp = 0, off_part = 0, off_flag = 0;
+  uint64_t off_xpart = 0;          // key-major: partial sums of the split tail positions
   uint64_t off_zero = 0, off_ilist = 0, off_imap = 0, off_kpos = 0, off_bt = 0;
   uint64_t bytes = 0;
   int64_t chunk_rows = 0;          // per-pair path: query rows per chunk
@@ -246,6 +247,9 @@ sfag_status make_plan(const sfag_dims* dims, const int32_t* sq, const int32_t* s
     off = align_up(off + (uint64_t)p->rows * rec_row);
     p->off_part = off;
     off = align_up(off + (uint64_t)p->hg_count * citems * sfag::kBk * kDacc * 4);
+    p->off_xpart = off;
+    off = align_up(off + (uint64_t)sfag::kv_shape((int)citems, p->hg_count).extra_slots() * sfag::kBk *
+                             sfag::kKvXCols * 4);
     p->off_flag = off;
     off = align_up(off + (uint64_t)p->hg_count * std::max<int64_t>(citems, 1) * 4);
     p->off_ilist = off;
@@ -530,6 +534,7 @@ sfag_status backward(const void* query, const void* key, const void* value, cons
     da.dsp = reinterpret_cast<uint16_t*>(ws + p.off_dsp);
     da.bt = reinterpret_cast<uint16_t*>(ws + p.off_bt);
     da.part = reinterpret_cast<float*>(ws + p.off_part);
+    da.xpart = reinterpret_cast<float*>(ws + p.off_xpart);
     da.flag = reinterpret_cast<int32_t*>(ws + p.off_flag);
     da.items = (int)p.items;
     da.citems = (int)p.citems;

@@ -211,12 +211,13 @@ __global__ void __launch_bounds__(1024) item_list_kernel(DenseArgs a) {
   }
 }
 
-// Workgroup = (live item, column slice, head group).  Workgroups are dealt to the 8 XCDs
-// round-robin (x = w % 8), so XCD x is given the contiguous run of live items
-// [x n, x n + n) and walks it as  half (dK slices, then dV slices) > item > slice: the
-// workgroups resident on one XCD are then neighbouring key blocks of one row segment x the 4
-// column slices of one half, which share the segment's Q / dO rows and dS / P records in
-// that XCD's L2.
+// Workgroup = (head group, live item, column slice), or a part of one (KvShape: the positions
+// of an XCD's last partial round are split over consecutive ranges of the item's rows).
+// Workgroups are dealt to the 8 XCDs round-robin (x = w % 8), so XCD x is given the contiguous
+// run of live items [x n, x n + n) and walks it as  head group > half (dK slices, then dV
+// slices) > item > slice: the workgroups resident on one XCD are then neighbouring key blocks of
+// one row segment x the 4 column slices of one half, which share the segment's Q / dO rows and
+// dS / P records in that XCD's L2.
 // Column slices 0..3: dK columns 144 s .. 144 s + 143 (the last one holds the rope columns);
 // 4..7: dV columns 128 (s - 4) .. + 127.  Wave w owns keys kb0 + 64 w .. + 63.
 //
@@ -250,14 +251,16 @@ struct KvCtx {
   bool isdk;
 };
 
-// Main loop of one workgroup with NFT column tiles (9: dK slice, 8: dV slice).  DUPS: some
-// row of the item repeats keys, so units are (row, layer) pairs; otherwise units are rows.
+// Main loop of one workgroup with NFT column tiles (9: dK slice, 8: dV slice) over the listed
+// rows ri_begin .. ri_end - 1 of the item.  DUPS: some row of the item repeats keys, so units are
+// (row, layer) pairs; otherwise units are rows.  The sums go to out[key][ocol + column] (row pitch
+// `pitch` floats), zeros for an empty range.
 template <int NFT, bool DUPS, bool F16>
-__device__ __forceinline__ void kv_dense_units(const DenseArgs& a, const KvCtx& x, uint16_t* Bt0, uint16_t* Bt1) {
+__device__ __forceinline__ void kv_dense_units(const DenseArgs& a, const KvCtx& x, uint16_t* Bt0, uint16_t* Bt1,
+                                               int ri_begin, int ri_end, float* out, int pitch, int ocol) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int g = lane >> 4, c = lane & 15;
-  const int nrows = x.nrows;
   const int16_t* s_row = x.s_row;
   const uint16_t* s_lay = x.s_lay;
   constexpr int kBLoads = (NFT * 128 + kThreads - 1) / kThreads;
@@ -324,7 +327,7 @@ __device__ __forceinline__ void kv_dense_units(const DenseArgs& a, const KvCtx& 
       ++ri;
     }
   };
-  int ri = 0, L = 0;
+  int ri = ri_begin, L = 0;
   i16x4 mc;                                          // map of the current unit's row
   constexpr int kBHalf = (kBLoads + 1) / 2;          // B loads staged in the first half-unit
   u32x4 bs[kBHalf];
@@ -349,8 +352,8 @@ __device__ __forceinline__ void kv_dense_units(const DenseArgs& a, const KvCtx& 
       f[kt][KS] = *reinterpret_cast<const bf16x8*>(src_);                                      \
     }                                                                                          \
   }
-  {
-    const int r0 = __builtin_amdgcn_readfirstlane((int)s_row[0]);
+  if (ri_begin < ri_end) {
+    const int r0 = __builtin_amdgcn_readfirstlane((int)s_row[ri_begin]);
     KV_MAP_LOAD(mc, r0)
     KV_B_LOAD(bs, r0, 0, kBHalf)
     KV_B_STORE(Bt0, bs, 0, kBHalf)
@@ -358,20 +361,19 @@ __device__ __forceinline__ void kv_dense_units(const DenseArgs& a, const KvCtx& 
     KV_B_STORE(Bt0, bs, kBHalf, kBLoads)
     KV_REC_LOAD(r0, 0, mc, 0)
     KV_REC_LOAD(r0, 0, mc, 1)
+    lds_barrier();
   }
-  lds_barrier();
 
   // Unit loop.  The MFMAs of a unit run head step by head step (all column tiles with the first
   // head step's A fragments, then all with the second), so that the registers of the first head
   // step are free halfway: the next unit's first-half records are requested there, its second
   // half at the end of the unit, each with the other half-unit (and the other workgroup) to land.
-  for (int u = 0; ri < nrows; ++u) {
+  for (int u = 0; ri < ri_end; ++u) {
     uint16_t* BC = (u & 1) ? Bt1 : Bt0;
     uint16_t* BN = (u & 1) ? Bt0 : Bt1;
     int ri2 = ri, L2 = L;
     advance(ri2, L2);
-    const bool more = ri2 < nrows;
-    const int rn = __builtin_amdgcn_readfirstlane((int)s_row[min(ri2, nrows - 1)]);
+    const int rn = __builtin_amdgcn_readfirstlane((int)s_row[min(ri2, ri_end - 1)]);
     i16x4 mn;
     KV_MAP_LOAD(mn, rn)
     KV_B_LOAD(bs, rn, 0, kBHalf)
@@ -420,7 +422,6 @@ __device__ __forceinline__ void kv_dense_units(const DenseArgs& a, const KvCtx& 
 #undef KV_MAP_LOAD
 
   const float mul = x.isdk ? a.scale : 1.f;
-  float* part = a.part + ((int64_t)x.hg * a.citems + x.citem) * (int64_t)kBk * kDacc;
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
@@ -428,7 +429,7 @@ __device__ __forceinline__ void kv_dense_units(const DenseArgs& a, const KvCtx& 
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int kk = 64 * wave + 16 * kt + 4 * g + v;
-        part[(int64_t)kk * kDacc + x.colbase + 16 * ft + c] = acc[kt][ft][v] * mul;
+        out[(int64_t)kk * pitch + ocol + 16 * ft + c] = acc[kt][ft][v] * mul;
       }
 }
 
@@ -442,14 +443,12 @@ __global__ void __launch_bounds__(kThreads, 2) kv_dense_kernel(DenseArgs a) {
   __shared__ uint16_t s_lay[kSegRows];     // their repeat layers (1 without repeated keys)
   __shared__ int32_t s_wcnt[4];
 
-  const int w = blockIdx.x;
-  const int xcd = w & 7, j = w >> 3;
-  const int per_xcd = (a.citems + 7) >> 3;
-  const int half = j / (4 * per_xcd), r = j - half * 4 * per_xcd;
-  const int citem = xcd * per_xcd + (r >> 2);
-  const int sl = 4 * half + (r & 3);
-  const int hg = blockIdx.y;
-  if (half >= 2 || citem >= a.citems) return;
+  const KvShape shp = kv_shape(a.citems, a.hgc);
+  const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+  if (j >= shp.wgs_per_xcd()) return;
+  const KvWork wk = kv_work(shp, xcd, j);
+  const int citem = wk.citem, sl = wk.sl, hg = wk.hg;
+  if (citem >= a.citems) return;
   const int item = a.ilist[citem];
   if (item < 0 || item >= a.items) return;     // host and device agree on the live count
   item_tables(a.lens, a.B, a.layout_tnd, a.S1, a.S2, cum, ibase);
@@ -519,12 +518,26 @@ __global__ void __launch_bounds__(kThreads, 2) kv_dense_kernel(DenseArgs a) {
   x.hg = hg;
   x.which = x.isdk ? 0 : kRecHalf;
   x.citem = citem;
-  if (x.isdk) {
-    if (dups) kv_dense_units<9, true, F16>(a, x, Bt0, Bt1);
-    else kv_dense_units<9, false, F16>(a, x, Bt0, Bt1);
+  // rows of this part: consecutive ranges of the listed rows, all of a row's repeat layers in one
+  const int ri0 = (int)((int64_t)nrows * wk.part / wk.nparts);
+  const int ri1 = (int)((int64_t)nrows * (wk.part + 1) / wk.nparts);
+  float* out;
+  int pitch, ocol;
+  if (wk.part == 0) {
+    out = a.part + ((int64_t)hg * a.citems + citem) * (int64_t)kBk * kDacc;
+    pitch = kDacc;
+    ocol = x.colbase;
   } else {
-    if (dups) kv_dense_units<8, true, F16>(a, x, Bt0, Bt1);
-    else kv_dense_units<8, false, F16>(a, x, Bt0, Bt1);
+    out = a.xpart + (int64_t)(wk.xslot + wk.part - 1) * kBk * kKvXCols;
+    pitch = kKvXCols;
+    ocol = 0;
+  }
+  if (x.isdk) {
+    if (dups) kv_dense_units<9, true, F16>(a, x, Bt0, Bt1, ri0, ri1, out, pitch, ocol);
+    else kv_dense_units<9, false, F16>(a, x, Bt0, Bt1, ri0, ri1, out, pitch, ocol);
+  } else {
+    if (dups) kv_dense_units<8, true, F16>(a, x, Bt0, Bt1, ri0, ri1, out, pitch, ocol);
+    else kv_dense_units<8, false, F16>(a, x, Bt0, Bt1, ri0, ri1, out, pitch, ocol);
   }
   if (threadIdx.x == 0) *flag = 1;
 }
@@ -538,6 +551,7 @@ __global__ void __launch_bounds__(kThreads) kv_reduce_kernel(DenseArgs a) {
   __shared__ int32_t ibase[257];
   __shared__ int32_t s_b;
   __shared__ int32_t fl[kMaxSegs];
+  __shared__ int32_t xs[kMaxSegs * 8];    // first extra slot of (head group, segment, slice), -1: none
   item_tables(a.lens, a.B, a.layout_tnd, a.S1, a.S2, cum, ibase);
   __syncthreads();
   const int64_t krow = blockIdx.x;
@@ -554,14 +568,20 @@ __global__ void __launch_bounds__(kThreads) kv_reduce_kernel(DenseArgs a) {
   const int nblk = (lkv + kBk - 1) / kBk;
   const int lb = j / kBk, kr = j % kBk;
   const bool live = j < lkv && lq > 0;
+  const KvShape shp = kv_shape(a.citems, a.hgc);
   if (live)
     for (int t = threadIdx.x; t < a.hgc * nseg; t += kThreads) {
       const int hg = t / nseg, seg = t % nseg;
       const int ci = a.imap[ibase[b] + seg * nblk + lb];
-      fl[t] = (ci >= 0 && a.flag[(int64_t)hg * a.citems + ci]) ? ci : -1;
+      const bool on = ci >= 0 && a.flag[(int64_t)hg * a.citems + ci];
+      fl[t] = on ? ci : -1;
+      for (int sl = 0; sl < 8; ++sl) xs[8 * t + sl] = on ? kv_xslot(shp, hg, ci, sl) : -1;
     }
   __syncthreads();
   for (int col = threadIdx.x; col < kDacc; col += kThreads) {
+    // slice holding this column and the column's offset in it
+    const int sl = col < kDk ? col / 144 : 4 + (col - kDk) / 128;
+    const int xcol = col < kDk ? col - 144 * sl : col - kDk - 128 * (sl - 4);
     float s = 0.f;
     if (live)
       for (int hg = 0; hg < a.hgc; ++hg)
@@ -569,6 +589,10 @@ __global__ void __launch_bounds__(kThreads) kv_reduce_kernel(DenseArgs a) {
           const int ci = fl[hg * nseg + seg];
           if (ci < 0) continue;
           s += a.part[(((int64_t)hg * a.citems + ci) * kBk + kr) * kDacc + col];
+          const int x0 = xs[8 * (hg * nseg + seg) + sl];
+          if (x0 >= 0)       // parts 1.. of a split position, in part order
+            for (int q = 0; q < shp.parts - 1; ++q)
+              s += a.xpart[((int64_t)(x0 + q) * kBk + kr) * kKvXCols + xcol];
         }
     const uint16_t v = f2x<F16>(s);
     if (col < kDn) a.dk[krow * kDn + col] = v;
@@ -593,11 +617,12 @@ hipError_t launch_item_list(const DenseArgs& a, hipStream_t st) {
 
 hipError_t launch_kv_dense(const DenseArgs& a, hipStream_t st) {
   if (a.citems == 0) return hipSuccess;
-  const unsigned per_xcd = (unsigned)((a.citems + 7) / 8);   // 8 XCDs x per_xcd items x 8 slices
+  const KvShape shp = kv_shape(a.citems, a.hgc);
+  const unsigned grid = 8u * (unsigned)shp.wgs_per_xcd();
   if (a.f16)
-    hipLaunchKernelGGL(kv_dense_kernel<true>, dim3(per_xcd * 64, (unsigned)a.hgc), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL(kv_dense_kernel<true>, dim3(grid), dim3(kThreads), 0, st, a);
   else
-    hipLaunchKernelGGL(kv_dense_kernel<false>, dim3(per_xcd * 64, (unsigned)a.hgc), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL(kv_dense_kernel<false>, dim3(grid), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 

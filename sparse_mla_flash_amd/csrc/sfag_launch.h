@@ -15,6 +15,88 @@ struct Lens {
 constexpr int kBk = 256;        // keys per block of the key-major dK / dV kernel
 constexpr int kSegRows = 512;   // query rows per segment of the key-major dK / dV kernel
 constexpr int kMaxSegs = 512;   // (head group, segment) pairs per batch the ordered reduce can hold
+// Launch shape of the key-major dK / dV kernel.  A position is (head group, live item, column
+// slice); workgroups are dealt round-robin to the 8 XCDs, and XCD x walks its run of per_xcd live
+// items as  head group > half (dK slices 0..3, then dV slices 4..7) > item > slice of the half,
+// n = hgc * per_xcd * 8 positions.  Two workgroups fit a CU, so an XCD runs 64 at a time; the
+// last rem = n % 64 positions would run as one partial round with most of the XCD idle, so each
+// of them is split into `parts` workgroups over consecutive ranges of the item's rows, with
+// `parts` chosen to minimise the time of that tail (ceil(rem parts / 64) rounds of 1 / parts of
+// a workgroup).  Part 0 of a split position writes the item's partial slot; parts 1.. write
+// extra slots [kBk keys][kKvXCols] that the reduce adds after it, in part order.  Host and device
+// derive the shape from (citems, hgc) alone, so the summation order depends on the shape only.
+constexpr int kKvSlotsPerXcd = 64;
+constexpr int kKvMaxParts = 4;
+constexpr int kKvXCols = 144;   // column pitch of an extra slot (the widest slice)
+
+struct KvShape {
+  int per_xcd;   // live items per XCD run
+  int n;         // positions per XCD
+  int j0;        // positions before the tail
+  int rem;       // tail positions
+  int parts;     // workgroups per tail position (1: no split)
+  __host__ __device__ int wgs_per_xcd() const { return j0 + rem * parts; }
+  __host__ __device__ int extra_slots() const { return 8 * rem * (parts - 1); }
+};
+
+__host__ __device__ inline KvShape kv_shape(int citems, int hgc) {
+  KvShape s;
+  s.per_xcd = (citems + 7) / 8;
+  s.n = hgc * s.per_xcd * 8;
+  s.rem = s.n % kKvSlotsPerXcd;
+  s.j0 = s.n - s.rem;
+  s.parts = 1;
+  int best_r = 1, best_p = 1;                      // unsplit: one round of whole workgroups
+  for (int P = 2; P <= kKvMaxParts && s.rem > 0; ++P) {
+    const int r = (s.rem * P + kKvSlotsPerXcd - 1) / kKvSlotsPerXcd;
+    if (r * best_p < best_r * P) {                 // r / P < best_r / best_p
+      best_r = r;
+      best_p = P;
+    }
+  }
+  s.parts = best_p;
+  return s;
+}
+
+// Work of the j-th workgroup of XCD xcd.  xslot: first extra slot of a split position (its part
+// p >= 1 writes slot xslot + p - 1), -1 when the position is not split.
+struct KvWork {
+  int hg, citem, sl, part, nparts, xslot;
+};
+
+__host__ __device__ inline KvWork kv_work(const KvShape& s, int xcd, int j) {
+  KvWork w;
+  int pos;
+  if (j < s.j0 || s.parts == 1) {
+    pos = j;
+    w.part = 0;
+    w.nparts = 1;
+    w.xslot = -1;
+  } else {
+    const int t = j - s.j0, q = t / s.parts;
+    pos = s.j0 + q;
+    w.part = t - q * s.parts;
+    w.nparts = s.parts;
+    w.xslot = (xcd * s.rem + q) * (s.parts - 1);
+  }
+  const int per_hg = s.per_xcd * 8;
+  w.hg = pos / per_hg;
+  const int r1 = pos - w.hg * per_hg;
+  const int half = r1 / (4 * s.per_xcd), r2 = r1 - half * 4 * s.per_xcd;
+  w.citem = xcd * s.per_xcd + (r2 >> 2);
+  w.sl = 4 * half + (r2 & 3);
+  return w;
+}
+
+// The reduce's side: first extra slot of (head group, live item, slice), -1 when not split.
+__host__ __device__ inline int kv_xslot(const KvShape& s, int hg, int citem, int sl) {
+  if (s.parts == 1) return -1;
+  const int xcd = citem / s.per_xcd, local = citem - xcd * s.per_xcd;
+  const int pos = hg * s.per_xcd * 8 + (sl >> 2) * 4 * s.per_xcd + 4 * local + (sl & 3);
+  if (pos < s.j0) return -1;
+  return (xcd * s.rem + (pos - s.j0)) * (s.parts - 1);
+}
+
 // dS | P records, per (row, head group) and chunk of 32 sorted positions:
 // [dS | P][head tile of 16][32 positions][16 heads] bf16
 constexpr int kRecChunk = 2 * 4 * 32 * 16;   // elements per chunk (8 KB)
@@ -64,6 +146,7 @@ struct DenseArgs {
   const uint16_t* dsp;    // [rows, hgc, rec_chunks, kRecChunk]
   const uint16_t* bt;     // [rows, hgc, 1088, 64] Q | QRope | dO with the 64 heads of a group innermost
   float* part;            // [hgc, citems, kBk, 1088]
+  float* xpart;           // [kv_shape().extra_slots(), kBk, kKvXCols] parts 1.. of split positions
   int32_t* flag;          // [hgc, citems]
   int32_t* ilist;         // [citems] live item -> item (key block x row segment)
   int32_t* imap;          // [items]  item -> live item, -1 when the causal mask rules it out

@@ -6,6 +6,9 @@
   "no device", so no call reaches a kernel.
 - The fp64 oracle is compiled with the sanitizers and run by tests/sanitize/oracle_driver.c;
   its checksums must equal those of a plain build (same arithmetic, any thread count).
+- The key-major launch shape (which workgroup computes which head group, live item, column
+  slice and row part; where the parts' sums go) is checked on the host by
+  tests/sanitize/kv_shape_check.cpp.
 """
 
 import os
@@ -92,3 +95,12 @@ def test_host_library_under_sanitizers(tmp_path):
     rc, out, err = _run([exe], str(tmp_path), env=env, timeout=300)
     assert rc == 0 and "runtime error" not in err and "AddressSanitizer" not in err, f"{out}\n{err}"
     assert "ok: 0 failed expectations" in out, out
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC), reason="ROCm compilers not available")
+def test_key_major_launch_shape(tmp_path):
+    exe = str(tmp_path / "kv_shape")
+    _checked([HIPCC, "-x", "hip", "--offload-arch=gfx950", "-O1", "-g", "-std=c++17", "-I", CSRC, *HOST_SAN,
+              os.path.join(SAN_DIR, "kv_shape_check.cpp"), "-o", exe], str(tmp_path))
+    rc, out, err = _run([exe], str(tmp_path), env=_env({**ENV_SAN, "ASAN_OPTIONS": "detect_leaks=0:halt_on_error=1"}))
+    assert rc == 0 and out.startswith("ok"), f"{out}\n{err}"
