@@ -573,28 +573,75 @@ __global__ void __launch_bounds__(kThreads) kv_reduce_kernel(DenseArgs a) {
     for (int t = threadIdx.x; t < a.hgc * nseg; t += kThreads) {
       const int hg = t / nseg, seg = t % nseg;
       const int ci = a.imap[ibase[b] + seg * nblk + lb];
-      const bool on = ci >= 0 && a.flag[(int64_t)hg * a.citems + ci];
-      fl[t] = on ? ci : -1;
-      for (int sl = 0; sl < 8; ++sl) xs[8 * t + sl] = on ? kv_xslot(shp, hg, ci, sl) : -1;
+      fl[t] = (ci >= 0 && a.flag[(int64_t)hg * a.citems + ci]) ? ci : -1;
     }
   __syncthreads();
-  for (int col = threadIdx.x; col < kDacc; col += kThreads) {
-    // slice holding this column and the column's offset in it
-    const int sl = col < kDk ? col / 144 : 4 + (col - kDk) / 128;
-    const int xcol = col < kDk ? col - 144 * sl : col - kDk - 128 * (sl - 4);
-    float s = 0.f;
-    if (live)
-      for (int hg = 0; hg < a.hgc; ++hg)
-        for (int seg = 0; seg < nseg; ++seg) {
-          const int ci = fl[hg * nseg + seg];
-          if (ci < 0) continue;
-          s += a.part[(((int64_t)hg * a.citems + ci) * kBk + kr) * kDacc + col];
-          const int x0 = xs[8 * (hg * nseg + seg) + sl];
-          if (x0 >= 0)       // parts 1.. of a split position, in part order
-            for (int q = 0; q < shp.parts - 1; ++q)
-              s += a.xpart[((int64_t)(x0 + q) * kBk + kr) * kKvXCols + xcol];
+  if (live && shp.parts > 1)
+    for (int i = threadIdx.x; i < a.hgc * nseg * 8; i += kThreads) {
+      const int t = i >> 3, ci = fl[t];
+      xs[i] = ci >= 0 ? kv_xslot(shp, t / nseg, ci, i & 7) : -1;
+    }
+  __syncthreads();
+  // bit 30 of fl: some slice of this (head group, segment) is split (few are: only an XCD's tail)
+  if (live && shp.parts > 1)
+    for (int t = threadIdx.x; t < a.hgc * nseg; t += kThreads) {
+      bool any = false;
+      for (int sl = 0; sl < 8; ++sl) any = any || xs[8 * t + sl] >= 0;
+      if (any) fl[t] |= 1 << 30;
+    }
+  __syncthreads();
+  // each thread sums the columns threadIdx.x + 256 i (i < 5; the last only for the first 64
+  // threads) over the (head group, segment) entries t = hg * nseg + seg in order, a split
+  // position's parts after its first; the partials of 4 entries x all of the thread's columns are
+  // requested together, then added in entry order
+  constexpr int kCols = (kDacc + kThreads - 1) / kThreads;
+  int sl[kCols], xcol[kCols];
+#pragma unroll
+  for (int i = 0; i < kCols; ++i) {
+    const int col = threadIdx.x + kThreads * i;
+    sl[i] = col < kDk ? col / 144 : 4 + (col - kDk) / 128;       // slice holding the column
+    xcol[i] = col < kDk ? col - 144 * sl[i] : col - kDk - 128 * (sl[i] - 4);
+  }
+  float s[kCols];
+#pragma unroll
+  for (int i = 0; i < kCols; ++i) s[i] = 0.f;
+  if (live) {
+    const int nt = a.hgc * nseg;
+    for (int t0 = 0; t0 < nt; t0 += 4) {
+      int e[4];
+      float v[kCols][4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) e[u] = t0 + u < nt ? fl[t0 + u] : -1;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float* pr = a.part + (((int64_t)((t0 + u) / nseg) * a.citems + (e[u] & 0x3fffffff)) * kBk + kr) * kDacc;
+#pragma unroll
+        for (int i = 0; i < kCols; ++i) {
+          const int col = threadIdx.x + kThreads * i;
+          v[i][u] = (e[u] >= 0 && col < kDacc) ? pr[col] : 0.f;
         }
-    const uint16_t v = f2x<F16>(s);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (e[u] < 0) continue;
+#pragma unroll
+        for (int i = 0; i < kCols; ++i) {
+          s[i] += v[i][u];
+          if (e[u] & (1 << 30)) {
+            const int x0 = xs[8 * (t0 + u) + sl[i]];
+            if (x0 >= 0 && threadIdx.x + kThreads * i < kDacc)   // parts 1.., in part order
+              for (int q = 0; q < shp.parts - 1; ++q)
+                s[i] += a.xpart[((int64_t)(x0 + q) * kBk + kr) * kKvXCols + xcol[i]];
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kCols; ++i) {
+    const int col = threadIdx.x + kThreads * i;
+    if (col >= kDacc) continue;
+    const uint16_t v = f2x<F16>(s[i]);
     if (col < kDn) a.dk[krow * kDn + col] = v;
     else if (col < kDk) {
       if (a.dkr) a.dkr[krow * kDr + col - kDn] = v;
