@@ -52,6 +52,10 @@ static_assert(kLdsTotal <= 160 * 1024, "LDS budget");
 // newest gather) and vmcnt(10) (all but a gather and one position load)
 constexpr int kWaitVm9 = 0x0009;
 constexpr int kWaitVm10 = 0x000a;
+// rounds of the heads-innermost copy (17 blocks of 64 columns, up to 8 per round), two
+// barriers each
+constexpr int kCopyRounds = (kDacc / 64 + 7) / 8;
+static_assert(8 * 64 * 72 * 2 <= 2 * kLdsK, "a copy round's tiles fit key buffers 2 and 3");
 }  // namespace
 
 template <bool F16>
@@ -90,41 +94,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
   const int32_t* srow = a.sorted + row * a.topk;
   const int nchunk = (count + kKC - 1) / kKC;
 
-  // ---- per-row setup --------------------------------------------------------------------------
-  // D = rowsum(dO * out) and the statistics of every head (8 threads per head, 64 dims each)
-  {
-    const int h = threadIdx.x >> 3, part = threadIdx.x & 7;
-    float d = 0.f;
-    if (h < nh) {
-      const uint16_t* dor = a.dout + (row * a.N1 + h0 + h) * kDn + part * 64;
-      const uint16_t* otr = a.out + (row * a.N1 + h0 + h) * kDn + part * 64;
-#pragma unroll
-      for (int e = 0; e < 64; e += 8) {
-        const u32x4 x = *reinterpret_cast<const u32x4*>(dor + e);
-        const u32x4 y = *reinterpret_cast<const u32x4*>(otr + e);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          d += x2f<F16>((uint16_t)(x[w] & 0xffffu)) * x2f<F16>((uint16_t)(y[w] & 0xffffu));
-          d += x2f<F16>((uint16_t)(x[w] >> 16)) * x2f<F16>((uint16_t)(y[w] >> 16));
-        }
-      }
-    }
-    d += __shfl_xor(d, 1);
-    d += __shfl_xor(d, 2);
-    d += __shfl_xor(d, 4);
-    if (part == 0) {
-      float m = 0.f, il = 0.f;
-      if (h < nh) {
-        const int64_t st = stat_index(a.layout_tnd, geo, row, a.N1, a.S1, h0 + h);
-        const float l = a.ssum[st];
-        m = a.smax[st];
-        il = l > 0.f ? 1.f / l : 0.f;
-      }
-      sD[h] = d;
-      sM[h] = m * kLog2e;
-      sIL[h] = il;
-    }
-  }
+  // ---- per-row setup: D and the statistics are formed by the score waves (below) --------------
   const float zscale = a.scale * kLog2e;
   // Loop-invariant bases, held in SGPRs: the empty asm makes them opaque, so the compiler
   // cannot re-load them from the kernel arguments inside the loop (a scalar load in flight
@@ -316,34 +286,71 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
         qA[16 + ks] = bf16x8{};
         if (hv && a.qr) qA[16 + ks] = *reinterpret_cast<const bf16x8*>(a.qr + hrow * kDr + 32 * ks + 8 * g);
       }
+      // D = rowsum(dO * out) of this lane's head: its dO fragments times the same elements of
+      // out, summed over the 4 lanes (g) that hold the head; then the head's statistics
+      const uint16_t* orow = a.out + hrow * kDn + 8 * g;
+      float d = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) {
+        const u32x4 y = *reinterpret_cast<const u32x4*>(orow + 32 * ks);
+        const u32x4 x = __builtin_bit_cast(u32x4, doA[ks]);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          d += x2f<F16>((uint16_t)(x[w] & 0xffffu)) * x2f<F16>((uint16_t)(y[w] & 0xffffu));
+          d += x2f<F16>((uint16_t)(x[w] >> 16)) * x2f<F16>((uint16_t)(y[w] >> 16));
+        }
+      }
+      d += __shfl_xor(d, 16);
+      d += __shfl_xor(d, 32);
+      if (g == 0) {
+        float m = 0.f, il = 0.f;
+        if (hv) {
+          const int64_t st = stat_index(a.layout_tnd, geo, row, a.N1, a.S1, h0 + h);
+          const float l = a.ssum[st];
+          m = a.smax[st];
+          il = l > 0.f ? 1.f / l : 0.f;
+        }
+        sD[h] = d;                                    // padded heads: 0 (their dO is zero)
+        sM[h] = m * kLog2e;
+        sIL[h] = il;
+      }
     }
     // The row's Q | QRope | dO with the 64 heads innermost (bt[row][hg][col][h]), the key-major
-    // kernel's B operand, written from the fragments already in registers.  Per 64-column block
-    // (two steps of every score wave) the [64 heads][64 cols] tile goes through LDS (pitch 72,
-    // key buffers 2 and 3 in turn, unused until the loop) and comes back by transposing reads:
-    // lane (g, c) of score wave w stores heads 32 s + 8 g .. + 7 of column 64 k + 16 w + c.  The
-    // dQ waves pass the same number of barriers meanwhile.  These stores drain during the loop.
+    // kernel's B operand, written from the fragments already in registers.  The 17 blocks of 64
+    // columns go in rounds of up to 8: each block's [64 heads][64 cols] tile goes through LDS
+    // (pitch 72; key buffers 2 and 3, unused until the loop, hold four tiles each) and comes back
+    // by transposing reads: lane (g, c) of score wave w stores heads 32 s + 8 g .. + 7 of column
+    // 64 k + 16 w + c.  Two barriers per round; the dQ waves pass as many meanwhile.  These
+    // stores drain during the loop.
     {
       uint16_t* bto = a.bt + (lrow * a.hgc + hg) * (int64_t)kDacc * 64;
       const int hrow = 16 * rw + c;
 #pragma unroll
-      for (int k = 0; k < kDacc / 64; ++k) {
-        uint16_t* t = (k & 1) ? Kb3 : Kb2;
+      for (int r = 0; r < kCopyRounds; ++r) {
+        const int kb = 8 * r, kn = min(8, kDacc / 64 - kb);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int ks = 2 * k + j;                       // 32-column step over Q | QRope | dO
-          const bf16x8 v = ks < 18 ? qA[ks] : doA[ks - 18];
-          *reinterpret_cast<bf16x8*>(t + hrow * 72 + 32 * j + 8 * g) = v;
+        for (int i = 0; i < kn; ++i) {
+          uint16_t* t = (i < 4 ? Kb2 : Kb3) + (i & 3) * (64 * 72);
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int ks = 2 * (kb + i) + j;                // 32-column step over Q | QRope | dO
+            const bf16x8 v = ks < 18 ? qA[ks] : doA[ks - 18];
+            *reinterpret_cast<bf16x8*>(t + hrow * 72 + 32 * j + 8 * g) = v;
+          }
         }
         lds_barrier();
 #pragma unroll
-        for (int sh = 0; sh < 2; ++sh) {
-          const bf16x8 v = lds_frag_trp(t, 32 * sh, 16 * rw, 72, lane);
-          *reinterpret_cast<bf16x8*>(bto + (64 * k + 16 * rw + c) * 64 + 32 * sh + 8 * g) = v;
+        for (int i = 0; i < kn; ++i) {
+          const uint16_t* t = (i < 4 ? Kb2 : Kb3) + (i & 3) * (64 * 72);
+#pragma unroll
+          for (int sh = 0; sh < 2; ++sh) {
+            const bf16x8 v = lds_frag_trp(t, 32 * sh, 16 * rw, 72, lane);
+            *reinterpret_cast<bf16x8*>(bto + (64 * (kb + i) + 16 * rw + c) * 64 + 32 * sh + 8 * g) = v;
+          }
         }
+        lds_barrier();
       }
     }
-    lds_barrier();
     f32x4 sacc[2], pacc[2];
     const int kse = ktile_off(g, c);                // chunk g of key c
 // Score step CI on key buffer KC and dS buffer DC; ends by waiting for this wave's LDS accesses
@@ -383,7 +390,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
     gsv = srow[min(kKC + gkey, count - 1)];
     SFAG_GATHER_ASYNC(Kb1, 1, gsv)
     gsv = srow[min(2 * kKC + gkey, count - 1)];
-    for (int k = 0; k < kDacc / 64; ++k) lds_barrier();   // the score waves' copy of Q | QRope | dO
+    for (int k = 0; k < 2 * kCopyRounds - 1; ++k) lds_barrier();   // the score waves' copy of Q | QRope | dO
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(kWaitVm10);
     __builtin_amdgcn_s_barrier();
