@@ -53,14 +53,15 @@ __device__ __forceinline__ float wsum16(float v) {  // sum over the 16 lanes c o
 // ------------------------------------------------------------------------------------------
 template <bool F16>
 __global__ void __launch_bounds__(kIxThreads, 1) ix_query_kernel(IxArgs a) {
-  // three chunk buffers (separate arrays, so that the compiler can tell a direct-to-LDS load
-  // into one from reads of the others): main key rows (9 chunk groups) and index key rows (2
-  // chunk groups), both in the swizzled [chunk group][key][slot] layout of sfag_ktile.h
+  // chunk buffers: three for the main key rows (9 chunk groups; separate arrays, so that the
+  // compiler can tell a direct-to-LDS load into one from reads of the others) and four for the
+  // index key rows (2 chunk groups; read one step longer), both in the swizzled [chunk
+  // group][key][slot] layout of sfag_ktile.h
   __shared__ __attribute__((aligned(16))) uint16_t Kt0[kIxKC * kDk], Kt1[kIxKC * kDk], Kt2[kIxKC * kDk];
-  __shared__ __attribute__((aligned(16))) uint16_t Ki0[kIxKC * kIxDi], Ki1[kIxKC * kIxDi], Ki2[kIxKC * kIxDi];
+  __shared__ __attribute__((aligned(16))) uint16_t Kib[4][kIxKC * kIxDi];   // index rows, chunk c in Kib[c % 4]
   __shared__ __attribute__((aligned(16))) uint16_t Dt[4][2][16 * kDsPitch];   // per index wave: dS', T
-  __shared__ float sP[4][kIxKC];                 // per main wave: softmax summed over its heads
-  __shared__ float sI[4][kIxKC];                 // per index wave: its part of I
+  __shared__ float sP[2][4][kIxKC];              // chunk c % 2, per main wave: softmax summed over its heads
+  __shared__ float sI[2][4][kIxKC];              // chunk c % 2, per index wave: its part of I
   __shared__ float sM[128], sIL[128];            // main statistics (log2 domain), 1 / sum
   __shared__ float sRed[4];
   __shared__ int32_t cum[2 * 257];
@@ -151,10 +152,11 @@ __global__ void __launch_bounds__(kIxThreads, 1) ix_query_kernel(IxArgs a) {
   constexpr int kWaitMain = 0x000b;
 
   // Two roles with separate loops (their registers are never live together) and the same
-  // barriers: one before step 0, two per step.  Step c: main waves form the scores of chunk c;
-  // index waves add dq~ of chunk c - 1 and form the index scores of chunk c; barrier A; every
-  // wave gathers its part of chunk c + 2 into the buffer chunk c - 1 used (the index waves
-  // first form the gradient terms of chunk c); wait for chunk c + 1; barrier B.
+  // barriers: one before step 0, one per step.  Step c: the main waves gather chunk c + 2 into
+  // the buffers chunk c - 1 (main rows) and c - 2 (index rows) used, form the scores of chunk c
+  // and its head-summed softmax, and wait for chunk c + 1; meanwhile the index waves form the
+  // gradient terms of chunk c - 1 (from the head sums and partial I of the previous step), add
+  // dq~ of chunk c - 1, and form the index scores of chunk c.
   if (wave < 4) {
     // A operands: Q of head 16 t + c (dims 32 ks + 8 g; steps 16, 17: rope), for t = w, w + 4
     bf16x8 qA[2][18];
@@ -176,15 +178,17 @@ __global__ void __launch_bounds__(kIxThreads, 1) ix_query_kernel(IxArgs a) {
                         : bf16x8{};
     }
     IX_GATHER_MAIN(Kt0, 0)
-    IX_GATHER_INDEX(Ki0, 0)
+    IX_GATHER_INDEX(Kib[0], 0)
     IX_GATHER_MAIN(Kt1, 1)
-    IX_GATHER_INDEX(Ki1, 1)
+    IX_GATHER_INDEX(Kib[1], 1)
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(kWaitMain);
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-#define IX_MSTEP(CI, KC, KN, KIN)                                                              \
+#define IX_MSTEP(CI, KC, KN)                                                                   \
   {                                                                                            \
+    IX_GATHER_MAIN(KN, min((CI) + 2, nchunk - 1))                                              \
+    IX_GATHER_INDEX(Kib[((CI) + 2) & 3], min((CI) + 2, nchunk - 1))                            \
     if ((CI) < nchunk) {                                                                       \
       float ps[2] = {0.f, 0.f};                                                                \
       _Pragma("unroll") for (int u = 0; u < 2; ++u) {                                          \
@@ -202,12 +206,9 @@ __global__ void __launch_bounds__(kIxThreads, 1) ix_query_kernel(IxArgs a) {
       }                                                                                        \
       _Pragma("unroll") for (int kt = 0; kt < 2; ++kt) {                                       \
         const float p_ = col4_sum(ps[kt]);                                                     \
-        if (g == 0) sP[wave][16 * kt + c] = (CI) * kIxKC + 16 * kt + c < nkeys ? p_ : 0.f;     \
+        if (g == 0) sP[(CI) & 1][wave][16 * kt + c] = (CI) * kIxKC + 16 * kt + c < nkeys ? p_ : 0.f; \
       }                                                                                        \
     }                                                                                          \
-    lds_barrier();                                                                             \
-    IX_GATHER_MAIN(KN, min((CI) + 2, nchunk - 1))                                              \
-    IX_GATHER_INDEX(KIN, min((CI) + 2, nchunk - 1))                                            \
     asm volatile("" ::: "memory");                                                             \
     __builtin_amdgcn_s_waitcnt(kWaitMain);                                                     \
     __builtin_amdgcn_s_barrier();                                                              \
@@ -215,15 +216,15 @@ __global__ void __launch_bounds__(kIxThreads, 1) ix_query_kernel(IxArgs a) {
   }
     int ci = 0;
     for (; ci + 3 <= nchunk + 1; ci += 3) {
-      IX_MSTEP(ci, Kt0, Kt2, Ki2)
-      IX_MSTEP(ci + 1, Kt1, Kt0, Ki0)
-      IX_MSTEP(ci + 2, Kt2, Kt1, Ki1)
+      IX_MSTEP(ci, Kt0, Kt2)
+      IX_MSTEP(ci + 1, Kt1, Kt0)
+      IX_MSTEP(ci + 2, Kt2, Kt1)
     }
     if (ci <= nchunk) {
-      IX_MSTEP(ci, Kt0, Kt2, Ki2)
+      IX_MSTEP(ci, Kt0, Kt2)
       ++ci;
     }
-    if (ci <= nchunk) IX_MSTEP(ci, Kt1, Kt0, Ki0)
+    if (ci <= nchunk) IX_MSTEP(ci, Kt1, Kt0)
 #undef IX_MSTEP
     __builtin_amdgcn_s_waitcnt(0);                // no gather may still write LDS at exit
     __syncthreads();                              // the index waves' row results
@@ -259,94 +260,74 @@ __global__ void __launch_bounds__(kIxThreads, 1) ix_query_kernel(IxArgs a) {
   for (int nt = 0; nt < 8; ++nt) qacc[nt] = tacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float aw[4] = {0.f, 0.f, 0.f, 0.f}, bw[4] = {0.f, 0.f, 0.f, 0.f};
   float l1 = 0.f, nrm = 0.f;
-  // head sums of the previous chunk, stored at the start of the next step so that the stores
-  // are older than that step's gather (stores count in vmcnt too)
-  float tot_prev[2] = {0.f, 0.f};
-  int key_prev = -1;
+  f32x4 iprev[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};   // S of the previous chunk
 
   // chunks 0 and 1 are gathered by the main waves
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
-#define IX_ISTEP(CI, KC, KP)                                                                   \
-  {                                                                                            \
-    if (it == 0 && g == 0 && key_prev >= 0) {                                                  \
-      float* tp_ = a.tot + row * a.kstride + key_prev;                                         \
-      if (key_prev + c < nkeys) tp_[c] = tot_prev[0];                                          \
-      if (key_prev + 16 + c < nkeys) tp_[16 + c] = tot_prev[1];                                \
-    }                                                                                          \
-    key_prev = -1;                                                                             \
-    /* dq~ += dS' K~ and the correction term T K~ of chunk CI - 1 */                            \
-    if (hasi && (CI) >= 1) {                                                                   \
-      const bf16x8 da = *reinterpret_cast<const bf16x8*>(&Dt[it][0][c * kDsPitch + 8 * g]);    \
-      const bf16x8 ta = *reinterpret_cast<const bf16x8*>(&Dt[it][1][c * kDsPitch + 8 * g]);    \
-      _Pragma("unroll") for (int nt = 0; nt < 8; ++nt) {                                       \
-        const bf16x8 kb_ = tr_frag((KP) + ((kq0 ^ (16 * (nt & 3))) + 2048 * (nt >> 2)), 1024);   \
-        qacc[nt] = mfma_t<F16>(da, kb_, qacc[nt]);                                             \
-        tacc[nt] = mfma_t<F16>(ta, kb_, tacc[nt]);                                             \
-      }                                                                                        \
-    }                                                                                          \
-    f32x4 iacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};                    \
-    if (hasi && (CI) < nchunk) {                                                               \
-      _Pragma("unroll") for (int ks = 0; ks < 4; ++ks)                                         \
-        _Pragma("unroll") for (int kt = 0; kt < 2; ++kt)                                       \
-          iacc[kt] = mfma_t<F16>(qiA[ks], IX_KFRAG(KC, ks, kt), iacc[kt]);                     \
-      _Pragma("unroll") for (int kt = 0; kt < 2; ++kt) {                                       \
-        float is = 0.f;                                                                        \
-        _Pragma("unroll") for (int v = 0; v < 4; ++v) is += wv[v] * fmaxf(iacc[kt][v], 0.f);   \
-        is = col4_sum(is);                                                                     \
-        if (g == 0) sI[it][16 * kt + c] = is;                                                  \
-      }                                                                                        \
-    }                                                                                          \
-    lds_barrier();                                                                             \
-    /* gradient terms of chunk CI */                                                           \
-    if (hasi && (CI) < nchunk) {                                                               \
-      const int s0 = (CI) * kIxKC;                                                             \
-      _Pragma("unroll") for (int kt = 0; kt < 2; ++kt) {                                       \
-        const int key = 16 * kt + c;                                                           \
-        const int kpos = 8 * (c >> 2) + (c & 3) + 4 * kt;   /* key's place in the dq~ key order */ \
-        const bool valid = s0 + key < nkeys;                                                   \
-        const float tot = valid ? sP[0][key] + sP[1][key] + sP[2][key] + sP[3][key] : 0.f;     \
-        float ival = 0.f;                                                                      \
-        for (int u = 0; u < nit; ++u) ival += sI[u][key];                                      \
-        const float lsm = ival - max_i - lsum_i;   /* log Softmax(I) */                        \
-        const float sm = valid ? __expf(lsm) : 0.f;                                            \
-        const float dip = sm - tot * inv_heads;    /* dI with the provisional norm */          \
-        _Pragma("unroll") for (int v = 0; v < 4; ++v) {                                        \
-          const float sv_ = iacc[kt][v];                                                       \
-          const float relu = fmaxf(sv_, 0.f);                                                  \
-          aw[v] += dip * relu;                                                                 \
-          bw[v] += tot * relu;                                                                 \
-          Dt[it][0][(4 * g + v) * kDsPitch + kpos] = f2x<F16>(sv_ > 0.f ? dip : 0.f);           \
-          Dt[it][1][(4 * g + v) * kDsPitch + kpos] = f2x<F16>(sv_ > 0.f ? tot : 0.f);           \
-        }                                                                                      \
-        if (it == 0 && g == 0 && valid) {                                                      \
-          if (tot > 0.f) l1 += tot * (__logf(tot) - lsm);                                      \
-          nrm += tot;                                                                          \
-        }                                                                                      \
-        tot_prev[kt] = tot;                                                                    \
-      }                                                                                        \
-      key_prev = s0;                                                                           \
-    }                                                                                          \
-    /* chunk CI + 2 goes into KP, gathered by the main waves */                                 \
-    asm volatile("" ::: "memory");                                                             \
-    __builtin_amdgcn_s_barrier();                                                              \
-    asm volatile("" ::: "memory");                                                             \
-  }
-  {
-    int ci = 0;
-    for (; ci + 3 <= nchunk + 1; ci += 3) {
-      IX_ISTEP(ci, Ki0, Ki2)
-      IX_ISTEP(ci + 1, Ki1, Ki0)
-      IX_ISTEP(ci + 2, Ki2, Ki1)
+  for (int ci = 0; ci <= nchunk; ++ci) {
+    if (hasi && ci >= 1) {
+      // gradient terms of chunk ci - 1: head sums (main waves) and partial I (index waves) of
+      // the previous step
+      const int s0 = (ci - 1) * kIxKC, pb = (ci - 1) & 1;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const int key = 16 * kt + c;
+        const int kpos = 8 * (c >> 2) + (c & 3) + 4 * kt;     // key's place in the dq~ key order
+        const bool valid = s0 + key < nkeys;
+        const float tot = valid ? sP[pb][0][key] + sP[pb][1][key] + sP[pb][2][key] + sP[pb][3][key] : 0.f;
+        float ival = 0.f;
+        for (int u = 0; u < nit; ++u) ival += sI[pb][u][key];
+        const float lsm = ival - max_i - lsum_i;             // log Softmax(I)
+        const float sm = valid ? __expf(lsm) : 0.f;
+        const float dip = sm - tot * inv_heads;              // dI with the provisional norm
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float sv_ = iprev[kt][v];
+          const float relu = fmaxf(sv_, 0.f);
+          aw[v] += dip * relu;
+          bw[v] += tot * relu;
+          Dt[it][0][(4 * g + v) * kDsPitch + kpos] = f2x<F16>(sv_ > 0.f ? dip : 0.f);
+          Dt[it][1][(4 * g + v) * kDsPitch + kpos] = f2x<F16>(sv_ > 0.f ? tot : 0.f);
+        }
+        if (it == 0 && g == 0 && valid) {
+          if (tot > 0.f) l1 += tot * (__logf(tot) - lsm);
+          nrm += tot;
+          a.tot[row * a.kstride + s0 + key] = tot;           // the head sum, for the key kernel
+        }
+      }
+      // dq~ += dS' K~ and the correction term T K~ of chunk ci - 1 (this wave's own tiles)
+      const uint16_t* KP = Kib[(ci + 3) & 3];
+      const bf16x8 da = *reinterpret_cast<const bf16x8*>(&Dt[it][0][c * kDsPitch + 8 * g]);
+      const bf16x8 ta = *reinterpret_cast<const bf16x8*>(&Dt[it][1][c * kDsPitch + 8 * g]);
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) {
+        const bf16x8 kb_ = tr_frag(KP + ((kq0 ^ (16 * (nt & 3))) + 2048 * (nt >> 2)), 1024);
+        qacc[nt] = mfma_t<F16>(da, kb_, qacc[nt]);
+        tacc[nt] = mfma_t<F16>(ta, kb_, tacc[nt]);
+      }
     }
-    if (ci <= nchunk) {
-      IX_ISTEP(ci, Ki0, Ki2)
-      ++ci;
+    if (hasi && ci < nchunk) {
+      // index scores of chunk ci and this wave's part of I
+      const uint16_t* KC = Kib[ci & 3];
+      f32x4 iacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) iacc[kt] = mfma_t<F16>(qiA[ks], IX_KFRAG(KC, ks, kt), iacc[kt]);
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        float is = 0.f;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) is += wv[v] * fmaxf(iacc[kt][v], 0.f);
+        is = col4_sum(is);
+        if (g == 0) sI[ci & 1][it][16 * kt + c] = is;
+        iprev[kt] = iacc[kt];
+      }
     }
-    if (ci <= nchunk) IX_ISTEP(ci, Ki1, Ki0)
+    lds_barrier();
   }
-#undef IX_ISTEP
 #undef IX_GATHER_MAIN
 #undef IX_GATHER_INDEX
 #undef IX_KFRAG
