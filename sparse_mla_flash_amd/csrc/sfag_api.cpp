@@ -39,9 +39,11 @@ constexpr int64_t kMaxSeq = 131072;           // S1, S2 up to 128K
 constexpr int64_t kMaxTopk = 131072;
 constexpr int kDacc = 1088;                   // fp32 accumulator row: dK 512 | dKRope 64 | dV 512
 constexpr uint64_t kAlign = 256;
-// per-chunk budget of the per-pair path's fp32 partials; the row chunk it implies depends only
-// on the shape, so the summation order (and the result) is fixed for a given shape
-constexpr uint64_t kPartialBudget = 8ull << 30;
+// per-chunk budget of the per-pair path's fp32 partials (a sixth of an MI355X's 288 GB: every
+// chunk re-reads and re-writes the fp32 accumulator rows of the keys it reaches, so fewer, larger
+// chunks move less).  Each key's sum runs over its pairs in row order whatever the chunking, so
+// the result does not depend on the budget.
+constexpr uint64_t kPartialBudget = 48ull << 30;
 
 uint64_t align_up(uint64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
