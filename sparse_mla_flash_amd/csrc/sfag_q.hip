@@ -30,6 +30,7 @@
 // [chunk group][key][slot] layout of sfag_ktile.h: each direct-to-LDS load reads eight whole
 // 128-byte runs of key rows, and a gathering lane always handles the same key.
 #include "sfag_device.h"
+#include "sfag_dpp.h"
 #include "sfag_ktile.h"
 #include "sfag_launch.h"
 
@@ -465,10 +466,15 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
         const int64_t hh2 = row * a.N1 + h0 + h;
 #pragma unroll
         for (int nt = 0; nt < 9; ++nt) {
+          // lanes c and c ^ 1 hold neighbouring dims: the even lane stores both as one word
+          const float x = dqacc[t][nt][v] * a.scale;
+          const float y = dpp_f<kDppXor1>(x);
           const int col = 16 * (rw + 4 * nt) + c;
-          const uint16_t bv = f2x<F16>(dqacc[t][nt][v] * a.scale);
-          if (col < kDn) a.dq[hh2 * kDn + col] = bv;
-          else if (a.dqr) a.dqr[hh2 * kDr + col - kDn] = bv;
+          if ((c & 1) == 0) {
+            const uint32_t pv = pack_x2<F16>(x, y);
+            if (col < kDn) *reinterpret_cast<uint32_t*>(a.dq + hh2 * kDn + col) = pv;
+            else if (a.dqr) *reinterpret_cast<uint32_t*>(a.dqr + hh2 * kDr + col - kDn) = pv;
+          }
         }
       }
     }
