@@ -19,7 +19,9 @@
  * Conventions shared by every entry point
  *   - All tensors are dense, row-major, contiguous.  Pointers named *_host are
  *     host memory read during the call only; every other pointer is device
- *     memory owned by the caller.  The library allocates no device memory and
+ *     memory owned by the caller.  Device pointers of the sparse operator's
+ *     tensors, and of the indexer's query / key / index rows and dQueryIndex,
+ *     must be 16-byte aligned (SFAG_ERR_PARAM_INVALID otherwise).  The library allocates no device memory and
  *     keeps no pointer after a call returns; the one exception is the fixed
  *     scratch array of the no-allocation entry point (SFAG_NOALLOC_SCRATCH_BYTES
  *     per GPU, created with the library's code on that device).

@@ -775,13 +775,13 @@ sfag_status sfag_dense_lightning_indexer_grad_kl_loss(
   (void)pre_tokens;
   (void)next_tokens;
   sfag_status st;
-  // 16-byte rows are read as whole pieces: these need 16-byte alignment; the others are read
-  // element by element
+  // 16-byte rows are read as whole pieces and dq~ is written in 4-byte pairs: these need 16-byte
+  // alignment; the others are accessed element by element
   const struct { const void* p; const char* n; bool al; } req[] = {
       {query, "query", true}, {key, "key", true}, {query_index, "query_index", true},
       {key_index, "key_index", true}, {weights, "weights", false}, {softmax_max, "softmax_max", false},
       {softmax_sum, "softmax_sum", false}, {softmax_max_index, "softmax_max_index", false},
-      {softmax_sum_index, "softmax_sum_index", false}, {d_query_index, "d_query_index", false},
+      {softmax_sum_index, "softmax_sum_index", false}, {d_query_index, "d_query_index", true},
       {d_key_index, "d_key_index", false}, {d_weights, "d_weights", false}, {loss, "loss", false}};
   for (const auto& r : req) {
     if (!r.p) return fail(SFAG_ERR_PARAM_NULLPTR, "%s is NULL", r.n);

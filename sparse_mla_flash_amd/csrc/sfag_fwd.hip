@@ -384,8 +384,13 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_kernel(FwdArgs a) {
         const int h = 16 * t + 4 * g + v;
         if (h >= nh) continue;
         uint16_t* orow = a.out + (row * a.N1 + h0 + h) * kDn + 128 * rw + c;
+        // lanes c and c ^ 1 hold neighbouring dims: the even lane stores both as one word
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt) orow[16 * nt] = f2x<F16>(oacc[t][nt][v] * il[v]);
+        for (int nt = 0; nt < 8; ++nt) {
+          const float x = oacc[t][nt][v] * il[v];
+          const float y = dpp_f<kDppXor1>(x);
+          if ((c & 1) == 0) *reinterpret_cast<uint32_t*>(orow + 16 * nt) = pack_x2<F16>(x, y);
+        }
       }
     }
   }

@@ -356,13 +356,16 @@ __global__ void __launch_bounds__(kIxThreads, 1) ix_query_kernel(IxArgs a) {
       const int hh = 16 * it + 4 * g + v;
       if (c == 0 && hh < G) a.dw[row * G + hh] = f2x<F16>(d);
     }
+    // lanes c and c ^ 1 hold neighbouring dims: the even lane stores both as one word
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int hh = 16 * it + 4 * g + v;
-        if (hh < G)
-          a.dqi[(row * G + hh) * kIxDi + 16 * nt + c] = f2x<F16>(wv[v] * (qacc[nt][v] + corr * tacc[nt][v]));
+        const float x = wv[v] * (qacc[nt][v] + corr * tacc[nt][v]);
+        const float y = dpp_f<kDppXor1>(x);
+        if (hh < G && (c & 1) == 0)
+          *reinterpret_cast<uint32_t*>(a.dqi + (row * G + hh) * kIxDi + 16 * nt + c) = pack_x2<F16>(x, y);
       }
   }
 }
