@@ -268,52 +268,39 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
     // Q and dO fragments straight from global memory (A operands of S and dP: lane (g, c) holds
     // head 16 rw + c, dims 32 ks + 8 g .. + 7; steps 16 and 17 are the rope dims); zero for
     // padded heads
+    // requested in the order they are used: Q | QRope and dO (the copy below), then out and the
+    // statistics (D, formed after the copy)
     bf16x8 qA[18], doA[16];
+    u32x4 oy[16];
+    float smv = 0.f, ssv = 0.f;
+    const int h = 16 * rw + c;
+    const bool hv = h < nh;
     {
-      const int h = 16 * rw + c;
-      const bool hv = h < nh;
       const int64_t hrow = row * a.N1 + h0 + (hv ? h : 0);
       const uint16_t* qrow = a.q + hrow * kDn + 8 * g;
       const uint16_t* drow = a.dout + hrow * kDn + 8 * g;
+      const uint16_t* orow = a.out + hrow * kDn + 8 * g;
 #pragma unroll
       for (int ks = 0; ks < 16; ++ks) {
         const bf16x8 qv = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
-        const bf16x8 dv = *reinterpret_cast<const bf16x8*>(drow + 32 * ks);
         qA[ks] = hv ? qv : bf16x8{};
-        doA[ks] = hv ? dv : bf16x8{};
       }
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         qA[16 + ks] = bf16x8{};
         if (hv && a.qr) qA[16 + ks] = *reinterpret_cast<const bf16x8*>(a.qr + hrow * kDr + 32 * ks + 8 * g);
       }
-      // D = rowsum(dO * out) of this lane's head: its dO fragments times the same elements of
-      // out, summed over the 4 lanes (g) that hold the head; then the head's statistics
-      const uint16_t* orow = a.out + hrow * kDn + 8 * g;
-      float d = 0.f;
 #pragma unroll
       for (int ks = 0; ks < 16; ++ks) {
-        const u32x4 y = *reinterpret_cast<const u32x4*>(orow + 32 * ks);
-        const u32x4 x = __builtin_bit_cast(u32x4, doA[ks]);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          d += x2f<F16>((uint16_t)(x[w] & 0xffffu)) * x2f<F16>((uint16_t)(y[w] & 0xffffu));
-          d += x2f<F16>((uint16_t)(x[w] >> 16)) * x2f<F16>((uint16_t)(y[w] >> 16));
-        }
+        const bf16x8 dv = *reinterpret_cast<const bf16x8*>(drow + 32 * ks);
+        doA[ks] = hv ? dv : bf16x8{};
       }
-      d += __shfl_xor(d, 16);
-      d += __shfl_xor(d, 32);
-      if (g == 0) {
-        float m = 0.f, il = 0.f;
-        if (hv) {
-          const int64_t st = stat_index(a.layout_tnd, geo, row, a.N1, a.S1, h0 + h);
-          const float l = a.ssum[st];
-          m = a.smax[st];
-          il = l > 0.f ? 1.f / l : 0.f;
-        }
-        sD[h] = d;                                    // padded heads: 0 (their dO is zero)
-        sM[h] = m * kLog2e;
-        sIL[h] = il;
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) oy[ks] = *reinterpret_cast<const u32x4*>(orow + 32 * ks);
+      if (hv && g == 0) {
+        const int64_t st = stat_index(a.layout_tnd, geo, row, a.N1, a.S1, h0 + h);
+        smv = a.smax[st];
+        ssv = a.ssum[st];
       }
     }
     // The row's Q | QRope | dO with the 64 heads innermost (bt[row][hg][col][h]), the key-major
@@ -350,6 +337,28 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_q_kernel(BwdArgs a) {
           }
         }
         lds_barrier();
+      }
+    }
+    {
+      // D = rowsum(dO * out) of this lane's head: its dO fragments times the same elements of
+      // out, summed over the 4 lanes (g) that hold the head; then the head's statistics
+      float d = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) {
+        const u32x4 y = oy[ks];
+        const u32x4 x = __builtin_bit_cast(u32x4, doA[ks]);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          d += x2f<F16>((uint16_t)(x[w] & 0xffffu)) * x2f<F16>((uint16_t)(y[w] & 0xffffu));
+          d += x2f<F16>((uint16_t)(x[w] >> 16)) * x2f<F16>((uint16_t)(y[w] >> 16));
+        }
+      }
+      d += __shfl_xor(d, 16);
+      d += __shfl_xor(d, 32);
+      if (g == 0) {
+        sD[h] = d;                                    // padded heads: 0 (their dO is zero)
+        sM[h] = smv * kLog2e;
+        sIL[h] = ssv > 0.f ? 1.f / ssv : 0.f;
       }
     }
     f32x4 sacc[2], pacc[2];
