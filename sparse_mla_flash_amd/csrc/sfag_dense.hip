@@ -383,6 +383,11 @@ __device__ __forceinline__ void kv_dense_units(const DenseArgs& a, const KvCtx& 
     bf16x8 bq[NFT];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
+      // a wave in its MFMA phase outranks the other workgroup's wave on the SIMD, so that a
+      // head step's MFMAs issue back to back and the other wave's record loads and B-tile
+      // stores (at priority 0) fill the gaps
+      __builtin_amdgcn_s_setprio(1);
+      __builtin_amdgcn_sched_barrier(0);
       bq[0] = KV_BFRAG(BC, ks);
       bq[1] = KV_BFRAG(BC, 2 + ks);
       bq[2] = KV_BFRAG(BC, 4 + ks);
@@ -402,6 +407,7 @@ __device__ __forceinline__ void kv_dense_units(const DenseArgs& a, const KvCtx& 
       // this head step's fragments are consumed: request the next unit's; the next unit's B tile
       // goes to LDS in two halves, the second loaded while the second head step runs
       __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(0);
       KV_REC_LOAD(rn, L2, mn, ks)      /* past the last unit: the last row again, unused */
       if (ks == 0) {
         KV_B_STORE(BN, bs, 0, kBHalf)
@@ -410,6 +416,8 @@ __device__ __forceinline__ void kv_dense_units(const DenseArgs& a, const KvCtx& 
       __builtin_amdgcn_sched_barrier(0);
     }
     KV_B_STORE(BN, bs, kBHalf, kBLoads)
+    // the next unit's map and B-tile loads, issued right after the barrier, go first as well
+    __builtin_amdgcn_s_setprio(1);
     lds_barrier();
     mc = mn;
     ri = ri2;
