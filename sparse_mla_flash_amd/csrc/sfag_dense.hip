@@ -48,17 +48,21 @@ __device__ __forceinline__ void item_tables(const Lens& L, int B, int tnd, int64
 
 // ------------------------------------------------------------------------------------------
 // Counting sort of one row's valid key positions.  The valid keys lie in [0, hi], which the
-// map covers in full blocks; the range is walked in windows of kSortWin keys.  Per window:
-// 16-bit occurrence counts in LDS (two per word, LDS atomics), then each thread takes 64
+// map covers in full blocks; the range is walked in windows of KPT * 256 keys.  Per window:
+// 16-bit occurrence counts in LDS (two per word, LDS atomics), then each thread takes KPT
 // consecutive keys, and a block-wide exclusive scan of the threads' totals gives every key's
 // first sorted position.  From that one pass come the sorted list (each key written as often as
 // it occurs), the key -> first-position map (-1: not selected), the block starts (the position
 // of the first key >= 256 lb) and the largest multiplicity.  Slots past the count hold kNoKey.
-constexpr int kSortWin = 64 * kThreads;           // 16384 keys per window
-constexpr int kSortWords = kSortWin / 2;
-
+// Each thread replaces its counts in LDS by its keys' map entries, 8 keys per step, and the
+// whole window's map then leaves LDS in the permuted layout as 16-byte stores.  KPT = 32 (a
+// 16 KB count window, twice the workgroups per CU) serves calls whose rows all fit one window.
+template <int KPT>
 __global__ void __launch_bounds__(kThreads) sort_rows_kernel(DenseArgs a) {
-  __shared__ __attribute__((aligned(16))) uint32_t cw[kSortWords];   // 16-bit counts, 32 KB
+  constexpr int kWin = KPT * kThreads;                // keys per window
+  constexpr int kWords = kWin / 2;
+  constexpr int kTw = KPT / 2;                        // count words per thread
+  __shared__ __attribute__((aligned(16))) uint32_t cw[kWords];   // 16-bit counts, then map entries
   __shared__ int32_t cum[2 * 257];
   __shared__ int32_t s_wsum[kThreads / 64], s_base, s_dup;
   if (a.layout_tnd) {
@@ -83,9 +87,10 @@ __global__ void __launch_bounds__(kThreads) sort_rows_kernel(DenseArgs a) {
     s_dup = 1;
   }
   int dup = 1;
-  for (int w0 = 0; w0 < map_end; w0 += kSortWin) {
-    const int w1 = min(map_end, w0 + kSortWin);
-    for (int k = t; k < kSortWords; k += kThreads) cw[k] = 0u;
+  for (int w0 = 0; w0 < map_end; w0 += kWin) {
+    const int w1 = min(map_end, w0 + kWin);
+    const int nw = (w1 - w0) / 2;                     // count words in use (a multiple of 128)
+    for (int k = t; k < nw; k += kThreads) cw[k] = 0u;
     __syncthreads();
     for (int i = t; i < a.topk; i += kThreads) {
       const int j = slot_key(irow, i, a.bs);
@@ -95,14 +100,19 @@ __global__ void __launch_bounds__(kThreads) sort_rows_kernel(DenseArgs a) {
       }
     }
     __syncthreads();
-    // this thread's 64 keys: w0 + 64 t .. + 63 (32 count words)
-    const uint32_t* mine = &cw[32 * t];
+    // this thread's KPT keys: w0 + KPT t .. + KPT - 1; w1 - w0 is a multiple of 256, so they are
+    // all inside or all outside the window
+    const int k0 = w0 + KPT * t;
+    const bool mine_in = k0 < w1;
+    uint32_t* mine = &cw[kTw * t];
     int tsum = 0;
+    if (mine_in) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(mine + 4 * q);
-      tsum += (int)((v.x & 0xffffu) + (v.x >> 16) + (v.y & 0xffffu) + (v.y >> 16) + (v.z & 0xffffu) + (v.z >> 16) +
-                    (v.w & 0xffffu) + (v.w >> 16));
+      for (int q = 0; q < kTw / 4; ++q) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(mine + 4 * q);
+        tsum += (int)((v.x & 0xffffu) + (v.x >> 16) + (v.y & 0xffffu) + (v.y >> 16) + (v.z & 0xffffu) +
+                      (v.z >> 16) + (v.w & 0xffffu) + (v.w >> 16));
+      }
     }
     // block-wide exclusive scan of tsum
     int incl = tsum;
@@ -115,36 +125,47 @@ __global__ void __launch_bounds__(kThreads) sort_rows_kernel(DenseArgs a) {
     __syncthreads();
     int pos = s_base + incl - tsum;
     for (int v = 0; v < wave; ++v) pos += s_wsum[v];
-    const int k0 = w0 + 64 * t;
-    // w1 - w0 is a multiple of 256, so a thread's 64 keys are all inside or all outside
-    if (k0 < w1) {
+    if (mine_in) {
       if ((k0 & (kBk - 1)) == 0) orow[k0 / kBk] = pos;                   // block start
-      short mv[64];                                                       // map of keys k0 + i
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {                                       // 8 keys per step
+#pragma unroll 1
+      for (int q = 0; q < kTw / 4; ++q) {                                 // 8 keys per step
         const u32x4 v = *reinterpret_cast<const u32x4*>(mine + 4 * q);
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        uint32_t m[4];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int n = (int)((w[e >> 1] >> (16 * (e & 1))) & 0xffffu);
-          mv[8 * q + e] = n > 0 ? (short)pos : (short)-1;
-          for (int r = 0; r < n; ++r) srow[pos + r] = k0 + 8 * q + e;
-          pos += n;
-          dup = max(dup, n);
+        for (int h = 0; h < 4; ++h) {
+          uint32_t packed = 0u;
+#pragma unroll
+          for (int e2 = 0; e2 < 2; ++e2) {
+            const int n = (int)((w[h] >> (16 * e2)) & 0xffffu);
+            const int key = k0 + 8 * q + 2 * h + e2;
+            // map entry: the first position as 16 bits, 0xffff (-1) when not selected
+            packed |= (n > 0 ? ((uint32_t)pos & 0xffffu) : 0xffffu) << (16 * e2);
+            if (n > 0) srow[pos] = key;
+            if (n > 1)
+              for (int r = 1; r < n; ++r) srow[pos + r] = key;          // a repeated key
+            pos += n;
+            dup = max(dup, n);
+          }
+          m[h] = packed;
         }
-      }
-      // stored permuted inside the 64-key group: key 16 kt + c at 4 c + kt
-      if (keep_map) {
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          i16x8 m;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) m[e] = mv[16 * (e & 3) + 2 * q + (e >> 2)];
-          *reinterpret_cast<i16x8*>(kp + k0 + 8 * q) = m;
-        }
+        *reinterpret_cast<u32x4*>(mine + 4 * q) = u32x4{m[0], m[1], m[2], m[3]};
       }
     }
     __syncthreads();
+    // the window's map, stored permuted inside each 64-key group: key 16 kt + c at 4 c + kt, so
+    // that 8-entry chunk q of a group holds keys 16 (e % 4) + 2 q + e / 4, e = 0..7
+    if (keep_map) {
+      const uint16_t* m16 = reinterpret_cast<const uint16_t*>(cw);
+      for (int ch = t; ch < (w1 - w0) / 8; ch += kThreads) {
+        const int grp = ch >> 3, q = ch & 7;
+        const uint16_t* g16 = m16 + 64 * grp;
+        i16x8 m;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m[e] = (short)g16[16 * (e & 3) + 2 * q + (e >> 2)];
+        *reinterpret_cast<i16x8*>(kp + w0 + 8 * ch) = m;
+      }
+    }
     if (t == kThreads - 1) s_base = pos;                                // total so far
     __syncthreads();
   }
@@ -660,7 +681,11 @@ __global__ void __launch_bounds__(kThreads) kv_reduce_kernel(DenseArgs a) {
 
 // ------------------------------------------------------------------------------------------
 hipError_t launch_sort_rows(const DenseArgs& a, int64_t rows, hipStream_t st) {
-  hipLaunchKernelGGL(sort_rows_kernel, dim3((unsigned)rows), dim3(kThreads), 0, st, a);
+  // every row's keys fit one 8192-key window: the half-size window (twice the workgroups per CU)
+  if ((int64_t)a.maxblk * kBk <= 32 * kThreads)
+    hipLaunchKernelGGL(sort_rows_kernel<32>, dim3((unsigned)rows), dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL(sort_rows_kernel<64>, dim3((unsigned)rows), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
