@@ -303,20 +303,6 @@ sfag_status check_ptr(const void* ptr, const char* name) {
   return SFAG_OK;
 }
 
-std::once_flag g_attr_once;
-hipError_t g_attr_err = hipSuccess;
-
-sfag_status init_device() {
-  std::call_once(g_attr_once, [] {
-    g_attr_err = sfag::set_fwd_attributes();
-    if (g_attr_err == hipSuccess) g_attr_err = sfag::set_dense_attributes();
-    if (g_attr_err == hipSuccess) g_attr_err = sfag::set_q_attributes();
-  });
-  if (g_attr_err != hipSuccess)
-    return fail(SFAG_ERR_DEVICE, "kernel attribute setup failed: %s", hipGetErrorString(g_attr_err));
-  return SFAG_OK;
-}
-
 #define SFAG_HIP(call)                                                                    \
   do {                                                                                    \
     hipError_t e_ = (call);                                                               \
@@ -466,7 +452,6 @@ sfag_status backward(const void* query, const void* key, const void* value, cons
                 (unsigned long long)workspace_size, workspace ? "" : " (NULL)");
   if (reinterpret_cast<uintptr_t>(workspace) % kAlign)
     return fail(SFAG_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-  if ((st = init_device()) != SFAG_OK) return st;
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   unsigned char* ws = static_cast<unsigned char*>(workspace);
@@ -727,7 +712,6 @@ sfag_status sfag_sparse_flash_attention_forward(const void* query, const void* k
   st = make_plan(dims, seq_len_q_host, seq_len_kv_host, scale_value, sparse_block_size, layout, sparse_mode, 0,
                  false, &p);
   if (st != SFAG_OK) return st;
-  if ((st = init_device()) != SFAG_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   sfag::FwdArgs a{};
   a.q = static_cast<const uint16_t*>(query);
@@ -801,7 +785,6 @@ sfag_status sfag_dense_lightning_indexer_grad_kl_loss(
                 (unsigned long long)workspace_size, workspace ? "" : " (NULL)");
   if (reinterpret_cast<uintptr_t>(workspace) % kAlign)
     return fail(SFAG_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-  if ((st = init_device()) != SFAG_OK) return st;
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   sfag::IxArgs a{};
   a.q = static_cast<const uint16_t*>(query);

@@ -714,6 +714,5 @@ hipError_t launch_kv_reduce(const DenseArgs& a, int64_t keys, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t set_dense_attributes() { return hipSuccess; }
 
 }  // namespace sfag

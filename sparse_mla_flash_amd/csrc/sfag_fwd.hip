@@ -404,6 +404,5 @@ hipError_t launch_fwd(const FwdArgs& a, int64_t nrows, int hg_count, hipStream_t
   return hipGetLastError();
 }
 
-hipError_t set_fwd_attributes() { return hipSuccess; }
 
 }  // namespace sfag

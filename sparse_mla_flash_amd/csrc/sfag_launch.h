@@ -246,13 +246,10 @@ __host__ __device__ inline int64_t stat_index(int tnd, const Geo& g, int64_t row
 hipError_t launch_fwd(const FwdArgs& a, int64_t nrows, int hg_count, hipStream_t st);
 hipError_t launch_bwd_q(const BwdArgs& a, int64_t nrows, int hg_count, hipStream_t st);
 hipError_t launch_pair_chunk(const PairArgs& a, hipStream_t st);
-hipError_t set_q_attributes();
 hipError_t launch_sort_rows(const DenseArgs& a, int64_t rows, hipStream_t st);
 hipError_t launch_item_list(const DenseArgs& a, hipStream_t st);
 hipError_t launch_kv_dense(const DenseArgs& a, hipStream_t st);
 hipError_t launch_kv_reduce(const DenseArgs& a, int64_t keys, hipStream_t st);
-hipError_t set_dense_attributes();
-hipError_t set_fwd_attributes();
 hipError_t launch_indexer(const IxArgs& a, int64_t key_tiles, hipStream_t st);
 
 }  // namespace sfag

@@ -504,6 +504,5 @@ hipError_t launch_bwd_q(const BwdArgs& a, int64_t nrows, int hg_count, hipStream
   return hipGetLastError();
 }
 
-hipError_t set_q_attributes() { return hipSuccess; }
 
 }  // namespace sfag
