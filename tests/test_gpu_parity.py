@@ -41,6 +41,10 @@ CASES = {
     "tnd_b256_n2_varlen": (dict(layout="TND", B=256, seq_q=[(7 * b) % 5 for b in range(256)],
                                 seq_kv=[1 + (11 * b) % 23 for b in range(256)], N1=2, topk=8, sparse_mode=3),
                            "uniform", 14),
+    # the index sort's 16384-key windows (rows reaching past 8192 keys): one window, then two
+    "bsnd_n8_sort_window_9k": (dict(layout="BSND", B=1, S1=12, S2=9000, N1=8, topk=200, sparse_mode=3), "uniform", 15),
+    "bsnd_n8_sort_windows_20k": (dict(layout="BSND", B=1, S1=12, S2=20000, N1=8, topk=300, sparse_mode=3),
+                                 "uniform", 16),
 }
 
 
